@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against values fixed outside it: published test vectors,
+textbook tables, closed forms, invariants and brute force on small inputs."""
+import math
+
+import numpy as np
+import pytest
+from scipy import special, stats
+
+import oracle
+from oracle import attention, codebook, quantize, rng, rotation
+from tq_synth import random_unit_vectors
+
+D = 128
+
+
+# ---------------------------------------------------------------- generator --
+
+def test_splitmix64_published_vectors(golden):
+    for row in golden("splitmix64_vectors.txt"):
+        seed, outs = int(row[0]), [int(x) for x in row[1:]]
+        got = [int(v) for v in rng.splitmix64(seed, len(outs))]
+        assert got == outs
+
+
+def test_uniforms_open_interval_and_top_bits():
+    z = rng.splitmix64(7, 1000)
+    u = rng.uniforms(7, 1000)
+    assert np.all(u > 0) and np.all(u <= 1)
+    # u is the top 53 bits of each output plus one half, scaled by 2**-53
+    k = (z >> np.uint64(11))
+    small = k < np.uint64(1 << 52)
+    assert np.array_equal(u[small] * 2.0**53 - 0.5, k[small].astype(np.float64))
+    assert np.all(np.abs(u * 2.0**53 - k.astype(np.float64)) <= 1.0)
+
+
+def test_box_muller_is_standard_normal():
+    x = rng.normals(123, 400_000)
+    assert abs(x.mean()) < 4 / math.sqrt(len(x))
+    assert abs(x.var() - 1) < 4 * math.sqrt(2 / len(x))
+    assert stats.kstest(x, "norm").pvalue > 1e-3
+    # pairs: z0^2 + z1^2 = -2 ln u1 (the radius of the pair)
+    u = rng.uniforms(123, 4)
+    assert np.allclose(x[0] ** 2 + x[1] ** 2, -2 * np.log(u[0]), rtol=1e-12)
+
+
+# ----------------------------------------------------------------- rotation --
+
+def test_rotation_orthogonal_fp32():
+    P = rotation.haar_rotation(42, D)
+    assert np.abs(P.T @ P - np.eye(D)).max() <= 1e-5
+    assert np.abs(P @ P.T - np.eye(D)).max() <= 1e-5
+
+
+def test_rotation_is_q_of_seeded_gaussian_with_positive_r_diagonal():
+    G = rotation.gaussian_matrix(42, D)
+    P = rotation.haar_rotation_f64(42, D)
+    R = P.T @ G
+    assert np.abs(np.tril(R, -1)).max() < 1e-10
+    assert np.all(np.diag(R) > 0)
+
+
+def test_rotation_deterministic_and_seed_dependent():
+    a = rotation.haar_rotation(42, D).astype(np.float32).tobytes()
+    b = rotation.haar_rotation(42, D).astype(np.float32).tobytes()
+    c = rotation.haar_rotation(43, D).astype(np.float32).tobytes()
+    assert a == b and a != c
+
+
+def test_rotation_entries_mean_zero_variance_one_over_d():
+    P = rotation.haar_rotation(42, D)
+    e = P.ravel()
+    n = e.size
+    assert abs(e.mean()) < 4 * math.sqrt(1 / D / n)
+    # rows are unit vectors, so the mean square is exactly 1/d
+    assert abs(np.mean(e * e) - 1 / D) < 1e-9
+    # entries of a Haar matrix are close to N(0, 1/d): chi-square of the normalised entries
+    z = e * math.sqrt(D)
+    counts, edges = np.histogram(z, bins=np.linspace(-3, 3, 13))
+    expected = n * np.diff(stats.norm.cdf(edges))
+    chi2 = np.sum((counts - expected) ** 2 / expected)
+    assert chi2 < stats.chi2.ppf(0.999, len(counts) - 1)
+
+
+def test_haar_first_column_uniform_on_sphere():
+    # Pi e1 over many seeds: each coordinate has variance 1/d and Pi e1 . e1 has
+    # mean 0 (a sign bias would show if the sign fix were missing or wrong).
+    vals = np.array([rotation.haar_rotation_f64(s, 16)[:, 0] for s in range(1500)])
+    assert abs(vals[:, 0].mean()) < 4 * math.sqrt(1 / 16 / 1500)
+    assert abs(np.mean(vals ** 2) - 1 / 16) < 0.01 / 16 * 4
+
+
+def test_qjl_projection_gaussian():
+    S = rotation.qjl_projection(4242, D)
+    assert stats.kstest(S.ravel(), "norm").pvalue > 1e-3
+    assert np.array_equal(S, rotation.gaussian_matrix(4242, D).astype(np.float32).astype(np.float64))
+
+
+# ----------------------------------------------------------------- codebook --
+
+def _max_table(golden):
+    tab = {}
+    for row in golden("lloyd_max_gaussian_max1960.txt"):
+        tab[(int(row[0]), row[1])] = [float(x) for x in row[2:]]
+    return tab
+
+
+def test_one_bit_closed_form():
+    c, _, _ = codebook.lloyd_max_gaussian(1)
+    assert np.allclose(c, [-math.sqrt(2 / math.pi), math.sqrt(2 / math.pi)], atol=1e-13)
+    assert abs(codebook.mse_fixed_point(c) - (1 - 2 / math.pi)) < 1e-13
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_lloyd_max_matches_max_1960(golden, bits):
+    tab = _max_table(golden)
+    L = 1 << bits
+    c, _, _ = codebook.lloyd_max_gaussian(bits)
+    pos = c[L // 2:]
+    assert np.allclose(pos, tab[(L, "output")], atol=1.1e-3)
+    mse = codebook.mse_fixed_point(c)
+    assert abs(mse - tab[(L, "mse")][0]) / mse < 1e-3
+    if (L, "threshold") in tab:
+        _, t = codebook.canonical(bits)
+        assert np.allclose(t[len(t) // 2:], tab[(L, "threshold")], atol=1.1e-3)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_lloyd_fixed_point_symmetric(bits):
+    c, it, delta = codebook.lloyd_max_gaussian(bits)
+    assert delta < 1e-14
+    assert codebook.lloyd_residual(c) < 1e-12
+    assert np.array_equal(c, -c[::-1])
+    assert np.all(np.diff(c) > 0)
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_canonical_codebook_fp16_exact_midpoints(bits):
+    c16, t = codebook.canonical(bits)
+    assert np.array_equal(c16.astype(np.float16).astype(np.float64), c16)
+    assert np.array_equal(t.astype(np.float32).astype(np.float64), t)
+    mid = (c16[:-1] + c16[1:]) / 2
+    assert np.array_equal(t, mid)
+    assert t[len(t) // 2] == 0.0 and not np.signbit(t[len(t) // 2])
+    c, _, _ = codebook.lloyd_max_gaussian(bits)
+    assert np.abs(c16 - c).max() <= np.abs(c).max() * 2.0**-11
+    # rounding barely moves the MSE
+    assert abs(codebook.expected_sq_error(c16, t) - codebook.mse_fixed_point(c)) < 1e-6
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_expected_sq_error_matches_monte_carlo(bits):
+    c16, t = codebook.canonical(bits)
+    x = np.random.default_rng(5).standard_normal(2_000_000)
+    idx = np.searchsorted(t, x, side="right")
+    err = (x - c16[idx]) ** 2
+    closed = codebook.expected_sq_error(c16, t)
+    assert abs(err.mean() - closed) < 4 * err.std() / math.sqrt(len(x))
+
+
+# ----------------------------------------------------------------- quantize --
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_threshold_rule_is_nearest_centroid(bits):
+    c16, t = codebook.canonical(bits)
+    u = np.random.default_rng(bits).standard_normal((1000, D)) / math.sqrt(D)
+    codes = quantize.codes_from_unit(u, t, D)
+    cu = c16 / math.sqrt(D)
+    nearest = np.argmin(np.abs(u[..., None] - cu), axis=-1)
+    assert np.array_equal(codes, nearest)
+
+
+def test_threshold_rule_ties_and_zero():
+    c16, t = codebook.canonical(3)
+    s = math.sqrt(D)
+    u = np.array([[t[0] / s, t[3] / s, -0.0, 0.0, np.nextafter(t[3] / s, -1)] + [0.0] * (D - 5)])
+    codes = quantize.codes_from_unit(u, t, D)[0]
+    assert list(codes[:5]) == [1, 4, 4, 4, 3]
+    q = quantize.quantize_head(np.zeros((2, D)), np.eye(D), c16, t)
+    assert np.all(q["codes"] == 4) and np.all(q["norm"] == 0)
+
+
+@pytest.mark.parametrize("bits,cos_lo,cos_hi,mse_rel", [
+    (2, 0.9395, 0.9420, 0.03), (3, 0.9822, 0.9840, 0.03), (4, 0.9948, 0.9960, 0.04)])
+def test_cosine_on_random_unit_vectors(bits, cos_lo, cos_hi, mse_rel):
+    """Haar-rotated unit vectors at d=128: coordinate MSE close to the Gaussian
+    Lloyd-Max value (sphere coordinates are slightly lighter-tailed) and the
+    reconstruction cosine per bit width."""
+    c16, t = codebook.canonical(bits)
+    P = rotation.haar_rotation(42, D)
+    X = random_unit_vectors(4000, D, 11 + bits)
+    q = quantize.quantize_head(X, P, c16, t)
+    xh = attention.dequantize_head(q["codes"], q["norm"], P, c16, D)
+    cos = attention.cosine(X, xh).mean()
+    assert cos_lo < cos < cos_hi
+    mse = np.mean((q["u"] * math.sqrt(D) - c16[q["codes"]]) ** 2)
+    assert abs(mse - codebook.expected_sq_error(c16, t)) / mse < mse_rel
+
+
+def test_two_bit_cosine_matches_page_value(golden):
+    page = {(r[0], int(r[1])): float(r[2]) for r in golden("page_claims.txt")}
+    c16, t = codebook.canonical(2)
+    P = rotation.haar_rotation(42, D)
+    X = random_unit_vectors(4000, D, 77)
+    q = quantize.quantize_head(X, P, c16, t)
+    cos = attention.cosine(X, attention.dequantize_head(q["codes"], q["norm"], P, c16, D)).mean()
+    assert abs(cos - page[("value_cosine", 2)]) < 0.005
+
+
+# ------------------------------------------------------------------ packing --
+
+def _expand(words):
+    if words[-1].startswith("x"):
+        return [int(w, 16) for w in words[:-1]] * int(words[-1][1:])
+    return [int(w, 16) for w in words]
+
+
+def test_packing_worked_words(golden):
+    j = np.arange(D)
+    for row in golden("packing_worked_words.txt"):
+        layout, bits, pattern, words = row[0], int(row[1]), row[2], _expand(row[3:])
+        if layout == "key":
+            codes = {"j_mod_8": j % 8, "all_4": np.full(D, 4), "j_mod_4": j % 4, "j_mod_16": j % 16}[pattern]
+            got = quantize.pack_keys(codes[None, :], bits)[0]
+        else:
+            tok = np.arange(8)
+            codes = {"token_index": tok, "token_index_mod_4": tok % 4}[pattern]
+            got = quantize.pack_values(np.repeat(codes[:, None], D, axis=1), bits)[0]
+        assert [int(w) for w in got] == words, (layout, bits, pattern)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_pack_roundtrip(bits):
+    g = np.random.default_rng(bits)
+    codes = g.integers(0, 1 << bits, size=(64, D))
+    assert np.array_equal(quantize.unpack_keys(quantize.pack_keys(codes, bits), bits, D), codes)
+    assert np.array_equal(quantize.unpack_values(quantize.pack_values(codes, bits), bits, D), codes)
+    # both layouts spend d*bits/8 bytes per token
+    assert quantize.pack_keys(codes, bits).nbytes == quantize.pack_values(codes, bits).nbytes == 64 * D * bits // 8
+
+
+def test_value_layout_single_bit_positions():
+    # token 8*blk + i, coordinate j, bits b  ->  block stream bit b*(8j+i)
+    bits = 3
+    codes = np.zeros((16, D), dtype=np.int64)
+    codes[8 + 5, 77] = 1
+    w = quantize.pack_values(codes, bits)
+    pos = bits * (8 * 77 + 5)
+    expect = np.zeros_like(w)
+    expect[1, pos // 32] = 1 << (pos % 32)
+    assert np.array_equal(w, expect)
+
+
+# ---------------------------------------------------------------------- QJL --
+
+def test_qjl_estimator_unbiased_with_closed_form_variance():
+    """Over random Gaussian projections S, sqrt(pi/2)/d * |r| * (S y) . sign(S r)
+    has mean y . r and variance (pi/2 |r|^2 |y|^2 - (y . r)^2) / d."""
+    g = np.random.default_rng(9)
+    y = g.standard_normal(D)
+    r = 0.3 * g.standard_normal(D) / math.sqrt(D)
+    M = 10000
+    est = np.empty(M)
+    for c in range(0, M, 500):
+        S = g.standard_normal((500, D, D))
+        Sy = S @ y
+        sg = np.where(S @ r >= 0, 1.0, -1.0)
+        est[c:c + 500] = math.sqrt(math.pi / 2) / D * np.linalg.norm(r) * np.sum(Sy * sg, axis=1)
+    mean_true = y @ r
+    var_true = (math.pi / 2 * (r @ r) * (y @ y) - mean_true ** 2) / D
+    assert abs(est.mean() - mean_true) < 4 * math.sqrt(var_true / M)
+    assert abs(est.var() / var_true - 1) < 0.06
+
+
+def test_oracle_qjl_score_matches_estimator_definition():
+    """The oracle's rotated-domain QJL score term equals the estimator written
+    against the unrotated query (y = Pi q, residual r)."""
+    c16, t = codebook.canonical(2)
+    P = rotation.haar_rotation(42, D)
+    S = rotation.qjl_projection(4242, D)
+    g = np.random.default_rng(3)
+    X = g.standard_normal((50, D))
+    q = g.standard_normal((3, D))
+    k = quantize.quantize_head(X, P, c16, t, S=S)
+    s = attention.rotated_scores(q, k["codes"], k["norm"], P, c16, D, 1.0, k["signs"], k["gamma"], S)
+    y = q @ P.T
+    mse_part = y @ (c16[k["codes"]] / math.sqrt(D)).T
+    sg = np.where(k["z"] >= 0, 1.0, -1.0)
+    qjl_part = (y @ S.T) @ sg.T * (k["gamma"].astype(np.float64) * math.sqrt(math.pi / 2) / D)
+    assert np.allclose(s, (mse_part + qjl_part) * k["norm"].astype(np.float64), rtol=1e-12, atol=1e-12)
+
+
+def test_qjl_keys_unbiased_scores_mse_keys_shrunk():
+    """QJL keys: slope of estimated vs true scores is 1; MSE-only 3-bit keys shrink
+    scores by about 1 - MSE (the estimate is biased toward zero)."""
+    P = rotation.haar_rotation(42, D)
+    S = rotation.qjl_projection(4242, D)
+    g = np.random.default_rng(4)
+    X = g.standard_normal((6000, D))
+    q = g.standard_normal((4, D))
+    true = q @ X.T
+    c2, t2 = codebook.canonical(2)
+    k = quantize.quantize_head(X, P, c2, t2, S=S)
+    est = attention.rotated_scores(q, k["codes"], k["norm"], P, c2, D, 1.0, k["signs"], k["gamma"], S)
+    slope = np.sum(est * true) / np.sum(true * true)
+    c3, t3 = codebook.canonical(3)
+    k3 = quantize.quantize_head(X, P, c3, t3)
+    est3 = attention.rotated_scores(q, k3["codes"], k3["norm"], P, c3, D, 1.0)
+    slope3 = np.sum(est3 * true) / np.sum(true * true)
+    assert abs(slope - 1) < 0.02
+    assert abs(slope3 - (1 - codebook.expected_sq_error(c3, t3))) < 0.01
+
+
+# ---------------------------------------------------------------- attention --
+
+def _head_case(bits_k=3, bits_v=3, T=300, G=4, qjl=False, seed=0):
+    g = np.random.default_rng(seed)
+    P = rotation.haar_rotation(42, D)
+    S = rotation.qjl_projection(4242, D) if qjl else None
+    ck, tk = codebook.canonical(bits_k)
+    cv, tv = codebook.canonical(bits_v)
+    K = g.standard_normal((T, D)) * 3
+    V = g.standard_normal((T, D))
+    q = g.standard_normal((G, D))
+    k = quantize.quantize_head(K, P, ck, tk, S=S)
+    v = quantize.quantize_head(V, P, cv, tv)
+    return P, S, ck, cv, K, V, q, k, v
+
+
+@pytest.mark.parametrize("qjl", [False, True])
+def test_rotated_domain_equals_textbook(qjl):
+    P, S, ck, cv, K, V, q, k, v = _head_case(bits_k=2 if qjl else 3, qjl=qjl)
+    Kh = attention.dequantize_head(k["codes"], k["norm"], P, ck, D,
+                                   k.get("signs"), k.get("gamma"), S)
+    Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, D)
+    scale = 1 / math.sqrt(D)
+    a = attention.attend_textbook(q, Kh, Vh, scale)
+    b = attention.attend_rotated(q, k, v, P, P, ck, cv, D, scale, S=S)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+
+
+def test_textbook_matches_pure_python_loop():
+    P, S, ck, cv, K, V, q, k, v = _head_case(T=20, G=2)
+    Kh = attention.dequantize_head(k["codes"], k["norm"], P, ck, D)
+    Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, D)
+    scale = 1 / math.sqrt(D)
+    out = attention.attend_textbook(q, Kh, Vh, scale)
+    for h in range(2):
+        s = [scale * sum(q[h, j] * Kh[t, j] for j in range(D)) for t in range(20)]
+        m = max(s)
+        e = [math.exp(x - m) for x in s]
+        z = sum(e)
+        o = [sum(e[t] / z * Vh[t, j] for t in range(20)) for j in range(D)]
+        assert np.allclose(out[h], o, rtol=1e-12, atol=1e-14)
+    assert np.allclose(attention.softmax(np.array([[1.0, 2.0, -3.0]])), special.softmax([1.0, 2.0, -3.0]))
+
+
+def test_single_token_returns_its_value():
+    P, S, ck, cv, K, V, q, k, v = _head_case(T=1)
+    Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, D)
+    o = attention.attend_rotated(q, k, v, P, P, ck, cv, D, 1 / math.sqrt(D))
+    assert np.allclose(o, np.repeat(Vh, q.shape[0], axis=0), rtol=1e-12, atol=1e-14)
+
+
+def test_identical_keys_average_values():
+    P, S, ck, cv, K, V, q, k, v = _head_case(T=50)
+    k = {"codes": np.repeat(k["codes"][:1], 50, axis=0), "norm": np.repeat(k["norm"][:1], 50)}
+    Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, D)
+    o = attention.attend_rotated(q, k, v, P, P, ck, cv, D, 1 / math.sqrt(D))
+    assert np.allclose(o, np.repeat(Vh.mean(axis=0, keepdims=True), q.shape[0], axis=0), rtol=1e-10, atol=1e-13)
+
+
+def test_ctx_len_truncates_and_zero_context_gives_zero():
+    P, S, ck, cv, K, V, q, k, v = _head_case(T=100)
+    sc = 1 / math.sqrt(D)
+    a = attention.attend_rotated(q, k, v, P, P, ck, cv, D, sc, ctx_len=37)
+    kk = {key: val[:37] for key, val in k.items() if key in ("codes", "norm")}
+    vv = {key: val[:37] for key, val in v.items() if key in ("codes", "norm")}
+    b = attention.attend_rotated(q, kk, vv, P, P, ck, cv, D, sc)
+    assert np.array_equal(a, b)
+    assert np.all(attention.attend_rotated(q, k, v, P, P, ck, cv, D, sc, ctx_len=0) == 0)
+
+
+@pytest.mark.parametrize("bounds", [[(0, 300)], [(0, 32), (32, 64), (64, 300)],
+                                    [(0, 100), (100, 100), (100, 299), (299, 300)]])
+def test_split_merge_equals_one_pass(bounds):
+    P, S, ck, cv, K, V, q, k, v = _head_case(T=300)
+    sc = 1 / math.sqrt(D)
+    s = attention.rotated_scores(q, k["codes"], k["norm"], P, ck, D, sc)
+    vr = v["norm"].astype(np.float64)[:, None] * cv[v["codes"]] / math.sqrt(D)
+    o_rot = attention.merge_partials(attention.split_partials(s, vr, bounds))
+    one = attention.softmax(s) @ vr
+    assert np.abs(o_rot - one).max() <= 1e-12 * np.abs(one).max()
+
+
+def test_package_imports_only_numpy_scipy():
+    import sys
+    assert "decode_attention_tq_amd" not in oracle.__dict__
+    for m in (rng, rotation, codebook, quantize, attention):
+        src = open(m.__file__).read()
+        assert "decode_attention_tq_amd" not in src and "torch" not in src
