@@ -1,0 +1,254 @@
+"""Python binding of libtq.so, the TurboQuant packed-KV library for MI355X (gfx950).
+
+Argument marshalling only: every step of quantization and decode attention runs
+in the library's HIP kernels. PyTorch provides device memory and the stream.
+The names follow the C ABI in include/tq.h:
+
+    make_codebook(bits)                        -> (centroids, thresholds)   host
+    make_rotation(seed, kind=HAAR)             -> float32 [128, 128]        host
+    quantize_kv(x, cache, t_offset=0)          x: [B, T, H_kv, 128] on the GPU
+    dequantize(cache, t0, t1)                  -> float32 [B, H_kv, t1-t0, 128]
+    decode_attention(k, v, q, ...)             -> float32 [B, H_q, 128]
+    decode_workspace_bytes(...), decode_splits(...), status_string(code)
+
+Cache bundles the device buffers of one packed cache (keys or values) with its
+rotation, QJL projection and codebook.
+
+If libtq.so is missing the import fails: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m decode_attention_tq_amd.build` "
+        "(hipcc for gfx950); this package has no CPU fallback")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE = range(6)
+F32, BF16 = 0, 1
+HAAR, GAUSSIAN = 0, 1
+KEYS, VALUES = 0, 1
+D = 128
+VALUE_BLOCK = 8
+
+EXPORTS = ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
+           "tq_decode_attention", "tq_decode_splits", "tq_decode_workspace_bytes", "tq_status_string")
+
+
+class TQCache(ctypes.Structure):
+    _fields_ = [
+        ("role", ctypes.c_int32), ("bits", ctypes.c_int32), ("qjl", ctypes.c_int32), ("d", ctypes.c_int32),
+        ("B", ctypes.c_int64), ("H_kv", ctypes.c_int64), ("T_cap", ctypes.c_int64),
+        ("codes", ctypes.c_void_p), ("norms", ctypes.c_void_p),
+        ("qjl_signs", ctypes.c_void_p), ("qjl_gamma", ctypes.c_void_p),
+        ("rot", ctypes.c_void_p), ("qjl_proj", ctypes.c_void_p),
+        ("centroids", ctypes.c_float * 16),
+    ]
+
+
+_P = ctypes.c_void_p
+_I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
+_lib.tq_make_codebook.argtypes = [_I32, _I32, _P, _P]
+_lib.tq_make_rotation.argtypes = [_U64, _I32, _I32, _P]
+_lib.tq_quantize_kv.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache), _I64, _P]
+_lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
+_lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P, _I64,
+                                     _F, _I32, _P, _P, ctypes.c_size_t, _P]
+_lib.tq_decode_splits.argtypes = [_I64, _I64, _I64, _I32]
+_lib.tq_decode_splits.restype = _I32
+_lib.tq_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32, _I32]
+_lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+_lib.tq_status_string.argtypes = [ctypes.c_int]
+_lib.tq_status_string.restype = ctypes.c_char_p
+for _name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
+    getattr(_lib, _name).restype = ctypes.c_int
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+def lib():
+    """The loaded ctypes library (for tests that call the C ABI directly)."""
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return _lib.tq_status_string(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise TQError(status, what)
+
+
+# ------------------------------------------------------------------ host ----
+
+def make_codebook(bits: int, d: int = D):
+    """Gaussian Lloyd-Max codebook: (centroids float32 [2^bits], thresholds float32 [2^bits - 1])."""
+    L = 1 << bits
+    c = np.zeros(L, dtype=np.float32)
+    t = np.zeros(max(L - 1, 1), dtype=np.float32)
+    _check(_lib.tq_make_codebook(bits, d, c.ctypes.data, t.ctypes.data), "tq_make_codebook")
+    return c, t[:L - 1]
+
+
+def make_rotation(seed: int, kind: int = HAAR, d: int = D) -> np.ndarray:
+    """Seeded d x d float32 matrix (HAAR rotation Pi or GAUSSIAN projection S)."""
+    out = np.zeros((d, d), dtype=np.float32)
+    _check(_lib.tq_make_rotation(seed & 0xFFFFFFFFFFFFFFFF, d, kind, out.ctypes.data), "tq_make_rotation")
+    return out
+
+
+def decode_splits(B: int, H_kv: int, T: int, n_split: int = 0) -> int:
+    return int(_lib.tq_decode_splits(B, H_kv, T, n_split))
+
+
+def decode_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0, k_qjl: int = 0) -> int:
+    return int(_lib.tq_decode_workspace_bytes(B, H_q, H_kv, T, n_split, k_qjl))
+
+
+# ---------------------------------------------------------------- device ----
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(device) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+class Cache:
+    """Device buffers of one packed cache (keys or values of one layer).
+
+    codes  int32 words [B, H_kv, T_cap * d * bits / 32] (layout set by `role`)
+    norms  float32 [B, H_kv, T_cap]
+    signs  int32 [B, H_kv, T_cap, d/32] and gamma float32 [B, H_kv, T_cap] for QJL keys
+    rot    float32 [d, d] (Pi), proj float32 [d, d] (S, QJL keys), centroids (host)
+    """
+
+    def __init__(self, role: int, bits: int, B: int, H_kv: int, T_cap: int, device="cuda",
+                 rot=None, proj=None, qjl: bool = False, centroids=None, rot_seed: int = 42,
+                 qjl_seed: int = 4242):
+        torch = _torch()
+        self.role, self.bits, self.qjl = role, bits, int(bool(qjl))
+        self.B, self.H_kv, self.T_cap, self.d = B, H_kv, T_cap, D
+        self.device = torch.device(device)
+        W = D * bits // 32
+        self.codes = torch.zeros((B, H_kv, T_cap * W), dtype=torch.int32, device=self.device)
+        self.norms = torch.zeros((B, H_kv, T_cap), dtype=torch.float32, device=self.device)
+        if rot is None:
+            rot = make_rotation(rot_seed, HAAR)
+        self.rot = torch.as_tensor(np.asarray(rot, dtype=np.float32)).to(self.device).contiguous()
+        if self.qjl:
+            if proj is None:
+                proj = make_rotation(qjl_seed, GAUSSIAN)
+            self.proj = torch.as_tensor(np.asarray(proj, dtype=np.float32)).to(self.device).contiguous()
+            self.signs = torch.zeros((B, H_kv, T_cap, D // 32), dtype=torch.int32, device=self.device)
+            self.gamma = torch.zeros((B, H_kv, T_cap), dtype=torch.float32, device=self.device)
+        else:
+            self.proj = self.signs = self.gamma = None
+        if centroids is None:
+            centroids, _ = make_codebook(bits)
+        self.centroids = np.asarray(centroids, dtype=np.float32)
+
+    def struct(self) -> TQCache:
+        s = TQCache()
+        s.role, s.bits, s.qjl, s.d = self.role, self.bits, self.qjl, self.d
+        s.B, s.H_kv, s.T_cap = self.B, self.H_kv, self.T_cap
+        s.codes = self.codes.data_ptr()
+        s.norms = self.norms.data_ptr()
+        s.qjl_signs = self.signs.data_ptr() if self.qjl else None
+        s.qjl_gamma = self.gamma.data_ptr() if self.qjl else None
+        s.rot = self.rot.data_ptr()
+        s.qjl_proj = self.proj.data_ptr() if self.qjl else None
+        for i, c in enumerate(self.centroids):
+            s.centroids[i] = float(c)
+        return s
+
+    @property
+    def nbytes(self) -> int:
+        n = self.codes.numel() * 4 + self.norms.numel() * 4
+        if self.qjl:
+            n += self.signs.numel() * 4 + self.gamma.numel() * 4
+        return n
+
+
+def quantize_kv(x, cache: Cache, t_offset: int = 0):
+    """Quantize x [B, T, H_kv, 128] (float32 or bfloat16, last dim contiguous, on the
+    cache's device) into tokens t_offset .. t_offset+T-1 of `cache`."""
+    if x.dim() != 4 or x.shape[-1] != D or x.stride(-1) != 1:
+        raise ValueError("x must be [B, T, H_kv, 128] with a contiguous last dimension")
+    B, T, H, _ = x.shape
+    s = cache.struct()
+    _check(_lib.tq_quantize_kv(x.data_ptr(), _dtype_code(x), B, T, H, x.stride(0), x.stride(1), x.stride(2),
+                               ctypes.byref(s), t_offset, _stream_handle(x.device)), "tq_quantize_kv")
+
+
+def dequantize(cache: Cache, t0: int = 0, t1: int | None = None, out=None):
+    torch = _torch()
+    t1 = cache.T_cap if t1 is None else t1
+    if out is None:
+        out = torch.empty((cache.B, cache.H_kv, t1 - t0, D), dtype=torch.float32, device=cache.device)
+    s = cache.struct()
+    _check(_lib.tq_dequantize(ctypes.byref(s), t0, t1, out.data_ptr(), _stream_handle(cache.device)),
+           "tq_dequantize")
+    return out
+
+
+class Workspace:
+    """Reusable device workspace for decode_attention."""
+
+    def __init__(self, nbytes: int, device="cuda"):
+        torch = _torch()
+        self.buf = torch.empty(max(nbytes, 256) + 256, dtype=torch.uint8, device=device)
+        base = self.buf.data_ptr()
+        self.ptr = (base + 255) & ~255
+        self.nbytes = self.buf.numel() - (self.ptr - base)
+
+
+def decode_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None, scale: float = 0.0,
+                     n_split: int = 0, out=None, workspace: Workspace | None = None):
+    """Decode attention of q [B, H_q, 128] over the packed caches -> float32 [B, H_q, 128]."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    B, H_q, _ = q.shape
+    T = k.T_cap if T is None else T
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H_q, k.H_kv, T, n_split, k.qjl)
+    if workspace is None or workspace.nbytes < need:
+        workspace = Workspace(need, q.device)
+    sk, sv = k.struct(), v.struct()
+    cl = 0
+    if ctx_lens is not None:
+        if ctx_lens.dtype != torch.int32 or not ctx_lens.is_contiguous() or ctx_lens.numel() != B:
+            raise ValueError("ctx_lens must be a contiguous int32 tensor of B entries")
+        cl = ctx_lens.data_ptr()
+    _check(_lib.tq_decode_attention(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q,
+                                    cl or None, T, scale, n_split, out.data_ptr(), workspace.ptr,
+                                    workspace.nbytes, _stream_handle(q.device)), "tq_decode_attention")
+    return out

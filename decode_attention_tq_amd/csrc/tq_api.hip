@@ -1,0 +1,172 @@
+// C ABI of the TurboQuant packed-KV library: argument validation (before any
+// HIP call), workspace planning and kernel dispatch.
+#include <math.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool is_fp16_exact(float v) { return (float)(_Float16)v == v; }
+
+// Validates the descriptor itself; returns TQ_OK or an error code.
+int check_cache(const tq_cache* c) {
+  if (c == nullptr) return TQ_ERR_INVALID_ARGUMENT;
+  if (c->role != TQ_KEYS && c->role != TQ_VALUES) return TQ_ERR_INVALID_ARGUMENT;
+  if (c->bits < 2 || c->bits > 4) return TQ_ERR_UNSUPPORTED;
+  if (c->qjl != 0 && c->qjl != 1) return TQ_ERR_INVALID_ARGUMENT;
+  if (c->qjl && c->role != TQ_KEYS) return TQ_ERR_UNSUPPORTED;
+  if (c->d != kD) return TQ_ERR_UNSUPPORTED;
+  if (c->B <= 0 || c->H_kv <= 0 || c->T_cap <= 0) return TQ_ERR_INVALID_ARGUMENT;
+  if (c->B > 65535 || c->H_kv > 65535) return TQ_ERR_UNSUPPORTED;
+  if (c->role == TQ_VALUES && c->T_cap % kValueBlock != 0) return TQ_ERR_INVALID_ARGUMENT;
+  // per-head byte ranges are addressed with 32-bit offsets
+  if (c->T_cap * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+  if (c->codes == nullptr || c->norms == nullptr || c->rot == nullptr) return TQ_ERR_INVALID_ARGUMENT;
+  if (c->qjl && (c->qjl_signs == nullptr || c->qjl_gamma == nullptr || c->qjl_proj == nullptr))
+    return TQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(c->codes) || !aligned16(c->norms) || !aligned16(c->rot)) return TQ_ERR_ALIGNMENT;
+  if (c->qjl && (!aligned16(c->qjl_signs) || !aligned16(c->qjl_gamma) || !aligned16(c->qjl_proj)))
+    return TQ_ERR_ALIGNMENT;
+  const int L = 1 << c->bits;
+  for (int i = 0; i < L; ++i) {
+    if (!isfinite(c->centroids[i]) || !is_fp16_exact(c->centroids[i])) return TQ_ERR_INVALID_ARGUMENT;
+    if (i > 0 && !(c->centroids[i] > c->centroids[i - 1])) return TQ_ERR_INVALID_ARGUMENT;
+  }
+  return TQ_OK;
+}
+
+int device_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_DEVICE; }
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
+                 DecodePlan* p) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || T < 0 || n_split < 0) return false;
+  if (H_q % H_kv != 0) return false;
+  const int64_t G = H_q / H_kv;
+  if (G > 16) return false;
+  p->B = B;
+  p->H_q = H_q;
+  p->H_kv = H_kv;
+  p->T = T;
+  p->G = (int32_t)G;
+  p->wide = G > 8;
+  p->nq = p->wide ? 32 : 16;
+  p->qjl = qjl ? 1 : 0;
+  const int64_t Tp = T > 0 ? T : 1;
+  int64_t target;
+  if (n_split > 0) {
+    target = n_split;
+  } else {
+    // about 16 wavefronts per compute unit on a 256-CU part, chunks of >= 256 tokens
+    const int64_t units = B * H_kv;
+    target = (4096 + units - 1) / units;
+    const int64_t cap = (Tp + 255) / 256;
+    if (target > cap) target = cap;
+    if (target < 1) target = 1;
+  }
+  int64_t chunk = (Tp + target - 1) / target;
+  chunk = (chunk + kStep - 1) / kStep * kStep;
+  p->chunk = (int32_t)chunk;
+  p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
+  size_t off = 0;
+  p->off_qop = off;
+  off = align256(off + (size_t)(B * H_kv) * (1 + p->qjl) * p->nq * kD * sizeof(_Float16));
+  p->off_qcs = off;
+  off = align256(off + (size_t)(B * H_kv) * 2 * 16 * sizeof(float));
+  p->off_ml = off;
+  off = align256(off + (size_t)(B * H_q) * p->n_split * 2 * sizeof(float));
+  p->off_acc = off;
+  off = align256(off + (size_t)(B * H_q) * p->n_split * kD * sizeof(float));
+  p->bytes = off;
+  return true;
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" const char* tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "ok";
+    case TQ_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case TQ_ERR_UNSUPPORTED: return "unsupported configuration";
+    case TQ_ERR_ALIGNMENT: return "misaligned device pointer";
+    case TQ_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case TQ_ERR_DEVICE: return "HIP device error";
+    default: return "unknown status";
+  }
+}
+
+extern "C" int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split) {
+  DecodePlan p;
+  if (!plan_decode(B, H_kv, H_kv, T, n_split, 0, &p)) return 0;
+  return p.n_split;
+}
+
+extern "C" size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
+                                            int32_t n_split, int32_t k_qjl) {
+  DecodePlan p;
+  if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p)) return 0;
+  return p.bytes;
+}
+
+extern "C" int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t T, int64_t H_kv,
+                              int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                              const tq_cache* dst, int64_t t_offset, void* hip_stream) {
+  int st = check_cache(dst);
+  if (st != TQ_OK) return st;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
+  if (B != dst->B || H_kv != dst->H_kv || T < 0 || t_offset < 0 || t_offset + T > dst->T_cap)
+    return TQ_ERR_INVALID_ARGUMENT;
+  if (T == 0) return TQ_OK;
+  if (x == nullptr || stride_b < 0 || stride_t < 0 || stride_h < 0) return TQ_ERR_INVALID_ARGUMENT;
+  const int64_t esz = x_dtype == TQ_F32 ? 4 : 2;
+  const int64_t vec_align = 16 / esz;   // every row starts on a 16-byte boundary
+  if (!aligned16(x) || stride_b % vec_align || stride_t % vec_align || stride_h % vec_align)
+    return TQ_ERR_ALIGNMENT;
+  return device_status(launch_quantize(x, x_dtype, B, T, H_kv, stride_b, stride_t, stride_h, dst, t_offset,
+                                       (hipStream_t)hip_stream));
+}
+
+extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void* hip_stream) {
+  int st = check_cache(src);
+  if (st != TQ_OK) return st;
+  if (t0 < 0 || t1 < t0 || t1 > src->T_cap) return TQ_ERR_INVALID_ARGUMENT;
+  if (t1 == t0) return TQ_OK;
+  if (out == nullptr) return TQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(out)) return TQ_ERR_ALIGNMENT;
+  return device_status(launch_dequantize(src, t0, t1, out, (hipStream_t)hip_stream));
+}
+
+extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
+                                   int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
+                                   int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+  int st = check_cache(k);
+  if (st != TQ_OK) return st;
+  st = check_cache(v);
+  if (st != TQ_OK) return st;
+  if (k->role != TQ_KEYS || v->role != TQ_VALUES) return TQ_ERR_INVALID_ARGUMENT;
+  if (k->B != v->B || k->H_kv != v->H_kv) return TQ_ERR_INVALID_ARGUMENT;
+  if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || out == nullptr || H_q <= 0 || T < 0 || n_split < 0) return TQ_ERR_INVALID_ARGUMENT;
+  if (T > k->T_cap || T > v->T_cap || T >= ((int64_t)1 << 30)) return TQ_ERR_INVALID_ARGUMENT;
+  if (H_q % k->H_kv != 0) return TQ_ERR_INVALID_ARGUMENT;
+  if (H_q / k->H_kv > 16 || H_q > 65535) return TQ_ERR_UNSUPPORTED;
+  if (!isfinite(scale)) return TQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
+  DecodePlan p;
+  if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p)) return TQ_ERR_INVALID_ARGUMENT;
+  if (workspace == nullptr || workspace_bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
+  if (((uintptr_t)workspace & 255u) != 0) return TQ_ERR_ALIGNMENT;
+  if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
+  return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
+                                     (hipStream_t)hip_stream));
+}

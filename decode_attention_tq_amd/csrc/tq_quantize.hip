@@ -1,0 +1,570 @@
+// Quantize and dequantize kernels for the packed TurboQuant cache, for gfx950.
+//
+// quantize (ai-accelerate.xyz TurboQuant article, section "TurboQuantの仕組み",
+// step 1, and step 2 for QJL keys), per vector x:
+//   n = |x|; y = Pi x on MFMA; z = y * sqrt(d) / n (the rotated unit vector in
+//   standard-normal units); code_j = #{ i : z_j >= t_i } for the Lloyd-Max
+//   thresholds t; codes are bit-packed into the key or value layout; n is stored.
+//   QJL keys: rho = z - c[code]; gamma = |rho| / sqrt(d); sign bits of S rho.
+//
+// Rotation precision: the input is scaled per vector by a power of two so its
+// largest entry lies in [2^13, 2^14) and converted to float16, which is exact for
+// bfloat16 input (8 significant bits) above float16's normal range floor;
+// float32 input is split into float16 hi + lo. Pi (and S) are split into float16
+// hi + lo once per workgroup, so the MFMA products carry ~22 significant bits and
+// the float32 accumulation gives y to ~1e-7 relative, far inside the 1e-6
+// decision-boundary band.
+//
+// Work decomposition: "slots" enumerate, per (row, head), the token range
+// [floor8(t_offset), ceil8(t_offset + T)); a tile is 16 slots per wavefront, so a
+// tile always holds whole 8-token value blocks and short appends (T = 1) of many
+// heads share one workgroup. Workgroups are persistent: each loads Pi once into
+// LDS (in MFMA operand order) and loops over tiles.
+#include <math.h>
+
+#include "tq_device.h"
+#include "tq_internal.h"
+
+namespace tq {
+
+namespace {
+
+struct QuantArgs {
+  const void* x;
+  int64_t sb, st, sh;          // element strides of x
+  int64_t B, T, H_kv, T_cap;
+  int64_t t_offset, t_base;    // t_base = floor8(t_offset)
+  int64_t nslot;               // slots per head (multiple of 8)
+  int64_t n_tiles;
+  uint32_t* codes;
+  float* norms;
+  uint32_t* signs;
+  float* gamma;
+  const float* rot;
+  const float* proj;
+  float cent[16];
+  float thr[16];
+};
+
+// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i,
+// by a branch-free binary search.
+template <int BITS>
+__device__ inline int encode(float z, const float* t) {
+  if constexpr (BITS == 2) {
+    const bool b1 = z >= t[1];
+    const bool b0 = z >= (b1 ? t[2] : t[0]);
+    return (b1 << 1) | b0;
+  } else if constexpr (BITS == 3) {
+    const bool b2 = z >= t[3];
+    const bool b1 = z >= (b2 ? t[5] : t[1]);
+    const float tc = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);
+    const bool b0 = z >= tc;
+    return (b2 << 2) | (b1 << 1) | b0;
+  } else {
+    const bool b3 = z >= t[7];
+    const bool b2 = z >= (b3 ? t[11] : t[3]);
+    const float t1 = b3 ? (b2 ? t[13] : t[9]) : (b2 ? t[5] : t[1]);
+    const bool b1 = z >= t1;
+    const int base = (b3 << 3) | (b2 << 2) | (b1 << 1);
+    float t0 = t[0];
+#pragma unroll
+    for (int i = 2; i < 16; i += 2) t0 = (base == i) ? t[i] : t0;
+    const bool b0 = z >= t0;
+    return base | b0;
+  }
+}
+
+// Pack 32 codes (bytes of q[0..7], LSB first) into BITS words, stream position BITS*k.
+template <int BITS>
+__device__ inline void pack32(const uint32_t* q, uint32_t* w) {
+#pragma unroll
+  for (int i = 0; i < BITS; ++i) w[i] = 0u;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) {
+    const uint32_t code = (q[k >> 2] >> (8 * (k & 3))) & 0xFFu;
+    const int pos = BITS * k;
+    const int wi = pos >> 5, off = pos & 31;
+    w[wi] |= code << off;
+    if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
+  }
+}
+
+// Load Pi (or S), split into float16 hi/lo, into LDS in B-operand order:
+// op[pass][ks][nb][lane][8] = M[16nb + n][32g + 8ks + e], lane = 16g + n.
+__device__ void stage_matrix(const float* M, _Float16* op, int nthreads) {
+  for (int idx = threadIdx.x; idx < kD * kD; idx += nthreads) {
+    const int row = idx / kD, col = idx % kD;   // coalesced global read
+    const float v = M[idx];
+    const _Float16 hi = (_Float16)v;
+    const _Float16 lo = (_Float16)(v - (float)hi);
+    const int nb = row >> 4, n = row & 15;
+    const int g = col >> 5, ks = (col >> 3) & 3, e = col & 7;
+    const int lane = 16 * g + n;
+    const int o = (((ks * 8 + nb) * 64 + lane) << 3) + e;
+    op[o] = hi;
+    op[4 * 8 * 64 * 8 + o] = lo;
+  }
+}
+
+template <int BITS, int ROLE, int QJL, int XF32>
+__global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) {
+  constexpr int WAVES = QJL ? 2 : 4;
+  constexpr int NT = 64 * WAVES;
+  constexpr int TILE = 16 * WAVES;
+  constexpr int OPH = 4 * 8 * 64 * 8;   // halves per pass of an operand matrix
+  constexpr int KW = 4 * BITS;          // words per key token
+  constexpr int VBW = 32 * BITS;        // words per value block
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* piop = (_Float16*)smem;                                  // 2 * OPH halves
+  _Float16* sop = piop + 2 * OPH;                                   // QJL: 2 * OPH halves
+  unsigned char* cbuf_all = (unsigned char*)(piop + (QJL ? 4 : 2) * OPH);   // WAVES * 16 * 128 bytes
+  _Float16* rbuf_all = (_Float16*)(cbuf_all + WAVES * 16 * kD);       // QJL: WAVES * 2 * 16 * 128 halves
+
+  stage_matrix(a.rot, piop, NT);
+  if constexpr (QJL) stage_matrix(a.proj, sop, NT);
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  unsigned char* cbuf = cbuf_all + wave * 16 * kD;
+  _Float16* rhi = rbuf_all + wave * 2 * 16 * kD;
+  _Float16* rlo = rhi + 16 * kD;
+  const float sqrt_d = sqrtf((float)kD);
+  const int64_t heads = a.B * a.H_kv;
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // ---- slot of this lane (row i16 of the wave's 16)
+    const int64_t slot = tile * TILE + wave * 16 + i16;
+    const int64_t bh = slot / a.nslot;
+    const int64_t t = a.t_base + slot % a.nslot;
+    const bool valid = bh < heads && t >= a.t_offset && t < a.t_offset + a.T;
+    const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
+
+    // ---- load the lane's 32 coordinates (32g .. 32g+31)
+    float xv[32];
+    if (valid) {
+      const int64_t off = b * a.sb + (t - a.t_offset) * a.st + h * a.sh + 32 * g;
+      if constexpr (XF32) {
+        const float4* p = (const float4*)((const float*)a.x + off);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float4 v = p[k];
+          xv[4 * k] = v.x; xv[4 * k + 1] = v.y; xv[4 * k + 2] = v.z; xv[4 * k + 3] = v.w;
+        }
+      } else {
+        const u32x4* p = (const u32x4*)((const uint16_t*)a.x + off);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const u32x4 v = p[k];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            xv[8 * k + 2 * u] = __uint_as_float(v[u] << 16);
+            xv[8 * k + 2 * u + 1] = __uint_as_float(v[u] & 0xFFFF0000u);
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int k = 0; k < 32; ++k) xv[k] = 0.f;
+    }
+
+    // ---- power-of-two scale, norm
+    float mx = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) mx = fmaxf(mx, fabsf(xv[k]));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const int sexp = (mx > 0.f) ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 32; ++k) {
+      xv[k] = ldexpf(xv[k], sexp);
+      ss = fmaf(xv[k], xv[k], ss);
+    }
+    ss += shfl_xor_f(ss, 16);
+    ss += shfl_xor_f(ss, 32);
+    const float ns = sqrtf(ss);                      // |x| * 2^sexp
+    const float fz = ns > 0.f ? sqrt_d / ns : 0.f;   // z = y_scaled * fz
+
+    // ---- A operand (x as float16 hi/lo), coordinates 32g + 8ks + e
+    half8 xa[4], xl[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = xv[8 * ks + e];
+        const _Float16 hi = (_Float16)v;
+        xa[ks][e] = hi;
+        if constexpr (XF32) xl[ks][e] = (_Float16)(v - (float)hi);
+      }
+    }
+
+    // ---- y = Pi x on MFMA: D[nb] lane (g, n) = y[slot 4g + r][16nb + n]
+    floatx4 y[8];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      floatx4 accv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const int o = ((ks * 8 + nb) * 64 + lane) << 3;
+        const half8 bh8 = *(const half8*)(piop + o);
+        const half8 bl8 = *(const half8*)(piop + OPH + o);
+        accv = mfma16(xa[ks], bh8, accv);
+        accv = mfma16(xa[ks], bl8, accv);
+        if constexpr (XF32) accv = mfma16(xl[ks], bh8, accv);
+      }
+      y[nb] = accv;
+    }
+
+    // ---- codes
+    float fr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) fr[r] = __shfl(fz, 4 * g + r);
+    int code[8][4];
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float z = y[nb][r] * fr[r];
+        y[nb][r] = z;
+        code[nb][r] = encode<BITS>(z, a.thr);
+        cbuf[(4 * g + r) * kD + 16 * nb + i16] = (unsigned char)code[nb][r];
+      }
+    }
+
+    // ---- QJL residual sketch (keys)
+    float gam[4];
+    if constexpr (QJL) {
+      float rs[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float cc = a.cent[0];
+#pragma unroll
+          for (int q = 1; q < (1 << BITS); ++q) cc = (code[nb][r] == q) ? a.cent[q] : cc;
+          const float rho = y[nb][r] - cc;
+          rs[r] = fmaf(rho, rho, rs[r]);
+          const _Float16 hi = (_Float16)rho;
+          rhi[(4 * g + r) * kD + 16 * nb + i16] = hi;
+          rlo[(4 * g + r) * kD + 16 * nb + i16] = (_Float16)(rho - (float)hi);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int m = 1; m < 16; m <<= 1) rs[r] += shfl_xor_f(rs[r], m);
+        gam[r] = sqrtf(rs[r]) / sqrt_d;
+      }
+    }
+    __syncthreads();
+
+    if constexpr (QJL) {
+      // z' = S rho on MFMA; A operand rows = slots, coordinates 32g + 8ks + e
+      half8 ra[4], rl[4];
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        ra[ks] = *(const half8*)(rhi + i16 * kD + 32 * g + 8 * ks);
+        rl[ks] = *(const half8*)(rlo + i16 * kD + 32 * g + 8 * ks);
+      }
+      __syncthreads();
+      unsigned char* sbuf = (unsigned char*)rhi;   // reuse: sign bytes [slot][coord]
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        floatx4 accv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+          const int o = ((ks * 8 + nb) * 64 + lane) << 3;
+          const half8 bh8 = *(const half8*)(sop + o);
+          const half8 bl8 = *(const half8*)(sop + OPH + o);
+          accv = mfma16(ra[ks], bh8, accv);
+          accv = mfma16(ra[ks], bl8, accv);
+          accv = mfma16(rl[ks], bh8, accv);
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sbuf[(4 * g + r) * kD + 16 * nb + i16] = accv[r] >= 0.f ? 1 : 0;
+      }
+      __syncthreads();
+      // signs + gamma: lane (v = lane/4, grp = lane%4) packs 32 sign bits of slot v
+      {
+        const int v = lane >> 2, grp = lane & 3;
+        const int64_t s2 = tile * TILE + wave * 16 + v;
+        const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+        const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
+        const uint32_t* q = (const uint32_t*)(sbuf + v * kD + 32 * grp);
+        uint32_t wbits = 0u;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) wbits |= ((q[k >> 2] >> (8 * (k & 3))) & 1u) << k;
+        if (ok) a.signs[(bh2 * a.T_cap + t2) * 4 + grp] = wbits;
+      }
+      // gamma: lane (g, n = 0) holds slots 4g + r
+      if (i16 == 0) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int64_t s2 = tile * TILE + wave * 16 + 4 * g + r;
+          const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+          if (bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T) a.gamma[bh2 * a.T_cap + t2] = gam[r];
+        }
+      }
+    }
+
+    // ---- norms
+    if (valid && g == 0) a.norms[bh * a.T_cap + t] = ldexpf(ns, -sexp);
+
+    // ---- pack and store codes
+    if constexpr (ROLE == TQ_KEYS) {
+      const int v = lane >> 2, grp = lane & 3;
+      const int64_t s2 = tile * TILE + wave * 16 + v;
+      const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+      const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
+      uint32_t q[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kD + 32 * grp + 4 * k);
+      uint32_t w[BITS];
+      pack32<BITS>(q, w);
+      if (ok) {
+        uint32_t* dst = a.codes + (bh2 * a.T_cap + t2) * KW + grp * BITS;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+      }
+    } else {
+      // lane (blk = lane/32, cg = lane%32): coordinates 4cg .. 4cg+3 of the block's 8 tokens
+      const int blk = lane >> 5, cg = lane & 31;
+      const int64_t s0 = tile * TILE + wave * 16 + 8 * blk;   // first slot of the block
+      const int64_t bh2 = s0 / a.nslot, tb = a.t_base + s0 % a.nslot;
+      uint32_t w[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) w[k] = 0u;
+      uint32_t keep[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) keep[k] = 0u;
+      bool any_valid = false, all_valid = true;
+#pragma unroll
+      for (int ti = 0; ti < 8; ++ti) {
+        const int64_t tt = tb + ti;
+        const bool ok = bh2 < heads && tt >= a.t_offset && tt < a.t_offset + a.T;
+        any_valid |= ok;
+        all_valid &= ok;
+        const uint32_t q4 = *(const uint32_t*)(cbuf + (8 * blk + ti) * kD + 4 * cg);
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const uint32_t code = (q4 >> (8 * jj)) & 0xFFu;
+          const int pos = BITS * (8 * jj + ti);
+          const int wi = pos >> 5, off = pos & 31;
+          const uint32_t fm = (1u << BITS) - 1u;
+          if (ok) {
+            w[wi] |= code << off;
+            if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
+          } else {
+            keep[wi] |= fm << off;
+            if (off + BITS > 32) keep[wi + 1] |= fm >> (32 - off);
+          }
+        }
+      }
+      if (any_valid) {
+        uint32_t* dst = a.codes + (bh2 * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) dst[k] = all_valid ? w[k] : ((dst[k] & keep[k]) | w[k]);
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- dequantize --
+
+struct DequantArgs {
+  const uint32_t* codes;
+  const float* norms;
+  const uint32_t* signs;
+  const float* gamma;
+  const float* rot;
+  const float* proj;
+  float* out;
+  int64_t H_kv, T_cap, t0, t1;
+  float cent[16];
+};
+
+template <int BITS, int ROLE, int QJL>
+__global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
+  __shared__ float wv[32 * kD];
+  __shared__ float sg[QJL ? 32 * kD : 1];
+  __shared__ float nrm[32], gm[32];
+  constexpr int KW = 4 * BITS;
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int64_t bh = (int64_t)b * a.H_kv + h;
+  const int64_t tbase = a.t0 + (int64_t)blockIdx.x * 32;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
+  const uint32_t* cb = a.codes + bh * a.T_cap * KW;
+  for (int idx = tid; idx < 32 * kD; idx += 256) {
+    const int v = idx / kD, j = idx % kD;
+    const int64_t t = tbase + v;
+    float val = 0.f;
+    if (t < a.t1) {
+      int64_t bit;
+      if constexpr (ROLE == TQ_KEYS) bit = t * KW * 32 + (int64_t)BITS * j;
+      else bit = (t / 8) * (int64_t)(32 * BITS) * 32 + (int64_t)BITS * (8 * j + (t % 8));
+      const int64_t wi = bit >> 5;
+      const int off = (int)(bit & 31);
+      uint32_t x = cb[wi] >> off;
+      if (off + BITS > 32) x |= cb[wi + 1] << (32 - off);
+      const int code = (int)(x & ((1u << BITS) - 1u));
+      float cc = a.cent[0];
+#pragma unroll
+      for (int q = 1; q < (1 << BITS); ++q) cc = (code == q) ? a.cent[q] : cc;
+      val = cc * inv_sqrt_d;
+      if constexpr (QJL) {
+        const uint32_t sw = a.signs[(bh * a.T_cap + t) * 4 + (j >> 5)];
+        sg[idx] = ((sw >> (j & 31)) & 1u) ? 1.f : -1.f;
+      }
+    } else if constexpr (QJL) {
+      sg[idx] = 0.f;
+    }
+    wv[idx] = val;
+  }
+  if (tid < 32) {
+    const int64_t t = tbase + tid;
+    nrm[tid] = t < a.t1 ? a.norms[bh * a.T_cap + t] : 0.f;
+    if constexpr (QJL) gm[tid] = t < a.t1 ? a.gamma[bh * a.T_cap + t] : 0.f;
+  }
+  __syncthreads();
+  const int col = tid & 127, half = tid >> 7;   // output coordinate, vector half
+  float acc[16];
+  if constexpr (QJL) {
+    // w += gamma sqrt(pi/2)/d * S^T sigma
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+    for (int i = 0; i < kD; ++i) {
+      const float s = a.proj[i * kD + col];
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[v] = fmaf(s, sg[(16 * half + v) * kD + i], acc[v]);
+    }
+    __syncthreads();
+    const float cq = sqrtf((float)M_PI / 2.0f) / (float)kD;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) wv[(16 * half + v) * kD + col] += gm[16 * half + v] * cq * acc[v];
+    __syncthreads();
+  }
+  // x_hat = n Pi^T w
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+  for (int j = 0; j < kD; ++j) {
+    const float p = a.rot[j * kD + col];
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = fmaf(p, wv[(16 * half + v) * kD + j], acc[v]);
+  }
+  const int64_t nt = a.t1 - a.t0;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const int64_t t = tbase + 16 * half + v;
+    if (t < a.t1) a.out[(bh * nt + (t - a.t0)) * kD + col] = nrm[16 * half + v] * acc[v];
+  }
+}
+
+template <int BITS, int ROLE, int QJL, int XF32>
+hipError_t launch_q(const QuantArgs& qa, hipStream_t stream) {
+  constexpr int WAVES = QJL ? 2 : 4;
+  constexpr size_t OPH = 4 * 8 * 64 * 8;
+  const size_t smem = (QJL ? 4 : 2) * OPH * 2 + WAVES * 16 * kD + (QJL ? WAVES * 2 * 16 * kD * 2 : 0);
+  auto kern = quantize_kernel<BITS, ROLE, QJL, XF32>;
+  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (e != hipSuccess) return e;
+  int dev = 0, ncu = 256;
+  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+  const int per_cu = QJL ? 1 : 2;
+  int64_t grid = (int64_t)ncu * per_cu;
+  if (grid > qa.n_tiles) grid = qa.n_tiles;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), smem, stream, qa);
+  return hipGetLastError();
+}
+
+template <int BITS, int ROLE, int QJL>
+hipError_t dispatch_x(int xf32, const QuantArgs& qa, hipStream_t s) {
+  return xf32 ? launch_q<BITS, ROLE, QJL, 1>(qa, s) : launch_q<BITS, ROLE, QJL, 0>(qa, s);
+}
+
+template <int BITS>
+hipError_t dispatch_role(int role, int qjl, int xf32, const QuantArgs& qa, hipStream_t s) {
+  if (role == TQ_VALUES) return dispatch_x<BITS, TQ_VALUES, 0>(xf32, qa, s);
+  return qjl ? dispatch_x<BITS, TQ_KEYS, 1>(xf32, qa, s) : dispatch_x<BITS, TQ_KEYS, 0>(xf32, qa, s);
+}
+
+template <int BITS, int ROLE, int QJL>
+hipError_t launch_dq(const DequantArgs& da, int64_t B, hipStream_t stream) {
+  const int64_t n = da.t1 - da.t0;
+  dim3 grid((unsigned)((n + 31) / 32), (unsigned)da.H_kv, (unsigned)B);
+  hipLaunchKernelGGL((dequantize_kernel<BITS, ROLE, QJL>), grid, dim3(256), 0, stream, da);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t dispatch_dq(int role, int qjl, const DequantArgs& da, int64_t B, hipStream_t s) {
+  if (role == TQ_VALUES) return launch_dq<BITS, TQ_VALUES, 0>(da, B, s);
+  return qjl ? launch_dq<BITS, TQ_KEYS, 1>(da, B, s) : launch_dq<BITS, TQ_KEYS, 0>(da, B, s);
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
+                           int64_t sb, int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
+                           hipStream_t stream) {
+  QuantArgs qa;
+  qa.x = x;
+  qa.sb = sb;
+  qa.st = st;
+  qa.sh = sh;
+  qa.B = B;
+  qa.T = T;
+  qa.H_kv = H_kv;
+  qa.T_cap = dst->T_cap;
+  qa.t_offset = t_offset;
+  qa.t_base = (t_offset / kValueBlock) * kValueBlock;
+  const int64_t t_hi = ((t_offset + T + kValueBlock - 1) / kValueBlock) * kValueBlock;
+  qa.nslot = t_hi - qa.t_base;
+  const int tile = dst->qjl && dst->role == TQ_KEYS ? 32 : 64;
+  qa.n_tiles = (B * H_kv * qa.nslot + tile - 1) / tile;
+  qa.codes = dst->codes;
+  qa.norms = dst->norms;
+  qa.signs = dst->qjl_signs;
+  qa.gamma = dst->qjl_gamma;
+  qa.rot = dst->rot;
+  qa.proj = dst->qjl_proj;
+  const int L = 1 << dst->bits;
+  for (int i = 0; i < 16; ++i) qa.cent[i] = i < L ? dst->centroids[i] : 0.f;
+  thresholds_from_centroids(dst->centroids, L, qa.thr);
+  for (int i = L - 1; i < 16; ++i) qa.thr[i] = INFINITY;
+  const int xf32 = x_dtype == TQ_F32;
+  const int qjl = dst->role == TQ_KEYS && dst->qjl;
+  switch (dst->bits) {
+    case 2: return dispatch_role<2>(dst->role, qjl, xf32, qa, stream);
+    case 3: return dispatch_role<3>(dst->role, qjl, xf32, qa, stream);
+    default: return dispatch_role<4>(dst->role, qjl, xf32, qa, stream);
+  }
+}
+
+hipError_t launch_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, hipStream_t stream) {
+  DequantArgs da;
+  da.codes = src->codes;
+  da.norms = src->norms;
+  da.signs = src->qjl_signs;
+  da.gamma = src->qjl_gamma;
+  da.rot = src->rot;
+  da.proj = src->qjl_proj;
+  da.out = out;
+  da.H_kv = src->H_kv;
+  da.T_cap = src->T_cap;
+  da.t0 = t0;
+  da.t1 = t1;
+  const int L = 1 << src->bits;
+  for (int i = 0; i < 16; ++i) da.cent[i] = i < L ? src->centroids[i] : 0.f;
+  const int qjl = src->role == TQ_KEYS && src->qjl;
+  switch (src->bits) {
+    case 2: return dispatch_dq<2>(src->role, qjl, da, src->B, stream);
+    case 3: return dispatch_dq<3>(src->role, qjl, da, src->B, stream);
+    default: return dispatch_dq<4>(src->role, qjl, da, src->B, stream);
+  }
+}
+
+}  // namespace tq

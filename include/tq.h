@@ -1,0 +1,179 @@
+/*
+ * tq.h — C ABI of the TurboQuant packed-KV library for AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (TurboQuant as described in the ai-accelerate.xyz
+ * TurboQuant article, section "TurboQuantの仕組み"):
+ *   step 1  every key/value head vector x is multiplied by a seeded random
+ *           orthogonal matrix Pi; each rotated coordinate is quantized on its
+ *           own with the Gaussian Lloyd-Max scalar codebook at 2, 3 or 4 bits;
+ *           no per-block full-precision scale is kept, only the vector norm.
+ *   step 2  (optional, keys) one sign bit per coordinate of a Gaussian
+ *           projection S of the quantization residual, which makes the key
+ *           inner-product estimate unbiased.
+ * Decode attention reads the packed cache directly: the query is rotated once,
+ * scores are codebook levels times key norms, values are summed in the
+ * rotated domain and one inverse rotation produces the output.
+ *
+ * Conventions (all functions):
+ *   - return an int status (TQ_OK = 0); nothing throws; no global mutable state;
+ *   - argument errors are reported synchronously, before any HIP call;
+ *   - device calls are asynchronous on the given hipStream_t (passed as void*,
+ *     NULL = the default stream); a failed launch returns TQ_ERR_DEVICE, a fault
+ *     inside a kernel surfaces at the caller's next synchronisation;
+ *   - the caller owns every buffer; the library never allocates or frees device
+ *     memory;
+ *   - head dimension d = 128 only (other values return TQ_ERR_UNSUPPORTED).
+ *
+ * Packed formats (one cache per tensor and layer; keys and values set their bit
+ * width separately):
+ *   norms   float32 [B][H_kv][T_cap]: |x| of the input vector, 0 for x = 0.
+ *   codes   uint32 words, d*bits/32 words per token, [B][H_kv][T_cap*d*bits/32]:
+ *             TQ_KEYS    per-token record: coordinate j's code is at bits
+ *                        [bits*j, bits*j+bits) of the record's LSB-first stream
+ *                        (stream bit k = bit k%32 of word k/32);
+ *             TQ_VALUES  8-token blocks (tokens 8m..8m+7), one record of
+ *                        8*d*bits/32 words per block: token 8m+i, coordinate j
+ *                        at stream bits [bits*(8j+i), ...); T_cap % 8 == 0.
+ *           code c stands for centroid c (centroids ascend; c = #{thresholds <= u*sqrt(d)}).
+ *   QJL     keys only: qjl_signs uint32 [B][H_kv][T_cap][d/32], bit i = [(S r)_i >= 0];
+ *           qjl_gamma float32 [B][H_kv][T_cap] = |r|, r = u - centroid/sqrt(d).
+ *   Pi, S   float32 d x d row-major on the device; y = Pi x.
+ */
+#ifndef TQ_H_
+#define TQ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define TQ_OK 0
+#define TQ_ERR_INVALID_ARGUMENT 1   /* null pointer, bad size, inconsistent shapes */
+#define TQ_ERR_UNSUPPORTED 2        /* valid but not implemented (d != 128, G > 16, ...) */
+#define TQ_ERR_ALIGNMENT 3          /* a device pointer breaks its alignment rule */
+#define TQ_ERR_WORKSPACE_TOO_SMALL 4
+#define TQ_ERR_DEVICE 5             /* a HIP call or kernel launch failed */
+
+/* element types of inputs */
+#define TQ_F32 0
+#define TQ_BF16 1
+
+/* tq_make_rotation kinds */
+#define TQ_MAT_HAAR 0       /* Pi: Haar-random orthogonal */
+#define TQ_MAT_GAUSSIAN 1   /* S: i.i.d. N(0,1), not orthogonalised */
+
+/* cache roles: decide the code layout */
+#define TQ_KEYS 0
+#define TQ_VALUES 1
+
+#define TQ_MAX_LEVELS 16
+
+/*
+ * One packed cache (all heads of one layer's keys, or of its values).
+ * Device pointers must be 16-byte aligned. centroids[] is held by value (host
+ * memory, inside this struct): the 2^bits levels of tq_make_codebook, in
+ * standard-normal units, each exactly representable in float16.
+ */
+typedef struct tq_cache {
+  int32_t role;        /* TQ_KEYS or TQ_VALUES */
+  int32_t bits;        /* 2, 3 or 4 bits per coordinate (the Lloyd-Max part) */
+  int32_t qjl;         /* 1: keys carry the QJL sign sketch; 0 otherwise */
+  int32_t d;           /* head dimension, 128 */
+  int64_t B;           /* batch rows */
+  int64_t H_kv;        /* KV heads */
+  int64_t T_cap;       /* token capacity per (row, head); multiple of 8 for values */
+  uint32_t* codes;     /* device, B*H_kv*T_cap*d*bits/32 words */
+  float* norms;        /* device, B*H_kv*T_cap */
+  uint32_t* qjl_signs; /* device, B*H_kv*T_cap*d/32 words, or NULL when qjl == 0 */
+  float* qjl_gamma;    /* device, B*H_kv*T_cap, or NULL when qjl == 0 */
+  const float* rot;    /* device Pi, d*d, row-major */
+  const float* qjl_proj; /* device S, d*d, or NULL when qjl == 0 */
+  float centroids[TQ_MAX_LEVELS];
+} tq_cache;
+
+/*
+ * Gaussian Lloyd-Max codebook (ai-accelerate.xyz TurboQuant article, section
+ * "TurboQuantの仕組み", step 1: optimal scalar quantization of near-Gaussian
+ * coordinates). Lloyd's iteration for N(0,1) with 2^bits cells from
+ * c_i = Phi^-1((i+1/2)/2^bits) until the largest change is below 1e-14, then
+ * symmetrised and rounded to float16 (nearest even). thresholds[i] is the exact
+ * midpoint of centroids[i] and centroids[i+1]; the middle one is +0.0.
+ * centroids: host, 2^bits floats; thresholds: host, 2^bits - 1 floats (may be NULL).
+ * bits in 1..4; d must be 128. Host only: no HIP call.
+ */
+int tq_make_codebook(int32_t bits, int32_t d, float* centroids, float* thresholds);
+
+/*
+ * Seeded d x d matrix, row-major float32, into host memory `out`.
+ * The stream is SplitMix64 (output k = finalizer(seed + k*0x9E3779B97F4A7C15),
+ * k = 1, 2, ...), uniforms ((z>>11)+0.5)*2^-53, Box-Muller normals (cos then
+ * sin per pair), filled row-major. TQ_MAT_HAAR: Q*diag(sign(diag R)) of the
+ * Householder QR of that matrix (the random orthogonal matrix of step 1 of the
+ * method); TQ_MAT_GAUSSIAN: the matrix itself (the QJL projection of step 2).
+ * Computed in double precision, rounded to float32. Host only: no HIP call.
+ */
+int tq_make_rotation(uint64_t seed, int32_t d, int32_t kind, float* out);
+
+/*
+ * Quantize T new tokens of every (row, head) into dst at token positions
+ * t_offset .. t_offset+T-1 (step 1, and step 2 for QJL keys).
+ * x: device, element (b, t, h, j) at x[b*stride_b + t*stride_t + h*stride_h + j]
+ *    (strides in elements, j contiguous), dtype TQ_F32 or TQ_BF16, 16-byte
+ *    aligned rows. Requires B == dst->B, H_kv == dst->H_kv, T >= 0,
+ *    0 <= t_offset, t_offset + T <= dst->T_cap. Value blocks that the range only
+ *    partly covers keep the bits of their other tokens. T == 0 is a no-op.
+ */
+int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t T, int64_t H_kv,
+                   int64_t stride_b, int64_t stride_t, int64_t stride_h,
+                   const tq_cache* dst, int64_t t_offset, void* hip_stream);
+
+/*
+ * Reconstruct tokens t0 .. t1-1 of every (row, head):
+ *   x_hat = n * Pi^T (c[code]/sqrt(d) [+ gamma*sqrt(pi/2)/d * S^T sigma]),
+ * sigma_i = 2*bit_i - 1 (QJL keys). out: device float32 [B][H_kv][t1-t0][d].
+ * Requires 0 <= t0 <= t1 <= src->T_cap.
+ */
+int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void* hip_stream);
+
+/*
+ * Decode attention of one query per head over the packed caches:
+ *   out[b][h] = sum_{t < ctx_len[b]} softmax_t(scale * q[b][h] . k_hat[b][h/G][t]) v_hat[b][h/G][t]
+ * computed in the rotated domain (q' = Pi_K q once; scores from key codebook
+ * levels times key norms, plus the QJL term for QJL keys; values summed in the
+ * rotated domain; out = Pi_V^T o'). G = H_q / H_kv query heads share KV head
+ * h / G. Work is split over the context (n_split chunks per (row, KV head),
+ * 0 = chosen by the library) and merged in a fixed order, so results do not
+ * depend on timing.
+ *   q:        device [B][H_q][d], TQ_F32 or TQ_BF16
+ *   ctx_lens: device int32 [B] (each in 0..T) or NULL (= T for every row);
+ *             a row with ctx_len 0 gets a zero output
+ *   T:        largest context length, T <= k->T_cap and T <= v->T_cap
+ *   scale:    score scale; <= 0 selects 1/sqrt(d)
+ *   out:      device float32 [B][H_q][d]
+ *   workspace: device, at least tq_decode_workspace_bytes(...) bytes, 256-byte aligned
+ * Requires k->role == TQ_KEYS, v->role == TQ_VALUES, equal B and H_kv,
+ * H_q % H_kv == 0 and G <= 16. Value norms must stay below 7e5 (float16
+ * range of the weighted value operand).
+ */
+int tq_decode_attention(const tq_cache* k, const tq_cache* v,
+                        const void* q, int32_t q_dtype, int64_t H_q,
+                        const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
+                        float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Number of context chunks tq_decode_attention uses for these sizes (n_split 0 = auto). */
+int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split);
+
+/* Workspace bytes tq_decode_attention needs; 0 for invalid sizes. */
+size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
+                                 int32_t n_split, int32_t k_qjl);
+
+/* Static text for a status code. */
+const char* tq_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TQ_H_ */

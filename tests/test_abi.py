@@ -1,0 +1,174 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared symbol,
+its host-only functions agree with the oracle, and every argument error is
+reported before any HIP call."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_attention_tq_amd as tq
+from oracle import codebook as ocb
+from oracle import rotation as orot
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "tq.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_symbols()
+    assert set(names) == set(tq.EXPORTS)
+    for n in names:
+        assert hasattr(tq.lib(), n), n
+
+
+def test_struct_layout_matches_header():
+    # 4 x int32, 3 x int64, 6 pointers, 16 floats
+    assert ctypes.sizeof(tq.TQCache) == 16 + 24 + 48 + 64
+    assert tq.TQCache.centroids.offset == 88
+
+
+def test_status_strings():
+    for code in range(6):
+        assert tq.status_string(code)
+    assert tq.status_string(0) == "ok"
+    assert "unknown" in tq.status_string(99)
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_codebook_matches_oracle(bits):
+    c, t = tq.make_codebook(bits)
+    oc, ot = ocb.canonical(bits)
+    assert np.array_equal(c.astype(np.float64), oc)
+    assert np.array_equal(t.astype(np.float64), ot)
+    assert not np.signbit(t[len(t) // 2])
+
+
+def test_codebook_rejects_bad_arguments():
+    lib = tq.lib()
+    c = np.zeros(16, dtype=np.float32)
+    assert lib.tq_make_codebook(0, 128, c.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_codebook(5, 128, c.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_codebook(3, 128, None, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_codebook(3, 64, c.ctypes.data, None) == tq.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("seed", [42, 7, 2**63 + 5])
+def test_rotation_matches_oracle(seed):
+    P = tq.make_rotation(seed, tq.HAAR).astype(np.float64)
+    assert np.abs(P - orot.haar_rotation(seed, 128)).max() <= 1e-6
+    assert np.abs(P.T @ P - np.eye(128)).max() <= 1e-5
+    S = tq.make_rotation(seed, tq.GAUSSIAN).astype(np.float64)
+    assert np.abs(S - orot.qjl_projection(seed, 128)).max() <= 1e-6
+
+
+def test_rotation_rejects_bad_arguments():
+    lib = tq.lib()
+    out = np.zeros((128, 128), dtype=np.float32)
+    assert lib.tq_make_rotation(1, 128, 7, out.ctypes.data) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_rotation(1, 128, 0, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_rotation(1, 96, 0, out.ctypes.data) == tq.ERR_UNSUPPORTED
+
+
+def test_decode_planning():
+    # every chunk is a multiple of the 32-token step and the chunks cover T
+    for B, H, T in [(1, 8, 32768), (32, 8, 32768), (4, 4, 131072), (1, 1, 1024), (2, 3, 1), (1, 1, 0)]:
+        n = tq.decode_splits(B, H, T)
+        assert n >= 1
+        assert tq.decode_workspace_bytes(B, 4 * H, H, T) > 0
+    assert tq.decode_splits(1, 1, 1024, 3) == 3
+    assert tq.decode_splits(1, 1, 1024, 100000) == 32      # chunks never go below 32 tokens
+    assert tq.decode_workspace_bytes(1, 7, 2, 100) == 0     # H_q % H_kv != 0
+    assert tq.decode_workspace_bytes(1, 34, 2, 100) == 0    # G > 16
+
+
+# ------------------------------------------------------------------------
+# argument validation without a device: fake (never dereferenced) pointers
+
+FAKE = 1 << 20   # 16-byte aligned, never touched
+
+
+def _cache(role=tq.KEYS, bits=3, qjl=0, B=2, H=2, T_cap=64, **kw):
+    s = tq.TQCache()
+    s.role, s.bits, s.qjl, s.d = role, bits, qjl, 128
+    s.B, s.H_kv, s.T_cap = B, H, T_cap
+    s.codes = s.norms = s.rot = FAKE
+    if qjl:
+        s.qjl_signs = s.qjl_gamma = s.qjl_proj = FAKE
+    c, _ = tq.make_codebook(bits if 1 <= bits <= 4 else 3)
+    for i, v in enumerate(c):
+        s.centroids[i] = float(v)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def _quant(s, x=FAKE, dtype=tq.BF16, B=2, T=4, H=2, strides=(4 * 2 * 128, 2 * 128, 128), t_offset=0):
+    return tq.lib().tq_quantize_kv(x, dtype, B, T, H, *strides, ctypes.byref(s), t_offset, None)
+
+
+def test_quantize_validation_paths():
+    assert _quant(_cache(bits=5)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(bits=1)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(d=64)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(role=7)) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(role=tq.VALUES, qjl=1)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(role=tq.VALUES, T_cap=60)) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(codes=None)) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(qjl=1, qjl_signs=None)) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(codes=FAKE + 4)) == tq.ERR_ALIGNMENT
+    assert _quant(_cache(), x=None) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), x=FAKE + 2) == tq.ERR_ALIGNMENT
+    assert _quant(_cache(), strides=(4 * 2 * 128, 2 * 128, 100)) == tq.ERR_ALIGNMENT
+    assert _quant(_cache(), dtype=9) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), B=3) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), H=1) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), t_offset=62) == tq.ERR_INVALID_ARGUMENT       # 62 + 4 > T_cap
+    assert _quant(_cache(), t_offset=-1) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), T=-1) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(_cache(), T=0) == tq.OK                                   # no-op, no launch
+    s = _cache()
+    s.centroids[3] = 0.1   # not float16-exact
+    assert _quant(s) == tq.ERR_INVALID_ARGUMENT
+    s = _cache()
+    s.centroids[2], s.centroids[3] = s.centroids[3], s.centroids[2]   # not ascending
+    assert _quant(s) == tq.ERR_INVALID_ARGUMENT
+
+
+def _decode(k, v, q=FAKE, H_q=8, T=64, scale=0.0, n_split=0, out=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=tq.BF16):
+    return tq.lib().tq_decode_attention(ctypes.byref(k), ctypes.byref(v), q, dtype, H_q, None, T, scale, n_split,
+                                        out, ws, ws_bytes, None)
+
+
+def test_decode_validation_paths():
+    K, V = _cache(), _cache(role=tq.VALUES)
+    assert _decode(V, V) == tq.ERR_INVALID_ARGUMENT                 # keys must be keys
+    assert _decode(K, K) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, _cache(role=tq.VALUES, B=3)) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, V, H_q=7) == tq.ERR_INVALID_ARGUMENT          # H_q % H_kv
+    assert _decode(K, V, H_q=34) == tq.ERR_UNSUPPORTED              # G = 17 > 16
+    assert _decode(K, V, T=65) == tq.ERR_INVALID_ARGUMENT           # T > T_cap
+    assert _decode(K, V, q=None) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, V, out=FAKE + 4) == tq.ERR_ALIGNMENT
+    assert _decode(K, V, ws_bytes=16) == tq.ERR_WORKSPACE_TOO_SMALL
+    assert _decode(K, V, ws=None) == tq.ERR_WORKSPACE_TOO_SMALL
+    assert _decode(K, V, ws=FAKE + 16) == tq.ERR_ALIGNMENT
+    assert _decode(K, V, scale=float("nan")) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, V, n_split=-1) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, V, dtype=5) == tq.ERR_INVALID_ARGUMENT
+
+
+def test_dequantize_validation_paths():
+    lib = tq.lib()
+    K = _cache()
+    assert lib.tq_dequantize(ctypes.byref(K), 5, 4, FAKE, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_dequantize(ctypes.byref(K), 0, 65, FAKE, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_dequantize(ctypes.byref(K), 0, 8, None, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_dequantize(ctypes.byref(K), 0, 8, FAKE + 8, None) == tq.ERR_ALIGNMENT
+    assert lib.tq_dequantize(ctypes.byref(K), 3, 3, FAKE, None) == tq.OK

@@ -1,0 +1,260 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, element by
+element, on seeded workloads scaled so the oracle finishes in seconds while still
+spanning many 32-token steps, several context chunks and ragged tails."""
+import math
+
+import numpy as np
+import pytest
+
+import tq_synth
+from tqhelp import (BOUNDARY, TOL_ATTN, OracleModel, code_mismatch, device_inputs, device_queries, log,
+                    rel_l2, upload_oracle_cache)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+W = tq_synth.WORKLOADS
+CASES = {
+    "tiny": W["tiny"],                                                  # fp32, G = 16
+    "llama8b_T2000": W["llama8b"].scaled(T=2000),                       # ragged T, G = 4
+    "qwen_k4v2": W["qwen"].scaled(B=2, T=1500),                         # G = 7, K4/V2
+    "qwen_k4v4": W["qwen"].scaled(B=2, T=1024, v_bits=4),
+    "qjl_k2v3": W["qjl"].scaled(B=2, T=1024),                           # QJL keys
+    "stress70b_B2": W["stress70b"].scaled(B=2, T=4096),                 # G = 8
+}
+
+
+@pytest.fixture(scope="module")
+def tq():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_attention_tq_amd as lib
+    return lib
+
+
+def tcap(T):
+    return (T + 7) // 8 * 8
+
+
+def _lib_caches(tq, w, T_cap):
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, qjl=bool(w.k_qjl))
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap)
+    return kc, vc
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_quantize_codes_match_oracle(tq, name):
+    w = CASES[name]
+    T_cap = tcap(w.T)
+    log(f"quantize {name}: B={w.B} H_kv={w.H_kv} T={w.T} bits K{w.k_bits}{'+qjl' if w.k_qjl else ''}/V{w.v_bits}")
+    model = OracleModel(w)
+    kc, vc = _lib_caches(tq, w, T_cap)
+    tq.quantize_kv(device_inputs(w, "k"), kc)
+    tq.quantize_kv(device_inputs(w, "v"), vc)
+    torch.cuda.synchronize()
+    for which, cache, bits, thr in (("k", kc, w.k_bits, model.tK), ("v", vc, w.v_bits, model.tV)):
+        heads = model.heads(which)
+        codes = cache.codes.cpu().numpy()
+        norms = cache.norms.cpu().numpy()
+        tot = out = n = 0
+        for (b, h), ref in heads.items():
+            m, mo, c = code_mismatch(which, codes[b, h], ref, bits, thr, w.T)
+            tot, out, n = tot + m, out + mo, n + c
+            nr = norms[b, h, :w.T].astype(np.float64)
+            want = ref["norm"].astype(np.float64)
+            assert np.all(np.abs(nr - want) <= 1e-6 * np.maximum(want, 1e-30)), (which, b, h)
+        log(f"  {which}: {tot}/{n} codes differ ({tot / n:.2e}); outside the {BOUNDARY:g} band: {out}")
+        assert out == 0
+        if which == "k" and w.k_qjl:
+            signs = cache.signs.cpu().numpy().view(np.uint32)
+            gamma = cache.gamma.cpu().numpy()
+            from oracle import quantize as oq
+            bad_total = 0
+            for (b, h), ref in heads.items():
+                got = oq.unpack_signs(signs[b, h, :w.T], 128)
+                flip_vec = np.any(oq.boundary_distance(ref["u"], thr, 128) < BOUNDARY, axis=1)
+                bad = (got != ref["signs"]) & ~(np.abs(ref["z"]) < BOUNDARY) & ~flip_vec[:, None]
+                bad_total += int(bad.sum())
+                g = gamma[b, h, :w.T].astype(np.float64)
+                gw = ref["gamma"].astype(np.float64)
+                ok = np.abs(g - gw) <= 1e-5 * gw + 1e-7
+                assert np.all(ok | flip_vec), (b, h)
+            log(f"  qjl signs differing outside the band: {bad_total}")
+            assert bad_total == 0
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_on_oracle_cache_matches_oracle(tq, name):
+    """Decode kernel parity: same packed bytes on both sides."""
+    w = CASES[name]
+    T_cap = tcap(w.T)
+    log(f"decode {name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} T={w.T}")
+    model = OracleModel(w)
+    kh, vh = model.heads("k"), model.heads("v")
+    kc = upload_oracle_cache(tq, model, "k", kh, T_cap)
+    vc = upload_oracle_cache(tq, model, "v", vh, T_cap)
+    q = device_queries(w)
+    out = tq.decode_attention(kc, vc, q, T=w.T).cpu().numpy()
+    qn = tq_synth.queries_full(w)
+    ref = np.zeros_like(out, dtype=np.float64)
+    for b in range(w.B):
+        for kv in range(w.H_kv):
+            ref[b, kv * w.G:(kv + 1) * w.G] = model.decode(kh, vh, qn, b, kv)
+    err = rel_l2(out, ref)
+    worst = max(rel_l2(out[b, h], ref[b, h]) for b in range(w.B) for h in range(w.H_q))
+    log(f"  rel L2 {err:.3e} (worst head {worst:.3e})")
+    assert err <= TOL_ATTN
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_end_to_end_matches_oracle(tq, name):
+    """GPU quantize + GPU decode (library rotation and codebook) against the oracle
+    quantize + oracle decode of the same inputs."""
+    w = CASES[name]
+    T_cap = tcap(w.T)
+    log(f"end-to-end {name}")
+    model = OracleModel(w)
+    kc, vc = _lib_caches(tq, w, T_cap)
+    tq.quantize_kv(device_inputs(w, "k"), kc)
+    tq.quantize_kv(device_inputs(w, "v"), vc)
+    out = tq.decode_attention(kc, vc, device_queries(w), T=w.T).cpu().numpy()
+    kh, vh = model.heads("k"), model.heads("v")
+    qn = tq_synth.queries_full(w)
+    ref = np.zeros_like(out, dtype=np.float64)
+    for b in range(w.B):
+        for kv in range(w.H_kv):
+            ref[b, kv * w.G:(kv + 1) * w.G] = model.decode(kh, vh, qn, b, kv)
+    err = rel_l2(out, ref)
+    log(f"  rel L2 {err:.3e}")
+    assert err <= TOL_ATTN
+
+
+@pytest.mark.parametrize("name", ["tiny", "qwen_k4v2", "qjl_k2v3"])
+def test_dequantize_matches_oracle(tq, name):
+    from oracle import attention as oa
+    w = CASES[name]
+    T_cap = tcap(w.T)
+    log(f"dequantize {name}")
+    model = OracleModel(w)
+    for which in ("k", "v"):
+        heads = model.heads(which)
+        cache = upload_oracle_cache(tq, model, which, heads, T_cap)
+        got = tq.dequantize(cache, 0, w.T).cpu().numpy()
+        cos = []
+        for (b, h), r in heads.items():
+            c = model.cK if which == "k" else model.cV
+            qj = which == "k" and w.k_qjl
+            want = oa.dequantize_head(r["codes"], r["norm"], model.Pi, c, 128,
+                                      r.get("signs") if qj else None, r.get("gamma") if qj else None,
+                                      model.S if qj else None)
+            assert rel_l2(got[b, h], want) <= 1e-5
+            cos.append(oa.cosine(tq_synth.kv_head(w, which, b, h), got[b, h]).mean())
+        log(f"  {which}: mean cosine {np.mean(cos):.4f}")
+
+
+def test_dequantize_window(tq):
+    w = CASES["llama8b_T2000"]
+    model = OracleModel(w)
+    heads = model.heads("v")
+    cache = upload_oracle_cache(tq, model, "v", heads, tcap(w.T))
+    full = tq.dequantize(cache, 0, w.T).cpu().numpy()
+    part = tq.dequantize(cache, 37, 1501).cpu().numpy()
+    assert np.array_equal(full[:, :, 37:1501], part)
+
+
+def test_split_invariance_and_determinism(tq):
+    w = CASES["stress70b_B2"]
+    T_cap = tcap(w.T)
+    log("split invariance stress70b_B2")
+    kc, vc = _lib_caches(tq, w, T_cap)
+    tq.quantize_kv(device_inputs(w, "k"), kc)
+    tq.quantize_kv(device_inputs(w, "v"), vc)
+    q = device_queries(w)
+    base = tq.decode_attention(kc, vc, q, T=w.T)
+    again = tq.decode_attention(kc, vc, q, T=w.T)
+    assert torch.equal(base, again)
+    for ns in (1, 3, 7, 64, 128):
+        o = tq.decode_attention(kc, vc, q, T=w.T, n_split=ns)
+        assert rel_l2(o.cpu().numpy(), base.cpu().numpy()) <= 1e-5, ns
+
+
+def test_ragged_context_lengths(tq):
+    w = CASES["stress70b_B2"].scaled(B=4)
+    T_cap = tcap(w.T)
+    ctx = [w.T, 1000, 0, 33]
+    log(f"ragged contexts {ctx}")
+    model = OracleModel(w)
+    kh, vh = model.heads("k"), model.heads("v")
+    kc = upload_oracle_cache(tq, model, "k", kh, T_cap)
+    vc = upload_oracle_cache(tq, model, "v", vh, T_cap)
+    cl = torch.tensor(ctx, dtype=torch.int32, device="cuda")
+    out = tq.decode_attention(kc, vc, device_queries(w), ctx_lens=cl, T=w.T).cpu().numpy()
+    qn = tq_synth.queries_full(w)
+    for b in range(w.B):
+        ref = np.concatenate([model.decode(kh, vh, qn, b, kv, ctx=ctx[b]) for kv in range(w.H_kv)])
+        if ctx[b] == 0:
+            assert np.all(out[b] == 0)
+        else:
+            assert rel_l2(out[b], ref) <= TOL_ATTN, b
+
+
+def test_append_in_pieces_matches_bulk(tq):
+    """Writing tokens in pieces (offsets not multiples of 8, single tokens) gives
+    the same bytes as one bulk call, for both layouts."""
+    w = CASES["qjl_k2v3"].scaled(T=300)
+    T_cap = tcap(w.T)
+    log("append in pieces")
+    xk, xv = device_inputs(w, "k"), device_inputs(w, "v")
+    kb, vb = _lib_caches(tq, w, T_cap)
+    tq.quantize_kv(xk, kb)
+    tq.quantize_kv(xv, vb)
+    kp, vp = _lib_caches(tq, w, T_cap)
+    cuts = [0, 5, 6, 7, 8, 77, 131, 299, 300]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        tq.quantize_kv(xk[:, a:b], kp, t_offset=a)
+        tq.quantize_kv(xv[:, a:b], vp, t_offset=a)
+    torch.cuda.synchronize()
+    assert torch.equal(kb.codes, kp.codes) and torch.equal(kb.norms, kp.norms)
+    assert torch.equal(kb.signs, kp.signs) and torch.equal(kb.gamma, kp.gamma)
+    assert torch.equal(vb.codes, vp.codes) and torch.equal(vb.norms, vp.norms)
+
+
+def test_value_block_partial_write_keeps_neighbours(tq):
+    """A partial value block keeps the bits of tokens outside the written range."""
+    w = CASES["stress70b_B2"].scaled(T=64)
+    x = device_inputs(w, "v")
+    vc = tq.Cache(tq.VALUES, 3, w.B, w.H_kv, 64)
+    vc.codes.fill_(-1)
+    tq.quantize_kv(x[:, 10:13], vc, t_offset=10)
+    ref = tq.Cache(tq.VALUES, 3, w.B, w.H_kv, 64)
+    tq.quantize_kv(x, ref)
+    from tqhelp import unpack_head
+    got = unpack_head("v", vc.codes[0, 0].cpu().numpy(), 3, 64)
+    want = unpack_head("v", ref.codes[0, 0].cpu().numpy(), 3, 64)
+    assert np.array_equal(got[10:13], want[10:13])
+    assert np.all(got[:10] == 7) and np.all(got[13:] == 7)
+
+
+def test_degenerate_inputs(tq):
+    """Zero vectors (code 2^(b-1), norm 0), a single token, T = 0."""
+    w = CASES["stress70b_B2"].scaled(B=1, H_q=8, H_kv=1, T=8)
+    kc, vc = _lib_caches(tq, w, 8)
+    z = torch.zeros((1, 8, 1, 128), dtype=torch.bfloat16, device="cuda")
+    tq.quantize_kv(z, kc)
+    tq.quantize_kv(z, vc)
+    from tqhelp import unpack_head
+    assert np.all(unpack_head("k", kc.codes[0, 0].cpu().numpy(), 3, 8) == 4)
+    assert np.all(unpack_head("v", vc.codes[0, 0].cpu().numpy(), 3, 8) == 4)
+    assert torch.all(kc.norms == 0)
+    q = device_queries(w)
+    out = tq.decode_attention(kc, vc, q, T=8)
+    assert torch.all(out == 0)
+    out0 = tq.decode_attention(kc, vc, q, T=0)
+    assert torch.all(out0 == 0)
+    # single token: output is that token's reconstruction
+    x = device_inputs(w, "v")
+    tq.quantize_kv(x[:, :1], vc)
+    tq.quantize_kv(device_inputs(w, "k")[:, :1], kc)
+    o1 = tq.decode_attention(kc, vc, q, T=1).cpu().numpy()
+    v0 = tq.dequantize(vc, 0, 1).cpu().numpy()[0, 0, 0]
+    assert np.allclose(o1[0], np.repeat(v0[None], 8, axis=0), rtol=1e-5, atol=1e-6)

@@ -1,0 +1,130 @@
+"""Test glue between the seeded workloads, the CPU oracle and the GPU library."""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import tq_synth
+from oracle import attention as oa
+from oracle import codebook as ocb
+from oracle import quantize as oq
+from oracle import rotation as orot
+
+D = 128
+BOUNDARY = 1e-6      # decision-boundary band (unit domain) inside which codes may differ
+TOL_ATTN = 2e-3      # relative L2 tolerance of decode outputs
+
+
+def log(msg: str):
+    print(f"[case] {msg}", flush=True)
+
+
+def rel_l2(a, b) -> float:
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+class OracleModel:
+    """Oracle rotation, projection and codebooks of a workload."""
+
+    def __init__(self, w: tq_synth.Workload):
+        self.w = w
+        self.Pi = orot.haar_rotation(tq_synth.ROT_SEED, D)
+        self.S = orot.qjl_projection(tq_synth.QJL_SEED, D) if w.k_qjl else None
+        self.cK, self.tK = ocb.canonical(w.k_bits)
+        self.cV, self.tV = ocb.canonical(w.v_bits)
+
+    def quantize(self, which: str, X: np.ndarray) -> dict:
+        if which == "k":
+            return oq.quantize_head(X, self.Pi, self.cK, self.tK, S=self.S)
+        return oq.quantize_head(X, self.Pi, self.cV, self.tV)
+
+    def heads(self, which: str, bs=None, hs=None) -> dict:
+        w = self.w
+        out = {}
+        for b in (range(w.B) if bs is None else bs):
+            for h in (range(w.H_kv) if hs is None else hs):
+                out[(b, h)] = self.quantize(which, tq_synth.kv_head(w, which, b, h))
+        return out
+
+    def decode(self, kh: dict, vh: dict, q: np.ndarray, b: int, kv: int, ctx=None) -> np.ndarray:
+        w = self.w
+        G = w.G
+        qs = np.asarray(q[b, kv * G:(kv + 1) * G], dtype=np.float64)
+        return oa.attend_rotated(qs, kh[(b, kv)], vh[(b, kv)], self.Pi, self.Pi, self.cK, self.cV, D,
+                                 1.0 / math.sqrt(D), ctx_len=ctx, S=self.S)
+
+
+def pack_head(role: str, codes: np.ndarray, bits: int, T_cap: int) -> np.ndarray:
+    """Oracle-packed words of one head padded to T_cap tokens (uint32)."""
+    full = np.zeros((T_cap, D), dtype=np.int64)
+    full[:codes.shape[0]] = codes
+    if role == "k":
+        return oq.pack_keys(full, bits).reshape(-1)
+    return oq.pack_values(full, bits).reshape(-1)
+
+
+def unpack_head(role: str, words: np.ndarray, bits: int, T: int) -> np.ndarray:
+    words = np.asarray(words).view(np.uint32)
+    W = D * bits // 32
+    if role == "k":
+        return oq.unpack_keys(words.reshape(-1, W), bits, D)[:T]
+    return oq.unpack_values(words.reshape(-1, 8 * W), bits, D)[:T]
+
+
+def code_mismatch(role, gpu_words, ref: dict, bits: int, thresholds, T: int):
+    """(mismatches, mismatches outside the boundary band, coordinates compared)."""
+    got = unpack_head(role, gpu_words, bits, T)
+    want = ref["codes"][:T]
+    bad = got != want
+    exempt = oq.boundary_distance(ref["u"][:T], thresholds, D) < BOUNDARY
+    return int(bad.sum()), int((bad & ~exempt).sum()), bad.size
+
+
+def upload_oracle_cache(tq, model: OracleModel, which: str, heads: dict, T_cap: int, device="cuda"):
+    """A device Cache holding the oracle's packed cache (oracle rotation and codebook)."""
+    import torch
+
+    w = model.w
+    role = tq.KEYS if which == "k" else tq.VALUES
+    bits = w.k_bits if which == "k" else w.v_bits
+    qjl = which == "k" and w.k_qjl
+    cache = tq.Cache(role, bits, w.B, w.H_kv, T_cap, device=device, rot=model.Pi.astype(np.float32),
+                     proj=model.S.astype(np.float32) if qjl else None, qjl=qjl,
+                     centroids=(model.cK if which == "k" else model.cV).astype(np.float32))
+    codes = np.zeros((w.B, w.H_kv, T_cap * D * bits // 32), dtype=np.uint32)
+    norms = np.zeros((w.B, w.H_kv, T_cap), dtype=np.float32)
+    signs = np.zeros((w.B, w.H_kv, T_cap, 4), dtype=np.uint32) if qjl else None
+    gamma = np.zeros((w.B, w.H_kv, T_cap), dtype=np.float32) if qjl else None
+    for (b, h), r in heads.items():
+        T = r["codes"].shape[0]
+        codes[b, h] = pack_head(which, r["codes"], bits, T_cap)
+        norms[b, h, :T] = r["norm"]
+        if qjl:
+            signs[b, h, :T] = oq.pack_signs(r["signs"])
+            gamma[b, h, :T] = r["gamma"]
+    cache.codes.copy_(torch.from_numpy(codes.view(np.int32)))
+    cache.norms.copy_(torch.from_numpy(norms))
+    if qjl:
+        cache.signs.copy_(torch.from_numpy(signs.view(np.int32)))
+        cache.gamma.copy_(torch.from_numpy(gamma))
+    return cache
+
+
+def device_inputs(w: tq_synth.Workload, which: str, device="cuda"):
+    """Workload K or V as a device tensor [B, T, H_kv, d] in the workload dtype."""
+    import torch
+
+    x = torch.from_numpy(tq_synth.kv_full(w, which))
+    x = x.to(torch.bfloat16) if w.dtype == "bf16" else x
+    return x.to(device)
+
+
+def device_queries(w: tq_synth.Workload, device="cuda"):
+    import torch
+
+    q = torch.from_numpy(tq_synth.queries_full(w))
+    q = q.to(torch.bfloat16) if w.dtype == "bf16" else q
+    return q.to(device).contiguous()
