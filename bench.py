@@ -1,0 +1,243 @@
+"""Benchmark of the TurboQuant packed-KV decode path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress70b]
+
+One step is one pass of the whole hot path for one new token per batch row:
+quantize the new token's key and value vectors of every (row, KV head) into the
+packed caches (tq_quantize_kv, append at t = T-1), then decode attention of all
+query heads over the T-token packed caches (tq_decode_attention). Inputs are
+resident in HBM before timing starts. Prints one JSON line on stdout.
+
+Extra fields: `roofline` (decode launch group vs the HBM peak), `cpu_baseline`
+(the CPU oracle on a bounded sample of the same step, scaled to tokens/s),
+`quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+METRIC = "decode attention tokens/s and packed-KV HBM GB/s (% of peak) at 32k ctx, 3-bit"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
+F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, AMD published
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def decode_bytes(w, T):
+    """Algorithmic bytes of one decode call: packed K and V (codes + fp32 norms, QJL
+    signs + gamma), the query in, the fp32 output, the two rotations."""
+    d = w.d
+    wk = d * w.k_bits // 8 + 4 + (d // 8 + 4 if w.k_qjl else 0)
+    wv = d * w.v_bits // 8 + 4
+    qb = 2 if w.dtype == "bf16" else 4
+    return w.B * w.H_kv * T * (wk + wv) + w.B * w.H_q * d * (qb + 4) + 2 * d * d * 4
+
+
+def quantize_bytes(w, ntok, which):
+    d = w.d
+    bits = w.k_bits if which == "k" else w.v_bits
+    inb = 2 if w.dtype == "bf16" else 4
+    extra = (d // 8 + 4) if (which == "k" and w.k_qjl) else 0
+    return w.B * w.H_kv * ntok * (d * inb + d * bits // 8 + 4 + extra)
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The CPU oracle, as it stands, on (row, KV head) slices of the same step:
+    unpack the slice's packed key and value caches, quantize one new token of
+    each, decode the G query heads over T tokens. Scaled to decode tokens/s of
+    the whole batch."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import tq_synth
+    from oracle import attention as oa
+    from oracle import codebook as ocb
+    from oracle import quantize as oq
+    from oracle import rotation as orot
+
+    Pi = orot.haar_rotation(tq_synth.ROT_SEED, w.d)
+    cK, tK = ocb.canonical(w.k_bits)
+    cV, tV = ocb.canonical(w.v_bits)
+    step_times = []
+    slices = 0
+    t_setup = time.perf_counter()
+    while True:
+        b, h = divmod(slices, w.H_kv)
+        if b >= w.B:
+            break
+        K = tq_synth.kv_head(w, "k", b, h)
+        V = tq_synth.kv_head(w, "v", b, h)
+        kq = oq.quantize_head(K, Pi, cK, tK)
+        vq = oq.quantize_head(V, Pi, cV, tV)
+        kwords = oq.pack_keys(kq["codes"], w.k_bits)
+        vwords = oq.pack_values(vq["codes"], w.v_bits)
+        q = tq_synth.queries(w, b)[h * w.G:(h + 1) * w.G]
+        t0 = time.perf_counter()
+        new = oq.quantize_head(K[-1:], Pi, cK, tK), oq.quantize_head(V[-1:], Pi, cV, tV)
+        k = {"codes": oq.unpack_keys(kwords, w.k_bits, w.d), "norm": kq["norm"]}
+        v = {"codes": oq.unpack_values(vwords, w.v_bits, w.d), "norm": vq["norm"]}
+        k["codes"][-1], v["codes"][-1] = new[0]["codes"][0], new[1]["codes"][0]
+        oa.attend_rotated(q, k, v, Pi, Pi, cK, cV, w.d, 1.0 / math.sqrt(w.d))
+        step_times.append(time.perf_counter() - t0)
+        slices += 1
+        if sum(step_times) >= budget_s or time.perf_counter() - t_setup > 3 * budget_s:
+            break
+    per_slice = sum(step_times) / len(step_times)
+    full_step = per_slice * w.B * w.H_kv
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    return {
+        "value": w.B / full_step,
+        "unit": "tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{slices} of {w.B * w.H_kv} (row, KV head) slices of the same step: unpack the packed "
+                   f"K/V slice ({w.T} tokens), quantize 1 new token each, rotated-domain decode of "
+                   f"{w.G} query heads; {per_slice * 1e3:.1f} ms per slice, scaled by {w.B * w.H_kv} slices "
+                   f"to the batch of {w.B} rows"),
+        "host_cpus": len(os.sched_getaffinity(0)),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="stress70b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--prefill-iters", type=int, default=3)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import decode_attention_tq_amd as tq
+    import tq_synth
+
+    w = tq_synth.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    T = w.T
+    T_cap = (T + 7) // 8 * 8
+
+    log(f"[bench] workload {w.name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} T={T} K{w.k_bits}/V{w.v_bits}")
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl))
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev)
+
+    # ---- prefill: bulk quantization of the whole context (also builds the caches)
+    xk = tq_synth.torch_kv(w, "k", dev)
+    xv = tq_synth.torch_kv(w, "v", dev)
+    torch.cuda.synchronize()
+    pre_ms = []
+    for it in range(args.prefill_iters + 1):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.quantize_kv(xk, kc)
+        tq.quantize_kv(xv, vc)
+        e1.record()
+        torch.cuda.synchronize()
+        if it > 0:
+            pre_ms.append(e0.elapsed_time(e1))
+    pre = sum(pre_ms) / len(pre_ms)
+    ntok = w.B * w.H_kv * T * 2
+    qbytes = quantize_bytes(w, T, "k") + quantize_bytes(w, T, "v")
+    # algorithmic rotation flops (y = Pi x per vector, plus S r per QJL key); the MFMA
+    # issues 2 fp16 passes per product (hi and lo halves of Pi), 3 for QJL's S r
+    qflops = 2 * w.d * w.d * ntok + (2 * w.d * w.d * w.B * w.H_kv * T if w.k_qjl else 0)
+    issued = 2 * 2 * w.d * w.d * ntok + (3 * 2 * w.d * w.d * w.B * w.H_kv * T if w.k_qjl else 0)
+    new_k = xk[:, T - 1:T].contiguous()
+    new_v = xv[:, T - 1:T].contiguous()
+    del xk, xv
+    torch.cuda.empty_cache()
+
+    # ---- decode steps
+    qs = [tq_synth.torch_queries(w, dev, seed_offset=i) for i in range(4)]
+    out = torch.empty((w.B, w.H_q, w.d), dtype=torch.float32, device=dev)
+    ws = tq.Workspace(tq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, T, 0, w.k_qjl), dev)
+
+    def step(i):
+        tq.quantize_kv(new_k, kc, t_offset=T - 1)
+        tq.quantize_kv(new_v, vc, t_offset=T - 1)
+        tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+            torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        a, b, c = evs[i]
+        a.record()
+        tq.quantize_kv(new_k, kc, t_offset=T - 1)
+        tq.quantize_kv(new_v, vc, t_offset=T - 1)
+        b.record()
+        tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
+        c.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    dec_ms = sum(b.elapsed_time(c) for a, b, c in evs) / args.steps
+    app_ms = sum(a.elapsed_time(b) for a, b, c in evs) / args.steps
+    dbytes = decode_bytes(w, T)
+    achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    log(f"[bench] step {ms_step * 1e3:.1f} us (append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us); "
+        f"decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
+
+    # calibration copy of known size for the rocprofv3 byte counters (256 MiB read + write)
+    cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
+    cal2 = torch.empty_like(cal)
+    cal2.copy_(cal)
+    torch.cuda.synchronize()
+    del cal, cal2
+
+    res = {
+        "metric": METRIC,
+        "value": w.B / (ms_step * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d, "T": T,
+                   "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input_dtype": w.dtype,
+                   "step": "quantize 1 new K,V token per (row, KV head) + decode attention over T tokens",
+                   "n_split": tq.decode_splits(w.B, w.H_kv, T)},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "tq_decode_attention launch group (rotate_query + decode_scan + combine)",
+                     "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
+        "decode": {"us": dec_ms * 1e3, "kv_tokens_per_s": w.B * T / (dec_ms * 1e-3),
+                   "tokens_per_s": w.B / (dec_ms * 1e-3), "append_us": app_ms * 1e3},
+        "quantize_prefill": {"ms": pre, "vectors": ntok, "GB_s": qbytes / (pre * 1e-3) / 1e9,
+                             "hbm_frac": qbytes / (pre * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "rotation_TFLOP_s": qflops / (pre * 1e-3) / 1e12,
+                             "mfma_issued_TFLOP_s": issued / (pre * 1e-3) / 1e12,
+                             "mfma_frac": issued / (pre * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -57,20 +57,28 @@ class TQCache(ctypes.Structure):
 
 _P = ctypes.c_void_p
 _I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_float
-_lib.tq_make_codebook.argtypes = [_I32, _I32, _P, _P]
-_lib.tq_make_rotation.argtypes = [_U64, _I32, _I32, _P]
-_lib.tq_quantize_kv.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache), _I64, _P]
-_lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
-_lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P, _I64,
-                                     _F, _I32, _P, _P, ctypes.c_size_t, _P]
-_lib.tq_decode_splits.argtypes = [_I64, _I64, _I64, _I32]
-_lib.tq_decode_splits.restype = _I32
-_lib.tq_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32, _I32]
-_lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
-_lib.tq_status_string.argtypes = [ctypes.c_int]
-_lib.tq_status_string.restype = ctypes.c_char_p
-for _name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
-    getattr(_lib, _name).restype = ctypes.c_int
+
+
+def _bind(lib):
+    """Declare the C-ABI signatures on a loaded libtq."""
+    lib.tq_make_codebook.argtypes = [_I32, _I32, _P, _P]
+    lib.tq_make_rotation.argtypes = [_U64, _I32, _I32, _P]
+    lib.tq_quantize_kv.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache), _I64, _P]
+    lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
+    lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P,
+                                        _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
+    lib.tq_decode_splits.argtypes = [_I64, _I64, _I64, _I32]
+    lib.tq_decode_splits.restype = _I32
+    lib.tq_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32, _I32]
+    lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_status_string.argtypes = [ctypes.c_int]
+    lib.tq_status_string.restype = ctypes.c_char_p
+    for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+_bind(_lib)
 
 
 class TQError(RuntimeError):

@@ -36,6 +36,9 @@ def _flags():
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: ordinary float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs (no accumulation-register copies
+        # around the softmax rescale)
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]

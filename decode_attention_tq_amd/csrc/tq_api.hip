@@ -60,19 +60,23 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   p->nq = p->wide ? 32 : 16;
   p->qjl = qjl ? 1 : 0;
   const int64_t Tp = T > 0 ? T : 1;
+  // a chunk is one workgroup of kWavesPerDecodeWG wavefronts, each streaming a
+  // whole number of kStep-token steps
+  const int64_t quantum = (int64_t)kWavesPerDecodeWG * kStep;
   int64_t target;
   if (n_split > 0) {
     target = n_split;
   } else {
-    // about 16 wavefronts per compute unit on a 256-CU part, chunks of >= 256 tokens
+    // about 16 wavefronts per compute unit on a 256-CU part, >= 2 steps per wavefront
     const int64_t units = B * H_kv;
-    target = (4096 + units - 1) / units;
-    const int64_t cap = (Tp + 255) / 256;
+    const int64_t wgs = 4096 / kWavesPerDecodeWG;
+    target = (wgs + units - 1) / units;
+    const int64_t cap = (Tp + 2 * quantum - 1) / (2 * quantum);
     if (target > cap) target = cap;
     if (target < 1) target = 1;
   }
   int64_t chunk = (Tp + target - 1) / target;
-  chunk = (chunk + kStep - 1) / kStep * kStep;
+  chunk = (chunk + quantum - 1) / quantum * quantum;
   p->chunk = (int32_t)chunk;
   p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
   size_t off = 0;

@@ -78,6 +78,25 @@ __device__ inline float dpp_ror8(float x) {
 
 __device__ inline float shfl_xor_f(float x, int m) { return __shfl_xor(x, m); }
 
+// Value of lane 16 * (lane / 16) + N: DPP row_newbcast (gfx90a and later).
+template <int N>
+__device__ inline float bcast_row_c(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
+}
+// Same with n known only after loop unrolling (the switch folds away).
+__device__ inline float bcast_row(float x, int n) {
+  switch (n) {
+    case 0: return bcast_row_c<0>(x);
+    case 1: return bcast_row_c<1>(x);
+    case 2: return bcast_row_c<2>(x);
+    case 3: return bcast_row_c<3>(x);
+    case 4: return bcast_row_c<4>(x);
+    case 5: return bcast_row_c<5>(x);
+    case 6: return bcast_row_c<6>(x);
+    default: return bcast_row_c<7>(x);
+  }
+}
+
 __device__ inline uint32_t pack_half2(float lo, float hi) {
   half2v h = {(_Float16)lo, (_Float16)hi};
   return __builtin_bit_cast(uint32_t, h);

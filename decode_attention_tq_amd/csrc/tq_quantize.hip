@@ -91,18 +91,31 @@ __device__ inline void pack32(const uint32_t* q, uint32_t* w) {
 
 // Load Pi (or S), split into float16 hi/lo, into LDS in B-operand order:
 // op[pass][ks][nb][lane][8] = M[16nb + n][32g + 8ks + e], lane = 16g + n.
-__device__ void stage_matrix(const float* M, _Float16* op, int nthreads) {
-  for (int idx = threadIdx.x; idx < kD * kD; idx += nthreads) {
-    const int row = idx / kD, col = idx % kD;   // coalesced global read
-    const float v = M[idx];
-    const _Float16 hi = (_Float16)v;
-    const _Float16 lo = (_Float16)(v - (float)hi);
+// Every thread issues all of its 16-byte loads before converting, so the
+// matrix arrives in about one memory latency.
+template <int NT>
+__device__ void stage_matrix(const float* M, _Float16* op) {
+  constexpr int PER = kD * kD / 4 / NT;
+  float4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) v[k] = ((const float4*)M)[threadIdx.x + k * NT];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = 4 * (threadIdx.x + k * NT);
+    const int row = idx / kD, col = idx % kD;
     const int nb = row >> 4, n = row & 15;
-    const int g = col >> 5, ks = (col >> 3) & 3, e = col & 7;
-    const int lane = 16 * g + n;
-    const int o = (((ks * 8 + nb) * 64 + lane) << 3) + e;
-    op[o] = hi;
-    op[4 * 8 * 64 * 8 + o] = lo;
+    const int g = col >> 5, ks = (col >> 3) & 3, e = col & 7;   // e is 0 or 4
+    const int o = (((ks * 8 + nb) * 64 + 16 * g + n) << 3) + e;
+    const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    _Float16 hi[4], lo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      hi[u] = (_Float16)x[u];
+      lo[u] = (_Float16)(x[u] - (float)hi[u]);
+    }
+    *(uint2*)(op + o) = make_uint2(pack_half2((float)hi[0], (float)hi[1]), pack_half2((float)hi[2], (float)hi[3]));
+    *(uint2*)(op + 4 * 8 * 64 * 8 + o) =
+        make_uint2(pack_half2((float)lo[0], (float)lo[1]), pack_half2((float)lo[2], (float)lo[3]));
   }
 }
 
@@ -120,8 +133,8 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
   unsigned char* cbuf_all = (unsigned char*)(piop + (QJL ? 4 : 2) * OPH);   // WAVES * 16 * 128 bytes
   _Float16* rbuf_all = (_Float16*)(cbuf_all + WAVES * 16 * kD);       // QJL: WAVES * 2 * 16 * 128 halves
 
-  stage_matrix(a.rot, piop, NT);
-  if constexpr (QJL) stage_matrix(a.proj, sop, NT);
+  stage_matrix<NT>(a.rot, piop);
+  if constexpr (QJL) stage_matrix<NT>(a.proj, sop);
   __syncthreads();
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -83,7 +83,7 @@ def test_decode_planning():
         assert n >= 1
         assert tq.decode_workspace_bytes(B, 4 * H, H, T) > 0
     assert tq.decode_splits(1, 1, 1024, 3) == 3
-    assert tq.decode_splits(1, 1, 1024, 100000) == 32      # chunks never go below 32 tokens
+    assert tq.decode_splits(1, 1, 1024, 100000) == 8       # chunks never go below 4 x 32 tokens
     assert tq.decode_workspace_bytes(1, 7, 2, 100) == 0     # H_q % H_kv != 0
     assert tq.decode_workspace_bytes(1, 34, 2, 100) == 0    # G > 16
 
