@@ -57,20 +57,16 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   p->T = T;
   p->G = (int32_t)G;
   p->wide = G > 8;
-  p->nq = p->wide ? 32 : 16;
   p->qjl = qjl ? 1 : 0;
   const int64_t Tp = T > 0 ? T : 1;
-  // a chunk is one workgroup of kWavesPerDecodeWG wavefronts, each streaming a
-  // whole number of kStep-token steps
-  const int64_t quantum = (int64_t)kWavesPerDecodeWG * kStep;
+  const int64_t quantum = kChunkQuantum;
   int64_t target;
   if (n_split > 0) {
     target = n_split;
   } else {
-    // about 16 wavefronts per compute unit on a 256-CU part, >= 2 steps per wavefront
+    // about one workgroup per compute unit; a chunk keeps at least 2 quanta
     const int64_t units = B * H_kv;
-    const int64_t wgs = 4096 / kWavesPerDecodeWG;
-    target = (wgs + units - 1) / units;
+    target = (kDecodeTargetWGs + units - 1) / units;
     const int64_t cap = (Tp + 2 * quantum - 1) / (2 * quantum);
     if (target > cap) target = cap;
     if (target < 1) target = 1;
@@ -80,10 +76,6 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   p->chunk = (int32_t)chunk;
   p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
   size_t off = 0;
-  p->off_qop = off;
-  off = align256(off + (size_t)(B * H_kv) * (1 + p->qjl) * p->nq * kD * sizeof(_Float16));
-  p->off_qcs = off;
-  off = align256(off + (size_t)(B * H_kv) * 2 * 16 * sizeof(float));
   p->off_ml = off;
   off = align256(off + (size_t)(B * H_q) * p->n_split * 2 * sizeof(float));
   p->off_acc = off;

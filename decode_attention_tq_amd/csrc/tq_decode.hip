@@ -1,19 +1,22 @@
 // Decode attention over the packed TurboQuant cache, for gfx950.
 //
-// Three launches on the caller's stream:
-//   rotate_query   q' = Pi_K q once per query head (and q'' = S q' for QJL keys),
-//                  scaled by a per-head power of two and split into float16
-//                  hi + lo halves that together carry ~22 bits;
-//   decode_scan    one workgroup of 4 wavefronts per (row, KV head, context
-//                  chunk); each wavefront streams a quarter of the chunk: scores
-//                  from the packed key codes on MFMA, online softmax in
-//                  registers, values accumulated in the rotated domain on MFMA;
-//                  the 4 wavefront partials are merged in LDS and written out;
-//   combine        fixed-order merge of the chunk partials of each query head,
-//                  then the single inverse rotation o = Pi_V^T o'.
-// (Merging across workgroups inside decode_scan would need a device-scope
-// release per workgroup, which on this multi-die part writes back L2; the
-// kernel boundary provides that ordering once.)
+// decode_scan: one workgroup per (context chunk, KV head, row) that fills a
+// compute unit (16 wavefronts; 8 for the QJL and G > 8 tiles):
+//   prologue  q' = Pi_K q for the G query heads of the KV head (and q'' = S q'
+//             for QJL keys), staged through LDS, scaled by a power of two per
+//             head and split into float16 hi + lo halves (~22 bits together);
+//             the first code words of the scan are already in flight;
+//   scan      each wavefront streams its share of the chunk: scores from the
+//             packed key codes on MFMA, online softmax in registers, values
+//             accumulated in the rotated domain on MFMA;
+//   epilogue  the wavefront partials are merged in LDS in a fixed order; with
+//             a single chunk (the usual case once B * H_kv fills the part) the
+//             workgroup applies o = Pi_V^T o' and writes the output itself.
+// combine (only when the context is split into several chunks): fixed-order
+// merge of the chunk partials of each query head, then o = Pi_V^T o'.
+// (Merging chunks inside decode_scan would need a device-scope release per
+// workgroup, which on this multi-die part writes back L2; the kernel boundary
+// provides that ordering once.)
 //
 // Rotated-domain identity used throughout (a reading of the method on the
 // ai-accelerate.xyz TurboQuant article, section "TurboQuantの仕組み": the
@@ -67,40 +70,38 @@ __device__ inline float pick16(const float (&c)[16], int idx) {
   return r;
 }
 
-// ---------------------------------------------------------------- rotate q --
+// ------------------------------------------------------ matrices in LDS --
 
-struct RotQArgs {
-  const void* q;
-  const float* rot;    // Pi_K
-  const float* proj;   // S, or null
-  _Float16* qop;       // [B][H_kv][1+qjl][nq][128]
-  float* qcs;          // [B][H_kv][2][16]
-  int q_dtype, H_q, H_kv, G, nq, qjl, wide;
-  float sc1, sc2;
-};
+constexpr int kRowPad = kD + 4;            // LDS row stride of a staged matrix (16-byte aligned rows)
+constexpr int kMatWords = kD * kRowPad;    // one staged d x d matrix
+constexpr int kVecWords = 16 * kD;         // [16][d] float vectors
+// Scratch region of a decode workgroup, in 32-bit words: a staged matrix and two
+// vector sets (query prologue, epilogue), the lookup tables (scan) or the
+// wavefront partials (merge), one after the other.
+constexpr int kScratchWords = kMatWords + 2 * kVecWords;
 
-constexpr int kRowPad = kD + 4;   // LDS row stride of a staged matrix (16-byte aligned rows)
-
-// Stage the d x d matrix M into LDS (row stride kRowPad) with coalesced 16-byte
-// loads, all of a thread's loads in flight at once.
-__device__ void stage_rows(const float* M, float* lds) {
-  constexpr int PER = kD * kD / 4 / 256;
+// Stage the d x d matrix M into LDS (row stride kRowPad) with NT threads:
+// coalesced 16-byte loads, all in flight before the first LDS write.
+template <int NT>
+__device__ void stage_matrix(const float* M, float* lds) {
+  constexpr int PER = kD * kD / 4 / NT;
   float4 v[PER];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) v[k] = ((const float4*)M)[threadIdx.x + 256 * k];
+  for (int k = 0; k < PER; ++k) v[k] = ((const float4*)M)[threadIdx.x + NT * k];
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
-    const int f = threadIdx.x + 256 * k;
+    const int f = threadIdx.x + NT * k;
     *(float4*)(lds + (f >> 5) * kRowPad + 4 * (f & 31)) = v[k];
   }
 }
 
-// out[h][i] = sum_j M[i][j] in[h][j] for the G heads; thread (i, hh) computes
-// heads hh, hh+2, ... from the staged rows (LDS) and inputs (LDS broadcast).
+// out[h][i] = sum_j M[i][j] in[h][j] for the G heads from the staged rows;
+// thread (i, h0) computes heads h0, h0 + NT/128, ...
+template <int NT>
 __device__ void matvec_rows(const float* Ml, const float* in, float* out, int G) {
-  const int i = threadIdx.x & 127, hh = threadIdx.x >> 7;
+  const int i = threadIdx.x & 127;
   const float4* row = (const float4*)(Ml + i * kRowPad);
-  for (int h = hh; h < G; h += 2) {
+  for (int h = threadIdx.x >> 7; h < G; h += NT / 128) {
     const float4* x = (const float4*)(in + h * kD);
     float acc = 0.f;
 #pragma unroll 8
@@ -112,136 +113,39 @@ __device__ void matvec_rows(const float* Ml, const float* in, float* out, int G)
   }
 }
 
-// Writes the float16 hi/lo operand columns and per-head power-of-two scales of
-// vals[G][128] * sc into part `part` of the operand block of (b, kv).
-__device__ void emit_query_operand(const RotQArgs& a, const float* vals, float sc, int part,
-                                   int64_t bkv, int* hexp) {
+// Float16 operand of vals[G][d] * sc: a power of two per head puts its largest
+// entry in [2^13, 2^14) (cs[h] = that power, 1 for absent heads); column h of
+// dst holds the hi halves, column half_cols + h the lo halves, ~22 bits
+// together (zero columns for absent heads). Needs NT >= 256; ends with the
+// operand written by each thread, no barrier.
+template <int NT>
+__device__ void emit_operand(const float* vals, float sc, int G, int half_cols, _Float16* dst, float* cs,
+                             int* hexp) {
   const int tid = threadIdx.x;
-  {
-    // thread (h, seg): max over 8 entries, then over the 16 segments of the head
+  if (tid < 256) {
+    // thread (h, seg): largest magnitude over 8 entries, then over the 16 segments
     const int h = tid >> 4, seg = tid & 15;
     float mx = 0.f;
-    if (h < a.G) {
+    if (h < G) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(vals[h * kD + 8 * seg + k] * sc));
     }
 #pragma unroll
     for (int m = 1; m < 16; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
     if (seg == 0) {
-      // scale so that the largest entry lies in [2^13, 2^14)
       const int e = (mx > 0.f) ? (__builtin_amdgcn_frexp_expf(mx) - 14) : 0;
       hexp[h] = e;
-      a.qcs[(bkv * 2 + part) * 16 + h] = ldexpf(1.0f, e);
+      cs[h] = ldexpf(1.0f, e);
     }
   }
   __syncthreads();
-  _Float16* dst = a.qop + (bkv * (1 + a.qjl) + part) * (int64_t)a.nq * kD;
-  const int half_cols = a.wide ? 16 : 8;
-  for (int idx = tid; idx < a.nq * kD; idx += blockDim.x) {
+  for (int idx = tid; idx < 2 * half_cols * kD; idx += NT) {
     const int col = idx / kD, i = idx % kD;
     const int h = col % half_cols;
-    const bool lo = col >= half_cols;
     float v = 0.f;
-    if (h < a.G) v = ldexpf(vals[h * kD + i] * sc, -hexp[h]);
+    if (h < G) v = ldexpf(vals[h * kD + i] * sc, -hexp[h]);
     const _Float16 hi = (_Float16)v;
-    dst[idx] = lo ? (_Float16)(v - (float)hi) : hi;
-  }
-  __syncthreads();
-}
-
-__global__ __launch_bounds__(256) void rotate_query_kernel(RotQArgs a) {
-  __shared__ __align__(16) float mat[kD * kRowPad];
-  __shared__ __align__(16) float qv[16 * kD];
-  __shared__ __align__(16) float qr[16 * kD];
-  __shared__ int hexp[16];
-  const int kv = blockIdx.x, b = blockIdx.y, tid = threadIdx.x;
-  const int64_t bkv = (int64_t)b * a.H_kv + kv;
-  const int G = a.G;
-  stage_rows(a.rot, mat);
-  for (int idx = tid; idx < G * kD; idx += blockDim.x) {
-    const int64_t e = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD + idx;
-    qv[idx] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[e]) : ((const float*)a.q)[e];
-  }
-  __syncthreads();
-  matvec_rows(mat, qv, qr, G);          // q' = Pi q
-  __syncthreads();
-  emit_query_operand(a, qr, a.sc1, 0, bkv, hexp);
-  if (a.qjl) {
-    stage_rows(a.proj, mat);
-    __syncthreads();
-    matvec_rows(mat, qr, qv, G);        // q'' = S q'
-    __syncthreads();
-    emit_query_operand(a, qv, a.sc2, 1, bkv, hexp);
-  }
-}
-
-// Query operand without QJL: workgroup (kv, b, chunk) produces coordinates
-// 32*chunk .. 32*chunk+31 of q' = Pi q for the G heads of KV head kv. The
-// per-head power of two comes from |q| (the rotation preserves the norm, so
-// every |q'_i| <= |q|), which keeps the chunks independent.
-constexpr int kRotChunks = 4;
-
-__global__ __launch_bounds__(256) void rotate_query_chunk_kernel(RotQArgs a) {
-  __shared__ __align__(16) float qv[16 * kD];
-  __shared__ int hexp[16];
-  const int kv = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z, tid = threadIdx.x;
-  const int64_t bkv = (int64_t)b * a.H_kv + kv;
-  const int G = a.G;
-  // thread (i, hq): output coordinate 32*chunk + i, heads hq, hq + 8
-  const int i = 32 * chunk + (tid & 31), hq = tid >> 5;
-  const float4* rowp = (const float4*)(a.rot + i * kD);
-  float4 row[kD / 4];
-#pragma unroll
-  for (int j4 = 0; j4 < kD / 4; ++j4) row[j4] = rowp[j4];
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int64_t e = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD + idx;
-    qv[idx] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[e]) : ((const float*)a.q)[e];
-  }
-  __syncthreads();
-  {
-    // thread (h, seg): sum of squares and largest magnitude over 8 entries,
-    // then over the 16 segments of the head
-    const int h = tid >> 4, seg = tid & 15;
-    float ss = 0.f, mx = 0.f;
-    if (h < G) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float v = qv[h * kD + 8 * seg + k];
-        ss = fmaf(v, v, ss);
-        mx = fmaxf(mx, fabsf(v));
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) {
-      ss += __shfl_xor(ss, m);
-      mx = fmaxf(mx, __shfl_xor(mx, m));
-    }
-    if (seg == 0) {
-      // |q| bounds every |q'_i|; sqrt(d) * max_j |q_j| bounds |q| and stays
-      // finite where the sum of squares overflows
-      const float bound = fminf(sqrtf(ss), mx * 11.3137085f) * a.sc1;
-      const int e = (bound > 0.f) ? (__builtin_amdgcn_frexp_expf(bound) - 13) : 0;
-      hexp[h] = e;
-      if (chunk == 0) a.qcs[(bkv * 2) * 16 + h] = ldexpf(1.0f, e);
-    }
-  }
-  __syncthreads();
-  _Float16* dst = a.qop + bkv * (int64_t)a.nq * kD;
-  const int half_cols = a.wide ? 16 : 8;
-  for (int h = hq; h < half_cols; h += 8) {
-    float acc = 0.f;
-    if (h < G) {
-      const float4* x = (const float4*)(qv + h * kD);
-#pragma unroll
-      for (int j4 = 0; j4 < kD / 4; ++j4) {
-        const float4 v = x[j4];
-        acc = fmaf(row[j4].w, v.w, fmaf(row[j4].z, v.z, fmaf(row[j4].y, v.y, fmaf(row[j4].x, v.x, acc))));
-      }
-      acc = ldexpf(acc * a.sc1, -hexp[h]);
-    }
-    const _Float16 hi = (_Float16)acc;
-    dst[h * kD + i] = hi;
-    dst[(half_cols + h) * kD + i] = (_Float16)(acc - (float)hi);
+    dst[idx] = col >= half_cols ? (_Float16)(v - (float)hi) : hi;
   }
 }
 
@@ -254,13 +158,17 @@ struct ScanArgs {
   const float* kgamma;
   const uint32_t* vcodes;
   const float* vnorms;
-  const _Float16* qop;
-  const float* qcs;
+  const void* q;
+  const float* rotK;   // Pi_K
+  const float* proj;   // S (QJL keys), or null
+  const float* rotV;   // Pi_V
   const int32_t* ctx_lens;
-  float* ml;     // [B][H_q][n_split][2]
+  float* out;    // [B][H_q][128], written when n_split == 1
+  float* ml;     // [B][H_q][n_split][2], partials when n_split > 1
   float* acc;    // [B][H_q][n_split][128]
   int64_t TcK, TcV;
-  int H_kv, H_q, G, T, n_split, wg_chunk, wave_chunk, nq;
+  int q_dtype, H_kv, H_q, G, T, n_split, wg_chunk, wave_chunk;
+  float sc1, sc2, inv_sqrt_d;
   float kc[16], vc[16];
 };
 
@@ -583,67 +491,66 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 }
 
 
+// Wavefronts per workgroup: one workgroup fills a compute unit (4 wavefronts
+// per SIMD, <= 128 VGPRs, for the common tiles; the QJL and G > 8 tiles carry
+// more operands and run 2 per SIMD).
+template <int QJL, int WIDE>
+constexpr int scan_waves() { return (QJL || WIDE) ? 8 : 16; }
+
 // merge buffer: [wave][column][128 + 2] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
 constexpr int merge_cols() { return WIDE ? 16 : 8; }
 
-// LDS: lookup tables, then the query operand of the workgroup's KV head
-// (16 columns x 128 halves); the merge area reuses both after the scan.
-constexpr int kQopWords = 16 * kD / 2;
+// LDS of a decode workgroup, in 32-bit words: the float16 query operand
+// ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, then the
+// scratch region.
+template <int QJL, int WIDE>
+constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kD / 2 + 48; }
 
 template <int KB, int VB, int QJL, int WIDE>
-constexpr int scan_lds_words() {
-  constexpr int lut = ((1 << (2 * KB)) + (1 << (2 * VB)) + (QJL ? 4 : 0)) * kLutRep + kQopWords;
-  constexpr int mrg = kWavesPerDecodeWG * merge_cols<WIDE>() * (kD + 2);
-  return lut > mrg ? lut : mrg;
+constexpr size_t scan_lds_bytes() {
+  static_assert(((1 << (2 * KB)) + (1 << (2 * VB)) + (QJL ? 4 : 0)) * kLutRep <= kScratchWords,
+                "lookup tables exceed the scratch region");
+  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * (kD + 2) <= kMatWords + kVecWords,
+                "merge area overlaps the merged output");
+  return (size_t)(scan_head_words<QJL, WIDE>() + kScratchWords) * 4;
 }
 
-// 4 wavefronts per SIMD (<= 128 VGPRs) keeps all 4 workgroups of a compute
-// unit resident for the common tiles; the QJL and G > 8 tiles carry more
-// operands and run 2 per SIMD without spilling.
-template <int QJL, int WIDE>
-constexpr int scan_waves_per_eu() { return (QJL || WIDE) ? 2 : 4; }
-
+// One workgroup per (context chunk, KV head, row):
+//   prologue  q' = Pi_K q for the G query heads (and q'' = S q' for QJL keys)
+//             into the float16 operand in LDS, while the first code words are
+//             already in flight;
+//   scan      each wavefront streams its share of the chunk;
+//   epilogue  the wavefront partials are merged in LDS in a fixed order; with
+//             one chunk the workgroup finishes the heads (o = Pi_V^T o'),
+//             otherwise it writes the chunk partial for the combine.
 template <int KB, int VB, int QJL, int WIDE>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(scan_waves_per_eu<QJL, WIDE>(), 4)))
-void decode_scan_kernel(ScanArgs a) {
+__global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_kernel(ScanArgs a) {
+  constexpr int NW = scan_waves<QJL, WIDE>(), NT = 64 * NW;
   constexpr int NK = 1 << (2 * KB), NV = 1 << (2 * VB), NS = QJL ? 4 : 0;
   constexpr int KW = 4 * KB;
   constexpr int MC = merge_cols<WIDE>();
-  __shared__ uint32_t smem[scan_lds_words<KB, VB, QJL, WIDE>()];
-  uint32_t* lutK = smem;
-  uint32_t* lutV = smem + NK * kLutRep;
-  uint32_t* lutS = smem + (NK + NV) * kLutRep;
-  uint32_t* qlds = smem + (NK + NV + NS) * kLutRep;   // 16-byte aligned (multiple of 32 words)
+  constexpr int NQ = WIDE ? 32 : 16;   // operand columns per part
+  constexpr int HALF = NQ / 2;
+  __shared__ __align__(16) uint32_t smem[scan_lds_bytes<KB, VB, QJL, WIDE>() / 4];
+  _Float16* qlds = (_Float16*)smem;                        // [1 + QJL][NQ][d]
+  float* qcs = (float*)(smem + (1 + QJL) * NQ * kD / 2);   // [2][16]
+  int* hexp = (int*)(qcs + 32);                            // [16]
+  uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
+  float* mat = (float*)U;
+  float* vA = mat + kMatWords;
+  float* vB = vA + kVecWords;
+  uint32_t* lutK = U;
+  uint32_t* lutV = U + NK * kLutRep;
+  uint32_t* lutS = U + (NK + NV) * kLutRep;
 
   const int tid = threadIdx.x;
-  for (int e = tid; e < NK * kLutRep; e += 256) {
-    const int f = e >> kLutShift;
-    lutK[e] = pack_half2(pick16(a.kc, f & ((1 << KB) - 1)), pick16(a.kc, f >> KB));
-  }
-  for (int e = tid; e < NV * kLutRep; e += 256) {
-    const int f = e >> kLutShift;
-    lutV[e] = pack_half2(pick16(a.vc, f & ((1 << VB) - 1)), pick16(a.vc, f >> VB));
-  }
-  if constexpr (QJL) {
-    for (int e = tid; e < NS * kLutRep; e += 256) {
-      const int f = e >> kLutShift;
-      lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
-    }
-  }
-  {
-    // query operand columns 0-15 of this (row, KV head): 4 KB, one 16-byte load per thread
-    const int64_t bkv0 = (int64_t)blockIdx.z * a.H_kv + blockIdx.y;
-    const u32x4* src = (const u32x4*)(a.qop + bkv0 * (1 + QJL) * (int64_t)a.nq * kD);
-    ((u32x4*)qlds)[tid] = src[tid];
-  }
-  __syncthreads();
-
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int lrep = lane & (kLutRep - 1);
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int G = a.G;
   int ctx = a.ctx_lens ? a.ctx_lens[b] : a.T;
   ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
   const int t_begin = split * a.wg_chunk + wave * a.wave_chunk;
@@ -671,20 +578,71 @@ void decode_scan_kernel(ScanArgs a) {
   lo.v = (uint32_t)(g * 32 * VB + c * 2 * VB) * 4u;
   lo.n = (uint32_t)(8 * g + (hf ? 4 : 0)) * 4u;
 
+  // the code words of the first two full steps are in flight during the prologue
+  const int t_full = t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0);
+  StepData<KB, VB, QJL, WIDE> A, Bd, Cd;
+  if (t_begin < t_full) load_step(A, s, lo, t_begin);
+  if (t_begin + kStep < t_full) load_step(Bd, s, lo, t_begin + kStep);
+
+  // ---- prologue: the query operand of this (row, KV head)
+  {
+    // the G query vectors ([G][d] contiguous) as float32 in vA, Pi_K in mat
+    constexpr int QPER = 16 * kD / NT;
+    const int64_t q0 = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD;
+    float qx[QPER];
+#pragma unroll
+    for (int k = 0; k < QPER; ++k) {
+      const int idx = tid + NT * k;
+      qx[k] = 0.f;
+      if (idx < G * kD)
+        qx[k] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[q0 + idx])
+                                     : ((const float*)a.q)[q0 + idx];
+    }
+    stage_matrix<NT>(a.rotK, mat);
+#pragma unroll
+    for (int k = 0; k < QPER; ++k) vA[tid + NT * k] = qx[k];
+    __syncthreads();
+    matvec_rows<NT>(mat, vA, vB, G);   // q' = Pi_K q
+    __syncthreads();
+    emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
+    if constexpr (QJL) {
+      stage_matrix<NT>(a.proj, mat);
+      __syncthreads();
+      matvec_rows<NT>(mat, vB, vA, G);   // q'' = S q'
+      __syncthreads();
+      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kD, qcs + 16, hexp);
+    }
+  }
+  __syncthreads();   // the scratch region becomes the lookup tables
+  for (int e = tid; e < NK * kLutRep; e += NT) {
+    const int f = e >> kLutShift;
+    lutK[e] = pack_half2(pick16(a.kc, f & ((1 << KB) - 1)), pick16(a.kc, f >> KB));
+  }
+  for (int e = tid; e < NV * kLutRep; e += NT) {
+    const int f = e >> kLutShift;
+    lutV[e] = pack_half2(pick16(a.vc, f & ((1 << VB) - 1)), pick16(a.vc, f >> VB));
+  }
+  if constexpr (QJL) {
+    for (int e = tid; e < NS * kLutRep; e += NT) {
+      const int f = e >> kLutShift;
+      lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+    }
+  }
+  __syncthreads();
+
   // query operand (B of QK) for this lane: column c, coordinates 32g + 8kk + 0..7
   QOps<WIDE, QJL> q;
-  const _Float16* qb = a.qop + bkv * (1 + QJL) * (int64_t)a.nq * kD;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qb + (16 + c) * kD + 32 * g + 8 * kk);
+    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * kD + 32 * g + 8 * kk);
     if constexpr (QJL) {
-      q.r0[kk] = *(const half8*)(qb + (a.nq + c) * kD + 32 * g + 8 * kk);
-      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qb + (a.nq + 16 + c) * kD + 32 * g + 8 * kk);
+      q.r0[kk] = *(const half8*)(qlds + (NQ + c) * kD + 32 * g + 8 * kk);
+      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qlds + (NQ + 16 + c) * kD + 32 * g + 8 * kk);
     }
   }
   const int hc = WIDE ? c : (c & 7);
-  q.cs1 = a.qcs[(bkv * 2 + 0) * 16 + hc];
-  q.cs2 = QJL ? a.qcs[(bkv * 2 + 1) * 16 + hc] : 0.f;
+  q.cs1 = qcs[hc];
+  q.cs2 = QJL ? qcs[16 + hc] : 0.f;
   q.hf = hf;
   q.q0l = (const half8*)(qlds) + (c * kD + 32 * g) / 8;
 
@@ -698,15 +656,11 @@ void decode_scan_kernel(ScanArgs a) {
     st.acc1[nb] = st.acc0[nb];
   }
 
-  // ---- stream the chunk: full 32-token steps with three register buffers in
+  // ---- stream the share: full 32-token steps with three register buffers in
   // turn (the code words of the next two steps are in flight while the current
   // step computes), then at most one masked step for a ragged end.
-  const int t_full = t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0);
   int t0 = t_begin;
   if (t0 < t_full) {
-    StepData<KB, VB, QJL, WIDE> A, Bd, Cd;
-    load_step(A, s, lo, t0);
-    if (t0 + kStep < t_full) load_step(Bd, s, lo, t0 + kStep);
 #define TQ_STEP(CUR, NEXT2)                                                                              \
     if (t0 + 2 * kStep < t_full) load_step(NEXT2, s, lo, t0 + 2 * kStep);                               \
     scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0); \
@@ -720,9 +674,9 @@ void decode_scan_kernel(ScanArgs a) {
 #undef TQ_STEP
   }
   if (t0 < t_end) {
-    StepData<KB, VB, QJL, WIDE> A;
-    load_step(A, s, lo, t0);
-    scan_step<KB, VB, QJL, WIDE, true>(A, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0);
+    StepData<KB, VB, QJL, WIDE> E;
+    load_step(E, s, lo, t0);
+    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0);
   }
 
   // ---- this wavefront's partial: lane (g, c) holds coordinates 32g + 8r + nb of column c
@@ -741,10 +695,11 @@ void decode_scan_kernel(ScanArgs a) {
   l += shfl_xor_f(l, 16);
   l += shfl_xor_f(l, 32);
 
-  // ---- merge the 4 wavefront partials of this workgroup in LDS (fixed order)
+  // ---- merge the wavefront partials in LDS (fixed order)
+  const bool finish = a.n_split == 1;
   __syncthreads();   // every wavefront is done with the lookup tables
-  float* mrg = (float*)smem;   // [wave][MC columns][128 + 2]
-  if (c < a.G) {
+  float* mrg = (float*)U;   // [wave][MC columns][128 + 2]
+  if (c < G) {
     float* dst = mrg + (wave * MC + c) * (kD + 2);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -757,15 +712,15 @@ void decode_scan_kernel(ScanArgs a) {
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < a.G * kD; idx += 256) {
+  for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx / kD, j = idx % kD;
     float M = -INFINITY;
 #pragma unroll
-    for (int wv = 0; wv < kWavesPerDecodeWG; ++wv) M = fmaxf(M, mrg[(wv * MC + h) * (kD + 2) + kD]);
+    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, mrg[(wv * MC + h) * (kD + 2) + kD]);
     float num = 0.f, den = 0.f;
     if (M > -INFINITY) {
 #pragma unroll
-      for (int wv = 0; wv < kWavesPerDecodeWG; ++wv) {
+      for (int wv = 0; wv < NW; ++wv) {
         const float* src = mrg + (wv * MC + h) * (kD + 2);
         const float mw = src[kD];
         const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
@@ -773,14 +728,30 @@ void decode_scan_kernel(ScanArgs a) {
         den = fmaf(f, src[kD + 1], den);
       }
     }
-    const int64_t pidx = ((int64_t)b * a.H_q + kv * a.G + h) * a.n_split + split;
-    a.acc[pidx * kD + j] = num;
-    if (j == 0) {
-      a.ml[pidx * 2] = M;
-      a.ml[pidx * 2 + 1] = den;
+    if (finish) {
+      vB[idx] = den > 0.f ? num / den * a.inv_sqrt_d : 0.f;
+    } else {
+      const int64_t pidx = ((int64_t)b * a.H_q + kv * G + h) * a.n_split + split;
+      a.acc[pidx * kD + j] = num;
+      if (j == 0) {
+        a.ml[pidx * 2] = M;
+        a.ml[pidx * 2 + 1] = den;
+      }
     }
   }
-
+  if (finish) {
+    __syncthreads();   // the merge area becomes Pi_V
+    stage_matrix<NT>(a.rotV, mat);
+    __syncthreads();
+    // out[h][i] = sum_j Pi_V[j][i] o'[h][j]; thread (i, h0) takes heads h0, h0 + NT/128, ...
+    const int i = tid & 127;
+    for (int h = tid >> 7; h < G; h += NT / 128) {
+      float r = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < kD; ++j) r = fmaf(mat[j * kRowPad + i], vB[h * kD + j], r);
+      a.out[((int64_t)b * a.H_q + kv * G + h) * kD + i] = r;
+    }
+  }
 }
 
 // ---------------------------------------------------------------- combine --
@@ -845,7 +816,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* ml, const flo
 template <int KB, int VB, int QJL, int WIDE>
 hipError_t launch_scan(const DecodePlan& p, const ScanArgs& sa, hipStream_t stream) {
   dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)p.B);
-  hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE>), grid, dim3(256), 0, stream, sa);
+  hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0, stream,
+                     sa);
   return hipGetLastError();
 }
 
@@ -874,34 +846,9 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
                          hipStream_t stream) {
   char* base = (char*)ws;
-  _Float16* qop = (_Float16*)(base + p.off_qop);
-  float* qcs = (float*)(base + p.off_qcs);
   float* ml = (float*)(base + p.off_ml);
   float* acc = (float*)(base + p.off_acc);
-
-  RotQArgs ra;
-  ra.q = q;
-  ra.rot = k->rot;
-  ra.proj = p.qjl ? k->qjl_proj : nullptr;
-  ra.qop = qop;
-  ra.qcs = qcs;
-  ra.q_dtype = q_dtype;
-  ra.H_q = (int)p.H_q;
-  ra.H_kv = (int)p.H_kv;
-  ra.G = p.G;
-  ra.nq = p.nq;
-  ra.qjl = p.qjl;
-  ra.wide = p.wide;
   const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
-  ra.sc1 = scale * kLog2e * inv_sqrt_d;
-  ra.sc2 = scale * kLog2e * sqrtf((float)M_PI / 2.0f) / (float)kD;
-  if (p.qjl)
-    hipLaunchKernelGGL(rotate_query_kernel, dim3((unsigned)p.H_kv, (unsigned)p.B), dim3(256), 0, stream, ra);
-  else
-    hipLaunchKernelGGL(rotate_query_chunk_kernel, dim3((unsigned)p.H_kv, (unsigned)p.B, kRotChunks), dim3(256), 0,
-                       stream, ra);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
 
   ScanArgs sa;
   sa.kcodes = k->codes;
@@ -910,31 +857,40 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   sa.kgamma = k->qjl_gamma;
   sa.vcodes = v->codes;
   sa.vnorms = v->norms;
-  sa.qop = qop;
-  sa.qcs = qcs;
+  sa.q = q;
+  sa.rotK = k->rot;
+  sa.proj = p.qjl ? k->qjl_proj : nullptr;
+  sa.rotV = v->rot;
   sa.ctx_lens = ctx_lens;
+  sa.out = out;
   sa.ml = ml;
   sa.acc = acc;
   sa.TcK = k->T_cap;
   sa.TcV = v->T_cap;
+  sa.q_dtype = q_dtype;
   sa.H_kv = (int)p.H_kv;
   sa.H_q = (int)p.H_q;
   sa.G = p.G;
   sa.T = (int)p.T;
   sa.n_split = p.n_split;
   sa.wg_chunk = p.chunk;
-  sa.wave_chunk = p.chunk / kWavesPerDecodeWG;
-  sa.nq = p.nq;
+  sa.wave_chunk = p.chunk / ((p.qjl || p.wide) ? 8 : 16);
+  // the query operand carries log2(e) * scale / sqrt(d) (scores in the log2
+  // domain); the QJL part log2(e) * scale * sqrt(pi/2) / d
+  sa.sc1 = scale * kLog2e * inv_sqrt_d;
+  sa.sc2 = scale * kLog2e * sqrtf((float)M_PI / 2.0f) / (float)kD;
+  sa.inv_sqrt_d = inv_sqrt_d;
   for (int i = 0; i < 16; ++i) {
     sa.kc[i] = i < (1 << k->bits) ? k->centroids[i] : 0.f;
     sa.vc[i] = i < (1 << v->bits) ? v->centroids[i] : 0.f;
   }
+  hipError_t err;
   switch (k->bits) {
     case 2: err = dispatch_vb<2>(v->bits, p, sa, stream); break;
     case 3: err = dispatch_vb<3>(v->bits, p, sa, stream); break;
     default: err = dispatch_vb<4>(v->bits, p, sa, stream); break;
   }
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || p.n_split == 1) return err;
 
   hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.H_kv, (unsigned)p.B, kD / 32), dim3(256), 0, stream, ml, acc,
                      v->rot, out, (int)p.H_q, p.G, p.n_split, inv_sqrt_d);

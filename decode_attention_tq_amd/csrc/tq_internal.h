@@ -12,18 +12,19 @@ namespace tq {
 constexpr int kD = 128;              // head dimension this build supports
 constexpr int kValueBlock = 8;       // tokens per value-layout block
 constexpr int kStep = 32;            // tokens per decode inner step
-constexpr int kWavesPerDecodeWG = 4;
+constexpr int kChunkQuantum = 512;   // context chunks are whole multiples of this many tokens
+                                     // (whole steps for each of up to 16 wavefronts)
+constexpr int kDecodeTargetWGs = 256;   // one workgroup per compute unit of a 256-CU part
 
 // Decode planning shared by the workspace-size helper and the launcher.
 struct DecodePlan {
   int64_t B, H_q, H_kv, T;
   int32_t G;           // query heads per KV head
   int32_t wide;        // 0: G <= 8 (hi/lo query halves share one 16-column MFMA tile), 1: 8 < G <= 16
-  int32_t nq;          // query operand columns per KV head (16 or 32)
   int32_t qjl;
   int32_t n_split;     // context chunks per (row, KV head)
   int32_t chunk;       // tokens per chunk, multiple of kStep
-  size_t off_qop, off_qcs, off_ml, off_acc, bytes;
+  size_t off_ml, off_acc, bytes;   // chunk partials (used when n_split > 1)
 };
 
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,

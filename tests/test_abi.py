@@ -77,13 +77,19 @@ def test_rotation_rejects_bad_arguments():
 
 
 def test_decode_planning():
-    # every chunk is a multiple of the 32-token step and the chunks cover T
+    # chunks are whole multiples of 512 tokens (32-token steps for up to 16
+    # wavefronts) and together cover T; auto mode aims at one workgroup per
+    # compute unit of a 256-CU part
     for B, H, T in [(1, 8, 32768), (32, 8, 32768), (4, 4, 131072), (1, 1, 1024), (2, 3, 1), (1, 1, 0)]:
         n = tq.decode_splits(B, H, T)
         assert n >= 1
+        assert (n - 1) * 512 < max(T, 1) or n == 1
         assert tq.decode_workspace_bytes(B, 4 * H, H, T) > 0
-    assert tq.decode_splits(1, 1, 1024, 3) == 3
-    assert tq.decode_splits(1, 1, 1024, 100000) == 8       # chunks never go below 4 x 32 tokens
+    assert tq.decode_splits(32, 8, 32768) == 1              # 256 (row, KV head) pairs: one chunk each
+    assert tq.decode_splits(1, 8, 32768) == 32              # 8 pairs: 32 chunks of 1024 tokens
+    assert tq.decode_splits(1, 1, 4096, 3) == 3             # ceil(4096 / 3) -> 1536 tokens
+    assert tq.decode_splits(1, 1, 1024, 3) == 2             # ceil(1024 / 3) -> 512 tokens
+    assert tq.decode_splits(1, 1, 1024, 100000) == 2        # chunks never go below 512 tokens
     assert tq.decode_workspace_bytes(1, 7, 2, 100) == 0     # H_q % H_kv != 0
     assert tq.decode_workspace_bytes(1, 34, 2, 100) == 0    # G > 16
 
