@@ -26,8 +26,42 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, AMD published
 F16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, AMD published
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM traffic of the decode kernel, from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+# (calibrated against a copy of known size), valid for the kernel sources whose
+# hash it records
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_scan_stress70b_hbm_traffic.md")
+KERNEL_SOURCES = ["decode_attention_tq_amd/csrc/tq_decode.hip", "decode_attention_tq_amd/csrc/tq_device.h",
+                  "decode_attention_tq_amd/csrc/tq_internal.h"]
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """Bytes per decode launch from the committed counter summary, or None when
+    it is missing, covers another workload or predates the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            kv = dict(line.split("=", 1) for line in (l.strip() for l in f) if "=" in line and " " not in line.split("=")[0])
+    except OSError:
+        return None
+    if kv.get("workload") != workload or kv.get("kernel_source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def decode_bytes(w, T):
@@ -193,6 +227,7 @@ def main():
     dec_ms = sum(b.elapsed_time(c) for a, b, c in evs) / args.steps
     app_ms = sum(a.elapsed_time(b) for a, b, c in evs) / args.steps
     dbytes = decode_bytes(w, T)
+    n_split = tq.decode_splits(w.B, w.H_kv, T)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
     log(f"[bench] step {ms_step * 1e3:.1f} us (append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us); "
         f"decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
@@ -220,10 +255,12 @@ def main():
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d, "T": T,
                    "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input_dtype": w.dtype,
                    "step": "quantize 1 new K,V token per (row, KV head) + decode attention over T tokens",
-                   "n_split": tq.decode_splits(w.B, w.H_kv, T)},
+                   "n_split": n_split},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "tq_decode_attention launch group (rotate_query + decode_scan + combine)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
+                     "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)}>"
+                                + (" (the whole tq_decode_attention call: one launch)" if n_split == 1
+                                   else f" + combine_kernel ({n_split} context chunks)")),
                      "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
         "decode": {"us": dec_ms * 1e3, "kv_tokens_per_s": w.B * T / (dec_ms * 1e-3),
                    "tokens_per_s": w.B / (dec_ms * 1e-3), "append_us": app_ms * 1e3},

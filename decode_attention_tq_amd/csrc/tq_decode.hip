@@ -260,7 +260,8 @@ __device__ inline void bload_floats_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 template <int KB, int VB, int QJL, int WIDE>
 __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo, int t0) {
   constexpr int KW = 4 * KB, VBW = 32 * VB;
-  const uint32_t st = (uint32_t)t0;   // wave-uniform
+  // wave-uniform; readfirstlane keeps the step offsets in scalar registers
+  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0);
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     bload_words_s<KB>(s.rk, lo.k[m], st * (KW * 4u), d.kw[m]);
@@ -278,7 +279,7 @@ struct StepNorms {
 
 template <int NT, int QJL>
 __device__ inline void load_norms(StepNorms<NT, QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
-  const uint32_t st = (uint32_t)t0 * 4u;
+  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0) * 4u;
   bload_floats_s<NT>(s.rkn, lo.n, st, n.kn);
   bload_floats_s<NT>(s.rvn, lo.n, st, n.vn);
   if constexpr (QJL) bload_floats_s<NT>(s.rg, lo.n, st, n.kg);
@@ -313,13 +314,8 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
   constexpr int NT = StepData<KB, VB, QJL, WIDE>::NT;
   StepNorms<NT, QJL> nm;
   load_norms(nm, sm, lo, t0);
-  // ---- scores on MFMA
-  half8 q0[4];
-  {
-    const half8* ql = (const half8*)((const char*)q.q0l + opaque(0u));
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) q0[kk] = ql[kk];
-  }
+  // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
+  // (two independent accumulation chains; one query block live at a time)
   floatx4 s0[2], s1[2], z0[2], z1[2];
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
@@ -327,24 +323,30 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     s1[m] = s0[m];
     z0[m] = s0[m];
     z1[m] = s0[m];
-#define TQ_QK(KK)                                                   \
-    {                                                               \
-      const half8 ka = key_operand<KB, KK>(d.kw[m], lutK, lane);    \
-      s0[m] = mfma16(ka, q0[KK], s0[m]);                            \
-      if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);      \
+  }
+  {
+    const half8* ql = (const half8*)((const char*)q.q0l + opaque(0u));
+#define TQ_QK(KK)                                                     \
+    {                                                                 \
+      const half8 qk = ql[KK];                                        \
+      _Pragma("unroll") for (int m = 0; m < 2; ++m) {                 \
+        const half8 ka = key_operand<KB, KK>(d.kw[m], lutK, lane);    \
+        s0[m] = mfma16(ka, qk, s0[m]);                                \
+        if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);      \
+      }                                                               \
     }
     TQ_QK(0) TQ_QK(1) TQ_QK(2) TQ_QK(3)
 #undef TQ_QK
-    if constexpr (QJL) {
-#define TQ_QJ(KK)                                                   \
-      {                                                             \
-        const half8 sa = sign_operand<KK>(d.sw[m], lutS, lane);     \
-        z0[m] = mfma16(sa, q.r0[KK], z0[m]);                        \
-        if constexpr (WIDE) z1[m] = mfma16(sa, q.r1[KK], z1[m]);    \
-      }
-      TQ_QJ(0) TQ_QJ(1) TQ_QJ(2) TQ_QJ(3)
-#undef TQ_QJ
+  }
+  if constexpr (QJL) {
+#define TQ_QJ(KK)                                                     \
+    _Pragma("unroll") for (int m = 0; m < 2; ++m) {                   \
+      const half8 sa = sign_operand<KK>(d.sw[m], lutS, lane);         \
+      z0[m] = mfma16(sa, q.r0[KK], z0[m]);                            \
+      if constexpr (WIDE) z1[m] = mfma16(sa, q.r1[KK], z1[m]);        \
     }
+    TQ_QJ(0) TQ_QJ(1) TQ_QJ(2) TQ_QJ(3)
+#undef TQ_QJ
   }
   const float cs = QJL ? 1.0f : q.cs1;
 
@@ -553,8 +555,10 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   const int G = a.G;
   int ctx = a.ctx_lens ? a.ctx_lens[b] : a.T;
   ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
+  // token range of this wavefront; wave-uniform, so that every step offset
+  // travels in the scalar offset of the buffer loads
   const int t_begin = split * a.wg_chunk + wave * a.wave_chunk;
-  const int t_end = min(t_begin + a.wave_chunk, ctx);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, ctx));
   const int64_t bkv = (int64_t)b * a.H_kv + kv;
 
   Streams s;
@@ -579,7 +583,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   lo.n = (uint32_t)(8 * g + (hf ? 4 : 0)) * 4u;
 
   // the code words of the first two full steps are in flight during the prologue
-  const int t_full = t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0);
+  const int t_full =
+      __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
   StepData<KB, VB, QJL, WIDE> A, Bd, Cd;
   if (t_begin < t_full) load_step(A, s, lo, t_begin);
   if (t_begin + kStep < t_full) load_step(Bd, s, lo, t_begin + kStep);
@@ -673,6 +678,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
 #undef TQ_STEP
   }
+  t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
   if (t0 < t_end) {
     StepData<KB, VB, QJL, WIDE> E;
     load_step(E, s, lo, t0);
