@@ -58,6 +58,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 2.0f;
 constexpr float kShift = kSlack + 3.5f;   // + log2(sqrt(128))
 constexpr int kLutRep = 32;              // LUT replicas (power of two)
+constexpr int kStreamAux = 2;            // cache policy of the streamed cache reads: non-temporal
 constexpr int kLutShift = 5;             // log2(kLutRep)
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
@@ -75,6 +76,9 @@ __device__ inline float pick16(const float (&c)[16], int idx) {
 constexpr int kRowPad = kD + 4;            // LDS row stride of a staged matrix (16-byte aligned rows)
 constexpr int kMatWords = kD * kRowPad;    // one staged d x d matrix
 constexpr int kVecWords = 16 * kD;         // [16][d] float vectors
+// Column stride (in halves) of the float16 query operand in LDS: the 16 lanes
+// that read one 16-byte piece of 16 different columns then hit distinct banks.
+constexpr int kQStride = kD + 8;
 // Scratch region of a decode workgroup, in 32-bit words: a staged matrix and two
 // vector sets (query prologue, epilogue), the lookup tables (scan) or the
 // wavefront partials (merge), one after the other.
@@ -145,7 +149,7 @@ __device__ void emit_operand(const float* vals, float sc, int G, int half_cols, 
     float v = 0.f;
     if (h < G) v = ldexpf(vals[h * kD + i] * sc, -hexp[h]);
     const _Float16 hi = (_Float16)v;
-    dst[idx] = col >= half_cols ? (_Float16)(v - (float)hi) : hi;
+    dst[col * kQStride + i] = col >= half_cols ? (_Float16)(v - (float)hi) : hi;
   }
 }
 
@@ -172,27 +176,49 @@ struct ScanArgs {
   float kc[16], vc[16];
 };
 
+// Codebook lookup tables in LDS: an entry holds the float16 levels of 2
+// adjacent codes (indexed by their 2*bits wide field), replicated kLutRep
+// times so that lane l reads replica l % kLutRep and the lanes of a wavefront
+// hit distinct banks. (Entries of 4 codes, 8 bytes, halve the VALU work of the
+// lookups but their unreplicated random reads cost more LDS time than they
+// save on this part.)
+template <int BITS>
+constexpr int lut_words() { return (1 << (2 * BITS)) * kLutRep; }
+
+template <int BITS>
+__device__ void build_lut(uint32_t* lut, const float (&cb)[16], int tid, int nt) {
+  constexpr int m = (1 << BITS) - 1;
+  for (int e = tid; e < lut_words<BITS>(); e += nt) {
+    const int f = e >> kLutShift;
+    lut[e] = pack_half2(pick16(cb, f & m), pick16(cb, f >> BITS));
+  }
+}
+
+// Float16 codebook levels of the 8 codes at bit offset POS of the lane's word
+// slice w (codes LSB first): an MFMA operand of 8 halves.
+template <int BITS, int POS>
+__device__ inline half8 levels8(const uint32_t* w, const uint32_t* lut, int lrep) {
+  constexpr int W = 2 * BITS;
+  const uint32_t r0 = lut[(field<POS + 0 * W, W>(w) << kLutShift) | lrep];
+  const uint32_t r1 = lut[(field<POS + 1 * W, W>(w) << kLutShift) | lrep];
+  const uint32_t r2 = lut[(field<POS + 2 * W, W>(w) << kLutShift) | lrep];
+  const uint32_t r3 = lut[(field<POS + 3 * W, W>(w) << kLutShift) | lrep];
+  return words_to_half8(r0, r1, r2, r3);
+}
+
 // A operand of the QK MFMA for step KK: coordinates 32g + 8KK + 0..7 of the
 // lane's token, from the lane's KB-word slice (coordinates 32g .. 32g+31).
 template <int KB, int KK>
-__device__ inline half8 key_operand(const uint32_t* w, const uint32_t* lut, int lane) {
-  const uint32_t r0 = lut[(field<2 * KB * (4 * KK + 0), 2 * KB>(w) << kLutShift) | lane];
-  const uint32_t r1 = lut[(field<2 * KB * (4 * KK + 1), 2 * KB>(w) << kLutShift) | lane];
-  const uint32_t r2 = lut[(field<2 * KB * (4 * KK + 2), 2 * KB>(w) << kLutShift) | lane];
-  const uint32_t r3 = lut[(field<2 * KB * (4 * KK + 3), 2 * KB>(w) << kLutShift) | lane];
-  return words_to_half8(r0, r1, r2, r3);
+__device__ inline half8 key_operand(const uint32_t* w, const uint32_t* lut, int lrep) {
+  return levels8<KB, 8 * KB * KK>(w, lut, lrep);
 }
 
 // A operand of the PV MFMA for coordinate block NB: value codes of the 8 tokens
 // of the lane's block at coordinate 8i + NB (i = lane % 16), from the lane's
 // 2*VB-word slice of the block record (coordinates 8i .. 8i+7).
 template <int VB, int NB>
-__device__ inline half8 value_operand(const uint32_t* w, const uint32_t* lut, int lane) {
-  const uint32_t r0 = lut[(field<8 * VB * NB + 2 * VB * 0, 2 * VB>(w) << kLutShift) | lane];
-  const uint32_t r1 = lut[(field<8 * VB * NB + 2 * VB * 1, 2 * VB>(w) << kLutShift) | lane];
-  const uint32_t r2 = lut[(field<8 * VB * NB + 2 * VB * 2, 2 * VB>(w) << kLutShift) | lane];
-  const uint32_t r3 = lut[(field<8 * VB * NB + 2 * VB * 3, 2 * VB>(w) << kLutShift) | lane];
-  return words_to_half8(r0, r1, r2, r3);
+__device__ inline half8 value_operand(const uint32_t* w, const uint32_t* lut, int lrep) {
+  return levels8<VB, 8 * VB * NB>(w, lut, lrep);
 }
 
 // A operand of the QJL MFMA for step KK: +-1 for coordinates 32g + 8KK + 0..7.
@@ -231,13 +257,13 @@ struct Streams {
 template <int N>
 __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
   if constexpr (N == 2) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamAux);
     w[0] = v.x; w[1] = v.y;
   } else if constexpr (N == 3) {
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, 0);
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kStreamAux);
     w[0] = v.x; w[1] = v.y; w[2] = v.z;
   } else if constexpr (N == 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamAux);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (N == 6) {
     bload_words_s<3>(r, voff, soff, w);
@@ -265,7 +291,7 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
     bload_words_s<KB>(s.rk, lo.k[m], st * (KW * 4u), d.kw[m]);
-    if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, 0);
+    if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, kStreamAux);
   }
   bload_words_s<2 * VB>(s.rv, lo.v, (st / 8u) * (VBW * 4u), d.vw);
 }
@@ -507,11 +533,11 @@ constexpr int merge_cols() { return WIDE ? 16 : 8; }
 // ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, then the
 // scratch region.
 template <int QJL, int WIDE>
-constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kD / 2 + 48; }
+constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 48; }
 
 template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
-  static_assert(((1 << (2 * KB)) + (1 << (2 * VB)) + (QJL ? 4 : 0)) * kLutRep <= kScratchWords,
+  static_assert(lut_words<KB>() + lut_words<VB>() + (QJL ? 4 : 0) * kLutRep <= kScratchWords,
                 "lookup tables exceed the scratch region");
   static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * (kD + 2) <= kMatWords + kVecWords,
                 "merge area overlaps the merged output");
@@ -529,22 +555,22 @@ constexpr size_t scan_lds_bytes() {
 template <int KB, int VB, int QJL, int WIDE>
 __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_kernel(ScanArgs a) {
   constexpr int NW = scan_waves<QJL, WIDE>(), NT = 64 * NW;
-  constexpr int NK = 1 << (2 * KB), NV = 1 << (2 * VB), NS = QJL ? 4 : 0;
+  constexpr int NS = QJL ? 4 : 0;
   constexpr int KW = 4 * KB;
   constexpr int MC = merge_cols<WIDE>();
   constexpr int NQ = WIDE ? 32 : 16;   // operand columns per part
   constexpr int HALF = NQ / 2;
   __shared__ __align__(16) uint32_t smem[scan_lds_bytes<KB, VB, QJL, WIDE>() / 4];
-  _Float16* qlds = (_Float16*)smem;                        // [1 + QJL][NQ][d]
-  float* qcs = (float*)(smem + (1 + QJL) * NQ * kD / 2);   // [2][16]
+  _Float16* qlds = (_Float16*)smem;                              // [1 + QJL][NQ][kQStride]
+  float* qcs = (float*)(smem + (1 + QJL) * NQ * kQStride / 2);   // [2][16]
   int* hexp = (int*)(qcs + 32);                            // [16]
   uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
   float* mat = (float*)U;
   float* vA = mat + kMatWords;
   float* vB = vA + kVecWords;
   uint32_t* lutK = U;
-  uint32_t* lutV = U + NK * kLutRep;
-  uint32_t* lutS = U + (NK + NV) * kLutRep;
+  uint32_t* lutV = U + lut_words<KB>();
+  uint32_t* lutS = lutV + lut_words<VB>();
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -582,12 +608,11 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   lo.v = (uint32_t)(g * 32 * VB + c * 2 * VB) * 4u;
   lo.n = (uint32_t)(8 * g + (hf ? 4 : 0)) * 4u;
 
-  // the code words of the first two full steps are in flight during the prologue
+  // the code words of the first full step are in flight during the prologue
   const int t_full =
       __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
-  StepData<KB, VB, QJL, WIDE> A, Bd, Cd;
+  StepData<KB, VB, QJL, WIDE> A, Bd;
   if (t_begin < t_full) load_step(A, s, lo, t_begin);
-  if (t_begin + kStep < t_full) load_step(Bd, s, lo, t_begin + kStep);
 
   // ---- prologue: the query operand of this (row, KV head)
   {
@@ -615,18 +640,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       __syncthreads();
       matvec_rows<NT>(mat, vB, vA, G);   // q'' = S q'
       __syncthreads();
-      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kD, qcs + 16, hexp);
+      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
     }
   }
   __syncthreads();   // the scratch region becomes the lookup tables
-  for (int e = tid; e < NK * kLutRep; e += NT) {
-    const int f = e >> kLutShift;
-    lutK[e] = pack_half2(pick16(a.kc, f & ((1 << KB) - 1)), pick16(a.kc, f >> KB));
-  }
-  for (int e = tid; e < NV * kLutRep; e += NT) {
-    const int f = e >> kLutShift;
-    lutV[e] = pack_half2(pick16(a.vc, f & ((1 << VB) - 1)), pick16(a.vc, f >> VB));
-  }
+  build_lut<KB>(lutK, a.kc, tid, NT);
+  build_lut<VB>(lutV, a.vc, tid, NT);
   if constexpr (QJL) {
     for (int e = tid; e < NS * kLutRep; e += NT) {
       const int f = e >> kLutShift;
@@ -639,17 +658,17 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   QOps<WIDE, QJL> q;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
-    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * kD + 32 * g + 8 * kk);
+    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * kQStride + 32 * g + 8 * kk);
     if constexpr (QJL) {
-      q.r0[kk] = *(const half8*)(qlds + (NQ + c) * kD + 32 * g + 8 * kk);
-      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qlds + (NQ + 16 + c) * kD + 32 * g + 8 * kk);
+      q.r0[kk] = *(const half8*)(qlds + (NQ + c) * kQStride + 32 * g + 8 * kk);
+      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qlds + (NQ + 16 + c) * kQStride + 32 * g + 8 * kk);
     }
   }
   const int hc = WIDE ? c : (c & 7);
   q.cs1 = qcs[hc];
   q.cs2 = QJL ? qcs[16 + hc] : 0.f;
   q.hf = hf;
-  q.q0l = (const half8*)(qlds) + (c * kD + 32 * g) / 8;
+  q.q0l = (const half8*)(qlds) + (c * kQStride + 32 * g) / 8;
 
   SoftState<WIDE> st;
   st.m_ref = -INFINITY;
@@ -661,20 +680,19 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     st.acc1[nb] = st.acc0[nb];
   }
 
-  // ---- stream the share: full 32-token steps with three register buffers in
-  // turn (the code words of the next two steps are in flight while the current
-  // step computes), then at most one masked step for a ragged end.
+  // ---- stream the share: full 32-token steps with two register buffers in
+  // turn (the code words of the next step are in flight while the current step
+  // computes), then at most one masked step for a ragged end.
   int t0 = t_begin;
   if (t0 < t_full) {
-#define TQ_STEP(CUR, NEXT2)                                                                              \
-    if (t0 + 2 * kStep < t_full) load_step(NEXT2, s, lo, t0 + 2 * kStep);                               \
+#define TQ_STEP(CUR, NEXT)                                                                               \
+    if (t0 + kStep < t_full) load_step(NEXT, s, lo, t0 + kStep);                                        \
     scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0); \
     t0 += kStep;                                                                                         \
     if (t0 >= t_full) break;
     while (true) {
-      TQ_STEP(A, Cd)
+      TQ_STEP(A, Bd)
       TQ_STEP(Bd, A)
-      TQ_STEP(Cd, Bd)
     }
 #undef TQ_STEP
   }
