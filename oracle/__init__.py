@@ -1,8 +1,8 @@
 """Plain CPU oracle for TurboQuant KV-cache quantization and decode attention.
 
-TEST INFRASTRUCTURE. Only the tests, the smoke check of the graft entry point and
-the cpu_baseline leg of bench.py may import or run anything in this package. The
-library (decode_attention_tq_amd) never imports it and shares no code with it.
+TEST INFRASTRUCTURE. Only tests/, __graft_entry__.smoke() and the cpu_baseline
+leg of bench.py may import or run anything in this package. The library
+(decode_attention_tq_amd) never imports it and shares no code with it.
 
 Everything is float64 NumPy, written from the method as the pages describe it:
 
@@ -17,8 +17,8 @@ Everything is float64 NumPy, written from the method as the pages describe it:
   (random rotation, scalar quantization, 1-bit QJL on the residual).
 
 Where the pages leave a step open (random generator, code order, bit layout,
-norm storage, attention scale) the readings are stated in each module and listed
-in DESIGN.md.
+norm storage, attention scale) the reading taken is stated in the module that
+implements the step.
 
 Modules:
   rng        SplitMix64 counter generator, uniforms, Box-Muller normals
