@@ -2,10 +2,12 @@
 //
 // decode_scan: one workgroup per (context chunk, KV head, row) that fills a
 // compute unit (16 wavefronts; 8 for the QJL and G > 8 tiles):
-//   prologue  q' = Pi_K q for the G query heads of the KV head (and q'' = S q'
-//             for QJL keys), staged through LDS, scaled by a power of two per
-//             head and split into float16 hi + lo halves (~22 bits together);
-//             the first code words of the scan are already in flight;
+//   prologue  codebook lookup tables in LDS; q' = Pi_K q for the G query heads
+//             of the KV head (and q'' = S q' for QJL keys), with the rows of
+//             the matrix read straight from memory in segments, scaled by a
+//             power of two per head and split into float16 hi + lo halves
+//             (~22 bits together); the first code words of the scan are
+//             already in flight;
 //   scan      each wavefront streams its share of the chunk: scores from the
 //             packed key codes on MFMA, online softmax in registers, values
 //             accumulated in the rotated domain on MFMA;
@@ -71,49 +73,42 @@ __device__ inline float pick16(const float (&c)[16], int idx) {
   return r;
 }
 
-// ------------------------------------------------------ matrices in LDS --
+// ------------------------------------------------------ small matrix work --
 
-constexpr int kRowPad = kD + 4;            // LDS row stride of a staged matrix (16-byte aligned rows)
-constexpr int kMatWords = kD * kRowPad;    // one staged d x d matrix
 constexpr int kVecWords = 16 * kD;         // [16][d] float vectors
 // Column stride (in halves) of the float16 query operand in LDS: the 16 lanes
 // that read one 16-byte piece of 16 different columns then hit distinct banks.
 constexpr int kQStride = kD + 8;
-// Scratch region of a decode workgroup, in 32-bit words: a staged matrix and two
-// vector sets (query prologue, epilogue), the lookup tables (scan) or the
-// wavefront partials (merge), one after the other.
-constexpr int kScratchWords = kMatWords + 2 * kVecWords;
+// Scratch region of a decode workgroup, in 32-bit words: the lookup tables
+// (scan), then the wavefront partials (merge) and the partial sums of the final
+// rotation, followed by two [16][d] float vector sets.
+constexpr int kRegionWords = 16640;
+constexpr int kScratchWords = kRegionWords + 2 * kVecWords;
 
-// Stage the d x d matrix M into LDS (row stride kRowPad) with NT threads:
-// coalesced 16-byte loads, all in flight before the first LDS write.
+// out[h][i] = sum_j M[i][j] in[h][j] for the G heads (in, out: LDS [G][d]).
+// NT threads split each row of M into NT/128 segments: thread (i, s) loads its
+// segment straight from memory (consecutive threads read consecutive 16-byte
+// pieces, so a wavefront reads whole rows), forms the partial dot products of
+// every head, and the segments of a row, held by adjacent lanes, are summed
+// with cross-lane adds. No staging of M, and each element of M is read once.
 template <int NT>
-__device__ void stage_matrix(const float* M, float* lds) {
-  constexpr int PER = kD * kD / 4 / NT;
-  float4 v[PER];
+__device__ void rotate_rows(const float* M, const float* in, float* out, int G) {
+  constexpr int SEGS = NT / 128, W = kD / SEGS;
+  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
+  float4 r[W / 4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) v[k] = ((const float4*)M)[threadIdx.x + NT * k];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int f = threadIdx.x + NT * k;
-    *(float4*)(lds + (f >> 5) * kRowPad + 4 * (f & 31)) = v[k];
-  }
-}
-
-// out[h][i] = sum_j M[i][j] in[h][j] for the G heads from the staged rows;
-// thread (i, h0) computes heads h0, h0 + NT/128, ...
-template <int NT>
-__device__ void matvec_rows(const float* Ml, const float* in, float* out, int G) {
-  const int i = threadIdx.x & 127;
-  const float4* row = (const float4*)(Ml + i * kRowPad);
-  for (int h = threadIdx.x >> 7; h < G; h += NT / 128) {
-    const float4* x = (const float4*)(in + h * kD);
+  for (int k = 0; k < W / 4; ++k) r[k] = *(const float4*)(M + i * kD + sg * W + 4 * k);
+  for (int h = 0; h < G; ++h) {
+    const float4* x = (const float4*)(in + h * kD + sg * W);
     float acc = 0.f;
-#pragma unroll 8
-    for (int j4 = 0; j4 < kD / 4; ++j4) {
-      const float4 r = row[j4], v = x[j4];
-      acc = fmaf(r.w, v.w, fmaf(r.z, v.z, fmaf(r.y, v.y, fmaf(r.x, v.x, acc))));
+#pragma unroll
+    for (int k = 0; k < W / 4; ++k) {
+      const float4 v = x[k];
+      acc = fmaf(r[k].w, v.w, fmaf(r[k].z, v.z, fmaf(r[k].y, v.y, fmaf(r[k].x, v.x, acc))));
     }
-    out[h * kD + i] = acc;
+#pragma unroll
+    for (int m = 1; m < SEGS; m <<= 1) acc += __shfl_xor(acc, m);
+    if (sg == (h % SEGS)) out[h * kD + i] = acc;
   }
 }
 
@@ -242,12 +237,23 @@ struct LaneOffsets {
 // Raw bytes of one 32-token step for one lane. Norms: for G <= 8 the two lanes
 // of a hi/lo column pair split the 8 tokens of their row block (lane half hf
 // takes tokens 4hf .. 4hf+3); for 8 < G <= 16 every lane takes all 8.
+// Norms (and QJL gammas) of the lane's tokens in one step.
+template <int NT, int QJL>
+struct StepNorms {
+  float kn[NT], vn[NT], kg[NT];
+};
+
+// Norms travel with the code words of their step (loaded a step ahead) rather
+// than being loaded when the step starts.
+constexpr bool kNormsAhead = false;
+
 template <int KB, int VB, int QJL, int WIDE>
 struct StepData {
   static constexpr int NT = WIDE ? 8 : 4;
   uint32_t kw[2][KB];
   uint32_t sw[2];
   uint32_t vw[2 * VB];
+  StepNorms<NT, QJL> nm;   // with kNormsAhead
 };
 
 struct Streams {
@@ -283,6 +289,14 @@ __device__ inline void bload_floats_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   for (int i = 0; i < NT; ++i) f[i] = as_float(w[i]);
 }
 
+template <int NT, int QJL>
+__device__ inline void load_norms(StepNorms<NT, QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
+  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0) * 4u;
+  bload_floats_s<NT>(s.rkn, lo.n, st, n.kn);
+  bload_floats_s<NT>(s.rvn, lo.n, st, n.vn);
+  if constexpr (QJL) bload_floats_s<NT>(s.rg, lo.n, st, n.kg);
+}
+
 template <int KB, int VB, int QJL, int WIDE>
 __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo, int t0) {
   constexpr int KW = 4 * KB, VBW = 32 * VB;
@@ -294,22 +308,10 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
     if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, kStreamAux);
   }
   bload_words_s<2 * VB>(s.rv, lo.v, (st / 8u) * (VBW * 4u), d.vw);
+  if constexpr (kNormsAhead) load_norms(d.nm, s, lo, t0);
 }
 
-// Norms (and QJL gammas) of the step: issued when the step starts, consumed
-// after the key MFMAs.
-template <int NT, int QJL>
-struct StepNorms {
-  float kn[NT], vn[NT], kg[NT];
-};
 
-template <int NT, int QJL>
-__device__ inline void load_norms(StepNorms<NT, QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
-  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0) * 4u;
-  bload_floats_s<NT>(s.rkn, lo.n, st, n.kn);
-  bload_floats_s<NT>(s.rvn, lo.n, st, n.vn);
-  if constexpr (QJL) bload_floats_s<NT>(s.rg, lo.n, st, n.kg);
-}
 
 template <int WIDE, int QJL>
 struct QOps {
@@ -338,8 +340,9 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
                                           const uint32_t* lutS, int lane, int tg, int t_end,
                                           const Streams& sm, const LaneOffsets& lo, int t0) {
   constexpr int NT = StepData<KB, VB, QJL, WIDE>::NT;
-  StepNorms<NT, QJL> nm;
-  load_norms(nm, sm, lo, t0);
+  StepNorms<NT, QJL> nml;
+  if constexpr (!kNormsAhead) load_norms(nml, sm, lo, t0);
+  const StepNorms<NT, QJL>& nm = kNormsAhead ? d.nm : nml;
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
   // (two independent accumulation chains; one query block live at a time)
   floatx4 s0[2], s1[2], z0[2], z1[2];
@@ -537,10 +540,12 @@ constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride
 
 template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
-  static_assert(lut_words<KB>() + lut_words<VB>() + (QJL ? 4 : 0) * kLutRep <= kScratchWords,
+  static_assert(lut_words<KB>() + lut_words<VB>() + (QJL ? 4 : 0) * kLutRep <= kRegionWords,
                 "lookup tables exceed the scratch region");
-  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * (kD + 2) <= kMatWords + kVecWords,
-                "merge area overlaps the merged output");
+  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * (kD + 2) <= kRegionWords,
+                "merge area exceeds the scratch region");
+  static_assert(scan_waves<QJL, WIDE>() / 2 * (WIDE ? 16 : 8) * kD <= kRegionWords,
+                "rotation partials exceed the scratch region");
   return (size_t)(scan_head_words<QJL, WIDE>() + kScratchWords) * 4;
 }
 
@@ -565,8 +570,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   float* qcs = (float*)(smem + (1 + QJL) * NQ * kQStride / 2);   // [2][16]
   int* hexp = (int*)(qcs + 32);                            // [16]
   uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
-  float* mat = (float*)U;
-  float* vA = mat + kMatWords;
+  float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
+  float* vA = R + kRegionWords;
   float* vB = vA + kVecWords;
   uint32_t* lutK = U;
   uint32_t* lutV = U + lut_words<KB>();
@@ -614,42 +619,29 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   StepData<KB, VB, QJL, WIDE> A, Bd;
   if (t_begin < t_full) load_step(A, s, lo, t_begin);
 
-  // ---- prologue: the query operand of this (row, KV head)
-  {
-    // the G query vectors ([G][d] contiguous) as float32 in vA, Pi_K in mat
-    constexpr int QPER = 16 * kD / NT;
-    const int64_t q0 = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD;
-    float qx[QPER];
-#pragma unroll
-    for (int k = 0; k < QPER; ++k) {
-      const int idx = tid + NT * k;
-      qx[k] = 0.f;
-      if (idx < G * kD)
-        qx[k] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[q0 + idx])
-                                     : ((const float*)a.q)[q0 + idx];
-    }
-    stage_matrix<NT>(a.rotK, mat);
-#pragma unroll
-    for (int k = 0; k < QPER; ++k) vA[tid + NT * k] = qx[k];
-    __syncthreads();
-    matvec_rows<NT>(mat, vA, vB, G);   // q' = Pi_K q
-    __syncthreads();
-    emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
-    if constexpr (QJL) {
-      stage_matrix<NT>(a.proj, mat);
-      __syncthreads();
-      matvec_rows<NT>(mat, vB, vA, G);   // q'' = S q'
-      __syncthreads();
-      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
-    }
-  }
-  __syncthreads();   // the scratch region becomes the lookup tables
+  // ---- prologue: lookup tables, then the query operand of this (row, KV head)
   build_lut<KB>(lutK, a.kc, tid, NT);
   build_lut<VB>(lutV, a.vc, tid, NT);
   if constexpr (QJL) {
     for (int e = tid; e < NS * kLutRep; e += NT) {
       const int f = e >> kLutShift;
       lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+    }
+  }
+  {
+    // the G query vectors ([G][d] contiguous) as float32 in vA
+    const int64_t q0 = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD;
+    for (int idx = tid; idx < G * kD; idx += NT)
+      vA[idx] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[q0 + idx])
+                                     : ((const float*)a.q)[q0 + idx];
+    __syncthreads();
+    rotate_rows<NT>(a.rotK, vA, vB, G);   // q' = Pi_K q
+    __syncthreads();
+    emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
+    if constexpr (QJL) {
+      rotate_rows<NT>(a.proj, vB, vA, G);   // q'' = S q'
+      __syncthreads();
+      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
     }
   }
   __syncthreads();
@@ -722,7 +714,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // ---- merge the wavefront partials in LDS (fixed order)
   const bool finish = a.n_split == 1;
   __syncthreads();   // every wavefront is done with the lookup tables
-  float* mrg = (float*)U;   // [wave][MC columns][128 + 2]
+  float* mrg = R;   // [wave][MC columns][128 + 2]
   if (c < G) {
     float* dst = mrg + (wave * MC + c) * (kD + 2);
 #pragma unroll
@@ -734,6 +726,16 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       dst[kD] = st.m_off;
       dst[kD + 1] = l;
     }
+  }
+  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, i)
+  // takes column i of Pi_V over rows s*RW .. s*RW+RW-1, loaded now (coalesced
+  // across i) so that the loads are in flight during the merge.
+  constexpr int SEGS = NT / 128, RW = kD / SEGS;
+  const int fi = tid & 127, fs = tid >> 7;
+  float pv[RW];
+  if (finish) {
+#pragma unroll
+    for (int k = 0; k < RW; ++k) pv[k] = a.rotV[(fs * RW + k) * kD + fi];
   }
   __syncthreads();
   for (int idx = tid; idx < G * kD; idx += NT) {
@@ -764,15 +766,24 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
   }
   if (finish) {
-    __syncthreads();   // the merge area becomes Pi_V
-    stage_matrix<NT>(a.rotV, mat);
+    __syncthreads();   // o' is complete in vB; the merge area takes the partial sums
+    float* P = R;      // [SEGS][G][d]
+    for (int h = 0; h < G; ++h) {
+      const float4* x = (const float4*)(vB + h * kD + fs * RW);   // same address across the wavefront
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < RW / 4; ++k) {
+        const float4 v = x[k];
+        acc = fmaf(pv[4 * k + 3], v.w, fmaf(pv[4 * k + 2], v.z, fmaf(pv[4 * k + 1], v.y, fmaf(pv[4 * k], v.x, acc))));
+      }
+      P[(fs * G + h) * kD + fi] = acc;
+    }
     __syncthreads();
-    // out[h][i] = sum_j Pi_V[j][i] o'[h][j]; thread (i, h0) takes heads h0, h0 + NT/128, ...
-    const int i = tid & 127;
-    for (int h = tid >> 7; h < G; h += NT / 128) {
+    for (int idx = tid; idx < G * kD; idx += NT) {
+      const int h = idx / kD, i = idx % kD;
       float r = 0.f;
-#pragma unroll 8
-      for (int j = 0; j < kD; ++j) r = fmaf(mat[j * kRowPad + i], vB[h * kD + j], r);
+#pragma unroll
+      for (int sg = 0; sg < SEGS; ++sg) r += P[(sg * G + h) * kD + i];
       a.out[((int64_t)b * a.H_q + kv * G + h) * kD + i] = r;
     }
   }

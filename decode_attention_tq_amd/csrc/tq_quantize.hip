@@ -16,11 +16,16 @@
 // decision-boundary band.
 //
 // Work decomposition: "slots" enumerate, per (row, head), the token range
-// [floor8(t_offset), ceil8(t_offset + T)); a tile is 16 slots per wavefront, so a
-// tile always holds whole 8-token value blocks and short appends (T = 1) of many
-// heads share one workgroup. Workgroups are persistent: each loads Pi once into
-// LDS (in MFMA operand order) and loops over tiles.
+// [floor8(t_offset), ceil8(t_offset + T)); a tile is 16 or 32 slots per
+// wavefront, so a tile always holds whole 8-token value blocks and short
+// appends (T = 1) of many heads share one workgroup. Workgroups are
+// persistent: each loads Pi once into LDS (in MFMA operand order) and loops
+// over tiles, with the next tile's input in flight. Bulk quantization without
+// QJL uses 32-slot tiles on 32x32x16 MFMAs (16 wavefronts per workgroup);
+// appends and QJL keys use 16-slot tiles on 16x16x32 MFMAs.
 #include <math.h>
+
+#include <atomic>
 
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -119,9 +124,50 @@ __device__ void stage_matrix(const float* M, _Float16* op) {
   }
 }
 
+// Wavefronts per quantize workgroup. Without QJL a workgroup of 8 shares one
+// copy of Pi (64 KB) and two fit a compute unit (16 wavefronts); the QJL
+// variant also holds S and its residual buffers.
+template <int QJL>
+constexpr int quant_waves() { return QJL ? 2 : 8; }
+
+// Wave-local exchange through LDS: the lanes of one wavefront write, then read
+// what other lanes wrote. LDS operations of a wavefront complete in order, so
+// this only has to keep the compiler from moving memory operations across it.
+__device__ inline void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Raw input of one slot-row of a tile: the lane's 32 coordinates, as loaded.
+template <int XF32>
+struct RawX {
+  u32x4 v[XF32 ? 8 : 4];
+  bool valid;
+};
+
+template <int WAVES, int XF32>
+__device__ inline void load_raw(RawX<XF32>& r, const QuantArgs& a, int64_t tile, int wave, int g, int i16) {
+  constexpr int TILE = 16 * WAVES;
+  const int64_t slot = tile * TILE + wave * 16 + i16;
+  const int64_t bh = slot / a.nslot;
+  const int64_t t = a.t_base + slot % a.nslot;
+  r.valid = bh < a.B * a.H_kv && t >= a.t_offset && t < a.t_offset + a.T;
+  if (r.valid) {
+    const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
+    const int64_t off = b * a.sb + (t - a.t_offset) * a.st + h * a.sh + 32 * g;
+    const u32x4* p = XF32 ? (const u32x4*)((const float*)a.x + off) : (const u32x4*)((const uint16_t*)a.x + off);
+#pragma unroll
+    for (int k = 0; k < (XF32 ? 8 : 4); ++k) r.v[k] = p[k];
+  } else {
+#pragma unroll
+    for (int k = 0; k < (XF32 ? 8 : 4); ++k) r.v[k] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <int BITS, int ROLE, int QJL, int XF32>
-__global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) {
-  constexpr int WAVES = QJL ? 2 : 4;
+__global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(QuantArgs a) {
+  constexpr int WAVES = quant_waves<QJL>();
   constexpr int NT = 64 * WAVES;
   constexpr int TILE = 16 * WAVES;
   constexpr int OPH = 4 * 8 * 64 * 8;   // halves per pass of an operand matrix
@@ -133,52 +179,48 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
   unsigned char* cbuf_all = (unsigned char*)(piop + (QJL ? 4 : 2) * OPH);   // WAVES * 16 * 128 bytes
   _Float16* rbuf_all = (_Float16*)(cbuf_all + WAVES * 16 * kD);       // QJL: WAVES * 2 * 16 * 128 halves
 
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, i16 = lane & 15;
+  // the first tile's input is in flight while Pi is staged
+  RawX<XF32> cur;
+  if (blockIdx.x < a.n_tiles) load_raw<WAVES, XF32>(cur, a, blockIdx.x, wave, g, i16);
   stage_matrix<NT>(a.rot, piop);
   if constexpr (QJL) stage_matrix<NT>(a.proj, sop);
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, i16 = lane & 15;
   unsigned char* cbuf = cbuf_all + wave * 16 * kD;
   _Float16* rhi = rbuf_all + wave * 2 * 16 * kD;
   _Float16* rlo = rhi + 16 * kD;
   const float sqrt_d = sqrtf((float)kD);
   const int64_t heads = a.B * a.H_kv;
 
+  // the input of the next tile is loaded while the current one is processed
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    RawX<XF32> nxt;
+    if (tile + gridDim.x < a.n_tiles) load_raw<WAVES, XF32>(nxt, a, tile + gridDim.x, wave, g, i16);
     // ---- slot of this lane (row i16 of the wave's 16)
     const int64_t slot = tile * TILE + wave * 16 + i16;
     const int64_t bh = slot / a.nslot;
     const int64_t t = a.t_base + slot % a.nslot;
-    const bool valid = bh < heads && t >= a.t_offset && t < a.t_offset + a.T;
-    const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
+    const bool valid = cur.valid;
 
-    // ---- load the lane's 32 coordinates (32g .. 32g+31)
+    // ---- the lane's 32 coordinates (32g .. 32g+31) as float32
     float xv[32];
-    if (valid) {
-      const int64_t off = b * a.sb + (t - a.t_offset) * a.st + h * a.sh + 32 * g;
-      if constexpr (XF32) {
-        const float4* p = (const float4*)((const float*)a.x + off);
+    if constexpr (XF32) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float4 v = p[k];
-          xv[4 * k] = v.x; xv[4 * k + 1] = v.y; xv[4 * k + 2] = v.z; xv[4 * k + 3] = v.w;
-        }
-      } else {
-        const u32x4* p = (const u32x4*)((const uint16_t*)a.x + off);
+      for (int k = 0; k < 8; ++k) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const u32x4 v = p[k];
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            xv[8 * k + 2 * u] = __uint_as_float(v[u] << 16);
-            xv[8 * k + 2 * u + 1] = __uint_as_float(v[u] & 0xFFFF0000u);
-          }
-        }
+        for (int u = 0; u < 4; ++u) xv[4 * k + u] = __uint_as_float(cur.v[k][u]);
       }
     } else {
 #pragma unroll
-      for (int k = 0; k < 32; ++k) xv[k] = 0.f;
+      for (int k = 0; k < 4; ++k) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          xv[8 * k + 2 * u] = __uint_as_float(cur.v[k][u] << 16);
+          xv[8 * k + 2 * u + 1] = __uint_as_float(cur.v[k][u] & 0xFFFF0000u);
+        }
+      }
     }
 
     // ---- power-of-two scale, norm
@@ -270,7 +312,7 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
         gam[r] = sqrtf(rs[r]) / sqrt_d;
       }
     }
-    __syncthreads();
+    wave_sync();
 
     if constexpr (QJL) {
       // z' = S rho on MFMA; A operand rows = slots, coordinates 32g + 8ks + e
@@ -280,7 +322,7 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
         ra[ks] = *(const half8*)(rhi + i16 * kD + 32 * g + 8 * ks);
         rl[ks] = *(const half8*)(rlo + i16 * kD + 32 * g + 8 * ks);
       }
-      __syncthreads();
+      wave_sync();
       unsigned char* sbuf = (unsigned char*)rhi;   // reuse: sign bytes [slot][coord]
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
@@ -297,7 +339,7 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
 #pragma unroll
         for (int r = 0; r < 4; ++r) sbuf[(4 * g + r) * kD + 16 * nb + i16] = accv[r] >= 0.f ? 1 : 0;
       }
-      __syncthreads();
+      wave_sync();
       // signs + gamma: lane (v = lane/4, grp = lane%4) packs 32 sign bits of slot v
       {
         const int v = lane >> 2, grp = lane & 3;
@@ -380,7 +422,251 @@ __global__ __launch_bounds__(QJL ? 128 : 256) void quantize_kernel(QuantArgs a) 
         for (int k = 0; k < BITS; ++k) dst[k] = all_valid ? w[k] : ((dst[k] & keep[k]) | w[k]);
       }
     }
-    __syncthreads();
+    wave_sync();   // the code buffer is rewritten by the next tile
+    cur = nxt;
+  }
+}
+
+// ------------------------------------------- quantize, 32-vector tiles --
+//
+// Without QJL the rotation runs on v_mfma_f32_32x32x16_f16 over 32-vector
+// tiles: each B operand read from LDS (a 16 x 32 slice of Pi^T, float16 hi or
+// lo) now serves 32 vectors instead of 16, which halves the LDS traffic per
+// vector (the limit of the 16-vector tiles). A workgroup of 16 wavefronts
+// shares one copy of Pi and fills a compute unit.
+//   A[i][k]  = x of vector i (32 per wave), lane i + 32*(k/8), element k % 8;
+//   B[k][j]  = Pi[j][k], lane j + 32*(k/8);
+//   D[i][j]  lane j + 32*((i/4)%2), element (i%4) + 4*(i/8).
+constexpr int kQ32Waves = 16;
+constexpr int kQ32OpHalves = 8 * 4 * 64 * 8;   // one float16 pass of Pi in B-operand order
+
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ inline floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// op[pass][ks][jb][lane][e] = Pi[32jb + lane%32][16ks + 8(lane/32) + e], hi and lo passes.
+__device__ void stage_matrix32(const float* M, _Float16* op) {
+  constexpr int PER = kD * kD / 4 / (64 * kQ32Waves);
+  float4 v[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) v[k] = ((const float4*)M)[threadIdx.x + k * 64 * kQ32Waves];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = 4 * (threadIdx.x + k * 64 * kQ32Waves);
+    const int row = idx / kD, col = idx % kD;   // Pi[row][col..col+3]
+    const int jb = row >> 5, jl = row & 31;
+    const int ks = col >> 4, kh = (col >> 3) & 1, e = col & 7;   // e is 0 or 4
+    const int o = (((ks * 4 + jb) * 64 + 32 * kh + jl) << 3) + e;
+    const float x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+    _Float16 hi[4], lo[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      hi[u] = (_Float16)x[u];
+      lo[u] = (_Float16)(x[u] - (float)hi[u]);
+    }
+    *(uint2*)(op + o) = make_uint2(pack_half2((float)hi[0], (float)hi[1]), pack_half2((float)hi[2], (float)hi[3]));
+    *(uint2*)(op + kQ32OpHalves + o) =
+        make_uint2(pack_half2((float)lo[0], (float)lo[1]), pack_half2((float)lo[2], (float)lo[3]));
+  }
+}
+
+// The 64 coordinates of one vector that lane (i, kh) holds: 16ks + 8kh + e.
+template <int XF32>
+struct RawX32 {
+  u32x4 v[XF32 ? 16 : 8];
+  bool valid;
+};
+
+template <int XF32>
+__device__ inline void load_raw32(RawX32<XF32>& r, const QuantArgs& a, int64_t tile, int wave, int vi, int kh) {
+  const int64_t slot = tile * (32 * kQ32Waves) + wave * 32 + vi;
+  const int64_t bh = slot / a.nslot;
+  const int64_t t = a.t_base + slot % a.nslot;
+  r.valid = bh < a.B * a.H_kv && t >= a.t_offset && t < a.t_offset + a.T;
+  if (r.valid) {
+    const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
+    const int64_t off = b * a.sb + (t - a.t_offset) * a.st + h * a.sh + 8 * kh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      if constexpr (XF32) {
+        const u32x4* p = (const u32x4*)((const float*)a.x + off + 16 * ks);
+        r.v[2 * ks] = p[0];
+        r.v[2 * ks + 1] = p[1];
+      } else {
+        r.v[ks] = *(const u32x4*)((const uint16_t*)a.x + off + 16 * ks);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < (XF32 ? 16 : 8); ++k) r.v[k] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int BITS, int ROLE, int XF32>
+__global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a) {
+  constexpr int TILE = 32 * kQ32Waves;
+  constexpr int KW = 4 * BITS;          // words per key token
+  constexpr int VBW = 32 * BITS;        // words per value block
+  extern __shared__ __align__(16) unsigned char smem[];
+  _Float16* piop = (_Float16*)smem;                                   // 2 passes
+  unsigned char* cbuf_all = (unsigned char*)(piop + 2 * kQ32OpHalves);   // [wave][32][128] codes
+  float* fz_all = (float*)(cbuf_all + kQ32Waves * 32 * kD);            // [wave][32]
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int vi = lane & 31, kh = lane >> 5;
+  // the first tile's input is in flight while Pi is staged
+  RawX32<XF32> cur;
+  if (blockIdx.x < a.n_tiles) load_raw32<XF32>(cur, a, blockIdx.x, wave, vi, kh);
+  stage_matrix32(a.rot, piop);
+  __syncthreads();
+
+  unsigned char* cbuf = cbuf_all + wave * 32 * kD;
+  float* fzb = fz_all + wave * 32;
+  const float sqrt_d = sqrtf((float)kD);
+  const int64_t heads = a.B * a.H_kv;
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    // (float32 input is not prefetched: its raw tile alone takes 64 VGPRs)
+    RawX32<XF32> nxt;
+    if (!XF32 && tile + gridDim.x < a.n_tiles) load_raw32<XF32>(nxt, a, tile + gridDim.x, wave, vi, kh);
+    const int64_t slot = tile * TILE + wave * 32 + vi;
+    const int64_t bh = slot / a.nslot;
+    const int64_t t = a.t_base + slot % a.nslot;
+
+    // ---- the lane's 64 coordinates, x[16ks + 8kh + e]: power-of-two scale
+    // (largest entry in [2^13, 2^14)), norm, float16 A operands (hi, and lo
+    // for float32 input)
+    auto coord = [&](int ks, int e) -> float {
+      if constexpr (XF32) return __uint_as_float(cur.v[2 * ks + (e >> 2)][e & 3]);
+      else return __uint_as_float((e & 1) ? (cur.v[ks][e >> 1] & 0xFFFF0000u) : (cur.v[ks][e >> 1] << 16));
+    };
+    float mx = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(coord(ks, e)));
+    }
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const int sexp = (mx > 0.f) ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    float ss = 0.f;
+    half8 xa[8], xl[8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = ldexpf(coord(ks, e), sexp);
+        ss = fmaf(v, v, ss);
+        const _Float16 hi = (_Float16)v;
+        xa[ks][e] = hi;
+        if constexpr (XF32) xl[ks][e] = (_Float16)(v - (float)hi);
+      }
+    }
+    ss += shfl_xor_f(ss, 32);
+    const float ns = sqrtf(ss);                      // |x| * 2^sexp
+    const float fz = ns > 0.f ? sqrt_d / ns : 0.f;   // z = y_scaled * fz
+    if (kh == 0) fzb[vi] = fz;
+    wave_sync();
+    // scale of the vectors this lane holds in D: i = 8q + 4kh + r
+    float fr[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f4 = *(const float4*)(fzb + 8 * q + 4 * kh);
+      fr[4 * q] = f4.x; fr[4 * q + 1] = f4.y; fr[4 * q + 2] = f4.z; fr[4 * q + 3] = f4.w;
+    }
+
+    // ---- y = Pi x, 32 output coordinates at a time, and the codes
+#pragma unroll 1
+    for (int jb = 0; jb < 4; ++jb) {
+      floatx16 acc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int o = ((ks * 4 + jb) * 64 + lane) << 3;
+        const half8 bh8 = *(const half8*)(piop + o);
+        const half8 bl8 = *(const half8*)(piop + kQ32OpHalves + o);
+        acc = mfma32(xa[ks], bh8, acc);
+        acc = mfma32(xa[ks], bl8, acc);
+        if constexpr (XF32) acc = mfma32(xl[ks], bh8, acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int i = 8 * (e >> 2) + 4 * kh + (e & 3);
+        cbuf[i * kD + 32 * jb + vi] = (unsigned char)encode<BITS>(acc[e] * fr[e], a.thr);
+      }
+    }
+
+    // ---- norm
+    if (cur.valid && kh == 0) a.norms[bh * a.T_cap + t] = ldexpf(ns, -sexp);
+    wave_sync();
+
+    // ---- pack and store codes, 16 vectors per pass
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      if constexpr (ROLE == TQ_KEYS) {
+        const int v = 16 * pass + (lane >> 2), grp = lane & 3;
+        const int64_t s2 = tile * TILE + wave * 32 + v;
+        const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+        const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
+        uint32_t q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kD + 32 * grp + 4 * k);
+        uint32_t w[BITS];
+        pack32<BITS>(q, w);
+        if (ok) {
+          uint32_t* dst = a.codes + (bh2 * a.T_cap + t2) * KW + grp * BITS;
+#pragma unroll
+          for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+        }
+      } else {
+        // lane (blk, cg): coordinates 4cg .. 4cg+3 of the 8 tokens of block 2*pass + blk
+        const int blk = 2 * pass + (lane >> 5), cg = lane & 31;
+        const int64_t s0 = tile * TILE + wave * 32 + 8 * blk;
+        const int64_t bh2 = s0 / a.nslot, tb = a.t_base + s0 % a.nslot;
+        uint32_t w[BITS], keep[BITS];
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) {
+          w[k] = 0u;
+          keep[k] = 0u;
+        }
+        bool any_valid = false, all_valid = true;
+#pragma unroll
+        for (int ti = 0; ti < 8; ++ti) {
+          const int64_t tt = tb + ti;
+          const bool ok = bh2 < heads && tt >= a.t_offset && tt < a.t_offset + a.T;
+          any_valid |= ok;
+          all_valid &= ok;
+          const uint32_t q4 = *(const uint32_t*)(cbuf + (8 * blk + ti) * kD + 4 * cg);
+#pragma unroll
+          for (int jj = 0; jj < 4; ++jj) {
+            const uint32_t code = (q4 >> (8 * jj)) & 0xFFu;
+            const int pos = BITS * (8 * jj + ti);
+            const int wi = pos >> 5, off = pos & 31;
+            const uint32_t fm = (1u << BITS) - 1u;
+            if (ok) {
+              w[wi] |= code << off;
+              if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
+            } else {
+              keep[wi] |= fm << off;
+              if (off + BITS > 32) keep[wi + 1] |= fm >> (32 - off);
+            }
+          }
+        }
+        if (any_valid) {
+          uint32_t* dst = a.codes + (bh2 * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+#pragma unroll
+          for (int k = 0; k < BITS; ++k) dst[k] = all_valid ? w[k] : ((dst[k] & keep[k]) | w[k]);
+        }
+      }
+    }
+    wave_sync();   // the code buffer and the scales are rewritten by the next tile
+    if constexpr (XF32) {
+      if (tile + gridDim.x < a.n_tiles) load_raw32<XF32>(cur, a, tile + gridDim.x, wave, vi, kh);
+    } else {
+      cur = nxt;
+    }
   }
 }
 
@@ -475,26 +761,67 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
   }
 }
 
+// Compute units of the current device (a per-device cache of a constant
+// attribute; concurrent first calls store the same value).
+int compute_units() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cache[dev].load(std::memory_order_relaxed);
+  if (n == 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
 template <int BITS, int ROLE, int QJL, int XF32>
 hipError_t launch_q(const QuantArgs& qa, hipStream_t stream) {
-  constexpr int WAVES = QJL ? 2 : 4;
+  constexpr int WAVES = quant_waves<QJL>();
   constexpr size_t OPH = 4 * 8 * 64 * 8;
-  const size_t smem = (QJL ? 4 : 2) * OPH * 2 + WAVES * 16 * kD + (QJL ? WAVES * 2 * 16 * kD * 2 : 0);
+  constexpr size_t smem = (QJL ? 4 : 2) * OPH * 2 + WAVES * 16 * kD + (QJL ? WAVES * 2 * 16 * kD * 2 : 0);
   auto kern = quantize_kernel<BITS, ROLE, QJL, XF32>;
-  hipError_t e = hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-  if (e != hipSuccess) return e;
-  int dev = 0, ncu = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
-  const int per_cu = QJL ? 1 : 2;
-  int64_t grid = (int64_t)ncu * per_cu;
+  // more than 64 KB of dynamic LDS needs the opt-in, once per process
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  const int per_cu = QJL ? 1 : 2;   // workgroups that fit a compute unit's 160 KB of LDS
+  int64_t grid = (int64_t)compute_units() * per_cu;
   if (grid > qa.n_tiles) grid = qa.n_tiles;
   if (grid < 1) grid = 1;
   hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * WAVES), smem, stream, qa);
   return hipGetLastError();
 }
 
+template <int BITS, int ROLE, int XF32>
+hipError_t launch_q32(const QuantArgs& qa, hipStream_t stream) {
+  constexpr size_t smem = 2 * kQ32OpHalves * 2 + kQ32Waves * 32 * kD + kQ32Waves * 32 * 4;
+  auto kern = quantize32_kernel<BITS, ROLE, XF32>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  int64_t grid = compute_units();   // one workgroup (16 wavefronts, ~130 KB of LDS) per compute unit
+  if (grid > qa.n_tiles) grid = qa.n_tiles;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kQ32Waves), smem, stream, qa);
+  return hipGetLastError();
+}
+
+// Bulk work (at least one 512-slot tile per compute unit) takes the 32-vector
+// tiles; short appends take the 16-vector tiles, which spread the same slots
+// over 4x more workgroups and finish sooner.
 template <int BITS, int ROLE, int QJL>
-hipError_t dispatch_x(int xf32, const QuantArgs& qa, hipStream_t s) {
+hipError_t dispatch_x(int xf32, QuantArgs qa, hipStream_t s) {
+  if constexpr (!QJL) {
+    const int64_t slots = qa.B * qa.H_kv * qa.nslot;
+    const int64_t tiles32 = (slots + 32 * kQ32Waves - 1) / (32 * kQ32Waves);
+    if (tiles32 >= compute_units()) {
+      qa.n_tiles = tiles32;
+      return xf32 ? launch_q32<BITS, ROLE, 1>(qa, s) : launch_q32<BITS, ROLE, 0>(qa, s);
+    }
+  }
+  const int64_t tile16 = 16 * quant_waves<QJL>();
+  qa.n_tiles = (qa.B * qa.H_kv * qa.nslot + tile16 - 1) / tile16;
   return xf32 ? launch_q<BITS, ROLE, QJL, 1>(qa, s) : launch_q<BITS, ROLE, QJL, 0>(qa, s);
 }
 
@@ -536,8 +863,7 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
   qa.t_base = (t_offset / kValueBlock) * kValueBlock;
   const int64_t t_hi = ((t_offset + T + kValueBlock - 1) / kValueBlock) * kValueBlock;
   qa.nslot = t_hi - qa.t_base;
-  const int tile = dst->qjl && dst->role == TQ_KEYS ? 32 : 64;
-  qa.n_tiles = (B * H_kv * qa.nslot + tile - 1) / tile;
+  qa.n_tiles = 0;   // set by the dispatch, which picks the tile shape
   qa.codes = dst->codes;
   qa.norms = dst->norms;
   qa.signs = dst->qjl_signs;

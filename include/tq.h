@@ -15,7 +15,8 @@
  * rotated domain and one inverse rotation produces the output.
  *
  * Conventions (all functions):
- *   - return an int status (TQ_OK = 0); nothing throws; no global mutable state;
+ *   - return an int status (TQ_OK = 0); nothing throws; the only process-wide
+ *     state is cached device attributes and kernel attributes set once;
  *   - argument errors are reported synchronously, before any HIP call;
  *   - device calls are asynchronous on the given hipStream_t (passed as void*,
  *     NULL = the default stream); a failed launch returns TQ_ERR_DEVICE, a fault
