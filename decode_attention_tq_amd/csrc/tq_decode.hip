@@ -56,6 +56,8 @@ namespace tq {
 
 namespace {
 
+typedef float float2v __attribute__((ext_vector_type(2)));
+
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kSlack = 2.0f;
 constexpr float kShift = kSlack + 3.5f;   // + log2(sqrt(128))
@@ -315,18 +317,10 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
 
 template <int WIDE, int QJL>
 struct QOps {
-  half8 q1[4], r0[4], r1[4];
-  const half8* q0l;   // LDS copy of this lane's column-c operand (4 x 8 halves), shared by the workgroup
+  half8 q0[4], q1[4], r0[4], r1[4];   // column c (and c + 16), coordinates 32g + 8kk + 0..7
   float cs1, cs2;
   bool hf;   // G <= 8: lane holds the lo half of its query column (column >= 8)
 };
-
-// Keeps a value opaque to the optimizer inside a loop (no instruction emitted),
-// so loads that depend on it are repeated instead of kept live in registers.
-__device__ inline uint32_t opaque(uint32_t x) {
-  asm volatile("" : "+v"(x));
-  return x;
-}
 
 template <int WIDE>
 struct SoftState {
@@ -354,13 +348,11 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     z1[m] = s0[m];
   }
   {
-    const half8* ql = (const half8*)((const char*)q.q0l + opaque(0u));
 #define TQ_QK(KK)                                                     \
     {                                                                 \
-      const half8 qk = ql[KK];                                        \
       _Pragma("unroll") for (int m = 0; m < 2; ++m) {                 \
         const half8 ka = key_operand<KB, KK>(d.kw[m], lutK, lane);    \
-        s0[m] = mfma16(ka, qk, s0[m]);                                \
+        s0[m] = mfma16(ka, q.q0[KK], s0[m]);                          \
         if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);      \
       }                                                               \
     }
@@ -436,10 +428,14 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     uint32_t hi2[2], lo2[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const _Float16 h0 = (_Float16)w[2 * k], h1 = (_Float16)w[2 * k + 1];
-      hi2[k] = __builtin_bit_cast(uint32_t, half2v{h0, h1});
-      lo2[k] = __builtin_bit_cast(uint32_t, half2v{(_Float16)(w[2 * k] - (float)h0),
-                                                   (_Float16)(w[2 * k + 1] - (float)h1)});
+      // w stays a float32 value in a register (empty asm), so the conversions are
+      // plain packed converts rather than fused mixed-precision FMAs
+      float a0 = w[2 * k], a1 = w[2 * k + 1];
+      asm volatile("" : "+v"(a0), "+v"(a1));
+      const half2v h = __builtin_convertvector((float2v){a0, a1}, half2v);
+      hi2[k] = __builtin_bit_cast(uint32_t, h);
+      const half2v l = __builtin_convertvector((float2v){a0 - (float)h[0], a1 - (float)h[1]}, half2v);
+      lo2[k] = __builtin_bit_cast(uint32_t, l);
     }
     // the hi lane keeps hi of tokens 0-3 and needs hi of tokens 4-7 from its partner;
     // the lo lane keeps lo of tokens 4-7 and needs lo of tokens 0-3
@@ -650,6 +646,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   QOps<WIDE, QJL> q;
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk) {
+    q.q0[kk] = *(const half8*)(qlds + c * kQStride + 32 * g + 8 * kk);
     if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * kQStride + 32 * g + 8 * kk);
     if constexpr (QJL) {
       q.r0[kk] = *(const half8*)(qlds + (NQ + c) * kQStride + 32 * g + 8 * kk);
@@ -660,7 +657,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   q.cs1 = qcs[hc];
   q.cs2 = QJL ? qcs[16 + hc] : 0.f;
   q.hf = hf;
-  q.q0l = (const half8*)(qlds) + (c * kQStride + 32 * g) / 8;
+
 
   SoftState<WIDE> st;
   st.m_ref = -INFINITY;
