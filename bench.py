@@ -224,8 +224,20 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    dec_ms = sum(b.elapsed_time(c) for a, b, c in evs) / args.steps
+    dec_list = sorted(b.elapsed_time(c) for a, b, c in evs)
+    dec_ms = sum(dec_list) / args.steps
     app_ms = sum(a.elapsed_time(b) for a, b, c in evs) / args.steps
+    dec_med = dec_list[len(dec_list) // 2]
+    dec_p10, dec_p90 = dec_list[len(dec_list) // 10], dec_list[(9 * len(dec_list)) // 10]
+
+    # decode alone, back to back (no appends in between), for reference
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(50):
+        tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    dec_only_us = e0.elapsed_time(e1) / 50 * 1e3
     dbytes = decode_bytes(w, T)
     n_split = tq.decode_splits(w.B, w.H_kv, T)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
@@ -262,7 +274,9 @@ def main():
                                 + (" (the whole tq_decode_attention call: one launch)" if n_split == 1
                                    else f" + combine_kernel ({n_split} context chunks)")),
                      "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
-        "decode": {"us": dec_ms * 1e3, "kv_tokens_per_s": w.B * T / (dec_ms * 1e-3),
+        "decode": {"us": dec_ms * 1e3, "us_median": dec_med * 1e3, "us_p10": dec_p10 * 1e3,
+                   "us_p90": dec_p90 * 1e3, "us_back_to_back": dec_only_us,
+                   "kv_tokens_per_s": w.B * T / (dec_ms * 1e-3),
                    "tokens_per_s": w.B / (dec_ms * 1e-3), "append_us": app_ms * 1e3},
         "quantize_prefill": {"ms": pre, "vectors": ntok, "GB_s": qbytes / (pre * 1e-3) / 1e9,
                              "hbm_frac": qbytes / (pre * 1e-3) / 1e9 / HBM_PEAK_GBS,

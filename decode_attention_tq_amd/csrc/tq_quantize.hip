@@ -670,6 +670,139 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
   }
 }
 
+// ------------------------------------------------- single-token append --
+//
+// One token per (row, head) (T = 1) without QJL: latency, not throughput,
+// decides here, so the rotation runs as float32 FMAs with the rows of Pi read
+// straight from memory (no LDS staging of Pi, no operand split), 8 vectors per
+// 256-thread workgroup. Same steps as the tiled kernels: power-of-two scale,
+// norm, y = Pi x, threshold search, packing (a value block keeps the bits of
+// its other tokens).
+constexpr int kAppendVecs = 8;
+
+template <int BITS, int ROLE, int XF32>
+__global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
+  constexpr int KW = 4 * BITS;          // words per key token
+  constexpr int VBW = 32 * BITS;        // words per value block
+  __shared__ __align__(16) float xs[kAppendVecs][kD];
+  __shared__ __align__(16) unsigned char cb[kAppendVecs][kD];
+  __shared__ float fzs[kAppendVecs];
+  const int tid = threadIdx.x;
+  const int64_t nvec = a.B * a.H_kv;
+  const int64_t v0 = (int64_t)blockIdx.x * kAppendVecs;
+  const float sqrt_d = sqrtf((float)kD);
+
+  // this thread's half row of Pi: row i, columns 64s .. 64s+63
+  const int i = tid >> 1, s = tid & 1;
+  float4 pr[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) pr[k] = ((const float4*)(a.rot + i * kD + 64 * s))[k];
+
+  {
+    // thread (v, c4): coordinates 4c4 .. 4c4+3 of vector v
+    const int v = tid >> 5, c4 = tid & 31;
+    const int64_t gv = v0 + v;
+    const bool ok = gv < nvec;
+    const int64_t b = gv / a.H_kv, h = gv % a.H_kv;
+    float x[4] = {0.f, 0.f, 0.f, 0.f};
+    if (ok) {
+      const int64_t off = b * a.sb + h * a.sh + 4 * c4;
+      if constexpr (XF32) {
+        const float4 f = *(const float4*)((const float*)a.x + off);
+        x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)a.x + off);
+        x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      }
+    }
+    float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    const int sexp = (mx > 0.f) ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      x[u] = ldexpf(x[u], sexp);
+      ss = fmaf(x[u], x[u], ss);
+    }
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m);
+    const float ns = sqrtf(ss);   // |x| * 2^sexp
+    *(float4*)&xs[v][4 * c4] = make_float4(x[0], x[1], x[2], x[3]);
+    if (c4 == 0) {
+      fzs[v] = ns > 0.f ? sqrt_d / ns : 0.f;
+      if (ok) a.norms[gv * a.T_cap + a.t_offset] = ldexpf(ns, -sexp);
+    }
+  }
+  __syncthreads();
+
+  // y_i = sum_j Pi[i][j] x_j for the 8 vectors; the two halves of a row sit in
+  // adjacent lanes
+#pragma unroll
+  for (int v = 0; v < kAppendVecs; ++v) {
+    const float4* xv = (const float4*)&xs[v][64 * s];
+    float acc = 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const float4 q = xv[k];
+      acc = fmaf(pr[k].w, q.w, fmaf(pr[k].z, q.z, fmaf(pr[k].y, q.y, fmaf(pr[k].x, q.x, acc))));
+    }
+    acc += __shfl_xor(acc, 1);
+    if (s == (v & 1)) cb[v][i] = (unsigned char)encode<BITS>(acc * fzs[v], a.thr);
+  }
+  __syncthreads();
+
+  if constexpr (ROLE == TQ_KEYS) {
+    if (tid < 4 * kAppendVecs) {
+      const int v = tid >> 2, grp = tid & 3;
+      const int64_t gv = v0 + v;
+      if (gv < nvec) {
+        uint32_t q[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)&cb[v][32 * grp + 4 * k];
+        uint32_t w[BITS];
+        pack32<BITS>(q, w);
+        uint32_t* dst = a.codes + (gv * a.T_cap + a.t_offset) * KW + grp * BITS;
+#pragma unroll
+        for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+      }
+    }
+  } else {
+    // thread (v, cg): the BITS words of the block record that hold coordinates
+    // 4cg .. 4cg+3 of all 8 tokens; only the new token's bits change
+    const int v = tid >> 5, cg = tid & 31;
+    const int64_t gv = v0 + v;
+    if (gv < nvec) {
+      const int64_t tb = a.t_offset & ~(int64_t)7;
+      const int ti = (int)(a.t_offset & 7);
+      uint32_t w[BITS], clr[BITS];
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) {
+        w[k] = 0u;
+        clr[k] = 0u;
+      }
+      const uint32_t q4 = *(const uint32_t*)&cb[v][4 * cg];
+      constexpr uint32_t fm = (1u << BITS) - 1u;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const uint32_t code = (q4 >> (8 * jj)) & 0xFFu;
+        const int pos = BITS * (8 * jj + ti);
+        const int wi = pos >> 5, off = pos & 31;
+        w[wi] |= code << off;
+        clr[wi] |= fm << off;
+        if (off + BITS > 32) {
+          w[wi + 1] |= code >> (32 - off);
+          clr[wi + 1] |= fm >> (32 - off);
+        }
+      }
+      uint32_t* dst = a.codes + (gv * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) dst[k] = (dst[k] & ~clr[k]) | w[k];
+    }
+  }
+}
+
 // ------------------------------------------------------------- dequantize --
 
 struct DequantArgs {
@@ -845,6 +978,19 @@ hipError_t dispatch_dq(int role, int qjl, const DequantArgs& da, int64_t B, hipS
   return qjl ? launch_dq<BITS, TQ_KEYS, 1>(da, B, s) : launch_dq<BITS, TQ_KEYS, 0>(da, B, s);
 }
 
+template <int BITS, int ROLE, int XF32>
+hipError_t launch_append(const QuantArgs& qa, hipStream_t stream) {
+  const int64_t grid = (qa.B * qa.H_kv + kAppendVecs - 1) / kAppendVecs;
+  hipLaunchKernelGGL((append_kernel<BITS, ROLE, XF32>), dim3((unsigned)grid), dim3(256), 0, stream, qa);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t dispatch_append(int role, int xf32, const QuantArgs& qa, hipStream_t s) {
+  if (role == TQ_VALUES) return xf32 ? launch_append<BITS, TQ_VALUES, 1>(qa, s) : launch_append<BITS, TQ_VALUES, 0>(qa, s);
+  return xf32 ? launch_append<BITS, TQ_KEYS, 1>(qa, s) : launch_append<BITS, TQ_KEYS, 0>(qa, s);
+}
+
 }  // namespace
 
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
@@ -876,6 +1022,13 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
   for (int i = L - 1; i < 16; ++i) qa.thr[i] = INFINITY;
   const int xf32 = x_dtype == TQ_F32;
   const int qjl = dst->role == TQ_KEYS && dst->qjl;
+  if (T == 1 && !qjl) {
+    switch (dst->bits) {
+      case 2: return dispatch_append<2>(dst->role, xf32, qa, stream);
+      case 3: return dispatch_append<3>(dst->role, xf32, qa, stream);
+      default: return dispatch_append<4>(dst->role, xf32, qa, stream);
+    }
+  }
   switch (dst->bits) {
     case 2: return dispatch_role<2>(dst->role, qjl, xf32, qa, stream);
     case 3: return dispatch_role<3>(dst->role, qjl, xf32, qa, stream);

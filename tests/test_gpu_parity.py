@@ -198,12 +198,33 @@ def test_ragged_context_lengths(tq):
             assert rel_l2(out[b], ref) <= TOL_ATTN, b
 
 
+def _check_against_oracle(tq, w, model, which, cache, T):
+    """Codes (outside the boundary band), norms (and QJL bits) of a cache against
+    the oracle's quantization of the workload."""
+    bits = w.k_bits if which == "k" else w.v_bits
+    thr = model.tK if which == "k" else model.tV
+    heads = model.heads(which)
+    codes = cache.codes.cpu().numpy()
+    norms = cache.norms.cpu().numpy()
+    out = n = 0
+    for (b, h), ref in heads.items():
+        _, mo, c = code_mismatch(which, codes[b, h], ref, bits, thr, T)
+        out, n = out + mo, n + c
+        nr = norms[b, h, :T].astype(np.float64)
+        want = ref["norm"].astype(np.float64)
+        assert np.all(np.abs(nr - want) <= 1e-6 * np.maximum(want, 1e-30)), (which, b, h)
+    assert out == 0, (which, out, n)
+
+
 def test_append_in_pieces_matches_bulk(tq):
     """Writing tokens in pieces (offsets not multiples of 8, single tokens) gives
-    the same bytes as one bulk call, for both layouts."""
+    the bulk result: the same bytes for multi-token pieces, and for single
+    tokens (a separate latency-oriented kernel with float32 rotation) the same
+    codes outside the decision-boundary band and the same norms to 1e-6."""
     w = CASES["qjl_k2v3"].scaled(T=300)
     T_cap = tcap(w.T)
     log("append in pieces")
+    model = OracleModel(w)
     xk, xv = device_inputs(w, "k"), device_inputs(w, "v")
     kb, vb = _lib_caches(tq, w, T_cap)
     tq.quantize_kv(xk, kb)
@@ -214,9 +235,33 @@ def test_append_in_pieces_matches_bulk(tq):
         tq.quantize_kv(xk[:, a:b], kp, t_offset=a)
         tq.quantize_kv(xv[:, a:b], vp, t_offset=a)
     torch.cuda.synchronize()
+    # QJL keys take the tiled kernel for every piece: identical bytes
     assert torch.equal(kb.codes, kp.codes) and torch.equal(kb.norms, kp.norms)
     assert torch.equal(kb.signs, kp.signs) and torch.equal(kb.gamma, kp.gamma)
-    assert torch.equal(vb.codes, vp.codes) and torch.equal(vb.norms, vp.norms)
+    _check_against_oracle(tq, w, model, "v", vp, w.T)
+    # tokens written by multi-token pieces are byte-identical to the bulk call
+    single = {5, 6, 7, 299}
+    multi = [t for t in range(w.T) if t not in single]
+    vbn, vpn = vb.norms.cpu().numpy(), vp.norms.cpu().numpy()
+    assert np.array_equal(vbn[:, :, multi], vpn[:, :, multi])
+
+
+@pytest.mark.parametrize("name", ["stress70b_B2", "llama8b_T2000", "tiny", "qwen_k4v2"])
+def test_single_token_appends_match_oracle(tq, name):
+    """Token-by-token appends (T = 1 at every offset, the decode-step path) of
+    keys and values against the oracle."""
+    w = CASES[name].scaled(T=43)
+    T_cap = tcap(w.T)
+    log(f"single-token appends {name}: B={w.B} H_kv={w.H_kv} K{w.k_bits}/V{w.v_bits} {w.dtype}")
+    model = OracleModel(w)
+    xk, xv = device_inputs(w, "k"), device_inputs(w, "v")
+    kc, vc = _lib_caches(tq, w, T_cap)
+    for t in range(w.T):
+        tq.quantize_kv(xk[:, t:t + 1], kc, t_offset=t)
+        tq.quantize_kv(xv[:, t:t + 1], vc, t_offset=t)
+    torch.cuda.synchronize()
+    _check_against_oracle(tq, w, model, "k", kc, w.T)
+    _check_against_oracle(tq, w, model, "v", vc, w.T)
 
 
 def test_value_block_partial_write_keeps_neighbours(tq):
