@@ -67,13 +67,6 @@ constexpr int kLutShift = 5;             // log2(kLutRep)
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
-// Select c[idx] for a runtime idx < 16 without dynamic register indexing.
-__device__ inline float pick16(const float (&c)[16], int idx) {
-  float r = c[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) r = (idx == i) ? c[i] : r;
-  return r;
-}
 
 // ------------------------------------------------------ small matrix work --
 
@@ -94,19 +87,38 @@ constexpr int kScratchWords = kRegionWords + 2 * kVecWords;
 // every head, and the segments of a row, held by adjacent lanes, are summed
 // with cross-lane adds. No staging of M, and each element of M is read once.
 template <int NT>
-__device__ void rotate_rows(const float* M, const float* in, float* out, int G) {
-  constexpr int SEGS = NT / 128, W = kD / SEGS;
-  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
+struct RowSegment {
+  static constexpr int SEGS = NT / 128, W = kD / SEGS;
   float4 r[W / 4];
+};
+
+// Thread (i, s) of the row split below loads its segment of row i of M.
+template <int NT>
+__device__ inline void load_row_segment(RowSegment<NT>& rs, const float* M) {
+  constexpr int SEGS = RowSegment<NT>::SEGS, W = RowSegment<NT>::W;
+  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
 #pragma unroll
-  for (int k = 0; k < W / 4; ++k) r[k] = *(const float4*)(M + i * kD + sg * W + 4 * k);
+  for (int k = 0; k < W / 4; ++k) rs.r[k] = *(const float4*)(M + i * kD + sg * W + 4 * k);
+}
+
+// out[h][i] = sum_j M[i][j] in[h][j] for the G heads (in, out: LDS [G][d]).
+// NT threads split each row of M into NT/128 segments: thread (i, s) holds its
+// segment (loaded from memory by load_row_segment; consecutive threads read
+// consecutive 16-byte pieces, so a wavefront reads whole rows), forms the
+// partial dot products of every head, and the segments of a row, held by
+// adjacent lanes, are summed with cross-lane adds. No staging of M, and each
+// element of M is read once.
+template <int NT>
+__device__ void rotate_rows(const RowSegment<NT>& rs, const float* in, float* out, int G) {
+  constexpr int SEGS = RowSegment<NT>::SEGS, W = RowSegment<NT>::W;
+  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
   for (int h = 0; h < G; ++h) {
     const float4* x = (const float4*)(in + h * kD + sg * W);
     float acc = 0.f;
 #pragma unroll
     for (int k = 0; k < W / 4; ++k) {
       const float4 v = x[k];
-      acc = fmaf(r[k].w, v.w, fmaf(r[k].z, v.z, fmaf(r[k].y, v.y, fmaf(r[k].x, v.x, acc))));
+      acc = fmaf(rs.r[k].w, v.w, fmaf(rs.r[k].z, v.z, fmaf(rs.r[k].y, v.y, fmaf(rs.r[k].x, v.x, acc))));
     }
 #pragma unroll
     for (int m = 1; m < SEGS; m <<= 1) acc += __shfl_xor(acc, m);
@@ -183,11 +195,11 @@ template <int BITS>
 constexpr int lut_words() { return (1 << (2 * BITS)) * kLutRep; }
 
 template <int BITS>
-__device__ void build_lut(uint32_t* lut, const float (&cb)[16], int tid, int nt) {
+__device__ void build_lut(uint32_t* lut, const float* cb, int tid, int nt) {
   constexpr int m = (1 << BITS) - 1;
   for (int e = tid; e < lut_words<BITS>(); e += nt) {
     const int f = e >> kLutShift;
-    lut[e] = pack_half2(pick16(cb, f & m), pick16(cb, f >> BITS));
+    lut[e] = pack_half2(cb[f & m], cb[f >> BITS]);
   }
 }
 
@@ -532,7 +544,7 @@ constexpr int merge_cols() { return WIDE ? 16 : 8; }
 // ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, then the
 // scratch region.
 template <int QJL, int WIDE>
-constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 48; }
+constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 80; }
 
 template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
@@ -565,6 +577,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   _Float16* qlds = (_Float16*)smem;                              // [1 + QJL][NQ][kQStride]
   float* qcs = (float*)(smem + (1 + QJL) * NQ * kQStride / 2);   // [2][16]
   int* hexp = (int*)(qcs + 32);                            // [16]
+  float* cents = qcs + 48;                                 // [2][16] key, value levels
   uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
   float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
   float* vA = R + kRegionWords;
@@ -616,14 +629,9 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   if (t_begin < t_full) load_step(A, s, lo, t_begin);
 
   // ---- prologue: lookup tables, then the query operand of this (row, KV head)
-  build_lut<KB>(lutK, a.kc, tid, NT);
-  build_lut<VB>(lutV, a.vc, tid, NT);
-  if constexpr (QJL) {
-    for (int e = tid; e < NS * kLutRep; e += NT) {
-      const int f = e >> kLutShift;
-      lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
-    }
-  }
+  if (tid < 32) cents[tid] = tid < 16 ? a.kc[tid] : a.vc[tid - 16];
+  RowSegment<NT> rseg;
+  load_row_segment<NT>(rseg, a.rotK);   // in flight with the query loads
   {
     // the G query vectors ([G][d] contiguous) as float32 in vA
     const int64_t q0 = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD;
@@ -631,11 +639,20 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       vA[idx] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[q0 + idx])
                                      : ((const float*)a.q)[q0 + idx];
     __syncthreads();
-    rotate_rows<NT>(a.rotK, vA, vB, G);   // q' = Pi_K q
+    build_lut<KB>(lutK, cents, tid, NT);
+    build_lut<VB>(lutV, cents + 16, tid, NT);
+    if constexpr (QJL) {
+      for (int e = tid; e < NS * kLutRep; e += NT) {
+        const int f = e >> kLutShift;
+        lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+      }
+    }
+    rotate_rows<NT>(rseg, vA, vB, G);   // q' = Pi_K q
     __syncthreads();
     emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
     if constexpr (QJL) {
-      rotate_rows<NT>(a.proj, vB, vA, G);   // q'' = S q'
+      load_row_segment<NT>(rseg, a.proj);
+      rotate_rows<NT>(rseg, vB, vA, G);   // q'' = S q'
       __syncthreads();
       emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
     }
