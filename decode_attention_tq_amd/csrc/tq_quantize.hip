@@ -49,12 +49,67 @@ struct QuantArgs {
   const float* proj;
   float cent[16];
   float thr[16];
+  int thr_sym;   // the thresholds mirror around 0 (middle one is 0)
 };
 
-// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i,
-// by a branch-free binary search.
+// Thresholds of one codebook held in registers (copied once from the kernel
+// arguments, so the selects below are register selects, not memory loads).
 template <int BITS>
-__device__ inline int encode(float z, const float* t) {
+struct Thresholds {
+  float t[(1 << BITS) - 1];
+  bool sym;   // t[L-2-k] == -t[k] and the middle one is 0
+};
+
+template <int BITS>
+__device__ inline Thresholds<BITS> load_thresholds(const QuantArgs& a) {
+  Thresholds<BITS> th;
+#pragma unroll
+  for (int i = 0; i < (1 << BITS) - 1; ++i) th.t[i] = a.thr[i];
+  th.sym = a.thr_sym != 0;
+  return th;
+}
+
+// (row * H_kv + head, token) of slot s0 + v, for a wave-uniform first slot s0
+// of a wavefront's tile and a small lane offset v: the 64-bit division runs
+// once on the scalar unit, each lane does a 32-bit one (nslot < 2^31).
+__device__ inline void slot_pos(const QuantArgs& a, int64_t s0, uint32_t v, int64_t& bh, int64_t& t) {
+  const int64_t bh0 = s0 / a.nslot;
+  const uint32_t ns = (uint32_t)a.nslot;
+  const uint32_t rr = (uint32_t)(s0 - bh0 * a.nslot) + v;
+  const uint32_t q = rr / ns;
+  bh = bh0 + q;
+  t = a.t_base + (int64_t)(rr - q * ns);
+}
+
+// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i.
+// For a codebook that mirrors around 0 (the canonical one), the search runs on
+// |z| over the positive half and a negative z takes the mirrored cell
+// (2^bits - 1 - cell of |z|); an exact tie with a threshold may then land in
+// the neighbouring cell, which is the decision boundary itself. Otherwise a
+// branch-free binary search over all thresholds.
+template <int BITS>
+__device__ inline int encode(float z, const Thresholds<BITS>& th) {
+  constexpr int half = 1 << (BITS - 1);
+  const float* t = th.t;
+  if (th.sym) {
+    const float* p = t + half;   // positive thresholds
+    const float x = fabsf(z);
+    int n;
+    if constexpr (BITS == 2) {
+      n = x >= p[0];
+    } else if constexpr (BITS == 3) {
+      const bool b1 = x >= p[1];
+      const bool b0 = x >= (b1 ? p[2] : p[0]);
+      n = (b1 << 1) | b0;
+    } else {
+      const bool b2 = x >= p[3];
+      const bool b1 = x >= (b2 ? p[5] : p[1]);
+      const float tc = b2 ? (b1 ? p[6] : p[4]) : (b1 ? p[2] : p[0]);
+      const bool b0 = x >= tc;
+      n = (b2 << 2) | (b1 << 1) | b0;
+    }
+    return (half + n) ^ (z < 0.f ? 2 * half - 1 : 0);
+  }
   if constexpr (BITS == 2) {
     const bool b1 = z >= t[1];
     const bool b0 = z >= (b1 ? t[2] : t[0]);
@@ -70,12 +125,10 @@ __device__ inline int encode(float z, const float* t) {
     const bool b2 = z >= (b3 ? t[11] : t[3]);
     const float t1 = b3 ? (b2 ? t[13] : t[9]) : (b2 ? t[5] : t[1]);
     const bool b1 = z >= t1;
-    const int base = (b3 << 3) | (b2 << 2) | (b1 << 1);
-    float t0 = t[0];
-#pragma unroll
-    for (int i = 2; i < 16; i += 2) t0 = (base == i) ? t[i] : t0;
+    const float t0 = b3 ? (b2 ? (b1 ? t[14] : t[12]) : (b1 ? t[10] : t[8]))
+                        : (b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]));
     const bool b0 = z >= t0;
-    return base | b0;
+    return (b3 << 3) | (b2 << 2) | (b1 << 1) | b0;
   }
 }
 
@@ -149,9 +202,8 @@ struct RawX {
 template <int WAVES, int XF32>
 __device__ inline void load_raw(RawX<XF32>& r, const QuantArgs& a, int64_t tile, int wave, int g, int i16) {
   constexpr int TILE = 16 * WAVES;
-  const int64_t slot = tile * TILE + wave * 16 + i16;
-  const int64_t bh = slot / a.nslot;
-  const int64_t t = a.t_base + slot % a.nslot;
+  int64_t bh, t;
+  slot_pos(a, tile * TILE + wave * 16, i16, bh, t);
   r.valid = bh < a.B * a.H_kv && t >= a.t_offset && t < a.t_offset + a.T;
   if (r.valid) {
     const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
@@ -168,6 +220,7 @@ __device__ inline void load_raw(RawX<XF32>& r, const QuantArgs& a, int64_t tile,
 template <int BITS, int ROLE, int QJL, int XF32>
 __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(QuantArgs a) {
   constexpr int WAVES = quant_waves<QJL>();
+  const Thresholds<BITS> th = load_thresholds<BITS>(a);
   constexpr int NT = 64 * WAVES;
   constexpr int TILE = 16 * WAVES;
   constexpr int OPH = 4 * 8 * 64 * 8;   // halves per pass of an operand matrix
@@ -179,7 +232,7 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
   unsigned char* cbuf_all = (unsigned char*)(piop + (QJL ? 4 : 2) * OPH);   // WAVES * 16 * 128 bytes
   _Float16* rbuf_all = (_Float16*)(cbuf_all + WAVES * 16 * kD);       // QJL: WAVES * 2 * 16 * 128 halves
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, i16 = lane & 15;
   // the first tile's input is in flight while Pi is staged
   RawX<XF32> cur;
@@ -199,9 +252,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
     RawX<XF32> nxt;
     if (tile + gridDim.x < a.n_tiles) load_raw<WAVES, XF32>(nxt, a, tile + gridDim.x, wave, g, i16);
     // ---- slot of this lane (row i16 of the wave's 16)
-    const int64_t slot = tile * TILE + wave * 16 + i16;
-    const int64_t bh = slot / a.nslot;
-    const int64_t t = a.t_base + slot % a.nslot;
+    int64_t bh, t;
+    slot_pos(a, tile * TILE + wave * 16, i16, bh, t);
     const bool valid = cur.valid;
 
     // ---- the lane's 32 coordinates (32g .. 32g+31) as float32
@@ -282,7 +334,7 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
       for (int r = 0; r < 4; ++r) {
         const float z = y[nb][r] * fr[r];
         y[nb][r] = z;
-        code[nb][r] = encode<BITS>(z, a.thr);
+        code[nb][r] = encode<BITS>(z, th);
         cbuf[(4 * g + r) * kD + 16 * nb + i16] = (unsigned char)code[nb][r];
       }
     }
@@ -343,8 +395,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
       // signs + gamma: lane (v = lane/4, grp = lane%4) packs 32 sign bits of slot v
       {
         const int v = lane >> 2, grp = lane & 3;
-        const int64_t s2 = tile * TILE + wave * 16 + v;
-        const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+        int64_t bh2, t2;
+        slot_pos(a, tile * TILE + wave * 16, v, bh2, t2);
         const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
         const uint32_t* q = (const uint32_t*)(sbuf + v * kD + 32 * grp);
         uint32_t wbits = 0u;
@@ -356,8 +408,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
       if (i16 == 0) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          const int64_t s2 = tile * TILE + wave * 16 + 4 * g + r;
-          const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+          int64_t bh2, t2;
+          slot_pos(a, tile * TILE + wave * 16, 4 * g + r, bh2, t2);
           if (bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T) a.gamma[bh2 * a.T_cap + t2] = gam[r];
         }
       }
@@ -369,8 +421,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
     // ---- pack and store codes
     if constexpr (ROLE == TQ_KEYS) {
       const int v = lane >> 2, grp = lane & 3;
-      const int64_t s2 = tile * TILE + wave * 16 + v;
-      const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+      int64_t bh2, t2;
+      slot_pos(a, tile * TILE + wave * 16, v, bh2, t2);
       const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
       uint32_t q[8];
 #pragma unroll
@@ -385,8 +437,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
     } else {
       // lane (blk = lane/32, cg = lane%32): coordinates 4cg .. 4cg+3 of the block's 8 tokens
       const int blk = lane >> 5, cg = lane & 31;
-      const int64_t s0 = tile * TILE + wave * 16 + 8 * blk;   // first slot of the block
-      const int64_t bh2 = s0 / a.nslot, tb = a.t_base + s0 % a.nslot;
+      int64_t bh2, tb;   // the block's first slot
+      slot_pos(a, tile * TILE + wave * 16, 8 * blk, bh2, tb);
       uint32_t w[BITS];
 #pragma unroll
       for (int k = 0; k < BITS; ++k) w[k] = 0u;
@@ -407,12 +459,12 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
           const int pos = BITS * (8 * jj + ti);
           const int wi = pos >> 5, off = pos & 31;
           const uint32_t fm = (1u << BITS) - 1u;
-          if (ok) {
-            w[wi] |= code << off;
-            if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
-          } else {
-            keep[wi] |= fm << off;
-            if (off + BITS > 32) keep[wi + 1] |= fm >> (32 - off);
+          const uint32_t okm = ok ? ~0u : 0u;   // branch-free: positions are compile-time
+          w[wi] |= (code << off) & okm;
+          keep[wi] |= (fm << off) & ~okm;
+          if (off + BITS > 32) {
+            w[wi + 1] |= (code >> (32 - off)) & okm;
+            keep[wi + 1] |= (fm >> (32 - off)) & ~okm;
           }
         }
       }
@@ -438,7 +490,10 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
 //   B[k][j]  = Pi[j][k], lane j + 32*(k/8);
 //   D[i][j]  lane j + 32*((i/4)%2), element (i%4) + 4*(i/8).
 constexpr int kQ32Waves = 16;
-constexpr int kQ32OpHalves = 8 * 4 * 64 * 8;   // one float16 pass of Pi in B-operand order
+constexpr int kQ32OpHalves = 8 * 4 * 64 * 8;   // one float16 pass of Pi in operand order
+// Row stride (bytes) of a wavefront's code buffer [32 vectors][128 codes]: the
+// 32 lanes that write one 4-code piece of 32 different rows hit distinct banks.
+constexpr int kQ32Row = kD + 4;
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
@@ -481,9 +536,8 @@ struct RawX32 {
 
 template <int XF32>
 __device__ inline void load_raw32(RawX32<XF32>& r, const QuantArgs& a, int64_t tile, int wave, int vi, int kh) {
-  const int64_t slot = tile * (32 * kQ32Waves) + wave * 32 + vi;
-  const int64_t bh = slot / a.nslot;
-  const int64_t t = a.t_base + slot % a.nslot;
+  int64_t bh, t;
+  slot_pos(a, tile * (32 * kQ32Waves) + wave * 32, vi, bh, t);
   r.valid = bh < a.B * a.H_kv && t >= a.t_offset && t < a.t_offset + a.T;
   if (r.valid) {
     const int64_t b = bh / a.H_kv, h = bh % a.H_kv;
@@ -507,14 +561,14 @@ __device__ inline void load_raw32(RawX32<XF32>& r, const QuantArgs& a, int64_t t
 template <int BITS, int ROLE, int XF32>
 __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a) {
   constexpr int TILE = 32 * kQ32Waves;
+  const Thresholds<BITS> th = load_thresholds<BITS>(a);
   constexpr int KW = 4 * BITS;          // words per key token
   constexpr int VBW = 32 * BITS;        // words per value block
   extern __shared__ __align__(16) unsigned char smem[];
   _Float16* piop = (_Float16*)smem;                                   // 2 passes
-  unsigned char* cbuf_all = (unsigned char*)(piop + 2 * kQ32OpHalves);   // [wave][32][128] codes
-  float* fz_all = (float*)(cbuf_all + kQ32Waves * 32 * kD);            // [wave][32]
+  unsigned char* cbuf_all = (unsigned char*)(piop + 2 * kQ32OpHalves);   // [wave][32][kQ32Row] codes
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int vi = lane & 31, kh = lane >> 5;
   // the first tile's input is in flight while Pi is staged
   RawX32<XF32> cur;
@@ -522,8 +576,7 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
   stage_matrix32(a.rot, piop);
   __syncthreads();
 
-  unsigned char* cbuf = cbuf_all + wave * 32 * kD;
-  float* fzb = fz_all + wave * 32;
+  unsigned char* cbuf = cbuf_all + wave * 32 * kQ32Row;
   const float sqrt_d = sqrtf((float)kD);
   const int64_t heads = a.B * a.H_kv;
 
@@ -531,9 +584,8 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
     // (float32 input is not prefetched: its raw tile alone takes 64 VGPRs)
     RawX32<XF32> nxt;
     if (!XF32 && tile + gridDim.x < a.n_tiles) load_raw32<XF32>(nxt, a, tile + gridDim.x, wave, vi, kh);
-    const int64_t slot = tile * TILE + wave * 32 + vi;
-    const int64_t bh = slot / a.nslot;
-    const int64_t t = a.t_base + slot % a.nslot;
+    int64_t bh, t;
+    slot_pos(a, tile * TILE + wave * 32, vi, bh, t);
 
     // ---- the lane's 64 coordinates, x[16ks + 8kh + e]: power-of-two scale
     // (largest entry in [2^13, 2^14)), norm, float16 A operands (hi, and lo
@@ -566,17 +618,11 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
     ss += shfl_xor_f(ss, 32);
     const float ns = sqrtf(ss);                      // |x| * 2^sexp
     const float fz = ns > 0.f ? sqrt_d / ns : 0.f;   // z = y_scaled * fz
-    if (kh == 0) fzb[vi] = fz;
-    wave_sync();
-    // scale of the vectors this lane holds in D: i = 8q + 4kh + r
-    float fr[16];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float4 f4 = *(const float4*)(fzb + 8 * q + 4 * kh);
-      fr[4 * q] = f4.x; fr[4 * q + 1] = f4.y; fr[4 * q + 2] = f4.z; fr[4 * q + 3] = f4.w;
-    }
 
-    // ---- y = Pi x, 32 output coordinates at a time, and the codes
+    // ---- y = Pi x, 32 output coordinates at a time, and the codes. With Pi
+    // as the A operand and x as B, lane (vi, kh) receives coordinates
+    // 32jb + 8q + 4kh + r (element 4q + r) of its own vector vi, so four
+    // adjacent codes leave as one 32-bit LDS write.
 #pragma unroll 1
     for (int jb = 0; jb < 4; ++jb) {
       floatx16 acc;
@@ -587,14 +633,16 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
         const int o = ((ks * 4 + jb) * 64 + lane) << 3;
         const half8 bh8 = *(const half8*)(piop + o);
         const half8 bl8 = *(const half8*)(piop + kQ32OpHalves + o);
-        acc = mfma32(xa[ks], bh8, acc);
-        acc = mfma32(xa[ks], bl8, acc);
-        if constexpr (XF32) acc = mfma32(xl[ks], bh8, acc);
+        acc = mfma32(bh8, xa[ks], acc);
+        acc = mfma32(bl8, xa[ks], acc);
+        if constexpr (XF32) acc = mfma32(bh8, xl[ks], acc);
       }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int i = 8 * (e >> 2) + 4 * kh + (e & 3);
-        cbuf[i * kD + 32 * jb + vi] = (unsigned char)encode<BITS>(acc[e] * fr[e], a.thr);
+      for (int q = 0; q < 4; ++q) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) word |= (uint32_t)encode<BITS>(acc[4 * q + r] * fz, th) << (8 * r);
+        *(uint32_t*)(cbuf + vi * kQ32Row + 32 * jb + 8 * q + 4 * kh) = word;
       }
     }
 
@@ -607,12 +655,12 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
     for (int pass = 0; pass < 2; ++pass) {
       if constexpr (ROLE == TQ_KEYS) {
         const int v = 16 * pass + (lane >> 2), grp = lane & 3;
-        const int64_t s2 = tile * TILE + wave * 32 + v;
-        const int64_t bh2 = s2 / a.nslot, t2 = a.t_base + s2 % a.nslot;
+        int64_t bh2, t2;
+        slot_pos(a, tile * TILE + wave * 32, v, bh2, t2);
         const bool ok = bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T;
         uint32_t q[8];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kD + 32 * grp + 4 * k);
+        for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kQ32Row + 32 * grp + 4 * k);
         uint32_t w[BITS];
         pack32<BITS>(q, w);
         if (ok) {
@@ -623,8 +671,8 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
       } else {
         // lane (blk, cg): coordinates 4cg .. 4cg+3 of the 8 tokens of block 2*pass + blk
         const int blk = 2 * pass + (lane >> 5), cg = lane & 31;
-        const int64_t s0 = tile * TILE + wave * 32 + 8 * blk;
-        const int64_t bh2 = s0 / a.nslot, tb = a.t_base + s0 % a.nslot;
+        int64_t bh2, tb;   // the block's first slot
+        slot_pos(a, tile * TILE + wave * 32, 8 * blk, bh2, tb);
         uint32_t w[BITS], keep[BITS];
 #pragma unroll
         for (int k = 0; k < BITS; ++k) {
@@ -638,19 +686,19 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
           const bool ok = bh2 < heads && tt >= a.t_offset && tt < a.t_offset + a.T;
           any_valid |= ok;
           all_valid &= ok;
-          const uint32_t q4 = *(const uint32_t*)(cbuf + (8 * blk + ti) * kD + 4 * cg);
+          const uint32_t q4 = *(const uint32_t*)(cbuf + (8 * blk + ti) * kQ32Row + 4 * cg);
 #pragma unroll
           for (int jj = 0; jj < 4; ++jj) {
             const uint32_t code = (q4 >> (8 * jj)) & 0xFFu;
             const int pos = BITS * (8 * jj + ti);
             const int wi = pos >> 5, off = pos & 31;
             const uint32_t fm = (1u << BITS) - 1u;
-            if (ok) {
-              w[wi] |= code << off;
-              if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
-            } else {
-              keep[wi] |= fm << off;
-              if (off + BITS > 32) keep[wi + 1] |= fm >> (32 - off);
+            const uint32_t okm = ok ? ~0u : 0u;   // branch-free: positions are compile-time
+            w[wi] |= (code << off) & okm;
+            keep[wi] |= (fm << off) & ~okm;
+            if (off + BITS > 32) {
+              w[wi + 1] |= (code >> (32 - off)) & okm;
+              keep[wi + 1] |= (fm >> (32 - off)) & ~okm;
             }
           }
         }
@@ -687,6 +735,7 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
   __shared__ __align__(16) float xs[kAppendVecs][kD];
   __shared__ __align__(16) unsigned char cb[kAppendVecs][kD];
   __shared__ float fzs[kAppendVecs];
+  const Thresholds<BITS> th = load_thresholds<BITS>(a);
   const int tid = threadIdx.x;
   const int64_t nvec = a.B * a.H_kv;
   const int64_t v0 = (int64_t)blockIdx.x * kAppendVecs;
@@ -749,7 +798,7 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
       acc = fmaf(pr[k].w, q.w, fmaf(pr[k].z, q.z, fmaf(pr[k].y, q.y, fmaf(pr[k].x, q.x, acc))));
     }
     acc += __shfl_xor(acc, 1);
-    if (s == (v & 1)) cb[v][i] = (unsigned char)encode<BITS>(acc * fzs[v], a.thr);
+    if (s == (v & 1)) cb[v][i] = (unsigned char)encode<BITS>(acc * fzs[v], th);
   }
   __syncthreads();
 
@@ -928,7 +977,7 @@ hipError_t launch_q(const QuantArgs& qa, hipStream_t stream) {
 
 template <int BITS, int ROLE, int XF32>
 hipError_t launch_q32(const QuantArgs& qa, hipStream_t stream) {
-  constexpr size_t smem = 2 * kQ32OpHalves * 2 + kQ32Waves * 32 * kD + kQ32Waves * 32 * 4;
+  constexpr size_t smem = 2 * kQ32OpHalves * 2 + kQ32Waves * 32 * kQ32Row;
   auto kern = quantize32_kernel<BITS, ROLE, XF32>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -1020,6 +1069,8 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
   for (int i = 0; i < 16; ++i) qa.cent[i] = i < L ? dst->centroids[i] : 0.f;
   thresholds_from_centroids(dst->centroids, L, qa.thr);
   for (int i = L - 1; i < 16; ++i) qa.thr[i] = INFINITY;
+  qa.thr_sym = qa.thr[L / 2 - 1] == 0.0f;
+  for (int k = 0; k < L / 2 - 1; ++k) qa.thr_sym &= qa.thr[L - 2 - k] == -qa.thr[k];
   const int xf32 = x_dtype == TQ_F32;
   const int qjl = dst->role == TQ_KEYS && dst->qjl;
   if (T == 1 && !qjl) {

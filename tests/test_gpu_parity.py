@@ -303,3 +303,42 @@ def test_degenerate_inputs(tq):
     o1 = tq.decode_attention(kc, vc, q, T=1).cpu().numpy()
     v0 = tq.dequantize(vc, 0, 1).cpu().numpy()[0, 0, 0]
     assert np.allclose(o1[0], np.repeat(v0[None], 8, axis=0), rtol=1e-5, atol=1e-6)
+
+
+@pytest.mark.parametrize("scale", [1e30, 1e-30])
+def test_extreme_magnitudes(tq, scale):
+    """Inputs near the ends of the bfloat16 range (the per-vector power-of-two
+    scaling keeps the rotation and the norm finite and exact to the bar), in
+    bulk and single-token calls, against the oracle on the same bytes."""
+    w = CASES["stress70b_B2"].scaled(T=24)
+    T_cap = tcap(w.T)
+    log(f"extreme magnitudes x{scale:g}")
+    base = {}
+    for which in ("k", "v"):
+        x = torch.from_numpy(tq_synth.kv_full(w, which) * np.float32(scale)).to(torch.bfloat16)
+        base[which] = x
+    # the oracle sees exactly the bfloat16 values the GPU gets
+    model = OracleModel(w)
+    for mode in ("bulk", "single"):
+        kc, vc = _lib_caches(tq, w, T_cap)
+        for which, cache in (("k", kc), ("v", vc)):
+            xd = base[which].to("cuda")
+            if mode == "bulk":
+                tq.quantize_kv(xd, cache)
+            else:
+                for t in range(w.T):
+                    tq.quantize_kv(xd[:, t:t + 1], cache, t_offset=t)
+        torch.cuda.synchronize()
+        for which, cache in (("k", kc), ("v", vc)):
+            bits = w.k_bits if which == "k" else w.v_bits
+            thr = model.tK if which == "k" else model.tV
+            xf = base[which].float().numpy().astype(np.float64)
+            codes = cache.codes.cpu().numpy()
+            norms = cache.norms.cpu().numpy()
+            for b in range(w.B):
+                for h in range(w.H_kv):
+                    ref = model.quantize(which, xf[b, :, h])
+                    _, mo, _ = code_mismatch(which, codes[b, h], ref, bits, thr, w.T)
+                    assert mo == 0, (mode, which, b, h)
+                    nr = norms[b, h, :w.T].astype(np.float64)
+                    assert np.all(np.abs(nr - ref["norm"]) <= 1e-6 * ref["norm"]), (mode, which, b, h)
