@@ -806,15 +806,23 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 // ---------------------------------------------------------------- combine --
 
 // Workgroup (kv, b, chunk): merge the context-chunk partials of the G query
-// heads of KV head kv in chunk order (every workgroup of the KV head merges all
-// 128 coordinates; all loads are issued before use), then output coordinates
-// 32*chunk .. 32*chunk+31 of o = Pi_V^T o', with those 32 columns of Pi_V
-// staged in LDS.
+// heads of KV head kv (every workgroup of the KV head merges all 128
+// coordinates), then output coordinates 32*chunk .. 32*chunk+31 of
+// o = Pi_V^T o', with those 32 columns of Pi_V staged in LDS. The merge first
+// takes each head's largest chunk maximum M, then sums the chunks in chunk
+// order with weights 2^(m - M) kept in LDS (blocks of kCombineBlock chunks),
+// so the loads of a thread's chunk partials are independent of each other.
+constexpr int kCombineBlock = 256;
+
 __global__ __launch_bounds__(256) void combine_kernel(const float* ml, const float* acc, const float* rotV,
                                                        float* out, int H_q, int G, int n_split, float inv_sqrt_d) {
   __shared__ __align__(16) float colv[kD * 32];
   __shared__ __align__(16) float ov[16 * kD];
+  __shared__ float wsp[16 * kCombineBlock];
+  __shared__ float Mh[16], dh[16];
   const int kv = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t bh0 = (int64_t)b * H_q + (int64_t)kv * G;
   {
     // Pi_V[j][32*chunk + 0..31] for all j: 1024 16-byte pieces, 4 per thread
     float4 v[4];
@@ -829,27 +837,62 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* ml, const flo
       *(float4*)(colv + 4 * f) = v[k];
     }
   }
-  for (int idx = tid; idx < G * kD; idx += 256) {
-    const int h = idx / kD, j = idx % kD;
-    const int64_t bh = (int64_t)b * H_q + kv * G + h;
-    const float* mlb = ml + bh * n_split * 2;
-    const float* ab = acc + bh * n_split * kD + j;
-    // one pass in chunk order, rescaling the running sums when the maximum grows
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float m = mlb[2 * sp], l = mlb[2 * sp + 1], x = ab[(int64_t)sp * kD];
-      if (m == -INFINITY) continue;
-      if (m > M) {
-        const float f = __builtin_amdgcn_exp2f(M - m);
-        num *= f;
-        den *= f;
-        M = m;
+  // per-head maximum of the chunk maxima: wavefront w takes heads w, w + 4, ...
+  for (int h = wave; h < G; h += 4) {
+    const float* mlb = ml + (bh0 + h) * n_split * 2;
+    float M = -INFINITY;
+    for (int sp = lane; sp < n_split; sp += 64) M = fmaxf(M, mlb[2 * sp]);
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
+    if (lane == 0) Mh[h] = M;
+  }
+  __syncthreads();
+
+  constexpr int PER = 16 * kD / 256;   // (head, coordinate) pairs per thread, for G <= 16
+  float num[PER];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) num[k] = 0.f;
+  float den = 0.f;   // thread h < G: denominator of head h
+  for (int base = 0; base < n_split; base += kCombineBlock) {
+    const int nb = min(kCombineBlock, n_split - base);
+    for (int e = tid; e < G * kCombineBlock; e += 256) {
+      const int h = e / kCombineBlock, sp = e % kCombineBlock;
+      float w = 0.f;
+      if (sp < nb) {
+        const float m = ml[((bh0 + h) * n_split + base + sp) * 2];
+        w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mh[h]);
       }
-      const float w = __builtin_amdgcn_exp2f(m - M);
-      num = fmaf(w, x, num);
-      den = fmaf(w, l, den);
+      wsp[e] = w;
     }
-    ov[idx] = den > 0.f ? num / den * inv_sqrt_d : 0.f;
+    __syncthreads();
+    if (tid < G) {
+      const float* mlb = ml + ((bh0 + tid) * n_split + base) * 2;
+#pragma unroll 8
+      for (int sp = 0; sp < nb; ++sp) den = fmaf(wsp[tid * kCombineBlock + sp], mlb[2 * sp + 1], den);
+      dh[tid] = den;
+    }
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int idx = tid + 256 * k;
+      if (idx < G * kD) {
+        const int h = idx / kD, j = idx % kD;
+        const float* ab = acc + ((bh0 + h) * n_split + base) * kD + j;
+        const float* wh = wsp + h * kCombineBlock;
+        float x = num[k];
+#pragma unroll 8
+        for (int sp = 0; sp < nb; ++sp) x = fmaf(wh[sp], ab[(int64_t)sp * kD], x);
+        num[k] = x;
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int idx = tid + 256 * k;
+    if (idx < G * kD) {
+      const float d = dh[idx / kD];
+      ov[idx] = d > 0.f ? num[k] / d * inv_sqrt_d : 0.f;
+    }
   }
   __syncthreads();
   // thread (i, hq): out[h][32*chunk + i] for heads hq, hq + 8
