@@ -27,6 +27,7 @@
 
 #include <atomic>
 
+#include "tq_codec.h"
 #include "tq_device.h"
 #include "tq_internal.h"
 
@@ -52,14 +53,6 @@ struct QuantArgs {
   int thr_sym;   // the thresholds mirror around 0 (middle one is 0)
 };
 
-// Thresholds of one codebook held in registers (copied once from the kernel
-// arguments, so the selects below are register selects, not memory loads).
-template <int BITS>
-struct Thresholds {
-  float t[(1 << BITS) - 1];
-  bool sym;   // t[L-2-k] == -t[k] and the middle one is 0
-};
-
 template <int BITS>
 __device__ inline Thresholds<BITS> load_thresholds(const QuantArgs& a) {
   Thresholds<BITS> th;
@@ -81,71 +74,6 @@ __device__ inline void slot_pos(const QuantArgs& a, int64_t s0, uint32_t v, int6
   t = a.t_base + (int64_t)(rr - q * ns);
 }
 
-// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i.
-// For a codebook that mirrors around 0 (the canonical one), the search runs on
-// |z| over the positive half and a negative z takes the mirrored cell
-// (2^bits - 1 - cell of |z|); an exact tie with a threshold may then land in
-// the neighbouring cell, which is the decision boundary itself. Otherwise a
-// branch-free binary search over all thresholds.
-template <int BITS>
-__device__ inline int encode(float z, const Thresholds<BITS>& th) {
-  constexpr int half = 1 << (BITS - 1);
-  const float* t = th.t;
-  if (th.sym) {
-    const float* p = t + half;   // positive thresholds
-    const float x = fabsf(z);
-    int n;
-    if constexpr (BITS == 2) {
-      n = x >= p[0];
-    } else if constexpr (BITS == 3) {
-      const bool b1 = x >= p[1];
-      const bool b0 = x >= (b1 ? p[2] : p[0]);
-      n = (b1 << 1) | b0;
-    } else {
-      const bool b2 = x >= p[3];
-      const bool b1 = x >= (b2 ? p[5] : p[1]);
-      const float tc = b2 ? (b1 ? p[6] : p[4]) : (b1 ? p[2] : p[0]);
-      const bool b0 = x >= tc;
-      n = (b2 << 2) | (b1 << 1) | b0;
-    }
-    return (half + n) ^ (z < 0.f ? 2 * half - 1 : 0);
-  }
-  if constexpr (BITS == 2) {
-    const bool b1 = z >= t[1];
-    const bool b0 = z >= (b1 ? t[2] : t[0]);
-    return (b1 << 1) | b0;
-  } else if constexpr (BITS == 3) {
-    const bool b2 = z >= t[3];
-    const bool b1 = z >= (b2 ? t[5] : t[1]);
-    const float tc = b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]);
-    const bool b0 = z >= tc;
-    return (b2 << 2) | (b1 << 1) | b0;
-  } else {
-    const bool b3 = z >= t[7];
-    const bool b2 = z >= (b3 ? t[11] : t[3]);
-    const float t1 = b3 ? (b2 ? t[13] : t[9]) : (b2 ? t[5] : t[1]);
-    const bool b1 = z >= t1;
-    const float t0 = b3 ? (b2 ? (b1 ? t[14] : t[12]) : (b1 ? t[10] : t[8]))
-                        : (b2 ? (b1 ? t[6] : t[4]) : (b1 ? t[2] : t[0]));
-    const bool b0 = z >= t0;
-    return (b3 << 3) | (b2 << 2) | (b1 << 1) | b0;
-  }
-}
-
-// Pack 32 codes (bytes of q[0..7], LSB first) into BITS words, stream position BITS*k.
-template <int BITS>
-__device__ inline void pack32(const uint32_t* q, uint32_t* w) {
-#pragma unroll
-  for (int i = 0; i < BITS; ++i) w[i] = 0u;
-#pragma unroll
-  for (int k = 0; k < 32; ++k) {
-    const uint32_t code = (q[k >> 2] >> (8 * (k & 3))) & 0xFFu;
-    const int pos = BITS * k;
-    const int wi = pos >> 5, off = pos & 31;
-    w[wi] |= code << off;
-    if (off + BITS > 32) w[wi + 1] |= code >> (32 - off);
-  }
-}
 
 // Load Pi (or S), split into float16 hi/lo, into LDS in B-operand order:
 // op[pass][ks][nb][lane][8] = M[16nb + n][32g + 8ks + e], lane = 16g + n.
@@ -746,6 +674,21 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
   float4 pr[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) pr[k] = ((const float4*)(a.rot + i * kD + 64 * s))[k];
+  // values: thread (v, cg) rewrites BITS words of its block record (coordinates
+  // 4cg .. 4cg+3 of the block's 8 tokens); the old words are read now, in
+  // flight during the rotation
+  uint32_t old_words[ROLE == TQ_VALUES ? BITS : 1];
+  uint32_t* vdst = nullptr;
+  if constexpr (ROLE == TQ_VALUES) {
+    const int v = tid >> 5, cg = tid & 31;
+    const int64_t gv = v0 + v;
+    if (gv < nvec) {
+      const int64_t tb = a.t_offset & ~(int64_t)7;
+      vdst = a.codes + (gv * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+#pragma unroll
+      for (int k = 0; k < BITS; ++k) old_words[k] = vdst[k];
+    }
+  }
 
   {
     // thread (v, c4): coordinates 4c4 .. 4c4+3 of vector v
@@ -821,9 +764,7 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
     // thread (v, cg): the BITS words of the block record that hold coordinates
     // 4cg .. 4cg+3 of all 8 tokens; only the new token's bits change
     const int v = tid >> 5, cg = tid & 31;
-    const int64_t gv = v0 + v;
-    if (gv < nvec) {
-      const int64_t tb = a.t_offset & ~(int64_t)7;
+    if (vdst != nullptr) {
       const int ti = (int)(a.t_offset & 7);
       uint32_t w[BITS], clr[BITS];
 #pragma unroll
@@ -845,9 +786,8 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
           clr[wi + 1] |= fm >> (32 - off);
         }
       }
-      uint32_t* dst = a.codes + (gv * a.T_cap + tb) * (VBW / 8) + cg * BITS;
 #pragma unroll
-      for (int k = 0; k < BITS; ++k) dst[k] = (dst[k] & ~clr[k]) | w[k];
+      for (int k = 0; k < BITS; ++k) vdst[k] = (old_words[k] & ~clr[k]) | w[k];
     }
   }
 }
