@@ -22,13 +22,18 @@ import ctypes
 import os
 
 import numpy as np
+# torch is loaded before libtq.so so that the process holds one HIP runtime:
+# torch brings its own copy of libamdhip64, and libtq.so then binds to it. The
+# other order loads a second runtime beside torch's, and the two do not share
+# the device.
+import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtq.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
-        f"{LIB_PATH} is missing: build it with `python -m decode_attention_tq_amd.build` "
+        f"{LIB_PATH} is missing: build it with `python decode_attention_tq_amd/build.py` "
         "(hipcc for gfx950); this package has no CPU fallback")
 
 _lib = ctypes.CDLL(LIB_PATH)
@@ -41,7 +46,8 @@ D = 128
 VALUE_BLOCK = 8
 
 EXPORTS = ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
-           "tq_decode_attention", "tq_decode_splits", "tq_decode_workspace_bytes", "tq_status_string")
+           "tq_decode_attention", "tq_decode_splits", "tq_decode_workspace_bytes", "tq_status_string",
+           "tq_last_hip_error")
 
 
 class TQCache(ctypes.Structure):
@@ -73,6 +79,8 @@ def _bind(lib):
     lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_status_string.argtypes = [ctypes.c_int]
     lib.tq_status_string.restype = ctypes.c_char_p
+    lib.tq_last_hip_error.argtypes = []
+    lib.tq_last_hip_error.restype = ctypes.c_char_p
     for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -98,6 +106,8 @@ def status_string(status: int) -> str:
 
 def _check(status: int, what: str):
     if status != OK:
+        if status == ERR_DEVICE:
+            what = f"{what} [{_lib.tq_last_hip_error().decode()}]"
         raise TQError(status, what)
 
 

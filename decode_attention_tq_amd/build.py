@@ -1,6 +1,9 @@
 """Build libtq.so (the C-ABI library) in-tree with hipcc for gfx950.
 
-    python -m decode_attention_tq_amd.build      # or build() from Python
+    python decode_attention_tq_amd/build.py      # or build() from Python
+
+(Run as a script, not as a module of the package: importing the package loads
+the library that this builds.)
 
 Objects go to _build/ at the repository root; the shared library is written next
 to this file, where the Python binding loads it.

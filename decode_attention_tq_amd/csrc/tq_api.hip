@@ -39,7 +39,22 @@ int check_cache(const tq_cache* c) {
   return TQ_OK;
 }
 
-int device_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_ERR_DEVICE; }
+// HIP error of the last failed device call made by an entry point on this thread.
+thread_local hipError_t t_last_hip_error = hipSuccess;
+
+// Status of a device call; the HIP error of a failure is kept for
+// tq_last_hip_error.
+int device_status(hipError_t e) {
+  if (e == hipSuccess) return TQ_OK;
+  t_last_hip_error = e;
+  return TQ_ERR_DEVICE;
+}
+
+// Entry points check the launch error of their own kernels: an error left
+// pending by an earlier, unrelated HIP call on this thread (one that did not
+// poison the device) is cleared before they launch, so it is not reported as
+// theirs. A device that did fault fails the launch itself.
+void clear_pending_error() { (void)hipGetLastError(); }
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -100,6 +115,8 @@ extern "C" const char* tq_status_string(int status) {
   }
 }
 
+extern "C" const char* tq_last_hip_error(void) { return hipGetErrorName(t_last_hip_error); }
+
 extern "C" int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split) {
   DecodePlan p;
   if (!plan_decode(B, H_kv, H_kv, T, n_split, 0, &p)) return 0;
@@ -127,6 +144,7 @@ extern "C" int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t
   const int64_t vec_align = 16 / esz;   // every row starts on a 16-byte boundary
   if (!aligned16(x) || stride_b % vec_align || stride_t % vec_align || stride_h % vec_align)
     return TQ_ERR_ALIGNMENT;
+  clear_pending_error();
   return device_status(launch_quantize(x, x_dtype, B, T, H_kv, stride_b, stride_t, stride_h, dst, t_offset,
                                        (hipStream_t)hip_stream));
 }
@@ -138,6 +156,7 @@ extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float*
   if (t1 == t0) return TQ_OK;
   if (out == nullptr) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(out)) return TQ_ERR_ALIGNMENT;
+  clear_pending_error();
   return device_status(launch_dequantize(src, t0, t1, out, (hipStream_t)hip_stream));
 }
 
@@ -163,6 +182,7 @@ extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const v
   if (workspace == nullptr || workspace_bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255u) != 0) return TQ_ERR_ALIGNMENT;
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
+  clear_pending_error();
   return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                      (hipStream_t)hip_stream));
 }

@@ -257,17 +257,12 @@ struct StepNorms {
   float kn[NT], vn[NT], kg[NT];
 };
 
-// Norms travel with the code words of their step (loaded a step ahead) rather
-// than being loaded when the step starts.
-constexpr bool kNormsAhead = false;
-
 template <int KB, int VB, int QJL, int WIDE>
 struct StepData {
   static constexpr int NT = WIDE ? 8 : 4;
   uint32_t kw[2][KB];
   uint32_t sw[2];
   uint32_t vw[2 * VB];
-  StepNorms<NT, QJL> nm;   // with kNormsAhead
 };
 
 struct Streams {
@@ -322,7 +317,6 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
     if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, kStreamAux);
   }
   bload_words_s<2 * VB>(s.rv, lo.v, (st / 8u) * (VBW * 4u), d.vw);
-  if constexpr (kNormsAhead) load_norms(d.nm, s, lo, t0);
 }
 
 
@@ -342,13 +336,9 @@ struct SoftState {
 
 template <int KB, int VB, int QJL, int WIDE, bool MASK>
 __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, const QOps<WIDE, QJL>& q,
+                                          const StepNorms<StepData<KB, VB, QJL, WIDE>::NT, QJL>& nm,
                                           SoftState<WIDE>& st, const uint32_t* lutK, const uint32_t* lutV,
-                                          const uint32_t* lutS, int lane, int tg, int t_end,
-                                          const Streams& sm, const LaneOffsets& lo, int t0) {
-  constexpr int NT = StepData<KB, VB, QJL, WIDE>::NT;
-  StepNorms<NT, QJL> nml;
-  if constexpr (!kNormsAhead) load_norms(nml, sm, lo, t0);
-  const StepNorms<NT, QJL>& nm = kNormsAhead ? d.nm : nml;
+                                          const uint32_t* lutS, int lane, int tg, int t_end) {
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
   // (two independent accumulation chains; one query block live at a time)
   floatx4 s0[2], s1[2], z0[2], z1[2];
@@ -533,18 +523,25 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 // Wavefronts per workgroup: one workgroup fills a compute unit (4 wavefronts
 // per SIMD, <= 128 VGPRs, for the common tiles; the QJL and G > 8 tiles carry
 // more operands and run 2 per SIMD).
+constexpr int kCommonWaves = 16;
 template <int QJL, int WIDE>
-constexpr int scan_waves() { return (QJL || WIDE) ? 8 : 16; }
+constexpr int scan_waves() { return (QJL || WIDE) ? 8 : kCommonWaves; }
+
+// Steps whose code words are in flight while a step computes (register
+// buffers: one more than this).
+constexpr int kAheadCommon = 1;
+template <int QJL, int WIDE>
+constexpr int scan_ahead() { return (QJL || WIDE) ? 1 : kAheadCommon; }
 
 // merge buffer: [wave][column][128 + 2] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
 constexpr int merge_cols() { return WIDE ? 16 : 8; }
 
 // LDS of a decode workgroup, in 32-bit words: the float16 query operand
-// ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, then the
-// scratch region.
+// ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, 32 codebook
+// levels, the step counter (padded to 4 words), then the scratch region.
 template <int QJL, int WIDE>
-constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 80; }
+constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 84; }
 
 template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
@@ -578,6 +575,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   float* qcs = (float*)(smem + (1 + QJL) * NQ * kQStride / 2);   // [2][16]
   int* hexp = (int*)(qcs + 32);                            // [16]
   float* cents = qcs + 48;                                 // [2][16] key, value levels
+  uint32_t* steps_done = (uint32_t*)(qcs + 80);            // steps begun by the workgroup
   uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
   float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
   float* vA = R + kRegionWords;
@@ -625,11 +623,19 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // the code words of the first full step are in flight during the prologue
   const int t_full =
       __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
-  StepData<KB, VB, QJL, WIDE> A, Bd;
-  if (t_begin < t_full) load_step(A, s, lo, t_begin);
+  constexpr int AH = scan_ahead<QJL, WIDE>();
+  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
+  if (t_begin < t_full) {
+#pragma unroll
+    for (int i = 0; i < AH; ++i) {
+      const int tl = t_begin + i * kStep;
+      load_step(buf[i], s, lo, tl < t_full ? tl : t_begin);
+    }
+  }
 
   // ---- prologue: lookup tables, then the query operand of this (row, KV head)
   if (tid < 32) cents[tid] = tid < 16 ? a.kc[tid] : a.vc[tid - 16];
+  if (tid == 0) *steps_done = 0u;
   RowSegment<NT> rseg;
   load_row_segment<NT>(rseg, a.rotK);   // in flight with the query loads
   {
@@ -686,27 +692,57 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     st.acc1[nb] = st.acc0[nb];
   }
 
-  // ---- stream the share: full 32-token steps with two register buffers in
-  // turn (the code words of the next step are in flight while the current step
-  // computes), then at most one masked step for a ragged end.
+  // ---- stream the share: full 32-token steps with AH + 1 register buffers in
+  // turn, then at most one masked step for a ragged end. A step first issues
+  // the norm loads of its own tokens, then the code words of the step AH
+  // ahead (near the end it reloads its own words instead, so the loads carry
+  // no branch), so that waiting for the norms leaves the later steps' words in
+  // flight for the whole step: loads complete in issue order.
+  // Balance: the sequencer favours older wavefronts, so with equal shares the
+  // younger ones would finish last and leave the compute unit a tail with few
+  // wavefronts (little memory parallelism). Each step a wavefront counts
+  // itself in a workgroup counter and runs at raised priority while it is more
+  // than one round of steps behind the workgroup average, at lowered priority
+  // while it is ahead.
+  using Norms = StepNorms<StepData<KB, VB, QJL, WIDE>::NT, QJL>;
   int t0 = t_begin;
   if (t0 < t_full) {
-#define TQ_STEP(CUR, NEXT)                                                                               \
-    if (t0 + kStep < t_full) load_step(NEXT, s, lo, t0 + kStep);                                        \
-    scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0); \
-    t0 += kStep;                                                                                         \
-    if (t0 >= t_full) break;
-    while (true) {
-      TQ_STEP(A, Bd)
-      TQ_STEP(Bd, A)
+    bool done = false;
+    uint32_t mine = 0;   // steps begun by this wavefront
+    while (!done) {
+#pragma unroll
+      for (int i = 0; i <= AH; ++i) {
+        if (!done) {
+          Norms nm;
+          load_norms(nm, s, lo, t0);
+          __builtin_amdgcn_sched_barrier(0);
+          const int tl = t0 + AH * kStep;
+          load_step(buf[(i + AH) % (AH + 1)], s, lo, tl < t_full ? tl : t0);
+          __builtin_amdgcn_sched_barrier(0);
+          uint32_t begun = 0u;
+          if (lane == 0)
+            begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+          scan_step<KB, VB, QJL, WIDE, false>(buf[i], q, nm, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
+          begun = __builtin_amdgcn_readfirstlane(begun);   // by the whole workgroup
+          const uint32_t even = mine * (uint32_t)NW;        // if every wavefront kept pace
+          if (begun > even + NW) __builtin_amdgcn_s_setprio(3);
+          else if (begun + NW < even) __builtin_amdgcn_s_setprio(0);
+          else __builtin_amdgcn_s_setprio(1);
+          ++mine;
+          t0 += kStep;
+          done = t0 >= t_full;
+        }
+      }
     }
-#undef TQ_STEP
+    __builtin_amdgcn_s_setprio(0);
   }
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
   if (t0 < t_end) {
     StepData<KB, VB, QJL, WIDE> E;
+    Norms nm;
     load_step(E, s, lo, t0);
-    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end, s, lo, t0);
+    load_norms(nm, s, lo, t0);
+    scan_step<KB, VB, QJL, WIDE, true>(E, q, nm, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
   }
 
   // ---- this wavefront's partial: lane (g, c) holds coordinates 32g + 8r + nb of column c
@@ -966,7 +1002,7 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   sa.T = (int)p.T;
   sa.n_split = p.n_split;
   sa.wg_chunk = p.chunk;
-  sa.wave_chunk = p.chunk / ((p.qjl || p.wide) ? 8 : 16);
+  sa.wave_chunk = p.chunk / ((p.qjl || p.wide) ? 8 : kCommonWaves);
   // the query operand carries log2(e) * scale / sqrt(d) (scores in the log2
   // domain); the QJL part log2(e) * scale * sqrt(pi/2) / d
   sa.sc1 = scale * kLog2e * inv_sqrt_d;

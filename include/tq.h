@@ -16,11 +16,14 @@
  *
  * Conventions (all functions):
  *   - return an int status (TQ_OK = 0); nothing throws; the only process-wide
- *     state is cached device attributes and kernel attributes set once;
+ *     state is cached device attributes and kernel attributes set once, plus
+ *     a per-thread record of the last HIP error (tq_last_hip_error);
  *   - argument errors are reported synchronously, before any HIP call;
  *   - device calls are asynchronous on the given hipStream_t (passed as void*,
- *     NULL = the default stream); a failed launch returns TQ_ERR_DEVICE, a fault
- *     inside a kernel surfaces at the caller's next synchronisation;
+ *     NULL = the default stream); a failed launch returns TQ_ERR_DEVICE (an
+ *     error left pending on the thread by an earlier, unrelated HIP call is
+ *     cleared before the launch and not reported), a fault inside a kernel
+ *     surfaces at the caller's next synchronisation;
  *   - the caller owns every buffer; the library never allocates or frees device
  *     memory;
  *   - head dimension d = 128 only (other values return TQ_ERR_UNSUPPORTED).
@@ -173,6 +176,11 @@ size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T
 
 /* Static text for a status code. */
 const char* tq_status_string(int status);
+
+/* Name of the HIP error (hipGetErrorName) behind the last TQ_ERR_DEVICE that an
+ * entry point returned on the calling thread; "hipSuccess" if there was none.
+ * Static text, owned by the HIP runtime. */
+const char* tq_last_hip_error(void);
 
 #ifdef __cplusplus
 }

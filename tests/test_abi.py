@@ -39,6 +39,8 @@ def test_status_strings():
         assert tq.status_string(code)
     assert tq.status_string(0) == "ok"
     assert "unknown" in tq.status_string(99)
+    # no device call has failed on this thread (argument errors are not device errors)
+    assert tq.lib().tq_last_hip_error() == b"hipSuccess"
 
 
 @pytest.mark.parametrize("bits", [1, 2, 3, 4])
