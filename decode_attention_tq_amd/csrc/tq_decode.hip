@@ -77,52 +77,75 @@ constexpr int kQStride = kD + 8;
 // Scratch region of a decode workgroup, in 32-bit words: the lookup tables
 // (scan), then the wavefront partials (merge) and the partial sums of the final
 // rotation, followed by two [16][d] float vector sets.
-constexpr int kRegionWords = 16640;
+constexpr int kRegionWords = 16896;
+// Row stride (in floats) of a wavefront partial in the merge area: 128
+// coordinates, m and l, padded to a 16-byte multiple.
+constexpr int kMergeStride = kD + 4;
 constexpr int kScratchWords = kRegionWords + 2 * kVecWords;
 
-// out[h][i] = sum_j M[i][j] in[h][j] for the G heads (in, out: LDS [G][d]).
-// NT threads split each row of M into NT/128 segments: thread (i, s) loads its
-// segment straight from memory (consecutive threads read consecutive 16-byte
-// pieces, so a wavefront reads whole rows), forms the partial dot products of
-// every head, and the segments of a row, held by adjacent lanes, are summed
-// with cross-lane adds. No staging of M, and each element of M is read once.
+// q' = M q for the G query heads of a workgroup: out[h][i] = sum_j M[i][j]
+// in[h][j] (in, out: LDS [G][d]). Thread t takes rows R*(t/16) .. R*(t/16)+R-1
+// of M (R = 2048 / NT) over the 8 columns 8*(t%16) .. 8*(t%16)+7, loaded
+// straight from memory (16 consecutive lanes read whole rows; each element of
+// M is read once, no staging), so every query element read from LDS serves R
+// rows. The 16 segments of a row group sit in the 16 lanes of a DPP row and
+// are summed with DPP exchanges, for all heads at once.
 template <int NT>
 struct RowSegment {
-  static constexpr int SEGS = NT / 128, W = kD / SEGS;
-  float4 r[W / 4];
+  static constexpr int R = 16 * kD / NT;   // rows per thread
+  float4 r[2 * R];                        // row k: r[2k], r[2k + 1]
 };
 
-// Thread (i, s) of the row split below loads its segment of row i of M.
 template <int NT>
 __device__ inline void load_row_segment(RowSegment<NT>& rs, const float* M) {
-  constexpr int SEGS = RowSegment<NT>::SEGS, W = RowSegment<NT>::W;
-  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
+  constexpr int R = RowSegment<NT>::R;
+  const int i0 = R * (threadIdx.x / 16), sg = threadIdx.x % 16;
 #pragma unroll
-  for (int k = 0; k < W / 4; ++k) rs.r[k] = *(const float4*)(M + i * kD + sg * W + 4 * k);
+  for (int k = 0; k < R; ++k) {
+    rs.r[2 * k] = *(const float4*)(M + (i0 + k) * kD + 8 * sg);
+    rs.r[2 * k + 1] = *(const float4*)(M + (i0 + k) * kD + 8 * sg + 4);
+  }
 }
 
-// out[h][i] = sum_j M[i][j] in[h][j] for the G heads (in, out: LDS [G][d]).
-// NT threads split each row of M into NT/128 segments: thread (i, s) holds its
-// segment (loaded from memory by load_row_segment; consecutive threads read
-// consecutive 16-byte pieces, so a wavefront reads whole rows), forms the
-// partial dot products of every head, and the segments of a row, held by
-// adjacent lanes, are summed with cross-lane adds. No staging of M, and each
-// element of M is read once.
-template <int NT>
+template <int NT, int MAXG>
 __device__ void rotate_rows(const RowSegment<NT>& rs, const float* in, float* out, int G) {
-  constexpr int SEGS = RowSegment<NT>::SEGS, W = RowSegment<NT>::W;
-  const int i = threadIdx.x / SEGS, sg = threadIdx.x % SEGS;
-  for (int h = 0; h < G; ++h) {
-    const float4* x = (const float4*)(in + h * kD + sg * W);
-    float acc = 0.f;
+  constexpr int R = RowSegment<NT>::R;
+  const int i0 = R * (threadIdx.x / 16), sg = threadIdx.x % 16;
+  float acc[MAXG][R];
 #pragma unroll
-    for (int k = 0; k < W / 4; ++k) {
-      const float4 v = x[k];
-      acc = fmaf(rs.r[k].w, v.w, fmaf(rs.r[k].z, v.z, fmaf(rs.r[k].y, v.y, fmaf(rs.r[k].x, v.x, acc))));
+  for (int h = 0; h < MAXG; ++h) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) acc[h][k] = 0.f;
+    if (h < G) {
+      const float4 a = *(const float4*)(in + h * kD + 8 * sg);
+      const float4 b = *(const float4*)(in + h * kD + 8 * sg + 4);
+#pragma unroll
+      for (int k = 0; k < R; ++k) {
+        const float4 m0 = rs.r[2 * k], m1 = rs.r[2 * k + 1];
+        const float v = fmaf(m0.x, a.x, fmaf(m0.y, a.y, fmaf(m0.z, a.z, m0.w * a.w)));
+        acc[h][k] = fmaf(m1.x, b.x, fmaf(m1.y, b.y, fmaf(m1.z, b.z, fmaf(m1.w, b.w, v))));
+      }
     }
+  }
+  // sums over the 16 lanes of the row: quads, then rotates by 4 and 8 (every
+  // lane ends with the full sum)
 #pragma unroll
-    for (int m = 1; m < SEGS; m <<= 1) acc += __shfl_xor(acc, m);
-    if (sg == (h % SEGS)) out[h * kD + i] = acc;
+  for (int h = 0; h < MAXG; ++h) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) {
+      float v = acc[h][k] + dpp_xor1(acc[h][k]);
+      v += dpp_xor2(v);
+      v += dpp_ror4(v);
+      v += dpp_ror8(v);
+      acc[h][k] = v;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) {
+    if (h < G && sg == h) {
+#pragma unroll
+      for (int k = 0; k < R; ++k) out[h * kD + i0 + k] = acc[h][k];
+    }
   }
 }
 
@@ -143,8 +166,11 @@ __device__ void emit_operand(const float* vals, float sc, int G, int half_cols, 
 #pragma unroll
       for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(vals[h * kD + 8 * seg + k] * sc));
     }
-#pragma unroll
-    for (int m = 1; m < 16; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
+    // maximum over the 16 lanes of the row: quads, then rotates by 4 and 8
+    mx = fmaxf(mx, dpp_xor1(mx));
+    mx = fmaxf(mx, dpp_xor2(mx));
+    mx = fmaxf(mx, dpp_ror4(mx));
+    mx = fmaxf(mx, dpp_ror8(mx));
     if (seg == 0) {
       const int e = (mx > 0.f) ? (__builtin_amdgcn_frexp_expf(mx) - 14) : 0;
       hexp[h] = e;
@@ -248,21 +274,26 @@ struct LaneOffsets {
   uint32_t n;        // norms (and gammas) of the lane's tokens
 };
 
-// Raw bytes of one 32-token step for one lane. Norms: for G <= 8 the two lanes
-// of a hi/lo column pair split the 8 tokens of their row block (lane half hf
-// takes tokens 4hf .. 4hf+3); for 8 < G <= 16 every lane takes all 8.
-// Norms (and QJL gammas) of the lane's tokens in one step.
-template <int NT, int QJL>
+// Norms (and QJL gammas) of one step: each lane reads one token's. For G <= 8
+// the two lanes of a hi/lo column pair split the 8 tokens of their row block
+// (lane half hf takes tokens 4hf .. 4hf+3) and lane (g, c) reads token
+// 8g + 4hf + c % 4, so the 4 tokens a lane needs are in its quad; for
+// 8 < G <= 16 every lane needs all 8 tokens of its row block and lane (g, c)
+// reads token 8g + c % 8, so they are in lanes 0-7 of its row. The values
+// reach the lanes that need them as DPP operands of their multiplies: one
+// 4-byte read per lane and stream instead of 16 or 32 bytes.
+template <int QJL>
 struct StepNorms {
-  float kn[NT], vn[NT], kg[NT];
+  float kn, vn, kg;
 };
 
+// Raw words of one 32-token step for one lane, with the step's norms.
 template <int KB, int VB, int QJL, int WIDE>
 struct StepData {
-  static constexpr int NT = WIDE ? 8 : 4;
   uint32_t kw[2][KB];
   uint32_t sw[2];
   uint32_t vw[2 * VB];
+  StepNorms<QJL> nm;
 };
 
 struct Streams {
@@ -290,20 +321,12 @@ __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   }
 }
 
-template <int NT>
-__device__ inline void bload_floats_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, float* f) {
-  uint32_t w[NT];
-  bload_words_s<NT>(r, voff, soff, w);
-#pragma unroll
-  for (int i = 0; i < NT; ++i) f[i] = as_float(w[i]);
-}
-
-template <int NT, int QJL>
-__device__ inline void load_norms(StepNorms<NT, QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
+template <int QJL>
+__device__ inline void load_norms(StepNorms<QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
   const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0) * 4u;
-  bload_floats_s<NT>(s.rkn, lo.n, st, n.kn);
-  bload_floats_s<NT>(s.rvn, lo.n, st, n.vn);
-  if constexpr (QJL) bload_floats_s<NT>(s.rg, lo.n, st, n.kg);
+  n.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, lo.n, st, kStreamAux));
+  n.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, lo.n, st, kStreamAux));
+  if constexpr (QJL) n.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, lo.n, st, kStreamAux));
 }
 
 template <int KB, int VB, int QJL, int WIDE>
@@ -317,6 +340,7 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
     if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, kStreamAux);
   }
   bload_words_s<2 * VB>(s.rv, lo.v, (st / 8u) * (VBW * 4u), d.vw);
+  load_norms(d.nm, s, lo, t0);
 }
 
 
@@ -336,9 +360,9 @@ struct SoftState {
 
 template <int KB, int VB, int QJL, int WIDE, bool MASK>
 __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, const QOps<WIDE, QJL>& q,
-                                          const StepNorms<StepData<KB, VB, QJL, WIDE>::NT, QJL>& nm,
                                           SoftState<WIDE>& st, const uint32_t* lutK, const uint32_t* lutV,
                                           const uint32_t* lutS, int lane, int tg, int t_end) {
+  const StepNorms<QJL>& nm = d.nm;
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
   // (two independent accumulation chains; one query block live at a time)
   floatx4 s0[2], s1[2], z0[2], z1[2];
@@ -397,9 +421,9 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       float x = q.hf ? x8[4 + r] : x8[r];
       if constexpr (QJL) {
         const float z = q.hf ? z8[4 + r] : z8[r];
-        x = fmaf(z * q.cs2, nm.kg[r], x * q.cs1);
+        x = fmaf(z * q.cs2, quad_bcast(nm.kg, r), x * q.cs1);
       }
-      float v = x * nm.kn[r];
+      float v = x * quad_bcast(nm.kn, r);
       if constexpr (MASK) v = (tg + 4 * (int)q.hf + r < t_end) ? v : -INFINITY;
       y[r] = v;
     }
@@ -423,7 +447,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     for (int r = 0; r < 4; ++r) {
       const float p = __builtin_amdgcn_exp2f(fmaf(y[r], cs, -st.m_off));
       st.l += p;
-      w[r] = p * nm.vn[r];
+      w[r] = p * quad_bcast(nm.vn, r);
       if constexpr (MASK) w[r] = (tg + 4 * (int)q.hf + r < t_end) ? w[r] : 0.f;
     }
     // own tokens as float16 hi and lo halves (pairs of tokens per register)
@@ -468,9 +492,9 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
         float x = s0[m][r] + s1[m][r];
         if constexpr (QJL) {
           const float yq = z0[m][r] + z1[m][r];
-          x = fmaf(yq * q.cs2, nm.kg[e], x * q.cs1);
+          x = fmaf(yq * q.cs2, bcast_row(nm.kg, e), x * q.cs1);
         }
-        float v = x * nm.kn[e];
+        float v = x * bcast_row(nm.kn, e);
         if constexpr (MASK) v = (tg + e < t_end) ? v : -INFINITY;
         y[e] = v;
       }
@@ -499,7 +523,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
         const int e = 2 * k + u;
         const float p = __builtin_amdgcn_exp2f(fmaf(y[e], cs, -st.m_off));
         st.l += p;
-        w2[u] = p * nm.vn[e];
+        w2[u] = p * bcast_row(nm.vn, e);
         if constexpr (MASK) w2[u] = (tg + e < t_end) ? w2[u] : 0.f;
       }
       const _Float16 h0 = (_Float16)w2[0], h1 = (_Float16)w2[1];
@@ -533,7 +557,7 @@ constexpr int kAheadCommon = 1;
 template <int QJL, int WIDE>
 constexpr int scan_ahead() { return (QJL || WIDE) ? 1 : kAheadCommon; }
 
-// merge buffer: [wave][column][128 + 2] floats, 8 columns (G <= 8) or 16
+// merge buffer: [wave][column][kMergeStride] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
 constexpr int merge_cols() { return WIDE ? 16 : 8; }
 
@@ -547,9 +571,9 @@ template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
   static_assert(lut_words<KB>() + lut_words<VB>() + (QJL ? 4 : 0) * kLutRep <= kRegionWords,
                 "lookup tables exceed the scratch region");
-  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * (kD + 2) <= kRegionWords,
+  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * kMergeStride <= kRegionWords,
                 "merge area exceeds the scratch region");
-  static_assert(scan_waves<QJL, WIDE>() / 2 * (WIDE ? 16 : 8) * kD <= kRegionWords,
+  static_assert(scan_waves<QJL, WIDE>() * (WIDE ? 16 : 8) * kD <= kRegionWords,
                 "rotation partials exceed the scratch region");
   return (size_t)(scan_head_words<QJL, WIDE>() + kScratchWords) * 4;
 }
@@ -591,13 +615,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   const int lrep = lane & (kLutRep - 1);
   const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
   const int G = a.G;
-  int ctx = a.ctx_lens ? a.ctx_lens[b] : a.T;
-  ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
-  // token range of this wavefront; wave-uniform, so that every step offset
-  // travels in the scalar offset of the buffer loads
-  const int t_begin = split * a.wg_chunk + wave * a.wave_chunk;
-  const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, ctx));
   const int64_t bkv = (int64_t)b * a.H_kv + kv;
+
+  // token range of this wavefront (before the context length clips it);
+  // wave-uniform, so that every step offset travels in the scalar offset of
+  // the buffer loads
+  const int t_begin = split * a.wg_chunk + wave * a.wave_chunk;
 
   Streams s;
   s.rk = make_rsrc(a.kcodes + bkv * a.TcK * KW, (uint32_t)(a.TcK * KW * 4));
@@ -618,47 +641,77 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     lo.s[m] = (uint32_t)(tk * 4 + g) * 4u;
   }
   lo.v = (uint32_t)(g * 32 * VB + c * 2 * VB) * 4u;
-  lo.n = (uint32_t)(8 * g + (hf ? 4 : 0)) * 4u;
+  lo.n = (uint32_t)(WIDE ? 8 * g + (c & 7) : 8 * g + (hf ? 4 : 0) + (c & 3)) * 4u;
 
-  // the code words of the first full step are in flight during the prologue
-  const int t_full =
-      __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
-  constexpr int AH = scan_ahead<QJL, WIDE>();
-  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
-  if (t_begin < t_full) {
+  // ---- prologue loads, in issue order: this thread's segment of the rows of
+  // Pi_K, its query elements, the code words of the first steps, the context
+  // length. Loads complete in issue order, so waiting for the matrix and the
+  // query never waits for the code words. The first steps are read before the
+  // context length is known: reads past the end of the cache return zeros
+  // (buffer range check), and steps past the context are never used.
+  RowSegment<NT> rseg;
+  load_row_segment<NT>(rseg, a.rotK);
+  constexpr int QE = 16 * kD / NT;   // query elements per thread (G <= 16)
+  uint32_t qraw[QE];
+  {
+    // one 32-bit load per element for either dtype (a bfloat16 element is
+    // taken from the word that holds it), so the loads carry no branch
+    const bool qbf = a.q_dtype == TQ_BF16;
+    const __amdgpu_buffer_rsrc_t rq =
+        make_rsrc((const char*)a.q + (((int64_t)b * a.H_q + (int64_t)kv * G) * kD) * (qbf ? 2 : 4),
+                  (uint32_t)(G * kD * (qbf ? 2 : 4)));
 #pragma unroll
-    for (int i = 0; i < AH; ++i) {
-      const int tl = t_begin + i * kStep;
-      load_step(buf[i], s, lo, tl < t_full ? tl : t_begin);
+    for (int k = 0; k < QE; ++k) {
+      const uint32_t idx = tid + k * NT;
+      qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (idx * 2u) & ~3u : idx * 4u, 0, 0);
     }
   }
+  constexpr int AH = scan_ahead<QJL, WIDE>();
+  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
+#pragma unroll
+  for (int i = 0; i < AH; ++i) load_step(buf[i], s, lo, t_begin + i * kStep);
+  int ctx = a.T;
+  if (a.ctx_lens) ctx = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.ctx_lens, (uint32_t)((b + 1) * 4)),
+                                                             (uint32_t)b * 4u, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 
   // ---- prologue: lookup tables, then the query operand of this (row, KV head)
-  if (tid < 32) cents[tid] = tid < 16 ? a.kc[tid] : a.vc[tid - 16];
+  if (tid < 32) {
+    // codebook levels from the kernel arguments (constant indices: scalar reads)
+    float cv = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      cv = tid == i ? a.kc[i] : cv;
+      cv = tid == 16 + i ? a.vc[i] : cv;
+    }
+    cents[tid] = cv;
+  }
   if (tid == 0) *steps_done = 0u;
-  RowSegment<NT> rseg;
-  load_row_segment<NT>(rseg, a.rotK);   // in flight with the query loads
+  __syncthreads();
+  build_lut<KB>(lutK, cents, tid, NT);
+  build_lut<VB>(lutV, cents + 16, tid, NT);
+  if constexpr (QJL) {
+    for (int e = tid; e < NS * kLutRep; e += NT) {
+      const int f = e >> kLutShift;
+      lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+    }
+  }
   {
     // the G query vectors ([G][d] contiguous) as float32 in vA
-    const int64_t q0 = ((int64_t)b * a.H_q + (int64_t)kv * G) * kD;
-    for (int idx = tid; idx < G * kD; idx += NT)
-      vA[idx] = a.q_dtype == TQ_BF16 ? bf16_bits_to_f32(((const uint16_t*)a.q)[q0 + idx])
-                                     : ((const float*)a.q)[q0 + idx];
-    __syncthreads();
-    build_lut<KB>(lutK, cents, tid, NT);
-    build_lut<VB>(lutV, cents + 16, tid, NT);
-    if constexpr (QJL) {
-      for (int e = tid; e < NS * kLutRep; e += NT) {
-        const int f = e >> kLutShift;
-        lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
-      }
+#pragma unroll
+    for (int k = 0; k < QE; ++k) {
+      const int idx = tid + k * NT;
+      if (idx < G * kD)
+        vA[idx] = a.q_dtype == TQ_BF16 ? __uint_as_float(((qraw[k] >> (16 * (idx & 1))) & 0xFFFFu) << 16)
+                                       : __uint_as_float(qraw[k]);
     }
-    rotate_rows<NT>(rseg, vA, vB, G);   // q' = Pi_K q
+    __syncthreads();
+    rotate_rows<NT, NQ / 2>(rseg, vA, vB, G);   // q' = Pi_K q
     __syncthreads();
     emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
     if constexpr (QJL) {
       load_row_segment<NT>(rseg, a.proj);
-      rotate_rows<NT>(rseg, vB, vA, G);   // q'' = S q'
+      rotate_rows<NT, NQ / 2>(rseg, vB, vA, G);   // q'' = S q'
       __syncthreads();
       emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
     }
@@ -682,6 +735,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   q.hf = hf;
 
 
+  // the share of this wavefront, clipped by the context length
+  ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, ctx));
+  const int t_full =
+      __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
+
   SoftState<WIDE> st;
   st.m_ref = -INFINITY;
   st.m_off = -INFINITY;
@@ -694,17 +753,16 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 
   // ---- stream the share: full 32-token steps with AH + 1 register buffers in
   // turn, then at most one masked step for a ragged end. A step first issues
-  // the norm loads of its own tokens, then the code words of the step AH
-  // ahead (near the end it reloads its own words instead, so the loads carry
-  // no branch), so that waiting for the norms leaves the later steps' words in
-  // flight for the whole step: loads complete in issue order.
+  // the loads (code words and norms) of the step AH ahead (near the end it
+  // reloads its own instead, so the loads carry no branch), then computes on
+  // words loaded AH steps earlier: loads complete in issue order, so waiting
+  // for those leaves the later steps' loads in flight for the whole step.
   // Balance: the sequencer favours older wavefronts, so with equal shares the
   // younger ones would finish last and leave the compute unit a tail with few
   // wavefronts (little memory parallelism). Each step a wavefront counts
   // itself in a workgroup counter and runs at raised priority while it is more
   // than one round of steps behind the workgroup average, at lowered priority
   // while it is ahead.
-  using Norms = StepNorms<StepData<KB, VB, QJL, WIDE>::NT, QJL>;
   int t0 = t_begin;
   if (t0 < t_full) {
     bool done = false;
@@ -713,16 +771,13 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 #pragma unroll
       for (int i = 0; i <= AH; ++i) {
         if (!done) {
-          Norms nm;
-          load_norms(nm, s, lo, t0);
-          __builtin_amdgcn_sched_barrier(0);
           const int tl = t0 + AH * kStep;
           load_step(buf[(i + AH) % (AH + 1)], s, lo, tl < t_full ? tl : t0);
           __builtin_amdgcn_sched_barrier(0);
           uint32_t begun = 0u;
           if (lane == 0)
             begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          scan_step<KB, VB, QJL, WIDE, false>(buf[i], q, nm, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
+          scan_step<KB, VB, QJL, WIDE, false>(buf[i], q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
           begun = __builtin_amdgcn_readfirstlane(begun);   // by the whole workgroup
           const uint32_t even = mine * (uint32_t)NW;        // if every wavefront kept pace
           if (begun > even + NW) __builtin_amdgcn_s_setprio(3);
@@ -739,10 +794,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
   if (t0 < t_end) {
     StepData<KB, VB, QJL, WIDE> E;
-    Norms nm;
     load_step(E, s, lo, t0);
-    load_norms(nm, s, lo, t0);
-    scan_step<KB, VB, QJL, WIDE, true>(E, q, nm, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
+    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
   }
 
   // ---- this wavefront's partial: lane (g, c) holds coordinates 32g + 8r + nb of column c
@@ -764,76 +817,98 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // ---- merge the wavefront partials in LDS (fixed order)
   const bool finish = a.n_split == 1;
   __syncthreads();   // every wavefront is done with the lookup tables
-  float* mrg = R;   // [wave][MC columns][128 + 2]
+  float* mrg = R;    // [wave][MC columns][kMergeStride]: 128 coordinates, m, l
   if (c < G) {
-    float* dst = mrg + (wave * MC + c) * (kD + 2);
+    float* dst = mrg + (wave * MC + c) * kMergeStride;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-#pragma unroll
-      for (int nb = 0; nb < 8; ++nb) dst[32 * g + 8 * r + nb] = o[nb][r];
+      *(float4*)(dst + 32 * g + 8 * r) = float4{o[0][r], o[1][r], o[2][r], o[3][r]};
+      *(float4*)(dst + 32 * g + 8 * r + 4) = float4{o[4][r], o[5][r], o[6][r], o[7][r]};
     }
     if (g == 0) {
       dst[kD] = st.m_off;
       dst[kD + 1] = l;
     }
   }
-  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, i)
-  // takes column i of Pi_V over rows s*RW .. s*RW+RW-1, loaded now (coalesced
-  // across i) so that the loads are in flight during the merge.
-  constexpr int SEGS = NT / 128, RW = kD / SEGS;
-  const int fi = tid & 127, fs = tid >> 7;
-  float pv[RW];
+  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, p)
+  // takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded now
+  // (a wavefront reads whole rows) so that the loads are in flight during the
+  // merge.
+  constexpr int FSEGS = NT / 64, RW = kD / FSEGS;
+  const int fp = tid & 63, fs = tid >> 6;
+  float2 pv[RW];
   if (finish) {
 #pragma unroll
-    for (int k = 0; k < RW; ++k) pv[k] = a.rotV[(fs * RW + k) * kD + fi];
+    for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
+  }
+  __syncthreads();
+  // weights of the wavefront partials: lane (h, w) of the first G * 16 threads
+  // (head h in a 16-lane row) takes f = 2^(m_w - M) with M the largest m_w of
+  // the head, and the row sums f * l_w into the denominator
+  float* fw = vA;            // [G][16]
+  float* Mh = vA + 256;      // [16]
+  float* dh = vA + 272;      // [16]
+  if (tid < G * 16) {
+    const int h = tid >> 4, w = tid & 15;
+    float m = -INFINITY, lw = 0.f;
+    if (w < NW) {
+      m = mrg[(w * MC + h) * kMergeStride + kD];
+      lw = mrg[(w * MC + h) * kMergeStride + kD + 1];
+    }
+    float M = fmaxf(m, dpp_xor1(m));
+    M = fmaxf(M, dpp_xor2(M));
+    M = fmaxf(M, dpp_ror4(M));
+    M = fmaxf(M, dpp_ror8(M));
+    const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - M);
+    float den = f * lw;
+    den += dpp_xor1(den);
+    den += dpp_xor2(den);
+    den += dpp_ror4(den);
+    den += dpp_ror8(den);
+    fw[h * 16 + w] = f;
+    if (w == 0) {
+      Mh[h] = M;
+      dh[h] = den;
+    }
   }
   __syncthreads();
   for (int idx = tid; idx < G * kD; idx += NT) {
     const int h = idx / kD, j = idx % kD;
-    float M = -INFINITY;
+    float num = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) M = fmaxf(M, mrg[(wv * MC + h) * (kD + 2) + kD]);
-    float num = 0.f, den = 0.f;
-    if (M > -INFINITY) {
-#pragma unroll
-      for (int wv = 0; wv < NW; ++wv) {
-        const float* src = mrg + (wv * MC + h) * (kD + 2);
-        const float mw = src[kD];
-        const float f = (mw == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(mw - M);
-        num = fmaf(f, src[j], num);
-        den = fmaf(f, src[kD + 1], den);
-      }
-    }
+    for (int wv = 0; wv < NW; ++wv) num = fmaf(fw[h * 16 + wv], mrg[(wv * MC + h) * kMergeStride + j], num);
+    const float den = dh[h];
     if (finish) {
       vB[idx] = den > 0.f ? num / den * a.inv_sqrt_d : 0.f;
     } else {
       const int64_t pidx = ((int64_t)b * a.H_q + kv * G + h) * a.n_split + split;
       a.acc[pidx * kD + j] = num;
       if (j == 0) {
-        a.ml[pidx * 2] = M;
+        a.ml[pidx * 2] = Mh[h];
         a.ml[pidx * 2 + 1] = den;
       }
     }
   }
   if (finish) {
     __syncthreads();   // o' is complete in vB; the merge area takes the partial sums
-    float* P = R;      // [SEGS][G][d]
+    float* P = R;      // [FSEGS][G][d]
     for (int h = 0; h < G; ++h) {
       const float4* x = (const float4*)(vB + h * kD + fs * RW);   // same address across the wavefront
-      float acc = 0.f;
+      float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
       for (int k = 0; k < RW / 4; ++k) {
         const float4 v = x[k];
-        acc = fmaf(pv[4 * k + 3], v.w, fmaf(pv[4 * k + 2], v.z, fmaf(pv[4 * k + 1], v.y, fmaf(pv[4 * k], v.x, acc))));
+        acc0 = fmaf(pv[4 * k + 3].x, v.w, fmaf(pv[4 * k + 2].x, v.z, fmaf(pv[4 * k + 1].x, v.y, fmaf(pv[4 * k].x, v.x, acc0))));
+        acc1 = fmaf(pv[4 * k + 3].y, v.w, fmaf(pv[4 * k + 2].y, v.z, fmaf(pv[4 * k + 1].y, v.y, fmaf(pv[4 * k].y, v.x, acc1))));
       }
-      P[(fs * G + h) * kD + fi] = acc;
+      *(float2*)(P + (fs * G + h) * kD + 2 * fp) = float2{acc0, acc1};
     }
     __syncthreads();
     for (int idx = tid; idx < G * kD; idx += NT) {
       const int h = idx / kD, i = idx % kD;
       float r = 0.f;
 #pragma unroll
-      for (int sg = 0; sg < SEGS; ++sg) r += P[(sg * G + h) * kD + i];
+      for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * G + h) * kD + i];
       a.out[((int64_t)b * a.H_q + kv * G + h) * kD + i] = r;
     }
   }

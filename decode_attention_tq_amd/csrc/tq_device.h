@@ -78,6 +78,31 @@ __device__ inline float dpp_ror8(float x) {
 
 __device__ inline float shfl_xor_f(float x, int m) { return __shfl_xor(x, m); }
 
+// DPP lane exchanges inside a 16-lane row: the values of lanes lane ^ 1 and
+// lane ^ 2 (quad permutes) and of lane (lane - 4) mod 16 (row rotate right).
+__device__ inline float dpp_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float dpp_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+__device__ inline float dpp_ror4(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+}
+
+// Value of lane 4 * (lane / 4) + R: DPP quad permute [R, R, R, R] (R known
+// after loop unrolling; the switch folds away). A multiply that consumes it
+// takes the permute as its DPP source operand.
+__device__ inline float quad_bcast(float x, int r) {
+  const int v = __builtin_bit_cast(int, x);
+  switch (r) {
+    case 0: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x00, 0xF, 0xF, false));
+    case 1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0x55, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xAA, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, v, 0xFF, 0xF, 0xF, false));
+  }
+}
+
 // Value of lane 16 * (lane / 16) + N: DPP row_newbcast (gfx90a and later).
 template <int N>
 __device__ inline float bcast_row_c(float x) {
