@@ -329,6 +329,22 @@ __device__ inline void load_norms(StepNorms<QJL>& n, const Streams& s, const Lan
   if constexpr (QJL) n.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, lo.n, st, kStreamAux));
 }
 
+// Waits until the loads of d have landed (an empty asm that reads every word:
+// the compiler places the counter wait before it).
+template <int KB, int VB, int QJL, int WIDE>
+__device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE>& d) {
+#pragma unroll
+  for (int m = 0; m < 2; ++m) {
+#pragma unroll
+    for (int k = 0; k < KB; ++k) asm volatile("" ::"v"(d.kw[m][k]));
+    if constexpr (QJL) asm volatile("" ::"v"(d.sw[m]));
+  }
+#pragma unroll
+  for (int k = 0; k < 2 * VB; ++k) asm volatile("" ::"v"(d.vw[k]));
+  asm volatile("" ::"v"(d.nm.kn), "v"(d.nm.vn));
+  if constexpr (QJL) asm volatile("" ::"v"(d.nm.kg));
+}
+
 template <int KB, int VB, int QJL, int WIDE>
 __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo, int t0) {
   constexpr int KW = 4 * KB, VBW = 32 * VB;
@@ -551,12 +567,6 @@ constexpr int kCommonWaves = 16;
 template <int QJL, int WIDE>
 constexpr int scan_waves() { return (QJL || WIDE) ? 8 : kCommonWaves; }
 
-// Steps whose code words are in flight while a step computes (register
-// buffers: one more than this).
-constexpr int kAheadCommon = 1;
-template <int QJL, int WIDE>
-constexpr int scan_ahead() { return (QJL || WIDE) ? 1 : kAheadCommon; }
-
 // merge buffer: [wave][column][kMergeStride] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
 constexpr int merge_cols() { return WIDE ? 16 : 8; }
@@ -666,10 +676,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (idx * 2u) & ~3u : idx * 4u, 0, 0);
     }
   }
-  constexpr int AH = scan_ahead<QJL, WIDE>();
-  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
-#pragma unroll
-  for (int i = 0; i < AH; ++i) load_step(buf[i], s, lo, t_begin + i * kStep);
+  StepData<KB, VB, QJL, WIDE> buf[2];
+  load_step(buf[0], s, lo, t_begin);
   int ctx = a.T;
   if (a.ctx_lens) ctx = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.ctx_lens, (uint32_t)((b + 1) * 4)),
                                                              (uint32_t)b * 4u, 0, 0);
@@ -751,12 +759,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     st.acc1[nb] = st.acc0[nb];
   }
 
-  // ---- stream the share: full 32-token steps with AH + 1 register buffers in
-  // turn, then at most one masked step for a ragged end. A step first issues
-  // the loads (code words and norms) of the step AH ahead (near the end it
-  // reloads its own instead, so the loads carry no branch), then computes on
-  // words loaded AH steps earlier: loads complete in issue order, so waiting
-  // for those leaves the later steps' loads in flight for the whole step.
+  // ---- stream the share: full 32-token steps with two register buffers in
+  // turn, then at most one masked step for a ragged end. A step first waits
+  // for its own loads (code words and norms, issued a step earlier, so
+  // normally complete), then issues the loads of the next step, if any, and
+  // computes: the next step's loads stay in flight for the whole step, and no
+  // wait inside the step depends on whether they were issued.
   // Balance: the sequencer favours older wavefronts, so with equal shares the
   // younger ones would finish last and leave the compute unit a tail with few
   // wavefronts (little memory parallelism). Each step a wavefront counts
@@ -765,30 +773,29 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // while it is ahead.
   int t0 = t_begin;
   if (t0 < t_full) {
-    bool done = false;
     uint32_t mine = 0;   // steps begun by this wavefront
-    while (!done) {
-#pragma unroll
-      for (int i = 0; i <= AH; ++i) {
-        if (!done) {
-          const int tl = t0 + AH * kStep;
-          load_step(buf[(i + AH) % (AH + 1)], s, lo, tl < t_full ? tl : t0);
-          __builtin_amdgcn_sched_barrier(0);
-          uint32_t begun = 0u;
-          if (lane == 0)
-            begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-          scan_step<KB, VB, QJL, WIDE, false>(buf[i], q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
-          begun = __builtin_amdgcn_readfirstlane(begun);   // by the whole workgroup
-          const uint32_t even = mine * (uint32_t)NW;        // if every wavefront kept pace
-          if (begun > even + NW) __builtin_amdgcn_s_setprio(3);
-          else if (begun + NW < even) __builtin_amdgcn_s_setprio(0);
-          else __builtin_amdgcn_s_setprio(1);
-          ++mine;
-          t0 += kStep;
-          done = t0 >= t_full;
-        }
-      }
+#define TQ_STEP(CUR, NEXT)                                                                                  \
+    {                                                                                                       \
+      wait_step(CUR);                                                                                       \
+      if (t0 + kStep < t_full) load_step(NEXT, s, lo, t0 + kStep);                                          \
+      uint32_t begun = 0u;                                                                                  \
+      if (lane == 0)                                                                                        \
+        begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);      \
+      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);             \
+      begun = __builtin_amdgcn_readfirstlane(begun);   /* by the whole workgroup */                          \
+      const uint32_t even = mine * (uint32_t)NW;        /* if every wavefront kept pace */                   \
+      if (begun > even + NW) __builtin_amdgcn_s_setprio(3);                                                 \
+      else if (begun + NW < even) __builtin_amdgcn_s_setprio(0);                                            \
+      else __builtin_amdgcn_s_setprio(1);                                                                   \
+      ++mine;                                                                                               \
+      t0 += kStep;                                                                                          \
+      if (t0 >= t_full) break;                                                                              \
     }
+    while (true) {
+      TQ_STEP(buf[0], buf[1])
+      TQ_STEP(buf[1], buf[0])
+    }
+#undef TQ_STEP
     __builtin_amdgcn_s_setprio(0);
   }
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
