@@ -22,7 +22,8 @@
 // persistent: each loads Pi once into LDS (in MFMA operand order) and loops
 // over tiles, with the next tile's input in flight. Bulk quantization without
 // QJL uses 32-slot tiles on 32x32x16 MFMAs (16 wavefronts per workgroup);
-// appends and QJL keys use 16-slot tiles on 16x16x32 MFMAs.
+// short inputs and QJL keys use 16-slot tiles on 16x16x32 MFMAs; a single
+// token per (row, head) without QJL takes the append kernel (float32 FMAs).
 #include <math.h>
 
 #include <atomic>
