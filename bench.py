@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prefill-iters", type=int, default=3)
+    ap.add_argument("--paged-block", type=int, default=256,
+                    help="also time decode on paged caches with this many tokens per block (0: skip)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -244,6 +246,48 @@ def main():
     log(f"[bench] step {ms_step * 1e3:.1f} us (append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us); "
         f"decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
 
+    # the same step on paged caches: logical blocks of every row mapped to a
+    # seeded permutation of physical blocks (a runtime's block-table cache)
+    paged = None
+    bt = args.paged_block
+    if bt > 0 and T_cap % bt == 0:
+        maxblk = T_cap // bt
+        perm = torch.randperm(w.B * maxblk, generator=torch.Generator().manual_seed(5), dtype=torch.int64)
+        table = perm.to(torch.int32).reshape(w.B, maxblk).to(dev)
+        pk = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl),
+                      block_table=table, block_tokens=bt, n_blocks=w.B * maxblk)
+        pv = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev,
+                      block_table=table, block_tokens=bt, n_blocks=w.B * maxblk)
+        tq.quantize_kv(tq_synth.torch_kv(w, "k", dev), pk)
+        tq.quantize_kv(tq_synth.torch_kv(w, "v", dev), pv)
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        pout = torch.empty_like(out)
+        for i in range(5):
+            tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(50):
+            tq.quantize_kv(new_k, pk, t_offset=T - 1)
+            tq.quantize_kv(new_v, pv, t_offset=T - 1)
+            tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
+        e1.record()
+        e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e2.record()
+        for i in range(50):
+            tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
+        e3.record()
+        torch.cuda.synchronize()
+        p_step = e0.elapsed_time(e1) / 50 * 1e3
+        p_dec = e2.elapsed_time(e3) / 50 * 1e3
+        paged = {"block_tokens": bt, "physical_blocks": w.B * maxblk, "table": "seeded permutation",
+                 "step_us": p_step, "decode_us_back_to_back": p_dec,
+                 "decode_GB_s": dbytes / (p_dec * 1e-6) / 1e9,
+                 "decode_frac": dbytes / (p_dec * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] paged (block {bt}): step {p_step:.1f} us, decode {p_dec:.1f} us back to back")
+        del pk, pv
+        torch.cuda.empty_cache()
+
     # calibration copy of known size for the rocprofv3 byte counters (256 MiB read + write)
     cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
     cal2 = torch.empty_like(cal)
@@ -284,6 +328,8 @@ def main():
                              "mfma_issued_TFLOP_s": issued / (pre * 1e-3) / 1e12,
                              "mfma_frac": issued / (pre * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS},
     }
+    if paged is not None:
+        res["paged"] = paged
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)

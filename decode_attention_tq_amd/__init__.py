@@ -58,6 +58,7 @@ class TQCache(ctypes.Structure):
         ("qjl_signs", ctypes.c_void_p), ("qjl_gamma", ctypes.c_void_p),
         ("rot", ctypes.c_void_p), ("qjl_proj", ctypes.c_void_p),
         ("centroids", ctypes.c_float * 16),
+        ("block_table", ctypes.c_void_p), ("block_tokens", ctypes.c_int64), ("n_blocks", ctypes.c_int64),
     ]
 
 
@@ -161,22 +162,34 @@ def _dtype_code(t) -> int:
 class Cache:
     """Device buffers of one packed cache (keys or values of one layer).
 
-    codes  int32 words [B, H_kv, T_cap * d * bits / 32] (layout set by `role`)
-    norms  float32 [B, H_kv, T_cap]
-    signs  int32 [B, H_kv, T_cap, d/32] and gamma float32 [B, H_kv, T_cap] for QJL keys
+    Contiguous layout (block_table None):
+      codes  int32 words [B, H_kv, T_cap * d * bits / 32] (layout set by `role`)
+      norms  float32 [B, H_kv, T_cap]
+      signs  int32 [B, H_kv, T_cap, d/32] and gamma float32 [B, H_kv, T_cap] for QJL keys
+    Paged layout (block_table int32 [B, T_cap / block_tokens] on the device,
+    entries in [0, n_blocks)): the same arrays with [n_blocks, H_kv, block_tokens ...]
+    in place of [B, H_kv, T_cap ...].
     rot    float32 [d, d] (Pi), proj float32 [d, d] (S, QJL keys), centroids (host)
     """
 
     def __init__(self, role: int, bits: int, B: int, H_kv: int, T_cap: int, device="cuda",
                  rot=None, proj=None, qjl: bool = False, centroids=None, rot_seed: int = 42,
-                 qjl_seed: int = 4242):
+                 qjl_seed: int = 4242, block_table=None, block_tokens: int = 0, n_blocks: int = 0):
         torch = _torch()
         self.role, self.bits, self.qjl = role, bits, int(bool(qjl))
         self.B, self.H_kv, self.T_cap, self.d = B, H_kv, T_cap, D
         self.device = torch.device(device)
+        self.block_table = block_table
+        self.block_tokens, self.n_blocks = int(block_tokens), int(n_blocks)
+        if block_table is not None:
+            if block_table.dtype != torch.int32 or tuple(block_table.shape) != (B, T_cap // max(block_tokens, 1)):
+                raise ValueError("block_table must be int32 [B, T_cap / block_tokens]")
+            lead, per = (n_blocks, H_kv), block_tokens
+        else:
+            lead, per = (B, H_kv), T_cap
         W = D * bits // 32
-        self.codes = torch.zeros((B, H_kv, T_cap * W), dtype=torch.int32, device=self.device)
-        self.norms = torch.zeros((B, H_kv, T_cap), dtype=torch.float32, device=self.device)
+        self.codes = torch.zeros((*lead, per * W), dtype=torch.int32, device=self.device)
+        self.norms = torch.zeros((*lead, per), dtype=torch.float32, device=self.device)
         if rot is None:
             rot = make_rotation(rot_seed, HAAR)
         self.rot = torch.as_tensor(np.asarray(rot, dtype=np.float32)).to(self.device).contiguous()
@@ -184,8 +197,8 @@ class Cache:
             if proj is None:
                 proj = make_rotation(qjl_seed, GAUSSIAN)
             self.proj = torch.as_tensor(np.asarray(proj, dtype=np.float32)).to(self.device).contiguous()
-            self.signs = torch.zeros((B, H_kv, T_cap, D // 32), dtype=torch.int32, device=self.device)
-            self.gamma = torch.zeros((B, H_kv, T_cap), dtype=torch.float32, device=self.device)
+            self.signs = torch.zeros((*lead, per, D // 32), dtype=torch.int32, device=self.device)
+            self.gamma = torch.zeros((*lead, per), dtype=torch.float32, device=self.device)
         else:
             self.proj = self.signs = self.gamma = None
         if centroids is None:
@@ -204,6 +217,9 @@ class Cache:
         s.qjl_proj = self.proj.data_ptr() if self.qjl else None
         for i, c in enumerate(self.centroids):
             s.centroids[i] = float(c)
+        if self.block_table is not None:
+            s.block_table = self.block_table.data_ptr()
+            s.block_tokens, s.n_blocks = self.block_tokens, self.n_blocks
         return s
 
     @property

@@ -23,8 +23,19 @@ int check_cache(const tq_cache* c) {
   if (c->B <= 0 || c->H_kv <= 0 || c->T_cap <= 0) return TQ_ERR_INVALID_ARGUMENT;
   if (c->B > 65535 || c->H_kv > 65535) return TQ_ERR_UNSUPPORTED;
   if (c->role == TQ_VALUES && c->T_cap % kValueBlock != 0) return TQ_ERR_INVALID_ARGUMENT;
-  // per-head byte ranges are addressed with 32-bit offsets
-  if (c->T_cap * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+  if (c->block_table != nullptr) {
+    // paged: power-of-two blocks of 32 .. 65536 tokens (a decode step never
+    // crosses one), whole blocks per row, each array below 2 GiB (32-bit offsets)
+    const int64_t bt = c->block_tokens;
+    if (bt < 32 || bt > 65536 || (bt & (bt - 1)) != 0) return TQ_ERR_INVALID_ARGUMENT;
+    if (c->T_cap % bt != 0 || c->n_blocks <= 0) return TQ_ERR_INVALID_ARGUMENT;
+    if (((uintptr_t)c->block_table & 3) != 0) return TQ_ERR_ALIGNMENT;
+    if (c->n_blocks > ((int64_t)1 << 31) / (c->H_kv * bt)) return TQ_ERR_UNSUPPORTED;
+    if (cache_rows(c) * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+  } else {
+    // per-head byte ranges are addressed with 32-bit offsets
+    if (c->T_cap * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+  }
   if (c->codes == nullptr || c->norms == nullptr || c->rot == nullptr) return TQ_ERR_INVALID_ARGUMENT;
   if (c->qjl && (c->qjl_signs == nullptr || c->qjl_gamma == nullptr || c->qjl_proj == nullptr))
     return TQ_ERR_INVALID_ARGUMENT;

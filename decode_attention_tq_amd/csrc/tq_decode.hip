@@ -14,6 +14,9 @@
 //   epilogue  the wavefront partials are merged in LDS in a fixed order; with
 //             a single chunk (the usual case once B * H_kv fills the part) the
 //             workgroup applies o = Pi_V^T o' and writes the output itself.
+// Paged caches: a step's token rows come from the block table (an entry read
+// one step ahead); a 32-token step never crosses a block. A separate
+// instantiation keeps the contiguous path free of that work.
 // combine (only when the context is split into several chunks): fixed-order
 // merge of the chunk partials of each query head, then o = Pi_V^T o'.
 // (Merging chunks inside decode_scan would need a device-scope release per
@@ -206,6 +209,7 @@ struct ScanArgs {
   float* ml;     // [B][H_q][n_split][2], partials when n_split > 1
   float* acc;    // [B][H_q][n_split][128]
   int64_t TcK, TcV;
+  PageMap kpm, vpm;   // block tables of paged caches (table == nullptr: contiguous)
   int q_dtype, H_kv, H_q, G, T, n_split, wg_chunk, wave_chunk;
   float sc1, sc2, inv_sqrt_d;
   float kc[16], vc[16];
@@ -300,6 +304,23 @@ struct Streams {
   __amdgpu_buffer_rsrc_t rk, rkn, rv, rvn, rs, rg;
 };
 
+// Block-table entry of the block holding token t (paged caches): an
+// asynchronous read through the range-checked table row rt.
+__device__ inline uint32_t page_entry(__amdgpu_buffer_rsrc_t rt, const PageMap& m, int t) {
+  return __builtin_amdgcn_raw_buffer_load_b32(rt, (uint32_t)(t >> m.lg) * 4u, 0, 0);
+}
+
+// Token row (relative to the stream base) of the step starting at token t: t
+// itself for a contiguous cache; for a paged one, row t % 2^lg of head kv in
+// physical block e (clamped into the arrays, so entries the caller left
+// unset are never dereferenced out of bounds). A step never crosses a block
+// (blocks are multiples of 32 tokens, steps start at multiples of 32).
+__device__ inline uint32_t step_row(const PageMap& m, int kv, int H_kv, uint32_t e, int t) {
+  if (m.table == nullptr) return (uint32_t)t;
+  const uint32_t p = min(__builtin_amdgcn_readfirstlane(e), (uint32_t)(m.nblk - 1));
+  return ((p * (uint32_t)H_kv + (uint32_t)kv) << m.lg) + ((uint32_t)t & ((1u << m.lg) - 1u));
+}
+
 template <int N>
 __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
   if constexpr (N == 2) {
@@ -322,11 +343,11 @@ __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
 }
 
 template <int QJL>
-__device__ inline void load_norms(StepNorms<QJL>& n, const Streams& s, const LaneOffsets& lo, int t0) {
-  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0) * 4u;
-  n.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, lo.n, st, kStreamAux));
-  n.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, lo.n, st, kStreamAux));
-  if constexpr (QJL) n.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, lo.n, st, kStreamAux));
+__device__ inline void load_norms(StepNorms<QJL>& n, const Streams& s, const LaneOffsets& lo, uint32_t rk,
+                                  uint32_t rv) {
+  n.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, lo.n, rk * 4u, kStreamAux));
+  n.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, lo.n, rv * 4u, kStreamAux));
+  if constexpr (QJL) n.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, lo.n, rk * 4u, kStreamAux));
 }
 
 // Waits until the loads of d have landed (an empty asm that reads every word:
@@ -345,18 +366,22 @@ __device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE>& d) {
   if constexpr (QJL) asm volatile("" ::"v"(d.nm.kg));
 }
 
+// Loads one step: rk, rv are the token rows of the step's first token in the
+// key and value arrays (relative to the stream bases; 32 consecutive rows).
 template <int KB, int VB, int QJL, int WIDE>
-__device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo, int t0) {
+__device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo,
+                                 uint32_t rk, uint32_t rv) {
   constexpr int KW = 4 * KB, VBW = 32 * VB;
   // wave-uniform; readfirstlane keeps the step offsets in scalar registers
-  const uint32_t st = __builtin_amdgcn_readfirstlane((uint32_t)t0);
+  rk = __builtin_amdgcn_readfirstlane(rk);
+  rv = __builtin_amdgcn_readfirstlane(rv);
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    bload_words_s<KB>(s.rk, lo.k[m], st * (KW * 4u), d.kw[m]);
-    if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], st * 16u, kStreamAux);
+    bload_words_s<KB>(s.rk, lo.k[m], rk * (KW * 4u), d.kw[m]);
+    if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], rk * 16u, kStreamAux);
   }
-  bload_words_s<2 * VB>(s.rv, lo.v, (st / 8u) * (VBW * 4u), d.vw);
-  load_norms(d.nm, s, lo, t0);
+  bload_words_s<2 * VB>(s.rv, lo.v, (rv / 8u) * (VBW * 4u), d.vw);
+  load_norms(d.nm, s, lo, rk, rv);
 }
 
 
@@ -596,7 +621,7 @@ constexpr size_t scan_lds_bytes() {
 //   epilogue  the wavefront partials are merged in LDS in a fixed order; with
 //             one chunk the workgroup finishes the heads (o = Pi_V^T o'),
 //             otherwise it writes the chunk partial for the combine.
-template <int KB, int VB, int QJL, int WIDE>
+template <int KB, int VB, int QJL, int WIDE, int PAGED>
 __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_kernel(ScanArgs a) {
   constexpr int NW = scan_waves<QJL, WIDE>(), NT = 64 * NW;
   constexpr int NS = QJL ? 4 : 0;
@@ -632,16 +657,33 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // the buffer loads
   const int t_begin = split * a.wg_chunk + wave * a.wave_chunk;
 
+  // Streams: contiguous caches start at this (row, KV head)'s first token row
+  // and span its T_cap rows; paged caches span the whole arrays and a step's
+  // rows come from the block table (step_row).
+  // (PAGED: at least one of the two caches is paged; the contiguous-only
+  // instantiation carries none of the table work)
+  const bool kpg = PAGED && a.kpm.table != nullptr, vpg = PAGED && a.vpm.table != nullptr;
+  const int64_t kbase = kpg ? 0 : bkv * a.TcK, vbase = vpg ? 0 : bkv * a.TcV;
+  const int64_t krows = kpg ? (a.kpm.nblk * a.H_kv) << a.kpm.lg : a.TcK;
+  const int64_t vrows = vpg ? (a.vpm.nblk * a.H_kv) << a.vpm.lg : a.TcV;
   Streams s;
-  s.rk = make_rsrc(a.kcodes + bkv * a.TcK * KW, (uint32_t)(a.TcK * KW * 4));
-  s.rkn = make_rsrc(a.knorms + bkv * a.TcK, (uint32_t)(a.TcK * 4));
-  s.rv = make_rsrc(a.vcodes + bkv * a.TcV * 4 * VB, (uint32_t)(a.TcV * 4 * VB * 4));
-  s.rvn = make_rsrc(a.vnorms + bkv * a.TcV, (uint32_t)(a.TcV * 4));
+  s.rk = make_rsrc(a.kcodes + kbase * KW, (uint32_t)(krows * KW * 4));
+  s.rkn = make_rsrc(a.knorms + kbase, (uint32_t)(krows * 4));
+  s.rv = make_rsrc(a.vcodes + vbase * 4 * VB, (uint32_t)(vrows * 4 * VB * 4));
+  s.rvn = make_rsrc(a.vnorms + vbase, (uint32_t)(vrows * 4));
   // QJL sketch (empty ranges when the keys carry none)
-  s.rs = make_rsrc(QJL ? (const void*)(a.ksigns + bkv * a.TcK * 4) : (const void*)a.knorms,
-                   QJL ? (uint32_t)(a.TcK * 16) : 0u);
-  s.rg = make_rsrc(QJL ? (const void*)(a.kgamma + bkv * a.TcK) : (const void*)a.knorms,
-                   QJL ? (uint32_t)(a.TcK * 4) : 0u);
+  s.rs = make_rsrc(QJL ? (const void*)(a.ksigns + kbase * 4) : (const void*)a.knorms,
+                   QJL ? (uint32_t)(krows * 16) : 0u);
+  s.rg = make_rsrc(QJL ? (const void*)(a.kgamma + kbase) : (const void*)a.knorms,
+                   QJL ? (uint32_t)(krows * 4) : 0u);
+  // block-table rows of this batch row (range-checked reads: a block past the
+  // table reads entry 0)
+  const __amdgpu_buffer_rsrc_t rtk =
+      make_rsrc(kpg ? (const void*)(a.kpm.table + b * a.kpm.maxblk) : (const void*)a.knorms,
+                kpg ? (uint32_t)(a.kpm.maxblk * 4) : 0u);
+  const __amdgpu_buffer_rsrc_t rtv =
+      make_rsrc(vpg ? (const void*)(a.vpm.table + b * a.vpm.maxblk) : (const void*)a.knorms,
+                vpg ? (uint32_t)(a.vpm.maxblk * 4) : 0u);
   const bool hf = !WIDE && c >= 8;
   LaneOffsets lo;
 #pragma unroll
@@ -677,7 +719,16 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
   }
   StepData<KB, VB, QJL, WIDE> buf[2];
-  load_step(buf[0], s, lo, t_begin);
+  // (a wavefront whose share starts past the caches has no work; it reads the
+  // first step instead: the scalar offset of a buffer load is not range
+  // checked, only the per-lane offset is)
+  const int t_first = t_begin < min(a.TcK, a.TcV) ? t_begin : 0;
+  uint32_t ek = 0u, ev = 0u;   // block-table entries of the next step to load (paged caches)
+  if (kpg) ek = page_entry(rtk, a.kpm, t_first);
+  if (vpg) ev = page_entry(rtv, a.vpm, t_first);
+  load_step(buf[0], s, lo, step_row(a.kpm, kv, a.H_kv, ek, t_first), step_row(a.vpm, kv, a.H_kv, ev, t_first));
+  if (kpg) ek = page_entry(rtk, a.kpm, t_first + kStep);
+  if (vpg) ev = page_entry(rtv, a.vpm, t_first + kStep);
   int ctx = a.T;
   if (a.ctx_lens) ctx = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.ctx_lens, (uint32_t)((b + 1) * 4)),
                                                              (uint32_t)b * 4u, 0, 0);
@@ -777,7 +828,14 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 #define TQ_STEP(CUR, NEXT)                                                                                  \
     {                                                                                                       \
       wait_step(CUR);                                                                                       \
-      if (t0 + kStep < t_full) load_step(NEXT, s, lo, t0 + kStep);                                          \
+      if (t0 + kStep < t_full) {                                                                            \
+        const uint32_t rk = step_row(a.kpm, kv, a.H_kv, ek, t0 + kStep);                                    \
+        const uint32_t rv = step_row(a.vpm, kv, a.H_kv, ev, t0 + kStep);                                    \
+        /* the entry changes only where the following step starts a block */                               \
+        if (kpg && ((t0 + 2 * kStep) & ((1 << a.kpm.lg) - 1)) == 0) ek = page_entry(rtk, a.kpm, t0 + 2 * kStep); \
+        if (vpg && ((t0 + 2 * kStep) & ((1 << a.vpm.lg) - 1)) == 0) ev = page_entry(rtv, a.vpm, t0 + 2 * kStep); \
+        load_step(NEXT, s, lo, rk, rv);                                                                     \
+      }                                                                                                     \
       uint32_t begun = 0u;                                                                                  \
       if (lane == 0)                                                                                        \
         begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);      \
@@ -801,7 +859,9 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
   if (t0 < t_end) {
     StepData<KB, VB, QJL, WIDE> E;
-    load_step(E, s, lo, t0);
+    if (kpg) ek = page_entry(rtk, a.kpm, t0);
+    if (vpg) ev = page_entry(rtv, a.vpm, t0);
+    load_step(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
     scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
   }
 
@@ -1026,8 +1086,12 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* ml, const flo
 template <int KB, int VB, int QJL, int WIDE>
 hipError_t launch_scan(const DecodePlan& p, const ScanArgs& sa, hipStream_t stream) {
   dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)p.B);
-  hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0, stream,
-                     sa);
+  if (sa.kpm.table != nullptr || sa.vpm.table != nullptr)
+    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 1>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0,
+                       stream, sa);
+  else
+    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 0>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0,
+                       stream, sa);
   return hipGetLastError();
 }
 
@@ -1077,6 +1141,8 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   sa.acc = acc;
   sa.TcK = k->T_cap;
   sa.TcV = v->T_cap;
+  sa.kpm = page_map(k);
+  sa.vpm = page_map(v);
   sa.q_dtype = q_dtype;
   sa.H_kv = (int)p.H_kv;
   sa.H_q = (int)p.H_q;

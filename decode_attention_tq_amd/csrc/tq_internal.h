@@ -30,6 +30,32 @@ struct DecodePlan {
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
                  DecodePlan* p);
 
+// Block table of a cache in the paged layout; table == nullptr for the
+// contiguous layout. Token t of (row b, head h) is token row
+// (table[b][t >> lg] * H_kv + h) * 2^lg + t % 2^lg of the arrays.
+struct PageMap {
+  const int32_t* table;   // [B][maxblk] physical block of each logical block
+  int64_t maxblk;         // logical blocks per row: T_cap >> lg
+  int64_t nblk;           // physical blocks in the arrays
+  int32_t lg;             // log2(block_tokens)
+};
+
+inline PageMap page_map(const tq_cache* c) {
+  PageMap m{nullptr, 0, 0, 0};
+  if (c->block_table != nullptr) {
+    m.table = c->block_table;
+    m.nblk = c->n_blocks;
+    while ((int64_t(1) << m.lg) < c->block_tokens) ++m.lg;
+    m.maxblk = c->T_cap >> m.lg;
+  }
+  return m;
+}
+
+// Token rows in a cache's arrays (B*H_kv*T_cap contiguous, n_blocks*H_kv*block_tokens paged).
+inline int64_t cache_rows(const tq_cache* c) {
+  return c->block_table != nullptr ? c->n_blocks * c->H_kv * c->block_tokens : c->B * c->H_kv * c->T_cap;
+}
+
 // Host-side codebook helpers (tq_host.cpp).
 void thresholds_from_centroids(const float* c, int levels, float* t);
 

@@ -52,7 +52,22 @@ struct QuantArgs {
   float cent[16];
   float thr[16];
   int thr_sym;   // the thresholds mirror around 0 (middle one is 0)
+  PageMap pm;    // block table of a paged cache (pm.table == nullptr: contiguous)
 };
+
+// Token row of (row*H_kv + head, token) in a cache's arrays: contiguous, or
+// through the block table. -1 when the table maps the token's block outside
+// the arrays (such a write is skipped: the table is the caller's).
+__device__ inline int64_t tok_row(const PageMap& pm, int64_t H_kv, int64_t T_cap, int64_t bh, int64_t t) {
+  if (pm.table == nullptr) return bh * T_cap + t;
+  const uint32_t hk = (uint32_t)H_kv;
+  const uint32_t b = (uint32_t)bh / hk, h = (uint32_t)bh - b * hk;   // B, H_kv < 2^16
+  const int64_t blk = t >> pm.lg;
+  if (blk < 0 || blk >= pm.maxblk) return -1;
+  const int32_t p = pm.table[(int64_t)b * pm.maxblk + blk];
+  if (p < 0 || p >= pm.nblk) return -1;
+  return (((int64_t)p * H_kv + h) << pm.lg) + (t & ((int64_t(1) << pm.lg) - 1));
+}
 
 template <int BITS>
 __device__ inline Thresholds<BITS> load_thresholds(const QuantArgs& a) {
@@ -331,7 +346,8 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
         uint32_t wbits = 0u;
 #pragma unroll
         for (int k = 0; k < 32; ++k) wbits |= ((q[k >> 2] >> (8 * (k & 3))) & 1u) << k;
-        if (ok) a.signs[(bh2 * a.T_cap + t2) * 4 + grp] = wbits;
+        const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, bh2, t2) : -1;
+        if (row >= 0) a.signs[row * 4 + grp] = wbits;
       }
       // gamma: lane (g, n = 0) holds slots 4g + r
       if (i16 == 0) {
@@ -339,13 +355,19 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
         for (int r = 0; r < 4; ++r) {
           int64_t bh2, t2;
           slot_pos(a, tile * TILE + wave * 16, 4 * g + r, bh2, t2);
-          if (bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T) a.gamma[bh2 * a.T_cap + t2] = gam[r];
+          if (bh2 < heads && t2 >= a.t_offset && t2 < a.t_offset + a.T) {
+            const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh2, t2);
+            if (row >= 0) a.gamma[row] = gam[r];
+          }
         }
       }
     }
 
     // ---- norms
-    if (valid && g == 0) a.norms[bh * a.T_cap + t] = ldexpf(ns, -sexp);
+    if (valid && g == 0) {
+      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
+    }
 
     // ---- pack and store codes
     if constexpr (ROLE == TQ_KEYS) {
@@ -358,8 +380,9 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
       for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kD + 32 * grp + 4 * k);
       uint32_t w[BITS];
       pack32<BITS>(q, w);
-      if (ok) {
-        uint32_t* dst = a.codes + (bh2 * a.T_cap + t2) * KW + grp * BITS;
+      const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, bh2, t2) : -1;
+      if (row >= 0) {
+        uint32_t* dst = a.codes + row * KW + grp * BITS;
 #pragma unroll
         for (int k = 0; k < BITS; ++k) dst[k] = w[k];
       }
@@ -397,8 +420,9 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
           }
         }
       }
-      if (any_valid) {
-        uint32_t* dst = a.codes + (bh2 * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+      const int64_t row = any_valid ? tok_row(a.pm, a.H_kv, a.T_cap, bh2, tb) : -1;
+      if (row >= 0) {
+        uint32_t* dst = a.codes + row * (VBW / 8) + cg * BITS;
 #pragma unroll
         for (int k = 0; k < BITS; ++k) dst[k] = all_valid ? w[k] : ((dst[k] & keep[k]) | w[k]);
       }
@@ -576,7 +600,10 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
     }
 
     // ---- norm
-    if (cur.valid && kh == 0) a.norms[bh * a.T_cap + t] = ldexpf(ns, -sexp);
+    if (cur.valid && kh == 0) {
+      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
+    }
     wave_sync();
 
     // ---- pack and store codes, 16 vectors per pass
@@ -592,8 +619,9 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
         for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)(cbuf + v * kQ32Row + 32 * grp + 4 * k);
         uint32_t w[BITS];
         pack32<BITS>(q, w);
-        if (ok) {
-          uint32_t* dst = a.codes + (bh2 * a.T_cap + t2) * KW + grp * BITS;
+        const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, bh2, t2) : -1;
+        if (row >= 0) {
+          uint32_t* dst = a.codes + row * KW + grp * BITS;
 #pragma unroll
           for (int k = 0; k < BITS; ++k) dst[k] = w[k];
         }
@@ -631,8 +659,9 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
             }
           }
         }
-        if (any_valid) {
-          uint32_t* dst = a.codes + (bh2 * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+        const int64_t row = any_valid ? tok_row(a.pm, a.H_kv, a.T_cap, bh2, tb) : -1;
+        if (row >= 0) {
+          uint32_t* dst = a.codes + row * (VBW / 8) + cg * BITS;
 #pragma unroll
           for (int k = 0; k < BITS; ++k) dst[k] = all_valid ? w[k] : ((dst[k] & keep[k]) | w[k]);
         }
@@ -683,9 +712,9 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
   if constexpr (ROLE == TQ_VALUES) {
     const int v = tid >> 5, cg = tid & 31;
     const int64_t gv = v0 + v;
-    if (gv < nvec) {
-      const int64_t tb = a.t_offset & ~(int64_t)7;
-      vdst = a.codes + (gv * a.T_cap + tb) * (VBW / 8) + cg * BITS;
+    const int64_t row = gv < nvec ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset & ~(int64_t)7) : -1;
+    if (row >= 0) {
+      vdst = a.codes + row * (VBW / 8) + cg * BITS;
 #pragma unroll
       for (int k = 0; k < BITS; ++k) old_words[k] = vdst[k];
     }
@@ -725,7 +754,8 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
     *(float4*)&xs[v][4 * c4] = make_float4(x[0], x[1], x[2], x[3]);
     if (c4 == 0) {
       fzs[v] = ns > 0.f ? sqrt_d / ns : 0.f;
-      if (ok) a.norms[gv * a.T_cap + a.t_offset] = ldexpf(ns, -sexp);
+      const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset) : -1;
+      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
     }
   }
   __syncthreads();
@@ -750,13 +780,14 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
     if (tid < 4 * kAppendVecs) {
       const int v = tid >> 2, grp = tid & 3;
       const int64_t gv = v0 + v;
-      if (gv < nvec) {
+      const int64_t row = gv < nvec ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset) : -1;
+      if (row >= 0) {
         uint32_t q[8];
 #pragma unroll
         for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)&cb[v][32 * grp + 4 * k];
         uint32_t w[BITS];
         pack32<BITS>(q, w);
-        uint32_t* dst = a.codes + (gv * a.T_cap + a.t_offset) * KW + grp * BITS;
+        uint32_t* dst = a.codes + row * KW + grp * BITS;
 #pragma unroll
         for (int k = 0; k < BITS; ++k) dst[k] = w[k];
       }
@@ -805,6 +836,7 @@ struct DequantArgs {
   float* out;
   int64_t H_kv, T_cap, t0, t1;
   float cent[16];
+  PageMap pm;
 };
 
 template <int BITS, int ROLE, int QJL>
@@ -812,21 +844,28 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
   __shared__ float wv[32 * kD];
   __shared__ float sg[QJL ? 32 * kD : 1];
   __shared__ float nrm[32], gm[32];
+  __shared__ int64_t rows[32];   // token rows of the block's tokens (-1: none)
   constexpr int KW = 4 * BITS;
   const int tid = threadIdx.x;
   const int h = blockIdx.y, b = blockIdx.z;
   const int64_t bh = (int64_t)b * a.H_kv + h;
   const int64_t tbase = a.t0 + (int64_t)blockIdx.x * 32;
   const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
-  const uint32_t* cb = a.codes + bh * a.T_cap * KW;
+  const uint32_t* cb = a.codes;
+  if (tid < 32) {
+    const int64_t t = tbase + tid;
+    rows[tid] = t < a.t1 ? tok_row(a.pm, a.H_kv, a.T_cap, bh, t) : -1;
+  }
+  __syncthreads();
   for (int idx = tid; idx < 32 * kD; idx += 256) {
     const int v = idx / kD, j = idx % kD;
     const int64_t t = tbase + v;
+    const int64_t row = rows[v];
     float val = 0.f;
-    if (t < a.t1) {
+    if (row >= 0) {
       int64_t bit;
-      if constexpr (ROLE == TQ_KEYS) bit = t * KW * 32 + (int64_t)BITS * j;
-      else bit = (t / 8) * (int64_t)(32 * BITS) * 32 + (int64_t)BITS * (8 * j + (t % 8));
+      if constexpr (ROLE == TQ_KEYS) bit = row * KW * 32 + (int64_t)BITS * j;
+      else bit = (row / 8) * (int64_t)(32 * BITS) * 32 + (int64_t)BITS * (8 * j + (row % 8));
       const int64_t wi = bit >> 5;
       const int off = (int)(bit & 31);
       uint32_t x = cb[wi] >> off;
@@ -837,7 +876,7 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
       for (int q = 1; q < (1 << BITS); ++q) cc = (code == q) ? a.cent[q] : cc;
       val = cc * inv_sqrt_d;
       if constexpr (QJL) {
-        const uint32_t sw = a.signs[(bh * a.T_cap + t) * 4 + (j >> 5)];
+        const uint32_t sw = a.signs[row * 4 + (j >> 5)];
         sg[idx] = ((sw >> (j & 31)) & 1u) ? 1.f : -1.f;
       }
     } else if constexpr (QJL) {
@@ -847,8 +886,9 @@ __global__ __launch_bounds__(256) void dequantize_kernel(DequantArgs a) {
   }
   if (tid < 32) {
     const int64_t t = tbase + tid;
-    nrm[tid] = t < a.t1 ? a.norms[bh * a.T_cap + t] : 0.f;
-    if constexpr (QJL) gm[tid] = t < a.t1 ? a.gamma[bh * a.T_cap + t] : 0.f;
+    const int64_t row = rows[tid];
+    nrm[tid] = row >= 0 ? a.norms[row] : 0.f;
+    if constexpr (QJL) gm[tid] = row >= 0 ? a.gamma[row] : 0.f;
   }
   __syncthreads();
   const int col = tid & 127, half = tid >> 7;   // output coordinate, vector half
@@ -1006,6 +1046,7 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
   qa.gamma = dst->qjl_gamma;
   qa.rot = dst->rot;
   qa.proj = dst->qjl_proj;
+  qa.pm = page_map(dst);
   const int L = 1 << dst->bits;
   for (int i = 0; i < 16; ++i) qa.cent[i] = i < L ? dst->centroids[i] : 0.f;
   thresholds_from_centroids(dst->centroids, L, qa.thr);
@@ -1039,6 +1080,7 @@ hipError_t launch_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float*
   da.out = out;
   da.H_kv = src->H_kv;
   da.T_cap = src->T_cap;
+  da.pm = page_map(src);
   da.t0 = t0;
   da.t1 = t1;
   const int L = 1 << src->bits;

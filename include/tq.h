@@ -80,6 +80,27 @@ extern "C" {
  * Device pointers must be 16-byte aligned. centroids[] is held by value (host
  * memory, inside this struct): the 2^bits levels of tq_make_codebook, in
  * standard-normal units, each exactly representable in float16.
+ *
+ * Contiguous layout (block_table == NULL): every (row, head) owns T_cap token
+ * rows, at token row (b*H_kv + h)*T_cap + t of each array.
+ *
+ * Paged layout (block_table != NULL): the arrays hold n_blocks physical blocks
+ * of block_tokens tokens for all H_kv heads, and block_table (device int32,
+ * [B][T_cap / block_tokens]) maps logical block t / block_tokens of row b to
+ * a physical block p. Token t of (row b, head h) is at token row
+ * (p*H_kv + h)*block_tokens + t % block_tokens of each array (for value codes,
+ * its 8-token block is that row / 8). Rules: block_tokens is a power of two
+ * from 32 to 65536; T_cap is a multiple of it; every entry that a call reads
+ * or writes through (tokens below the context length, tokens being quantized)
+ * is in [0, n_blocks) (other entries are clamped into that range when the
+ * decode reads ahead, so they are never dereferenced out of bounds); a block
+ * written by tq_quantize_kv is mapped by one (row, logical block) only (two
+ * rows that share it would race); each array stays below 2 GiB. The layout
+ * serves a runtime's per-layer cache whose blocks are allocated as sequences
+ * grow (the ai-navigate-news.com post, Part 4: the serving sidecar builds one
+ * TurboQuant KV cache per transformer layer; the ai-accelerate.xyz article,
+ * section on what TurboQuant means for local LLM users: key and value cache
+ * types are chosen separately).
  */
 typedef struct tq_cache {
   int32_t role;        /* TQ_KEYS or TQ_VALUES */
@@ -89,13 +110,17 @@ typedef struct tq_cache {
   int64_t B;           /* batch rows */
   int64_t H_kv;        /* KV heads */
   int64_t T_cap;       /* token capacity per (row, head); multiple of 8 for values */
-  uint32_t* codes;     /* device, B*H_kv*T_cap*d*bits/32 words */
-  float* norms;        /* device, B*H_kv*T_cap */
-  uint32_t* qjl_signs; /* device, B*H_kv*T_cap*d/32 words, or NULL when qjl == 0 */
-  float* qjl_gamma;    /* device, B*H_kv*T_cap, or NULL when qjl == 0 */
+  uint32_t* codes;     /* device, R*d*bits/32 words, R token rows (see layouts above) */
+  float* norms;        /* device, R */
+  uint32_t* qjl_signs; /* device, R*d/32 words, or NULL when qjl == 0 */
+  float* qjl_gamma;    /* device, R, or NULL when qjl == 0 */
   const float* rot;    /* device Pi, d*d, row-major */
   const float* qjl_proj; /* device S, d*d, or NULL when qjl == 0 */
   float centroids[TQ_MAX_LEVELS];
+  /* R = B*H_kv*T_cap (contiguous) or n_blocks*H_kv*block_tokens (paged) */
+  const int32_t* block_table; /* device [B][T_cap/block_tokens], or NULL: contiguous */
+  int64_t block_tokens;       /* paged: tokens per block; ignored when contiguous */
+  int64_t n_blocks;           /* paged: physical blocks; ignored when contiguous */
 } tq_cache;
 
 /*

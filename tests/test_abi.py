@@ -29,9 +29,12 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_struct_layout_matches_header():
-    # 4 x int32, 3 x int64, 6 pointers, 16 floats
-    assert ctypes.sizeof(tq.TQCache) == 16 + 24 + 48 + 64
+    # 4 x int32, 3 x int64, 6 pointers, 16 floats, then the paged-layout fields
+    # (a pointer and 2 x int64)
+    assert ctypes.sizeof(tq.TQCache) == 16 + 24 + 48 + 64 + 24
     assert tq.TQCache.centroids.offset == 88
+    assert tq.TQCache.block_table.offset == 152
+    assert tq.TQCache.n_blocks.offset == 168
 
 
 def test_status_strings():
@@ -147,6 +150,24 @@ def test_quantize_validation_paths():
     s = _cache()
     s.centroids[2], s.centroids[3] = s.centroids[3], s.centroids[2]   # not ascending
     assert _quant(s) == tq.ERR_INVALID_ARGUMENT
+
+
+def test_paged_cache_validation_paths():
+    """Paged layout: block_tokens a power of two in 32..65536 dividing T_cap,
+    n_blocks > 0, a 4-byte aligned table, arrays below 2 GiB."""
+    def paged(**kw):
+        args = dict(T_cap=64, block_table=FAKE, block_tokens=32, n_blocks=4)
+        args.update(kw)
+        return _cache(**args)
+    for bad in (0, 16, 48, 96, 1 << 17):
+        assert _quant(paged(block_tokens=bad)) == tq.ERR_INVALID_ARGUMENT, bad
+    assert _quant(paged(T_cap=96, block_tokens=64)) == tq.ERR_INVALID_ARGUMENT   # 96 % 64
+    assert _quant(paged(n_blocks=0)) == tq.ERR_INVALID_ARGUMENT
+    assert _quant(paged(block_table=FAKE + 2)) == tq.ERR_ALIGNMENT
+    assert _quant(paged(n_blocks=1 << 22, block_tokens=64)) == tq.ERR_UNSUPPORTED   # codes >= 2 GiB
+    # a contiguous cache ignores block_tokens / n_blocks
+    assert _quant(_cache(block_tokens=48, n_blocks=-1), T=0) == tq.OK
+    assert _quant(paged(), T=0) == tq.OK
 
 
 def _decode(k, v, q=FAKE, H_q=8, T=64, scale=0.0, n_split=0, out=FAKE, ws=FAKE, ws_bytes=1 << 30, dtype=tq.BF16):
