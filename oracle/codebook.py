@@ -101,3 +101,83 @@ def canonical(bits: int):
     t = (c16[:-1] + c16[1:]) / 2.0
     t[len(t) // 2] = 0.0
     return c16, t
+
+
+# ---------------------------------------------------------------------------
+# Sphere-exact codebook (format variant).
+#
+# The article's step 1 says the rotated coordinates are close to Gaussian; the
+# exact law of one coordinate u of a uniformly random unit vector in d
+# dimensions has density proportional to (1 - u^2)^((d - 3)/2) on [-1, 1]
+# (equivalently (1 + u)/2 ~ Beta((d-1)/2, (d-1)/2)). This variant runs the same
+# Lloyd iteration on that law, in the same standard units z = u sqrt(d) (so
+# E[z^2] = 1), with the same canonical stored form (float16 centroids, exact
+# midpoints, middle threshold +0.0).
+#   P(a <= u < b)          = I_{(1+b)/2}(al, al) - I_{(1+a)/2}(al, al),  al = (d-1)/2
+#   int_a^b u f(u) du      = ((1 - a^2)^(k+1) - (1 - b^2)^(k+1)) / (2 (k+1) B(1/2, k+1)),  k = (d-3)/2
+# (the second from d/du (1 - u^2)^(k+1) = -2 (k+1) u (1 - u^2)^k, and
+# int_{-1}^{1} (1 - u^2)^k du = B(1/2, k+1)).
+
+def _sphere_cdf(u: float, d: int) -> float:
+    from scipy.special import betainc
+    al = (d - 1) / 2.0
+    x = min(max((1.0 + u) / 2.0, 0.0), 1.0)
+    return float(betainc(al, al, x))
+
+
+def _sphere_partial_mean(a: float, b: float, d: int) -> float:
+    """int_a^b u f(u) du for the sphere-coordinate density f (u in [-1, 1])."""
+    from scipy.special import betaln
+    k = (d - 3) / 2.0
+    lb = betaln(0.5, k + 1.0)
+    def g(u):
+        v = 1.0 - u * u
+        return 0.0 if v <= 0.0 else math.exp((k + 1.0) * math.log(v) - lb)
+    return (g(a) - g(b)) / (2.0 * (k + 1.0))
+
+
+def lloyd_max_sphere(bits: int, d: int, tol: float = 1e-14, max_iter: int = 200000):
+    """Unrounded Lloyd-Max centroids (standard units) of one coordinate of a
+    uniform unit vector in d >= 3 dimensions. Returns (centroids, iterations, last change)."""
+    from scipy.special import betaincinv
+    L = 1 << bits
+    sd = math.sqrt(d)
+    al = (d - 1) / 2.0
+    # start at the quantiles (i + 1/2) / L of the law, as the Gaussian iteration does
+    c = [sd * (2.0 * float(betaincinv(al, al, (i + 0.5) / L)) - 1.0) for i in range(L)]
+    delta = math.inf
+    it = 0
+    while delta >= tol and it < max_iter:
+        t = [-1.0] + [min(max((c[i] + c[i + 1]) / 2.0 / sd, -1.0), 1.0) for i in range(L - 1)] + [1.0]
+        new = []
+        for i in range(L):
+            p = _sphere_cdf(t[i + 1], d) - _sphere_cdf(t[i], d)
+            new.append(sd * _sphere_partial_mean(t[i], t[i + 1], d) / p)
+        delta = max(abs(a - b) for a, b in zip(new, c))
+        c = new
+        it += 1
+    c = np.array(c)
+    c = (c - c[::-1]) / 2.0
+    return c, it, delta
+
+
+def sphere_cell_probs(c: np.ndarray, d: int) -> np.ndarray:
+    """P(cell i) under the sphere law for the cells the midpoints of c (standard units) define."""
+    sd = math.sqrt(d)
+    L = len(c)
+    t = [-1.0] + [min(max((c[i] + c[i + 1]) / 2.0 / sd, -1.0), 1.0) for i in range(L - 1)] + [1.0]
+    return np.array([_sphere_cdf(t[i + 1], d) - _sphere_cdf(t[i], d) for i in range(L)])
+
+
+def mse_fixed_point_sphere(c: np.ndarray, d: int) -> float:
+    """MSE (standard units) of a Lloyd fixed point of the sphere law: 1 - sum c_i^2 P_i."""
+    return 1.0 - float(np.sum(np.asarray(c) ** 2 * sphere_cell_probs(c, d)))
+
+
+def canonical_sphere(bits: int, d: int = 128):
+    """Stored sphere codebook: fp16-exact centroids and exact midpoints (middle +0.0)."""
+    c, _, _ = lloyd_max_sphere(bits, d)
+    c16 = c.astype(np.float16).astype(np.float64)
+    t = (c16[:-1] + c16[1:]) / 2.0
+    t[len(t) // 2] = 0.0
+    return c16, t

@@ -41,3 +41,34 @@ def haar_rotation(seed: int, d: int) -> np.ndarray:
 def qjl_projection(seed: int, d: int) -> np.ndarray:
     """S as stored: float32-rounded Gaussian matrix, returned as float64 values."""
     return gaussian_matrix(seed, d).astype(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# Randomized Hadamard rotation (format variant).
+#
+# A cheaper orthogonal rotation than the dense Haar matrix: Pi = H D / sqrt(d),
+# with H the d x d Sylvester-Hadamard matrix (H[i][j] = (-1)^popcount(i & j),
+# d a power of two) and D = diag(s) of seeded random signs; applied with the
+# fast Walsh-Hadamard transform it costs O(d log d). Reading: s_j = +1 when the
+# top bit of SplitMix64 output j+1 of the seed is 0, else -1. Stored as a
+# dense float32 matrix like Pi, so every kernel takes it unchanged.
+
+def sylvester_hadamard(d: int) -> np.ndarray:
+    """H_d from the doubling recursion H_2n = [[H, H], [H, -H]] (float64)."""
+    if d < 1 or d & (d - 1):
+        raise ValueError("d must be a power of two")
+    h = np.ones((1, 1))
+    while h.shape[0] < d:
+        h = np.block([[h, h], [h, -h]])
+    return h
+
+
+def hadamard_signs(seed: int, d: int) -> np.ndarray:
+    z = rng.splitmix64(seed, d)
+    return np.where((z >> np.uint64(63)) == 0, 1.0, -1.0)
+
+
+def hadamard_rotation(seed: int, d: int) -> np.ndarray:
+    """Pi = H D / sqrt(d), float32-rounded, returned as float64 values."""
+    pi = sylvester_hadamard(d) * hadamard_signs(seed, d)[None, :] / np.sqrt(d)
+    return pi.astype(np.float32).astype(np.float64)

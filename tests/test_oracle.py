@@ -157,6 +157,98 @@ def test_expected_sq_error_matches_monte_carlo(bits):
     assert abs(err.mean() - closed) < 4 * err.std() / math.sqrt(len(x))
 
 
+# ------------------------------------------------- sphere-exact codebook --
+
+def test_sphere_codebook_d3_is_the_uniform_quantizer():
+    """d = 3: one coordinate of a uniform point on the 2-sphere is uniform on
+    [-1, 1] (Archimedes), whose Lloyd-Max quantizer splits [-1, 1] into L equal
+    cells with centroids at their middles; MSE (standard units, z = u sqrt 3)
+    is 3 (2/L)^2 / 12 = 1/L^2."""
+    for bits in (1, 2, 3):
+        L = 1 << bits
+        c, _, _ = codebook.lloyd_max_sphere(bits, 3)
+        want = (-1.0 + (2 * np.arange(L) + 1) / L) * math.sqrt(3)
+        assert np.allclose(c, want, atol=1e-12)
+        assert abs(codebook.mse_fixed_point_sphere(c, 3) - 1.0 / L ** 2) < 1e-12
+
+
+def test_sphere_codebook_one_bit_closed_form():
+    """1 bit: the centroids are +-sqrt(d) E|u| = +-sqrt(d) Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2));
+    d = 5 gives 3 sqrt(5) / 8 (density 3/4 (1 - u^2))."""
+    c, _, _ = codebook.lloyd_max_sphere(1, 5)
+    assert abs(c[1] - 3 * math.sqrt(5) / 8) < 1e-12
+    for d in (16, 128, 1000):
+        c, _, _ = codebook.lloyd_max_sphere(1, d)
+        e = math.sqrt(d) * math.exp(math.lgamma(d / 2) - math.lgamma((d + 1) / 2)) / math.sqrt(math.pi)
+        assert abs(c[1] - e) < 1e-12 and abs(c[0] + e) < 1e-12
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_sphere_codebook_tends_to_gaussian(bits):
+    """As d grows, sqrt(d) u tends to N(0, 1) and the codebooks agree, the gap
+    shrinking like 1/d."""
+    g, _, _ = codebook.lloyd_max_gaussian(bits)
+    gap = [np.abs(codebook.lloyd_max_sphere(bits, d, tol=1e-11)[0] - g).max() for d in (1000, 10000)]
+    assert gap[1] < 1e-3
+    assert 8 < gap[0] / gap[1] < 12
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_sphere_codebook_fixed_point_and_monte_carlo(bits):
+    """d = 128: centroids are the conditional means of their cells under
+    sampled sphere coordinates, and the fixed-point MSE matches the sampled
+    quantization error; the sphere codebook's MSE is below the Gaussian one's on
+    the same sphere data."""
+    c, _, _ = codebook.lloyd_max_sphere(bits, D)
+    assert np.allclose(c, -c[::-1], atol=0)
+    X = random_unit_vectors(30000, D, 77 + bits)
+    z = (X * math.sqrt(D)).ravel()
+    t = (c[:-1] + c[1:]) / 2
+    idx = np.searchsorted(t, z, side="right")
+    for i in range(len(c)):
+        sel = z[idx == i]
+        assert abs(sel.mean() - c[i]) < 5 * sel.std() / math.sqrt(len(sel)) + 1e-9, i
+    err = (z - c[idx]) ** 2
+    assert abs(err.mean() - codebook.mse_fixed_point_sphere(c, D)) < 4 * err.std() / math.sqrt(len(z))
+    g, _, _ = codebook.lloyd_max_gaussian(bits)
+    tg = (g[:-1] + g[1:]) / 2
+    err_g = (z - g[np.searchsorted(tg, z, side="right")]) ** 2
+    assert codebook.mse_fixed_point_sphere(c, D) < err_g.mean() + 4 * err_g.std() / math.sqrt(len(z))
+
+
+def test_sphere_canonical_fp16_exact_midpoints():
+    for bits in (2, 3, 4):
+        c16, t = codebook.canonical_sphere(bits, D)
+        assert np.array_equal(c16, c16.astype(np.float16).astype(np.float64))
+        assert np.all(np.diff(c16) > 0)
+        mid = (c16[:-1] + c16[1:]) / 2
+        mid[len(mid) // 2] = 0.0
+        assert np.array_equal(t, mid)
+
+
+# --------------------------------------------------- randomized Hadamard --
+
+def test_hadamard_recursion_equals_popcount_form():
+    for d in (1, 2, 8, 128):
+        h = rotation.sylvester_hadamard(d)
+        i, j = np.meshgrid(np.arange(d), np.arange(d), indexing="ij")
+        pc = np.vectorize(lambda v: bin(v).count("1"))(i & j)
+        assert np.array_equal(h, np.where(pc % 2 == 0, 1.0, -1.0))
+        assert np.array_equal(h @ h.T, d * np.eye(d))
+
+
+def test_hadamard_rotation_orthogonal_signs_from_generator():
+    P = rotation.hadamard_rotation(42, D)
+    assert np.abs(P.T @ P - np.eye(D)).max() <= 1e-6
+    assert np.all(np.abs(np.abs(P) - np.float32(1 / math.sqrt(D))) == 0)
+    # column j carries sign s_j: the top bit of SplitMix64 output j + 1
+    z = rng.splitmix64(42, D)
+    s = np.where(z >= np.uint64(1 << 63), -1.0, 1.0)
+    assert np.array_equal(np.sign(P[0]), s)            # row 0 of H is all ones
+    assert 40 < np.sum(s > 0) < 88                     # both signs present, roughly balanced
+    assert not np.array_equal(rotation.hadamard_rotation(43, D), P)
+
+
 # ----------------------------------------------------------------- quantize --
 
 @pytest.mark.parametrize("bits", [2, 3, 4])
