@@ -40,12 +40,12 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_WORKSPACE_TOO_SMALL, ERR_DEVICE = range(6)
 F32, BF16 = 0, 1
-HAAR, GAUSSIAN = 0, 1
+HAAR, GAUSSIAN, HADAMARD = 0, 1, 2
 KEYS, VALUES = 0, 1
 D = 128
 VALUE_BLOCK = 8
 
-EXPORTS = ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
+EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
            "tq_decode_attention", "tq_decode_splits", "tq_decode_workspace_bytes", "tq_status_string",
            "tq_last_hip_error")
 
@@ -69,6 +69,7 @@ _I32, _I64, _U64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c
 def _bind(lib):
     """Declare the C-ABI signatures on a loaded libtq."""
     lib.tq_make_codebook.argtypes = [_I32, _I32, _P, _P]
+    lib.tq_make_codebook_sphere.argtypes = [_I32, _I32, _P, _P]
     lib.tq_make_rotation.argtypes = [_U64, _I32, _I32, _P]
     lib.tq_quantize_kv.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache), _I64, _P]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
@@ -82,7 +83,7 @@ def _bind(lib):
     lib.tq_status_string.restype = ctypes.c_char_p
     lib.tq_last_hip_error.argtypes = []
     lib.tq_last_hip_error.restype = ctypes.c_char_p
-    for name in ("tq_make_codebook", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
+    for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -123,8 +124,19 @@ def make_codebook(bits: int, d: int = D):
     return c, t[:L - 1]
 
 
+def make_codebook_sphere(bits: int, d: int = D):
+    """Sphere-exact Lloyd-Max codebook (law of one coordinate of a uniform unit
+    vector in d dimensions): (centroids float32 [2^bits], thresholds float32 [2^bits - 1])."""
+    L = 1 << bits
+    c = np.zeros(L, dtype=np.float32)
+    t = np.zeros(max(L - 1, 1), dtype=np.float32)
+    _check(_lib.tq_make_codebook_sphere(bits, d, c.ctypes.data, t.ctypes.data), "tq_make_codebook_sphere")
+    return c, t[:L - 1]
+
+
 def make_rotation(seed: int, kind: int = HAAR, d: int = D) -> np.ndarray:
-    """Seeded d x d float32 matrix (HAAR rotation Pi or GAUSSIAN projection S)."""
+    """Seeded d x d float32 matrix (HAAR rotation Pi, HADAMARD randomized Hadamard
+    rotation, or GAUSSIAN projection S)."""
     out = np.zeros((d, d), dtype=np.float32)
     _check(_lib.tq_make_rotation(seed & 0xFFFFFFFFFFFFFFFF, d, kind, out.ctypes.data), "tq_make_rotation")
     return out

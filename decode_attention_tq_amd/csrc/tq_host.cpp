@@ -1,5 +1,6 @@
-// Host-only parts of the C ABI: the Gaussian Lloyd-Max codebook and the seeded
-// rotation / projection matrices. Plain C++17, no HIP calls.
+// Host-only parts of the C ABI: the Lloyd-Max codebooks (Gaussian and
+// sphere-exact) and the seeded rotation / projection matrices. Plain C++17, no
+// HIP calls.
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -51,6 +52,92 @@ void lloyd_max(int levels, double* c) {
     for (int i = 0; i < levels; ++i) {
       const double p = upper_tail(t[i]) - upper_tail(t[i + 1]);
       nc[i] = (pdf(t[i]) - pdf(t[i + 1])) / p;
+      delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
+    }
+    for (int i = 0; i < levels; ++i) c[i] = nc[i];
+    if (delta < 1e-14) break;
+  }
+  std::vector<double> s(c, c + levels);
+  for (int i = 0; i < levels; ++i) c[i] = 0.5 * (s[i] - s[levels - 1 - i]);
+}
+
+// ---- sphere-exact Lloyd-Max: the law of one coordinate u of a uniform unit
+// vector in d dimensions, density (1 - u^2)^((d-3)/2) / B(1/2, (d-1)/2) on
+// [-1, 1], so (1 + u)/2 ~ Beta((d-1)/2, (d-1)/2). Same iteration and standard
+// units (z = u sqrt(d)) as the Gaussian one.
+
+// Regularized incomplete beta I_x(a, b): the continued fraction of DLMF 8.17.22
+// (coefficients d_{2m+1} = -(a+m)(a+b+m)x / ((a+2m)(a+2m+1)),
+// d_{2m} = m(b-m)x / ((a+2m-1)(a+2m))) evaluated by the modified Lentz method,
+// on the side of the symmetry I_x(a,b) = 1 - I_{1-x}(b,a) where it converges fast.
+double inc_beta(double a, double b, double x) {
+  if (x <= 0.0) return 0.0;
+  if (x >= 1.0) return 1.0;
+  if (x > (a + 1.0) / (a + b + 2.0)) return 1.0 - inc_beta(b, a, 1.0 - x);
+  const double ln_pre = a * std::log(x) + b * std::log1p(-x) - std::log(a) -
+                        (std::lgamma(a) + std::lgamma(b) - std::lgamma(a + b));
+  const double tiny = 1e-300;
+  // f = 1 / (1 + d1 / (1 + d2 / (1 + ...)))
+  double f = tiny, C = f, D = 0.0;
+  for (int j = 1; j < 100000; ++j) {
+    double aj;
+    if (j == 1) {
+      aj = 1.0;
+    } else {
+      const int n = j - 1;   // coefficient d_n
+      const int m = n / 2;
+      aj = (n % 2 == 1) ? -(a + m) * (a + b + m) * x / ((a + 2 * m) * (a + 2 * m + 1))
+                        : m * (b - m) * x / ((a + 2 * m - 1) * (a + 2 * m));
+    }
+    D = 1.0 + aj * D;
+    if (std::fabs(D) < tiny) D = tiny;
+    C = 1.0 + aj / C;
+    if (std::fabs(C) < tiny) C = tiny;
+    D = 1.0 / D;
+    const double delta = C * D;
+    f *= delta;
+    if (std::fabs(delta - 1.0) < 1e-16) break;
+  }
+  return std::exp(ln_pre) * f;
+}
+
+double sphere_cdf(double u, int d) {
+  const double al = 0.5 * (d - 1);
+  return inc_beta(al, al, std::fmin(std::fmax(0.5 * (1.0 + u), 0.0), 1.0));
+}
+
+// int_a^b u f(u) du = ((1 - a^2)^(k+1) - (1 - b^2)^(k+1)) / (2 (k+1) B(1/2, k+1)), k = (d-3)/2
+double sphere_partial_mean(double a, double b, int d) {
+  const double k = 0.5 * (d - 3);
+  const double lb = std::lgamma(0.5) + std::lgamma(k + 1.0) - std::lgamma(k + 1.5);
+  auto g = [&](double u) {
+    const double v = 1.0 - u * u;
+    return v <= 0.0 ? 0.0 : std::exp((k + 1.0) * std::log(v) - lb);
+  };
+  return (g(a) - g(b)) / (2.0 * (k + 1.0));
+}
+
+void lloyd_max_sphere(int levels, int d, double* c) {
+  const double sd = std::sqrt((double)d);
+  // start at the quantiles (i + 1/2) / L of the law (bisection on the CDF)
+  for (int i = 0; i < levels; ++i) {
+    const double p = (i + 0.5) / levels;
+    double lo = -1.0, hi = 1.0;
+    for (int it = 0; it < 200; ++it) {
+      const double mid = 0.5 * (lo + hi);
+      if (sphere_cdf(mid, d) < p) lo = mid; else hi = mid;
+    }
+    c[i] = sd * 0.5 * (lo + hi);
+  }
+  std::vector<double> t(levels + 1), nc(levels);
+  for (int it = 0; it < 200000; ++it) {
+    t[0] = -1.0;
+    t[levels] = 1.0;
+    for (int i = 1; i < levels; ++i) t[i] = std::fmin(std::fmax(0.5 * (c[i - 1] + c[i]) / sd, -1.0), 1.0);
+    double delta = 0.0;
+    for (int i = 0; i < levels; ++i) {
+      const double p = sphere_cdf(t[i + 1], d) - sphere_cdf(t[i], d);
+      nc[i] = sd * sphere_partial_mean(t[i], t[i + 1], d) / p;
       delta = std::fmax(delta, std::fabs(nc[i] - c[i]));
     }
     for (int i = 0; i < levels; ++i) c[i] = nc[i];
@@ -162,9 +249,36 @@ extern "C" int tq_make_codebook(int32_t bits, int32_t d, float* centroids, float
   return TQ_OK;
 }
 
+extern "C" int tq_make_codebook_sphere(int32_t bits, int32_t d, float* centroids, float* thresholds) {
+  if (centroids == nullptr || bits < 1 || bits > 4 || d < 3 || d > 65536) return TQ_ERR_INVALID_ARGUMENT;
+  const int L = 1 << bits;
+  double c[16];
+  lloyd_max_sphere(L, d, c);
+  double c16[16];
+  for (int i = 0; i < L; ++i) c16[i] = round_to_half(c[i]);
+  for (int i = 0; i < L; ++i) centroids[i] = (float)c16[i];
+  if (thresholds != nullptr) {
+    for (int i = 0; i + 1 < L; ++i) thresholds[i] = (float)(0.5 * (c16[i] + c16[i + 1]));
+    thresholds[L / 2 - 1] = 0.0f;
+  }
+  return TQ_OK;
+}
+
 extern "C" int tq_make_rotation(uint64_t seed, int32_t d, int32_t kind, float* out) {
-  if (out == nullptr || d <= 0 || (kind != TQ_MAT_HAAR && kind != TQ_MAT_GAUSSIAN)) return TQ_ERR_INVALID_ARGUMENT;
+  if (out == nullptr || d <= 0 || (kind != TQ_MAT_HAAR && kind != TQ_MAT_GAUSSIAN && kind != TQ_MAT_HADAMARD))
+    return TQ_ERR_INVALID_ARGUMENT;
   if (d != tq::kD) return TQ_ERR_UNSUPPORTED;
+  if (kind == TQ_MAT_HADAMARD) {
+    // H D / sqrt(d): H[i][j] = (-1)^popcount(i & j), s_j from the top bit of output j+1
+    SplitMix64 sm{seed};
+    std::vector<double> sgn(d);
+    for (int j = 0; j < d; ++j) sgn[j] = (sm.next() >> 63) ? -1.0 : 1.0;
+    const double inv = 1.0 / std::sqrt((double)d);
+    for (int i = 0; i < d; ++i)
+      for (int j = 0; j < d; ++j)
+        out[i * d + j] = (float)(((__builtin_popcount((unsigned)(i & j)) & 1) ? -inv : inv) * sgn[j]);
+    return TQ_OK;
+  }
   std::vector<double> g;
   gaussian(seed, d, g);
   if (kind == TQ_MAT_GAUSSIAN) {

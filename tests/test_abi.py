@@ -55,6 +55,23 @@ def test_codebook_matches_oracle(bits):
     assert not np.signbit(t[len(t) // 2])
 
 
+@pytest.mark.parametrize("bits", [1, 2, 3, 4])
+def test_sphere_codebook_matches_oracle(bits):
+    c, t = tq.make_codebook_sphere(bits)
+    oc, ot = ocb.canonical_sphere(bits, 128)
+    assert np.array_equal(c.astype(np.float64), oc)
+    assert np.array_equal(t.astype(np.float64), ot)
+    # d = 3: the uniform quantizer of [-1, 1], in units of sqrt(3) (fp16-rounded)
+    c3, _ = tq.make_codebook_sphere(bits, 3)
+    L = 1 << bits
+    want = ((-1.0 + (2 * np.arange(L) + 1) / L) * np.sqrt(3)).astype(np.float16).astype(np.float32)
+    assert np.array_equal(c3, want)
+    lib = tq.lib()
+    buf = np.zeros(16, dtype=np.float32)
+    assert lib.tq_make_codebook_sphere(bits, 2, buf.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_make_codebook_sphere(5, 128, buf.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
+
+
 def test_codebook_rejects_bad_arguments():
     lib = tq.lib()
     c = np.zeros(16, dtype=np.float32)
@@ -71,6 +88,8 @@ def test_rotation_matches_oracle(seed):
     assert np.abs(P.T @ P - np.eye(128)).max() <= 1e-5
     S = tq.make_rotation(seed, tq.GAUSSIAN).astype(np.float64)
     assert np.abs(S - orot.qjl_projection(seed, 128)).max() <= 1e-6
+    H = tq.make_rotation(seed, tq.HADAMARD).astype(np.float64)
+    assert np.array_equal(H, orot.hadamard_rotation(seed, 128))
 
 
 def test_rotation_rejects_bad_arguments():

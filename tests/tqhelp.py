@@ -29,12 +29,13 @@ def rel_l2(a, b) -> float:
 class OracleModel:
     """Oracle rotation, projection and codebooks of a workload."""
 
-    def __init__(self, w: tq_synth.Workload):
+    def __init__(self, w: tq_synth.Workload, codebook: str = "gaussian", rotation: str = "haar"):
         self.w = w
-        self.Pi = orot.haar_rotation(tq_synth.ROT_SEED, D)
+        self.Pi = (orot.hadamard_rotation if rotation == "hadamard" else orot.haar_rotation)(tq_synth.ROT_SEED, D)
         self.S = orot.qjl_projection(tq_synth.QJL_SEED, D) if w.k_qjl else None
-        self.cK, self.tK = ocb.canonical(w.k_bits)
-        self.cV, self.tV = ocb.canonical(w.v_bits)
+        make = (lambda bits: ocb.canonical_sphere(bits, D)) if codebook == "sphere" else ocb.canonical
+        self.cK, self.tK = make(w.k_bits)
+        self.cV, self.tV = make(w.v_bits)
 
     def quantize(self, which: str, X: np.ndarray) -> dict:
         if which == "k":
