@@ -148,6 +148,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--prefill-iters", type=int, default=3)
+    ap.add_argument("--formats", default="llama8b,qwen,qjl",
+                    help="other workloads whose decode is also timed (their own bit widths); '' to skip")
     ap.add_argument("--paged-block", type=int, default=256,
                     help="also time decode on paged caches with this many tokens per block (0: skip)")
     args = ap.parse_args()
@@ -288,6 +290,37 @@ def main():
         del pk, pv
         torch.cuda.empty_cache()
 
+    # decode of the other workloads (other bit widths, QJL keys, G = 4 and 7,
+    # context splits), each on its own caches, back to back
+    formats = {}
+    for name in [n for n in args.formats.split(",") if n]:
+        fw = tq_synth.WORKLOADS[name]
+        fcap = (fw.T + 7) // 8 * 8
+        fk = tq.Cache(tq.KEYS, fw.k_bits, fw.B, fw.H_kv, fcap, device=dev, qjl=bool(fw.k_qjl))
+        fv = tq.Cache(tq.VALUES, fw.v_bits, fw.B, fw.H_kv, fcap, device=dev)
+        tq.quantize_kv(tq_synth.torch_kv(fw, "k", dev), fk)
+        tq.quantize_kv(tq_synth.torch_kv(fw, "v", dev), fv)
+        fq = tq_synth.torch_queries(fw, dev)
+        fws = tq.Workspace(tq.decode_workspace_bytes(fw.B, fw.H_q, fw.H_kv, fw.T, 0, fw.k_qjl), dev)
+        fo = torch.empty((fw.B, fw.H_q, fw.d), dtype=torch.float32, device=dev)
+        for _ in range(5):
+            tq.decode_attention(fk, fv, fq, T=fw.T, out=fo, workspace=fws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(50):
+            tq.decode_attention(fk, fv, fq, T=fw.T, out=fo, workspace=fws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 50 * 1e3
+        fb = decode_bytes(fw, fw.T)
+        formats[name] = {"B": fw.B, "H_q": fw.H_q, "H_kv": fw.H_kv, "T": fw.T, "k_bits": fw.k_bits,
+                         "v_bits": fw.v_bits, "k_qjl": fw.k_qjl,
+                         "n_split": tq.decode_splits(fw.B, fw.H_kv, fw.T), "decode_us": us,
+                         "bytes": fb, "GB_s": fb / (us * 1e-6) / 1e9, "frac": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] {name}: decode {us:.1f} us, {fb / (us * 1e-6) / 1e9:.0f} GB/s")
+        del fk, fv, fws
+        torch.cuda.empty_cache()
+
     # calibration copy of known size for the rocprofv3 byte counters (256 MiB read + write)
     cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
     cal2 = torch.empty_like(cal)
@@ -330,6 +363,8 @@ def main():
     }
     if paged is not None:
         res["paged"] = paged
+    if formats:
+        res["formats"] = formats
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
