@@ -80,6 +80,21 @@ def attend_rotated(q, k, v, PiK, PiV, cK, cV, d, scale, ctx_len=None, S=None):
     return o_rot @ PiV                                            # Pi^T o'
 
 
+def attend_chunk_causal(q, k, v, PiK, PiV, cK, cV, d, scale, ctx_len, S=None):
+    """Chunked prefill / multi-query attention over one KV head: q [M, G, d]
+    holds the M newest tokens of a context of ctx_len tokens (their keys and
+    values already in the cache), token i at position ctx_len - M + i; each
+    attends causally to cache tokens 0 .. ctx_len - M + i. Query i is therefore
+    the decode of its G heads over the first ctx_len - M + i + 1 tokens (the
+    plain definition, one query at a time)."""
+    M = q.shape[0]
+    out = np.zeros((M, q.shape[1], d))
+    for i in range(M):
+        n = max(int(ctx_len) - M + i + 1, 0)
+        out[i] = attend_rotated(q[i], k, v, PiK, PiV, cK, cV, d, scale, ctx_len=n, S=S)
+    return out
+
+
 def split_partials(s: np.ndarray, vr: np.ndarray, bounds):
     """Per-chunk (m, l, acc) of flash-decoding for scores s [G, T], rotated values vr [T, d]."""
     parts = []

@@ -446,6 +446,37 @@ def test_textbook_matches_pure_python_loop():
     assert np.allclose(attention.softmax(np.array([[1.0, 2.0, -3.0]])), special.softmax([1.0, 2.0, -3.0]))
 
 
+def test_chunk_causal_against_textbook_mask():
+    """The chunked causal attention equals textbook attention over the
+    dequantized cache with the causal mask written out (query i sees keys
+    0 .. ctx - M + i), and M = 1 is the decode."""
+    rs = np.random.default_rng(21)
+    T, M, G = 90, 6, 3
+    c16, t = codebook.canonical(3)
+    P = rotation.haar_rotation(42, D)
+    K = rs.standard_normal((T, D))
+    V = rs.standard_normal((T, D))
+    kq = quantize.quantize_head(K, P, c16, t)
+    vq = quantize.quantize_head(V, P, c16, t)
+    Kh = attention.dequantize_head(kq["codes"], kq["norm"], P, c16, D)
+    Vh = attention.dequantize_head(vq["codes"], vq["norm"], P, c16, D)
+    q = rs.standard_normal((M, G, D))
+    sc = 1 / math.sqrt(D)
+    for ctx in (T, 50, M, 3):
+        got = attention.attend_chunk_causal(q, kq, vq, P, P, c16, c16, D, sc, ctx)
+        for i in range(M):
+            n = max(ctx - M + i + 1, 0)
+            for g in range(G):
+                if n == 0:
+                    assert np.all(got[i, g] == 0)
+                    continue
+                s = (Kh[:n] @ q[i, g]) * sc
+                w = np.exp(s - s.max())
+                assert np.allclose(got[i, g], (w / w.sum()) @ Vh[:n], atol=1e-12)
+    one = attention.attend_chunk_causal(q[:1], kq, vq, P, P, c16, c16, D, sc, T)
+    assert np.allclose(one[0], attention.attend_rotated(q[0], kq, vq, P, P, c16, c16, D, sc), atol=0)
+
+
 def test_single_token_returns_its_value():
     P, S, ck, cv, K, V, q, k, v = _head_case(T=1)
     Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, D)
