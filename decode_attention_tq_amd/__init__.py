@@ -46,7 +46,8 @@ D = 128
 VALUE_BLOCK = 8
 
 EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
-           "tq_decode_attention", "tq_decode_splits", "tq_decode_workspace_bytes", "tq_status_string",
+           "tq_decode_attention", "tq_prefill_attention", "tq_decode_splits", "tq_decode_workspace_bytes",
+           "tq_prefill_workspace_bytes", "tq_status_string",
            "tq_last_hip_error")
 
 
@@ -75,6 +76,10 @@ def _bind(lib):
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P,
                                         _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
+    lib.tq_prefill_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _I64,
+                                         _P, _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
+    lib.tq_prefill_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64, _I32, _I32]
+    lib.tq_prefill_workspace_bytes.restype = ctypes.c_size_t
     lib.tq_decode_splits.argtypes = [_I64, _I64, _I64, _I32]
     lib.tq_decode_splits.restype = _I32
     lib.tq_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32, _I32]
@@ -83,7 +88,8 @@ def _bind(lib):
     lib.tq_status_string.restype = ctypes.c_char_p
     lib.tq_last_hip_error.argtypes = []
     lib.tq_last_hip_error.restype = ctypes.c_char_p
-    for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention"):
+    for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention",
+                 "tq_prefill_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
 
@@ -148,6 +154,10 @@ def decode_splits(B: int, H_kv: int, T: int, n_split: int = 0) -> int:
 
 def decode_workspace_bytes(B: int, H_q: int, H_kv: int, T: int, n_split: int = 0, k_qjl: int = 0) -> int:
     return int(_lib.tq_decode_workspace_bytes(B, H_q, H_kv, T, n_split, k_qjl))
+
+
+def prefill_workspace_bytes(B: int, H_q: int, H_kv: int, M: int, T: int, n_split: int = 0, k_qjl: int = 0) -> int:
+    return int(_lib.tq_prefill_workspace_bytes(B, H_q, H_kv, M, T, n_split, k_qjl))
 
 
 # ---------------------------------------------------------------- device ----
@@ -297,4 +307,32 @@ def decode_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None,
     _check(_lib.tq_decode_attention(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q,
                                     cl or None, T, scale, n_split, out.data_ptr(), workspace.ptr,
                                     workspace.nbytes, _stream_handle(q.device)), "tq_decode_attention")
+    return out
+
+
+def prefill_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None, scale: float = 0.0,
+                      n_split: int = 0, out=None, workspace: Workspace | None = None):
+    """Chunked causal attention of the M newest tokens of each row, q [B, M, H_q, 128]
+    (their keys and values already in the caches), over the packed caches ->
+    float32 [B, M, H_q, 128]; token i of row b attends to cache tokens
+    0 .. ctx_len[b] - M + i."""
+    torch = _torch()
+    if q.dim() != 4 or q.shape[-1] != D or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, M, H_q, 128] tensor")
+    B, M, H_q, _ = q.shape
+    T = k.T_cap if T is None else T
+    if out is None:
+        out = torch.empty((B, M, H_q, D), dtype=torch.float32, device=q.device)
+    need = prefill_workspace_bytes(B, H_q, k.H_kv, M, T, n_split, k.qjl)
+    if workspace is None or workspace.nbytes < need:
+        workspace = Workspace(need, q.device)
+    sk, sv = k.struct(), v.struct()
+    cl = 0
+    if ctx_lens is not None:
+        if ctx_lens.dtype != torch.int32 or not ctx_lens.is_contiguous() or ctx_lens.numel() != B:
+            raise ValueError("ctx_lens must be a contiguous int32 tensor of B entries")
+        cl = ctx_lens.data_ptr()
+    _check(_lib.tq_prefill_attention(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q, M,
+                                     cl or None, T, scale, n_split, out.data_ptr(), workspace.ptr,
+                                     workspace.nbytes, _stream_handle(q.device)), "tq_prefill_attention")
     return out

@@ -72,8 +72,8 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
-                 DecodePlan* p) {
-  if (B <= 0 || H_q <= 0 || H_kv <= 0 || T < 0 || n_split < 0) return false;
+                 DecodePlan* p, int64_t M) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || T < 0 || n_split < 0 || M <= 0) return false;
   if (H_q % H_kv != 0) return false;
   const int64_t G = H_q / H_kv;
   if (G > 16) return false;
@@ -81,8 +81,12 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   p->H_q = H_q;
   p->H_kv = H_kv;
   p->T = T;
+  p->M = M;
   p->G = (int32_t)G;
-  p->wide = G > 8;
+  p->wide = M * G > 8;
+  p->Mt = (int32_t)(p->wide ? (M < 16 / G ? M : 16 / G) : M);
+  p->nqt = (int32_t)((M + p->Mt - 1) / p->Mt);
+  if (B * p->nqt > 65535) return false;   // grid z
   p->qjl = qjl ? 1 : 0;
   const int64_t Tp = T > 0 ? T : 1;
   const int64_t quantum = kChunkQuantum;
@@ -91,7 +95,7 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
     target = n_split;
   } else {
     // about one workgroup per compute unit; a chunk keeps at least 2 quanta
-    const int64_t units = B * H_kv;
+    const int64_t units = B * H_kv * p->nqt;
     target = (kDecodeTargetWGs + units - 1) / units;
     const int64_t cap = (Tp + 2 * quantum - 1) / (2 * quantum);
     if (target > cap) target = cap;
@@ -101,11 +105,12 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   chunk = (chunk + quantum - 1) / quantum * quantum;
   p->chunk = (int32_t)chunk;
   p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
+  if (p->n_split > 1 && B * M > 65535) return false;   // grid y of the combine
   size_t off = 0;
   p->off_ml = off;
-  off = align256(off + (size_t)(B * H_q) * p->n_split * 2 * sizeof(float));
+  off = align256(off + (size_t)(B * M * H_q) * p->n_split * 2 * sizeof(float));
   p->off_acc = off;
-  off = align256(off + (size_t)(B * H_q) * p->n_split * kD * sizeof(float));
+  off = align256(off + (size_t)(B * M * H_q) * p->n_split * kD * sizeof(float));
   p->bytes = off;
   return true;
 }
@@ -132,6 +137,13 @@ extern "C" int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t 
   DecodePlan p;
   if (!plan_decode(B, H_kv, H_kv, T, n_split, 0, &p)) return 0;
   return p.n_split;
+}
+
+extern "C" size_t tq_prefill_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t M, int64_t T,
+                                             int32_t n_split, int32_t k_qjl) {
+  DecodePlan p;
+  if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p, M)) return 0;
+  return p.bytes;
 }
 
 extern "C" size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
@@ -171,10 +183,12 @@ extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float*
   return device_status(launch_dequantize(src, t0, t1, out, (hipStream_t)hip_stream));
 }
 
-extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
-                                   int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
-                                   int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
-                                   void* hip_stream) {
+namespace {
+
+// Shared validation and launch of decode (M = 1) and chunked causal attention.
+int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype, int64_t H_q, int64_t M,
+                   const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split, float* out, void* workspace,
+                   size_t workspace_bytes, void* hip_stream) {
   int st = check_cache(k);
   if (st != TQ_OK) return st;
   st = check_cache(v);
@@ -182,18 +196,37 @@ extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const v
   if (k->role != TQ_KEYS || v->role != TQ_VALUES) return TQ_ERR_INVALID_ARGUMENT;
   if (k->B != v->B || k->H_kv != v->H_kv) return TQ_ERR_INVALID_ARGUMENT;
   if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
-  if (q == nullptr || out == nullptr || H_q <= 0 || T < 0 || n_split < 0) return TQ_ERR_INVALID_ARGUMENT;
+  if (q == nullptr || out == nullptr || H_q <= 0 || T < 0 || n_split < 0 || M <= 0) return TQ_ERR_INVALID_ARGUMENT;
   if (T > k->T_cap || T > v->T_cap || T >= ((int64_t)1 << 30)) return TQ_ERR_INVALID_ARGUMENT;
   if (H_q % k->H_kv != 0) return TQ_ERR_INVALID_ARGUMENT;
   if (H_q / k->H_kv > 16 || H_q > 65535) return TQ_ERR_UNSUPPORTED;
+  if (M > 65535) return TQ_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
   DecodePlan p;
-  if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p)) return TQ_ERR_INVALID_ARGUMENT;
+  if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) return TQ_ERR_UNSUPPORTED;
   if (workspace == nullptr || workspace_bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255u) != 0) return TQ_ERR_ALIGNMENT;
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
   clear_pending_error();
   return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                      (hipStream_t)hip_stream));
+}
+
+}  // namespace
+
+extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
+                                   int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
+                                   int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
+                                   void* hip_stream) {
+  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
+                        hip_stream);
+}
+
+extern "C" int tq_prefill_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
+                                    int64_t H_q, int64_t M, const int32_t* ctx_lens, int64_t T, float scale,
+                                    int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
+                                    void* hip_stream) {
+  return attention_call(k, v, q, q_dtype, H_q, M, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
+                        hip_stream);
 }

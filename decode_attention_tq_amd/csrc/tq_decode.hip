@@ -211,6 +211,7 @@ struct ScanArgs {
   int64_t TcK, TcV;
   PageMap kpm, vpm;   // block tables of paged caches (table == nullptr: contiguous)
   int q_dtype, H_kv, H_q, G, T, n_split, wg_chunk, wave_chunk;
+  int M, Mt, nqt;   // query tokens per row, per workgroup tile, tiles per row
   float sc1, sc2, inv_sqrt_d;
   float kc[16], vc[16];
 };
@@ -402,7 +403,7 @@ struct SoftState {
 template <int KB, int VB, int QJL, int WIDE, bool MASK>
 __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, const QOps<WIDE, QJL>& q,
                                           SoftState<WIDE>& st, const uint32_t* lutK, const uint32_t* lutV,
-                                          const uint32_t* lutS, int lane, int tg, int t_end) {
+                                          const uint32_t* lutS, int lane, int tg, int lim) {
   const StepNorms<QJL>& nm = d.nm;
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
   // (two independent accumulation chains; one query block live at a time)
@@ -465,7 +466,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
         x = fmaf(z * q.cs2, quad_bcast(nm.kg, r), x * q.cs1);
       }
       float v = x * quad_bcast(nm.kn, r);
-      if constexpr (MASK) v = (tg + 4 * (int)q.hf + r < t_end) ? v : -INFINITY;
+      if constexpr (MASK) v = (tg + 4 * (int)q.hf + r < lim) ? v : -INFINITY;
       y[r] = v;
     }
     // the reference moves only when some score passes it by more than kSlack;
@@ -476,7 +477,9 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 16));
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
       const float m_new = fmaxf(st.m_ref, tmax * cs);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+      // (a column with nothing accumulated yet, m_ref = -inf, may still see no
+      // visible token while another column moves: its factor is 0, not NaN)
+      const float alpha = st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l *= alpha;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
@@ -486,10 +489,12 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     float w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(y[r], cs, -st.m_off));
+      float p = __builtin_amdgcn_exp2f(fmaf(y[r], cs, -st.m_off));
+      // (a column that has seen no visible token yet has m_off = -inf: p of a
+      // masked token is then NaN, so the mask selects 0 rather than scaling)
+      if constexpr (MASK) p = (tg + 4 * (int)q.hf + r < lim) ? p : 0.f;
       st.l += p;
       w[r] = p * quad_bcast(nm.vn, r);
-      if constexpr (MASK) w[r] = (tg + 4 * (int)q.hf + r < t_end) ? w[r] : 0.f;
     }
     // own tokens as float16 hi and lo halves (pairs of tokens per register)
     uint32_t hi2[2], lo2[2];
@@ -536,7 +541,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
           x = fmaf(yq * q.cs2, bcast_row(nm.kg, e), x * q.cs1);
         }
         float v = x * bcast_row(nm.kn, e);
-        if constexpr (MASK) v = (tg + e < t_end) ? v : -INFINITY;
+        if constexpr (MASK) v = (tg + e < lim) ? v : -INFINITY;
         y[e] = v;
       }
     }
@@ -545,7 +550,9 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       float tmax = fmaxf(lmax, shfl_xor_f(lmax, 16));
       tmax = fmaxf(tmax, shfl_xor_f(tmax, 32));
       const float m_new = fmaxf(st.m_ref, tmax * cs);
-      const float alpha = __builtin_amdgcn_exp2f(st.m_ref - m_new);
+      // (a column with nothing accumulated yet, m_ref = -inf, may still see no
+      // visible token while another column moves: its factor is 0, not NaN)
+      const float alpha = st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l *= alpha;
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
@@ -562,10 +569,10 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const int e = 2 * k + u;
-        const float p = __builtin_amdgcn_exp2f(fmaf(y[e], cs, -st.m_off));
+        float p = __builtin_amdgcn_exp2f(fmaf(y[e], cs, -st.m_off));
+        if constexpr (MASK) p = (tg + e < lim) ? p : 0.f;   // (NaN when no visible token yet)
         st.l += p;
         w2[u] = p * bcast_row(nm.vn, e);
-        if constexpr (MASK) w2[u] = (tg + e < t_end) ? w2[u] : 0.f;
       }
       const _Float16 h0 = (_Float16)w2[0], h1 = (_Float16)w2[1];
       pw0[k] = __builtin_bit_cast(uint32_t, half2v{h0, h1});
@@ -648,8 +655,14 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
   const int g = lane >> 4, c = lane & 15;
   const int lrep = lane & (kLutRep - 1);
-  const int split = blockIdx.x, kv = blockIdx.y, b = blockIdx.z;
+  const int split = blockIdx.x, kv = blockIdx.y;
+  const int b = blockIdx.z / a.nqt;                     // batch row
+  const int i0 = (blockIdx.z - b * a.nqt) * a.Mt;       // first query token of the tile
   const int G = a.G;
+  const int mq = min(a.Mt, a.M - i0);                   // query tokens of the tile
+  // operand columns: (token i, head g) -> column i * G + g (the G heads of one
+  // token for a decode)
+  const int NC = mq * G;
   const int64_t bkv = (int64_t)b * a.H_kv + kv;
 
   // token range of this wavefront (before the context length clips it);
@@ -708,14 +721,17 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   {
     // one 32-bit load per element for either dtype (a bfloat16 element is
     // taken from the word that holds it), so the loads carry no branch
+    // column c's vector: token i0 + c / G, head kv * G + c % G of row b
     const bool qbf = a.q_dtype == TQ_BF16;
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc((const char*)a.q + (((int64_t)b * a.H_q + (int64_t)kv * G) * kD) * (qbf ? 2 : 4),
-                  (uint32_t)(G * kD * (qbf ? 2 : 4)));
+        make_rsrc((const char*)a.q + ((((int64_t)b * a.M + i0) * a.H_q + (int64_t)kv * G) * kD) * (qbf ? 2 : 4),
+                  (uint32_t)((((int64_t)mq - 1) * a.H_q + G) * kD * (qbf ? 2 : 4)));
 #pragma unroll
     for (int k = 0; k < QE; ++k) {
       const uint32_t idx = tid + k * NT;
-      qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (idx * 2u) & ~3u : idx * 4u, 0, 0);
+      const uint32_t cq = idx / kD;
+      const uint32_t el = ((cq / (uint32_t)G) * (uint32_t)a.H_q + cq % (uint32_t)G) * kD + idx % kD;
+      qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (el * 2u) & ~3u : el * 4u, 0, 0);
     }
   }
   StepData<KB, VB, QJL, WIDE> buf[2];
@@ -756,23 +772,23 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
   }
   {
-    // the G query vectors ([G][d] contiguous) as float32 in vA
+    // the NC column vectors as float32 in vA ([NC][d])
 #pragma unroll
     for (int k = 0; k < QE; ++k) {
       const int idx = tid + k * NT;
-      if (idx < G * kD)
+      if (idx < NC * kD)
         vA[idx] = a.q_dtype == TQ_BF16 ? __uint_as_float(((qraw[k] >> (16 * (idx & 1))) & 0xFFFFu) << 16)
                                        : __uint_as_float(qraw[k]);
     }
     __syncthreads();
-    rotate_rows<NT, NQ / 2>(rseg, vA, vB, G);   // q' = Pi_K q
+    rotate_rows<NT, NQ / 2>(rseg, vA, vB, NC);   // q' = Pi_K q
     __syncthreads();
-    emit_operand<NT>(vB, a.sc1, G, HALF, qlds, qcs, hexp);
+    emit_operand<NT>(vB, a.sc1, NC, HALF, qlds, qcs, hexp);
     if constexpr (QJL) {
       load_row_segment<NT>(rseg, a.proj);
-      rotate_rows<NT, NQ / 2>(rseg, vB, vA, G);   // q'' = S q'
+      rotate_rows<NT, NQ / 2>(rseg, vB, vA, NC);   // q'' = S q'
       __syncthreads();
-      emit_operand<NT>(vA, a.sc2, G, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
+      emit_operand<NT>(vA, a.sc2, NC, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
     }
   }
   __syncthreads();
@@ -796,9 +812,18 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 
   // the share of this wavefront, clipped by the context length
   ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
-  const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, ctx));
+  // causal limits: token i0 + i of the tile (position ctx - M + i0 + i) sees
+  // cache tokens below lim0 + i (all ctx tokens for a decode)
+  const int lim0 = ctx - a.M + i0 + 1;
+  const int lim_lo = max(lim0, 0), lim_hi = max(lim0 + mq - 1, 0);
+  const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, lim_hi));
+  const int t_unm = min(t_end, lim_lo);   // below this every column sees every token
   const int t_full =
-      __builtin_amdgcn_readfirstlane(t_begin + (t_end > t_begin ? (t_end - t_begin) / kStep * kStep : 0));
+      __builtin_amdgcn_readfirstlane(t_begin + (t_unm > t_begin ? (t_unm - t_begin) / kStep * kStep : 0));
+  // this lane's column limit for the masked steps (columns past NC carry a zero
+  // query and keep the widest limit)
+  const int lcol = WIDE ? c : (c & 7);
+  const int lim_lane = lcol < NC ? max(lim0 + lcol / G, 0) : lim_hi;
 
   SoftState<WIDE> st;
   st.m_ref = -INFINITY;
@@ -839,7 +864,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       uint32_t begun = 0u;                                                                                  \
       if (lane == 0)                                                                                        \
         begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);      \
-      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);             \
+      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, lim_lane);          \
       begun = __builtin_amdgcn_readfirstlane(begun);   /* by the whole workgroup */                          \
       const uint32_t even = mine * (uint32_t)NW;        /* if every wavefront kept pace */                   \
       if (begun > even + NW) __builtin_amdgcn_s_setprio(3);                                                 \
@@ -856,13 +881,16 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 #undef TQ_STEP
     __builtin_amdgcn_s_setprio(0);
   }
+  // masked steps: the ragged end of the share, and for several query tokens the
+  // steps where their causal limits differ (at most two, limits differ by < 16)
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
-  if (t0 < t_end) {
+  while (t0 < t_end) {
     StepData<KB, VB, QJL, WIDE> E;
     if (kpg) ek = page_entry(rtk, a.kpm, t0);
     if (vpg) ev = page_entry(rtv, a.vpm, t0);
     load_step(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
-    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, t_end);
+    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, lim_lane);
+    t0 += kStep;
   }
 
   // ---- this wavefront's partial: lane (g, c) holds coordinates 32g + 8r + nb of column c
@@ -885,7 +913,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   const bool finish = a.n_split == 1;
   __syncthreads();   // every wavefront is done with the lookup tables
   float* mrg = R;    // [wave][MC columns][kMergeStride]: 128 coordinates, m, l
-  if (c < G) {
+  if (c < NC) {
     float* dst = mrg + (wave * MC + c) * kMergeStride;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -909,13 +937,13 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
   }
   __syncthreads();
-  // weights of the wavefront partials: lane (h, w) of the first G * 16 threads
-  // (head h in a 16-lane row) takes f = 2^(m_w - M) with M the largest m_w of
-  // the head, and the row sums f * l_w into the denominator
-  float* fw = vA;            // [G][16]
+  // weights of the wavefront partials: lane (h, w) of the first NC * 16 threads
+  // (column h in a 16-lane row) takes f = 2^(m_w - M) with M the largest m_w of
+  // the column, and the row sums f * l_w into the denominator
+  float* fw = vA;            // [NC][16]
   float* Mh = vA + 256;      // [16]
   float* dh = vA + 272;      // [16]
-  if (tid < G * 16) {
+  if (tid < NC * 16) {
     const int h = tid >> 4, w = tid & 15;
     float m = -INFINITY, lw = 0.f;
     if (w < NW) {
@@ -939,7 +967,11 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < G * kD; idx += NT) {
+  // column h -> query row b * M + i0 + h / G, head kv * G + h % G
+  auto out_row = [&](int h) -> int64_t {
+    return ((int64_t)b * a.M + i0 + h / G) * a.H_q + (int64_t)kv * G + h % G;
+  };
+  for (int idx = tid; idx < NC * kD; idx += NT) {
     const int h = idx / kD, j = idx % kD;
     float num = 0.f;
 #pragma unroll
@@ -948,7 +980,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     if (finish) {
       vB[idx] = den > 0.f ? num / den * a.inv_sqrt_d : 0.f;
     } else {
-      const int64_t pidx = ((int64_t)b * a.H_q + kv * G + h) * a.n_split + split;
+      const int64_t pidx = out_row(h) * a.n_split + split;
       a.acc[pidx * kD + j] = num;
       if (j == 0) {
         a.ml[pidx * 2] = Mh[h];
@@ -958,8 +990,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   }
   if (finish) {
     __syncthreads();   // o' is complete in vB; the merge area takes the partial sums
-    float* P = R;      // [FSEGS][G][d]
-    for (int h = 0; h < G; ++h) {
+    float* P = R;      // [FSEGS][NC][d]
+    for (int h = 0; h < NC; ++h) {
       const float4* x = (const float4*)(vB + h * kD + fs * RW);   // same address across the wavefront
       float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
@@ -968,15 +1000,15 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
         acc0 = fmaf(pv[4 * k + 3].x, v.w, fmaf(pv[4 * k + 2].x, v.z, fmaf(pv[4 * k + 1].x, v.y, fmaf(pv[4 * k].x, v.x, acc0))));
         acc1 = fmaf(pv[4 * k + 3].y, v.w, fmaf(pv[4 * k + 2].y, v.z, fmaf(pv[4 * k + 1].y, v.y, fmaf(pv[4 * k].y, v.x, acc1))));
       }
-      *(float2*)(P + (fs * G + h) * kD + 2 * fp) = float2{acc0, acc1};
+      *(float2*)(P + (fs * NC + h) * kD + 2 * fp) = float2{acc0, acc1};
     }
     __syncthreads();
-    for (int idx = tid; idx < G * kD; idx += NT) {
+    for (int idx = tid; idx < NC * kD; idx += NT) {
       const int h = idx / kD, i = idx % kD;
       float r = 0.f;
 #pragma unroll
-      for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * G + h) * kD + i];
-      a.out[((int64_t)b * a.H_q + kv * G + h) * kD + i] = r;
+      for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * NC + h) * kD + i];
+      a.out[out_row(h) * kD + i] = r;
     }
   }
 }
@@ -1085,7 +1117,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* ml, const flo
 
 template <int KB, int VB, int QJL, int WIDE>
 hipError_t launch_scan(const DecodePlan& p, const ScanArgs& sa, hipStream_t stream) {
-  dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)p.B);
+  dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)(p.B * p.nqt));
   if (sa.kpm.table != nullptr || sa.vpm.table != nullptr)
     hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 1>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0,
                        stream, sa);
@@ -1149,6 +1181,9 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   sa.G = p.G;
   sa.T = (int)p.T;
   sa.n_split = p.n_split;
+  sa.M = (int)p.M;
+  sa.Mt = p.Mt;
+  sa.nqt = p.nqt;
   sa.wg_chunk = p.chunk;
   sa.wave_chunk = p.chunk / ((p.qjl || p.wide) ? 8 : kCommonWaves);
   // the query operand carries log2(e) * scale / sqrt(d) (scores in the log2
@@ -1168,7 +1203,8 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   }
   if (err != hipSuccess || p.n_split == 1) return err;
 
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.H_kv, (unsigned)p.B, kD / 32), dim3(256), 0, stream, ml, acc,
+  // the combine sees B * M query rows of H_q heads
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.H_kv, (unsigned)(p.B * p.M), kD / 32), dim3(256), 0, stream, ml, acc,
                      v->rot, out, (int)p.H_q, p.G, p.n_split, inv_sqrt_d);
   return hipGetLastError();
 }

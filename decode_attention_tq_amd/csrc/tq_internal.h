@@ -19,16 +19,22 @@ constexpr int kDecodeTargetWGs = 256;   // one workgroup per compute unit of a 2
 // Decode planning shared by the workspace-size helper and the launcher.
 struct DecodePlan {
   int64_t B, H_q, H_kv, T;
+  int64_t M;           // query tokens per row (1: decode; M > 1: chunked causal attention)
+  int32_t Mt, nqt;     // query tokens per workgroup tile, tiles per row
   int32_t G;           // query heads per KV head
-  int32_t wide;        // 0: G <= 8 (hi/lo query halves share one 16-column MFMA tile), 1: 8 < G <= 16
+  int32_t wide;        // 0: Mt*G <= 8 (hi/lo query halves share one 16-column MFMA tile), 1: up to 16 columns
   int32_t qjl;
   int32_t n_split;     // context chunks per (row, KV head)
   int32_t chunk;       // tokens per chunk, multiple of kStep
   size_t off_ml, off_acc, bytes;   // chunk partials (used when n_split > 1)
 };
 
+// M query tokens per row (1 = decode). Columns of a workgroup are (query token,
+// head) pairs: M*G <= 8 runs the 16-wavefront tile with all M tokens; more
+// columns take the 16-column tile (8 wavefronts) with floor(16/G) tokens per
+// tile.
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
-                 DecodePlan* p);
+                 DecodePlan* p, int64_t M = 1);
 
 // Block table of a cache in the paged layout; table == nullptr for the
 // contiguous layout. Token t of (row b, head h) is token row

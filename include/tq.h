@@ -213,6 +213,35 @@ int tq_decode_attention(const tq_cache* k, const tq_cache* v,
                         const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
                         float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
 
+/*
+ * Chunked prefill / multi-query attention over the packed caches: M new
+ * tokens per row, whose keys and values are already in the caches (appended
+ * with tq_quantize_kv), attend causally to the row's context. Token i of row b
+ * sits at position ctx_len[b] - M + i and attends to cache tokens
+ * 0 .. ctx_len[b] - M + i, with the decode's computation per (token, head):
+ *   out[b][i][h] = sum_{t <= ctx_len[b]-M+i} softmax_t(scale * q[b][i][h] . k_hat[b][h/G][t]) v_hat[b][h/G][t]
+ * (a query whose position is negative gets a zero output). M = 1 is
+ * tq_decode_attention. A workgroup takes a tile of tokens x the G heads of a KV
+ * head as the columns of its MFMA tiles (up to 8, or 16 on the 8-wavefront
+ * tile), so the codebook decode of each cache step serves every column of the
+ * tile; a row with more tokens than a tile reads the cache once per tile.
+ * (The prompt-processing cost of compressed caches is noted in the qxai.app
+ * item on Tether QVAC's TurboQuant release.)
+ *   q:        device [B][M][H_q][d], TQ_F32 or TQ_BF16
+ *   out:      device float32 [B][M][H_q][d]
+ *   workspace: device, at least tq_prefill_workspace_bytes(...) bytes, 256-byte aligned
+ * Other arguments and requirements as tq_decode_attention; M in 1..65535 and
+ * B * ceil(M / tile) <= 65535.
+ */
+int tq_prefill_attention(const tq_cache* k, const tq_cache* v,
+                         const void* q, int32_t q_dtype, int64_t H_q, int64_t M,
+                         const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
+                         float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/* Workspace bytes tq_prefill_attention needs; 0 for invalid sizes. */
+size_t tq_prefill_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t M, int64_t T,
+                                  int32_t n_split, int32_t k_qjl);
+
 /* Number of context chunks tq_decode_attention uses for these sizes (n_split 0 = auto). */
 int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split);
 

@@ -171,6 +171,24 @@ def test_quantize_validation_paths():
     assert _quant(s) == tq.ERR_INVALID_ARGUMENT
 
 
+def test_prefill_validation_paths():
+    K, V = _cache(), _cache(role=tq.VALUES)
+    lib = tq.lib()
+    def call(M=4, H_q=8, T=64, n_split=0, ws_bytes=1 << 30):
+        return lib.tq_prefill_attention(ctypes.byref(K), ctypes.byref(V), FAKE, tq.BF16, H_q, M, None, T, 0.0,
+                                        n_split, FAKE, FAKE, ws_bytes, None)
+    assert call(M=0) == tq.ERR_INVALID_ARGUMENT
+    assert call(M=-3) == tq.ERR_INVALID_ARGUMENT
+    assert call(M=70000) == tq.ERR_UNSUPPORTED
+    assert call(ws_bytes=16) == tq.ERR_WORKSPACE_TOO_SMALL
+    assert call(H_q=7) == tq.ERR_INVALID_ARGUMENT                 # H_q % H_kv
+    # workspace grows with M (chunk partials per query token and head)
+    one = tq.prefill_workspace_bytes(2, 8, 2, 1, 4096, 4, 0)
+    assert one == tq.decode_workspace_bytes(2, 8, 2, 4096, 4, 0)
+    assert tq.prefill_workspace_bytes(2, 8, 2, 6, 4096, 4, 0) > 5 * (one - 512)
+    assert tq.prefill_workspace_bytes(2, 8, 2, 0, 4096, 4, 0) == 0
+
+
 def test_paged_cache_validation_paths():
     """Paged layout: block_tokens a power of two in 32..65536 dividing T_cap,
     n_blocks > 0, a 4-byte aligned table, arrays below 2 GiB."""
