@@ -150,6 +150,8 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--formats", default="llama8b,qwen,qjl",
                     help="other workloads whose decode is also timed (their own bit widths); '' to skip")
+    ap.add_argument("--prefill-m", default="2,16",
+                    help="chunk sizes M of chunked causal attention timed on the same caches ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=256,
                     help="also time decode on paged caches with this many tokens per block (0: skip)")
     args = ap.parse_args()
@@ -321,6 +323,32 @@ def main():
         del fk, fv, fws
         torch.cuda.empty_cache()
 
+    # chunked causal (prefill) attention of the M newest tokens of every row over
+    # the same caches; the cache is read once per tile of query tokens
+    prefill = {}
+    for M in [int(m) for m in args.prefill_m.split(",") if m]:
+        pq = torch.randn((w.B, M, w.H_q, w.d), generator=torch.Generator(device=dev).manual_seed(M), device=dev)
+        pq = pq.to(torch.bfloat16) if w.dtype == "bf16" else pq
+        pws = tq.Workspace(tq.prefill_workspace_bytes(w.B, w.H_q, w.H_kv, M, T, 0, w.k_qjl), dev)
+        po = torch.empty((w.B, M, w.H_q, w.d), dtype=torch.float32, device=dev)
+        for _ in range(3):
+            tq.prefill_attention(kc, vc, pq, T=T, out=po, workspace=pws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(20):
+            tq.prefill_attention(kc, vc, pq, T=T, out=po, workspace=pws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / 20 * 1e3
+        Mt = M if M * w.G <= 8 else min(M, 16 // w.G)
+        tiles = -(-M // Mt)
+        pb = tiles * (decode_bytes(w, T) - w.B * w.H_q * w.d * 6) + w.B * M * w.H_q * w.d * 6
+        prefill[str(M)] = {"us": us, "query_tokens_per_s": w.B * M / (us * 1e-6), "tiles_per_row": tiles,
+                           "bytes": pb, "GB_s": pb / (us * 1e-6) / 1e9, "frac": pb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        log(f"[bench] prefill attention M={M}: {us:.1f} us, {w.B * M / (us * 1e-6):.0f} query tokens/s, "
+            f"{pb / (us * 1e-6) / 1e9:.0f} GB/s")
+        del pws, po, pq
+
     # calibration copy of known size for the rocprofv3 byte counters (256 MiB read + write)
     cal = torch.empty(64 << 20, dtype=torch.float32, device=dev)
     cal2 = torch.empty_like(cal)
@@ -365,6 +393,8 @@ def main():
         res["paged"] = paged
     if formats:
         res["formats"] = formats
+    if prefill:
+        res["prefill_attention"] = prefill
     if not args.no_cpu_baseline:
         log("[bench] timing the CPU oracle on a bounded sample")
         res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
