@@ -375,7 +375,7 @@ def main():
                    "n_split": n_split},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
-                     "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)}>"
+                     "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)},0>"
                                 + (" (the whole tq_decode_attention call: one launch)" if n_split == 1
                                    else f" + combine_kernel ({n_split} context chunks)")),
                      "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
