@@ -37,9 +37,18 @@
 //        hi and lo tiles). Row order is chosen so that after two MFMAs lane
 //        (g, col) holds the scores of tokens 8g .. 8g+7 of the step.
 //   PV   acc^T[coord][col] += sum_t Vhat^T[coord][t] * P^T[t][col]. B is the
-//        weight operand, which is exactly what the QK lanes hold; A is unpacked
-//        from the 8-token value blocks, lane (g, i) reading the 24-byte (3-bit)
-//        slice of block g that holds coordinates 8i .. 8i+7.
+//        weight operand in float16, which is what the QK lanes hold (G <= 8:
+//        the lanes of columns c and c+8 each own 4 of a block's 8 tokens and
+//        zero the other 4, so the two columns are partial sums that the
+//        epilogue adds); A is unpacked from the 8-token value blocks, lane
+//        (g, i) reading the 24-byte (3-bit) slice of block g that holds
+//        coordinates 8i .. 8i+7.
+//   Precision: the query operand keeps ~22 bits (hi + lo halves), since a
+//        score's error scales with the score itself and key norms reach the
+//        hundreds; a weight is rounded once to float16 (relative error at most
+//        2^-11, independent of the scores), which moves the output by about
+//        2^-11 / sqrt(3) relative for diffuse attention and at most 2^-11 when
+//        one token dominates.
 //   Codes become float16 pairs through a lookup table in LDS indexed by two
 //   adjacent codes (2*bits wide field), replicated kLutRep times so that lanes
 //   of a wavefront read distinct banks (lane l reads replica l % kLutRep).
@@ -397,7 +406,7 @@ struct QOps {
 template <int WIDE>
 struct SoftState {
   float m_ref, m_off, l;
-  floatx4 acc0[8], acc1[8];
+  floatx4 acc0[8];
 };
 
 template <int KB, int VB, int QJL, int WIDE, bool MASK>
@@ -496,28 +505,24 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       st.l += p;
       w[r] = p * quad_bcast(nm.vn, r);
     }
-    // own tokens as float16 hi and lo halves (pairs of tokens per register)
-    uint32_t hi2[2], lo2[2];
+    // float16 weights of the lane's 4 tokens, two per register. The B operand
+    // of lane (c, hf) holds them in k slots 4hf .. 4hf+3 of its 8-token block
+    // and zeros in the other four: MFMA column c sums tokens 0-3 and column c+8
+    // tokens 4-7 of every block, and the epilogue adds the two columns.
+    uint32_t h2[2];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      // w stays a float32 value in a register (empty asm), so the conversions are
-      // plain packed converts rather than fused mixed-precision FMAs
+      // w stays a float32 value in a register (empty asm), so the conversion is a
+      // plain packed convert rather than fused mixed-precision FMAs
       float a0 = w[2 * k], a1 = w[2 * k + 1];
       asm volatile("" : "+v"(a0), "+v"(a1));
-      const half2v h = __builtin_convertvector((float2v){a0, a1}, half2v);
-      hi2[k] = __builtin_bit_cast(uint32_t, h);
-      const half2v l = __builtin_convertvector((float2v){a0 - (float)h[0], a1 - (float)h[1]}, half2v);
-      lo2[k] = __builtin_bit_cast(uint32_t, l);
+      h2[k] = __builtin_bit_cast(uint32_t, __builtin_convertvector((float2v){a0, a1}, half2v));
     }
-    // the hi lane keeps hi of tokens 0-3 and needs hi of tokens 4-7 from its partner;
-    // the lo lane keeps lo of tokens 4-7 and needs lo of tokens 0-3
     uint32_t op[4];
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      const uint32_t send = q.hf ? hi2[k] : lo2[k];
-      const uint32_t recv = __builtin_amdgcn_update_dpp(0u, send, 0x128, 0xF, 0xF, false);
-      op[k] = q.hf ? recv : hi2[k];
-      op[2 + k] = q.hf ? lo2[k] : recv;
+      op[k] = q.hf ? 0u : h2[k];
+      op[2 + k] = q.hf ? h2[k] : 0u;
     }
     const half8 pb0 = words_to_half8(op[0], op[1], op[2], op[3]);
 #define TQ_PV(NB)                                                     \
@@ -528,7 +533,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
 #undef TQ_PV
   } else {
-    // ---- 8 < G <= 16: separate hi and lo tiles; every lane holds 8 tokens
+    // ---- 8 < G <= 16: separate hi and lo query tiles; every lane holds 8 tokens
     float y[8];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -555,14 +560,11 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       const float alpha = st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) {
-        st.acc0[nb] *= alpha;
-        st.acc1[nb] *= alpha;
-      }
+      for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
       st.m_ref = m_new;
       st.m_off = m_new + kShift;
     }
-    uint32_t pw0[4], pw1[4];
+    uint32_t pw[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       float w2[2];
@@ -574,17 +576,13 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
         st.l += p;
         w2[u] = p * bcast_row(nm.vn, e);
       }
-      const _Float16 h0 = (_Float16)w2[0], h1 = (_Float16)w2[1];
-      pw0[k] = __builtin_bit_cast(uint32_t, half2v{h0, h1});
-      pw1[k] = __builtin_bit_cast(uint32_t, half2v{(_Float16)(w2[0] - (float)h0), (_Float16)(w2[1] - (float)h1)});
+      pw[k] = __builtin_bit_cast(uint32_t, half2v{(_Float16)w2[0], (_Float16)w2[1]});
     }
-    const half8 pb0 = words_to_half8(pw0[0], pw0[1], pw0[2], pw0[3]);
-    const half8 pb1 = words_to_half8(pw1[0], pw1[1], pw1[2], pw1[3]);
+    const half8 pb = words_to_half8(pw[0], pw[1], pw[2], pw[3]);
 #define TQ_PV(NB)                                                     \
     {                                                                 \
       const half8 va = value_operand<VB, NB>(d.vw, lutV, lane);       \
-      st.acc0[NB] = mfma16(va, pb0, st.acc0[NB]);                     \
-      st.acc1[NB] = mfma16(va, pb1, st.acc1[NB]);                     \
+      st.acc0[NB] = mfma16(va, pb, st.acc0[NB]);                      \
     }
     TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
 #undef TQ_PV
@@ -830,10 +828,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   st.m_off = -INFINITY;
   st.l = 0.f;
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
-    st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
-    st.acc1[nb] = st.acc0[nb];
-  }
+  for (int nb = 0; nb < 8; ++nb) st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // ---- stream the share: full 32-token steps with two register buffers in
   // turn, then at most one masked step for a ragged end. A step first waits
@@ -900,7 +895,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = st.acc0[nb][r];
-      x += WIDE ? st.acc1[nb][r] : dpp_ror8(x);
+      if constexpr (!WIDE) x += dpp_ror8(x);   // columns c and c+8 hold the two token halves
       o[nb][r] = x;
     }
   }

@@ -19,7 +19,7 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import BOUNDARY, TOL_ATTN, OracleModel, code_mismatch, log, rel_l2, unpack_head
+from tqhelp import BOUNDARY, TOL_ATTN, TOL_RECUT, OracleModel, code_mismatch, log, rel_l2, unpack_head
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -143,7 +143,7 @@ def test_fullsize_stress70b(tq):
     out4 = tq.decode_attention(kc, vc, q, T=w.T, n_split=4, workspace=ws4)
     err = rel_l2(out4.cpu().numpy(), out.cpu().numpy())
     log(f"  4 chunks vs 1 chunk: rel L2 {err:.3e}")
-    assert err <= 1e-5
+    assert err <= TOL_RECUT
 
 
 def test_fullsize_stress70b_ragged(tq):

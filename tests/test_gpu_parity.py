@@ -7,7 +7,7 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import (BOUNDARY, TOL_ATTN, OracleModel, code_mismatch, device_inputs, device_queries, log,
+from tqhelp import (BOUNDARY, TOL_ATTN, TOL_RECUT, U_F16, OracleModel, code_mismatch, device_inputs, device_queries, log,
                     rel_l2, upload_oracle_cache)
 
 torch = pytest.importorskip("torch")
@@ -175,7 +175,7 @@ def test_split_invariance_and_determinism(tq):
     assert torch.equal(base, again)
     for ns in (1, 3, 7, 64, 128):
         o = tq.decode_attention(kc, vc, q, T=w.T, n_split=ns)
-        assert rel_l2(o.cpu().numpy(), base.cpu().numpy()) <= 1e-5, ns
+        assert rel_l2(o.cpu().numpy(), base.cpu().numpy()) <= TOL_RECUT, ns
 
 
 def test_ragged_context_lengths(tq):
@@ -296,13 +296,14 @@ def test_degenerate_inputs(tq):
     assert torch.all(out == 0)
     out0 = tq.decode_attention(kc, vc, q, T=0)
     assert torch.all(out0 == 0)
-    # single token: output is that token's reconstruction
+    # single token: output is that token's reconstruction (its weight, the value
+    # norm times a power of two, is rounded once to float16)
     x = device_inputs(w, "v")
     tq.quantize_kv(x[:, :1], vc)
     tq.quantize_kv(device_inputs(w, "k")[:, :1], kc)
     o1 = tq.decode_attention(kc, vc, q, T=1).cpu().numpy()
     v0 = tq.dequantize(vc, 0, 1).cpu().numpy()[0, 0, 0]
-    assert np.allclose(o1[0], np.repeat(v0[None], 8, axis=0), rtol=1e-5, atol=1e-6)
+    assert np.allclose(o1[0], np.repeat(v0[None], 8, axis=0), rtol=U_F16 + 1e-5, atol=1e-6)
 
 
 @pytest.mark.parametrize("scale", [1e30, 1e-30])

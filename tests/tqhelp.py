@@ -14,6 +14,13 @@ from oracle import rotation as orot
 D = 128
 BOUNDARY = 1e-6      # decision-boundary band (unit domain) inside which codes may differ
 TOL_ATTN = 2e-3      # relative L2 tolerance of decode outputs
+# Two GPU results of one attention that differ only in how the work is cut
+# (context chunks, query tiles, when the running maximum moves) round each
+# softmax weight to float16 on their own (unit roundoff 2^-11): on random data
+# they differ by about 2^-11 * sqrt(2/3) = 4e-4 relative L2, while a wrong
+# merge or rescale factor moves the result by O(1).
+TOL_RECUT = 1e-3
+U_F16 = 2.0 ** -11   # float16 unit roundoff (one rounding of a weight)
 
 
 def log(msg: str):
