@@ -352,14 +352,6 @@ __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
   }
 }
 
-template <int QJL>
-__device__ inline void load_norms(StepNorms<QJL>& n, const Streams& s, const LaneOffsets& lo, uint32_t rk,
-                                  uint32_t rv) {
-  n.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, lo.n, rk * 4u, kStreamAux));
-  n.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, lo.n, rv * 4u, kStreamAux));
-  if constexpr (QJL) n.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, lo.n, rk * 4u, kStreamAux));
-}
-
 // Waits until the loads of d have landed (an empty asm that reads every word:
 // the compiler places the counter wait before it).
 template <int KB, int VB, int QJL, int WIDE>
@@ -378,20 +370,35 @@ __device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE>& d) {
 
 // Loads one step: rk, rv are the token rows of the step's first token in the
 // key and value arrays (relative to the stream bases; 32 consecutive rows).
-template <int KB, int VB, int QJL, int WIDE>
+// Full steps (CHECKED false) pass the step offset as the scalar offset, which
+// the hardware does not range check: all 32 rows must lie inside the stream.
+// A step that may run past the end of a stream (the ragged end of a row whose
+// capacity is not a multiple of 32) adds it to the per-lane offsets instead,
+// so that lanes past the end read zeros.
+template <bool CHECKED, int KB, int VB, int QJL, int WIDE>
 __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo,
                                  uint32_t rk, uint32_t rv) {
   constexpr int KW = 4 * KB, VBW = 32 * VB;
   // wave-uniform; readfirstlane keeps the step offsets in scalar registers
   rk = __builtin_amdgcn_readfirstlane(rk);
   rv = __builtin_amdgcn_readfirstlane(rv);
+  const uint32_t ok = rk * (KW * 4u), os = rk * 16u, ov = (rv / 8u) * (VBW * 4u), onk = rk * 4u, onv = rv * 4u;
+  // (TQ_OFF: the scalar offset of a load; TQ_VOF: its per-lane offset)
+#define TQ_OFF(o) (CHECKED ? 0u : (o))
+#define TQ_VOF(v, o) (CHECKED ? (v) + (o) : (v))
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
-    bload_words_s<KB>(s.rk, lo.k[m], rk * (KW * 4u), d.kw[m]);
-    if constexpr (QJL) d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, lo.s[m], rk * 16u, kStreamAux);
+    bload_words_s<KB>(s.rk, TQ_VOF(lo.k[m], ok), TQ_OFF(ok), d.kw[m]);
+    if constexpr (QJL)
+      d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, TQ_VOF(lo.s[m], os), TQ_OFF(os), kStreamAux);
   }
-  bload_words_s<2 * VB>(s.rv, lo.v, (rv / 8u) * (VBW * 4u), d.vw);
-  load_norms(d.nm, s, lo, rk, rv);
+  bload_words_s<2 * VB>(s.rv, TQ_VOF(lo.v, ov), TQ_OFF(ov), d.vw);
+  d.nm.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, TQ_VOF(lo.n, onk), TQ_OFF(onk), kStreamAux));
+  d.nm.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, TQ_VOF(lo.n, onv), TQ_OFF(onv), kStreamAux));
+  if constexpr (QJL)
+    d.nm.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, TQ_VOF(lo.n, onk), TQ_OFF(onk), kStreamAux));
+#undef TQ_OFF
+#undef TQ_VOF
 }
 
 
@@ -596,6 +603,11 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 constexpr int kCommonWaves = 16;
 template <int QJL, int WIDE>
 constexpr int scan_waves() { return (QJL || WIDE) ? 8 : kCommonWaves; }
+// Steps whose loads are in flight while a wavefront computes one (register
+// buffers: ahead + 1).
+constexpr int kCommonAhead = 1;
+template <int QJL, int WIDE>
+constexpr int scan_ahead() { return (QJL || WIDE) ? 1 : kCommonAhead; }
 
 // merge buffer: [wave][column][kMergeStride] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
@@ -732,20 +744,32 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (el * 2u) & ~3u : el * 4u, 0, 0);
     }
   }
-  StepData<KB, VB, QJL, WIDE> buf[2];
-  // (a wavefront whose share starts past the caches has no work; it reads the
-  // first step instead: the scalar offset of a buffer load is not range
-  // checked, only the per-lane offset is)
-  const int t_first = t_begin < min(a.TcK, a.TcV) ? t_begin : 0;
+  constexpr int AH = scan_ahead<QJL, WIDE>();
+  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
+  // the first AH steps of the share (a step past the caches is replaced by the
+  // first step of the row: such a wavefront, or such a step, is never used,
+  // and the scalar offset of a buffer load is not range checked, only the
+  // per-lane offset is)
   uint32_t ek = 0u, ev = 0u;   // block-table entries of the next step to load (paged caches)
-  if (kpg) ek = page_entry(rtk, a.kpm, t_first);
-  if (vpg) ev = page_entry(rtv, a.vpm, t_first);
-  load_step(buf[0], s, lo, step_row(a.kpm, kv, a.H_kv, ek, t_first), step_row(a.vpm, kv, a.H_kv, ev, t_first));
-  if (kpg) ek = page_entry(rtk, a.kpm, t_first + kStep);
-  if (vpg) ev = page_entry(rtv, a.vpm, t_first + kStep);
-  int ctx = a.T;
-  if (a.ctx_lens) ctx = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.ctx_lens, (uint32_t)((b + 1) * 4)),
-                                                             (uint32_t)b * 4u, 0, 0);
+#pragma unroll
+  for (int j = 0; j < AH; ++j) {
+    const int tj = t_begin + (j + 1) * kStep <= min(a.TcK, a.TcV) ? t_begin + j * kStep : 0;
+    if (kpg) ek = page_entry(rtk, a.kpm, tj);
+    if (vpg) ev = page_entry(rtv, a.vpm, tj);
+    load_step<false>(buf[j], s, lo, step_row(a.kpm, kv, a.H_kv, ek, tj), step_row(a.vpm, kv, a.H_kv, ev, tj));
+  }
+  {
+    const int tn = t_begin + AH * kStep;
+    if (kpg) ek = page_entry(rtk, a.kpm, tn);
+    if (vpg) ev = page_entry(rtv, a.vpm, tn);
+  }
+  // (unconditional, through an empty range when there are no context lengths,
+  // and first touched after the prologue: a load under a branch, or one moved
+  // to a scalar register at once, would make the prologue wait for every load
+  // issued before it)
+  uint32_t ctx_word = __builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(a.ctx_lens ? (const void*)a.ctx_lens : (const void*)a.knorms, a.ctx_lens ? (uint32_t)((b + 1) * 4) : 0u),
+      (uint32_t)b * 4u, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
 
   // ---- prologue: lookup tables, then the query operand of this (row, KV head)
@@ -809,6 +833,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 
 
   // the share of this wavefront, clipped by the context length
+  asm volatile("" : "+v"(ctx_word));
+  int ctx = a.ctx_lens ? (int)ctx_word : a.T;
   ctx = ctx < 0 ? 0 : (ctx > a.T ? a.T : ctx);
   // causal limits: token i0 + i of the tile (position ctx - M + i0 + i) sees
   // cache tokens below lim0 + i (all ctx tokens for a decode)
@@ -848,13 +874,14 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 #define TQ_STEP(CUR, NEXT)                                                                                  \
     {                                                                                                       \
       wait_step(CUR);                                                                                       \
-      if (t0 + kStep < t_full) {                                                                            \
-        const uint32_t rk = step_row(a.kpm, kv, a.H_kv, ek, t0 + kStep);                                    \
-        const uint32_t rv = step_row(a.vpm, kv, a.H_kv, ev, t0 + kStep);                                    \
+      if (t0 + AH * kStep < t_full) {                                                                       \
+        const int tl = t0 + AH * kStep, tn = tl + kStep;                                                    \
+        const uint32_t rk = step_row(a.kpm, kv, a.H_kv, ek, tl);                                            \
+        const uint32_t rv = step_row(a.vpm, kv, a.H_kv, ev, tl);                                            \
         /* the entry changes only where the following step starts a block */                               \
-        if (kpg && ((t0 + 2 * kStep) & ((1 << a.kpm.lg) - 1)) == 0) ek = page_entry(rtk, a.kpm, t0 + 2 * kStep); \
-        if (vpg && ((t0 + 2 * kStep) & ((1 << a.vpm.lg) - 1)) == 0) ev = page_entry(rtv, a.vpm, t0 + 2 * kStep); \
-        load_step(NEXT, s, lo, rk, rv);                                                                     \
+        if (kpg && (tn & ((1 << a.kpm.lg) - 1)) == 0) ek = page_entry(rtk, a.kpm, tn);                      \
+        if (vpg && (tn & ((1 << a.vpm.lg) - 1)) == 0) ev = page_entry(rtv, a.vpm, tn);                      \
+        load_step<false>(NEXT, s, lo, rk, rv);                                                                     \
       }                                                                                                     \
       uint32_t begun = 0u;                                                                                  \
       if (lane == 0)                                                                                        \
@@ -870,8 +897,20 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       if (t0 >= t_full) break;                                                                              \
     }
     while (true) {
-      TQ_STEP(buf[0], buf[1])
-      TQ_STEP(buf[1], buf[0])
+      if constexpr (AH == 1) {
+        TQ_STEP(buf[0], buf[1])
+        TQ_STEP(buf[1], buf[0])
+      } else if constexpr (AH == 2) {
+        TQ_STEP(buf[0], buf[2])
+        TQ_STEP(buf[1], buf[0])
+        TQ_STEP(buf[2], buf[1])
+      } else {
+        static_assert(AH == 3, "prefetch depth");
+        TQ_STEP(buf[0], buf[3])
+        TQ_STEP(buf[1], buf[0])
+        TQ_STEP(buf[2], buf[1])
+        TQ_STEP(buf[3], buf[2])
+      }
     }
 #undef TQ_STEP
     __builtin_amdgcn_s_setprio(0);
@@ -883,7 +922,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     StepData<KB, VB, QJL, WIDE> E;
     if (kpg) ek = page_entry(rtk, a.kpm, t0);
     if (vpg) ev = page_entry(rtv, a.vpm, t0);
-    load_step(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
+    load_step<true>(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
     scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, lim_lane);
     t0 += kStep;
   }
