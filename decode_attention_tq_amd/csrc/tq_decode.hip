@@ -225,49 +225,82 @@ struct ScanArgs {
   float kc[16], vc[16];
 };
 
-// Codebook lookup tables in LDS: an entry holds the float16 levels of 2
-// adjacent codes (indexed by their 2*bits wide field), replicated kLutRep
-// times so that lane l reads replica l % kLutRep and the lanes of a wavefront
-// hit distinct banks. (Entries of 4 codes, 8 bytes, halve the VALU work of the
-// lookups but their unreplicated random reads cost more LDS time than they
-// save on this part.)
-template <int BITS>
-constexpr int lut_words() { return (1 << (2 * BITS)) * kLutRep; }
+// Codebook lookup table in LDS, shared by keys and values: 256 slots of 256
+// bytes, slot x for the 8 bits x that start at a code pair's position in the
+// packed words (the pair's 2*bits wide field, then bits of the next pair, which
+// the entry ignores). A slot holds the float16 levels of the key pair in
+// kLutRep replicas (bytes 0-127) and of the value pair (bytes 128-255); lane l
+// reads replica l % kLutRep, so the lanes of a wavefront hit distinct banks.
+// The address of a lookup is a register whose byte 0 holds the lane's replica
+// offset: one SDWA shift writes the 8 bits into byte 1 (x * 256) and leaves the
+// rest, so a lookup costs one VALU instruction (two where a pair straddles two
+// words). (Entries of 4 codes, 8 bytes, would halve the lookups, but their
+// unreplicated random reads cost more LDS time than they save on this part.)
+constexpr int kLutBytes = 256 * 256;
 
-template <int BITS>
-__device__ void build_lut(uint32_t* lut, const float* cb, int tid, int nt) {
-  constexpr int m = (1 << BITS) - 1;
-  for (int e = tid; e < lut_words<BITS>(); e += nt) {
-    const int f = e >> kLutShift;
-    lut[e] = pack_half2(cb[f & m], cb[f >> BITS]);
+template <int KB, int VB>
+__device__ void build_lut(uint32_t* lut, const float* cK, const float* cV, int tid, int nt) {
+  for (int e = tid; e < kLutBytes / 4; e += nt) {
+    const int x = e >> 6;               // slot
+    const bool val = (e >> 5) & 1;      // value half of the slot
+    const int bits = val ? VB : KB, m = (1 << bits) - 1;
+    const int f = x & ((1 << (2 * bits)) - 1);
+    const float* cb = val ? cV : cK;
+    lut[e] = pack_half2(cb[f & m], cb[f >> bits]);
   }
 }
 
-// Float16 codebook levels of the 8 codes at bit offset POS of the lane's word
-// slice w (codes LSB first): an MFMA operand of 8 halves.
-template <int BITS, int POS>
-__device__ inline half8 levels8(const uint32_t* w, const uint32_t* lut, int lrep) {
+// Address registers of the lookups (two sets, so that consecutive operands do
+// not wait on each other's reads): byte 0 = replica offset, byte 1 = slot.
+struct LutRegs {
+  uint32_t a[4], b[4];
+};
+
+// Byte 1 of r = the 8 bits at bit P of the lane's N-word slice w (zeros past
+// the slice); a field of W bits that straddles two words is first aligned.
+template <int N, int P, int W>
+__device__ inline void lut_slot(uint32_t& r, const uint32_t* w) {
+  constexpr int wi = P / 32, sh = P % 32;
+  if constexpr (sh + W <= 32 || wi + 1 >= N) {
+    asm("v_lshrrev_b32_sdwa %0, %2, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(r) : "v"(w[wi]), "i"(sh));
+  } else {
+    const uint32_t t = __builtin_amdgcn_alignbit(w[wi + 1], w[wi], sh);
+    asm("v_lshrrev_b32_sdwa %0, 0, %1 dst_sel:BYTE_1 dst_unused:UNUSED_PRESERVE src0_sel:DWORD src1_sel:DWORD"
+        : "+v"(r) : "v"(t));
+  }
+}
+
+// Float16 codebook levels of the 8 codes at bit offset POS of the lane's
+// N-word slice w (codes LSB first), from the key (OFF 0) or value (OFF 128)
+// half of the table: an MFMA operand of 8 halves.
+template <int BITS, int N, int POS, int OFF>
+__device__ inline half8 levels8(const uint32_t* w, const char* lut, uint32_t (&r)[4]) {
   constexpr int W = 2 * BITS;
-  const uint32_t r0 = lut[(field<POS + 0 * W, W>(w) << kLutShift) | lrep];
-  const uint32_t r1 = lut[(field<POS + 1 * W, W>(w) << kLutShift) | lrep];
-  const uint32_t r2 = lut[(field<POS + 2 * W, W>(w) << kLutShift) | lrep];
-  const uint32_t r3 = lut[(field<POS + 3 * W, W>(w) << kLutShift) | lrep];
+  lut_slot<N, POS + 0 * W, W>(r[0], w);
+  lut_slot<N, POS + 1 * W, W>(r[1], w);
+  lut_slot<N, POS + 2 * W, W>(r[2], w);
+  lut_slot<N, POS + 3 * W, W>(r[3], w);
+  const uint32_t r0 = *(const uint32_t*)(lut + r[0] + OFF);
+  const uint32_t r1 = *(const uint32_t*)(lut + r[1] + OFF);
+  const uint32_t r2 = *(const uint32_t*)(lut + r[2] + OFF);
+  const uint32_t r3 = *(const uint32_t*)(lut + r[3] + OFF);
   return words_to_half8(r0, r1, r2, r3);
 }
 
 // A operand of the QK MFMA for step KK: coordinates 32g + 8KK + 0..7 of the
 // lane's token, from the lane's KB-word slice (coordinates 32g .. 32g+31).
 template <int KB, int KK>
-__device__ inline half8 key_operand(const uint32_t* w, const uint32_t* lut, int lrep) {
-  return levels8<KB, 8 * KB * KK>(w, lut, lrep);
+__device__ inline half8 key_operand(const uint32_t* w, const char* lut, uint32_t (&r)[4]) {
+  return levels8<KB, KB, 8 * KB * KK, 0>(w, lut, r);
 }
 
 // A operand of the PV MFMA for coordinate block NB: value codes of the 8 tokens
 // of the lane's block at coordinate 8i + NB (i = lane % 16), from the lane's
 // 2*VB-word slice of the block record (coordinates 8i .. 8i+7).
 template <int VB, int NB>
-__device__ inline half8 value_operand(const uint32_t* w, const uint32_t* lut, int lrep) {
-  return levels8<VB, 8 * VB * NB>(w, lut, lrep);
+__device__ inline half8 value_operand(const uint32_t* w, const char* lut, uint32_t (&r)[4]) {
+  return levels8<VB, 2 * VB, 8 * VB * NB, 128>(w, lut, r);
 }
 
 // A operand of the QJL MFMA for step KK: +-1 for coordinates 32g + 8KK + 0..7.
@@ -418,7 +451,7 @@ struct SoftState {
 
 template <int KB, int VB, int QJL, int WIDE, bool MASK>
 __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, const QOps<WIDE, QJL>& q,
-                                          SoftState<WIDE>& st, const uint32_t* lutK, const uint32_t* lutV,
+                                          SoftState<WIDE>& st, const char* lut, LutRegs& lr,
                                           const uint32_t* lutS, int lane, int tg, int lim) {
   const StepNorms<QJL>& nm = d.nm;
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
@@ -435,7 +468,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 #define TQ_QK(KK)                                                     \
     {                                                                 \
       _Pragma("unroll") for (int m = 0; m < 2; ++m) {                 \
-        const half8 ka = key_operand<KB, KK>(d.kw[m], lutK, lane);    \
+        const half8 ka = key_operand<KB, KK>(d.kw[m], lut, m ? lr.b : lr.a); \
         s0[m] = mfma16(ka, q.q0[KK], s0[m]);                          \
         if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);      \
       }                                                               \
@@ -534,7 +567,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     const half8 pb0 = words_to_half8(op[0], op[1], op[2], op[3]);
 #define TQ_PV(NB)                                                     \
     {                                                                 \
-      const half8 va = value_operand<VB, NB>(d.vw, lutV, lane);       \
+      const half8 va = value_operand<VB, NB>(d.vw, lut, (NB & 1) ? lr.b : lr.a); \
       st.acc0[NB] = mfma16(va, pb0, st.acc0[NB]);                     \
     }
     TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
@@ -588,7 +621,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     const half8 pb = words_to_half8(pw[0], pw[1], pw[2], pw[3]);
 #define TQ_PV(NB)                                                     \
     {                                                                 \
-      const half8 va = value_operand<VB, NB>(d.vw, lutV, lane);       \
+      const half8 va = value_operand<VB, NB>(d.vw, lut, (NB & 1) ? lr.b : lr.a); \
       st.acc0[NB] = mfma16(va, pb, st.acc0[NB]);                      \
     }
     TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
@@ -621,8 +654,7 @@ constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride
 
 template <int KB, int VB, int QJL, int WIDE>
 constexpr size_t scan_lds_bytes() {
-  static_assert(lut_words<KB>() + lut_words<VB>() + (QJL ? 4 : 0) * kLutRep <= kRegionWords,
-                "lookup tables exceed the scratch region");
+  static_assert(kLutBytes / 4 + (QJL ? 4 : 0) * kLutRep <= kRegionWords, "lookup tables exceed the scratch region");
   static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * kMergeStride <= kRegionWords,
                 "merge area exceeds the scratch region");
   static_assert(scan_waves<QJL, WIDE>() * (WIDE ? 16 : 8) * kD <= kRegionWords,
@@ -656,9 +688,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
   float* vA = R + kRegionWords;
   float* vB = vA + kVecWords;
-  uint32_t* lutK = U;
-  uint32_t* lutV = U + lut_words<KB>();
-  uint32_t* lutS = lutV + lut_words<VB>();
+  uint32_t* lut = U;                      // keys and values
+  uint32_t* lutS = U + kLutBytes / 4;     // QJL signs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -785,8 +816,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   }
   if (tid == 0) *steps_done = 0u;
   __syncthreads();
-  build_lut<KB>(lutK, cents, tid, NT);
-  build_lut<VB>(lutV, cents + 16, tid, NT);
+  build_lut<KB, VB>(lut, cents, cents + 16, tid, NT);
   if constexpr (QJL) {
     for (int e = tid; e < NS * kLutRep; e += NT) {
       const int f = e >> kLutShift;
@@ -849,6 +879,9 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   const int lcol = WIDE ? c : (c & 7);
   const int lim_lane = lcol < NC ? max(lim0 + lcol / G, 0) : lim_hi;
 
+  LutRegs lr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lr.a[i] = lr.b[i] = (uint32_t)lrep * 4u;
   SoftState<WIDE> st;
   st.m_ref = -INFINITY;
   st.m_off = -INFINITY;
@@ -886,7 +919,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       uint32_t begun = 0u;                                                                                  \
       if (lane == 0)                                                                                        \
         begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);      \
-      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, lim_lane);          \
+      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);\
       begun = __builtin_amdgcn_readfirstlane(begun);   /* by the whole workgroup */                          \
       const uint32_t even = mine * (uint32_t)NW;        /* if every wavefront kept pace */                   \
       if (begun > even + NW) __builtin_amdgcn_s_setprio(3);                                                 \
@@ -923,7 +956,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     if (kpg) ek = page_entry(rtk, a.kpm, t0);
     if (vpg) ev = page_entry(rtv, a.vpm, t0);
     load_step<true>(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
-    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, lutK, lutV, lutS, lrep, t0 + 8 * g, lim_lane);
+    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);
     t0 += kStep;
   }
 
