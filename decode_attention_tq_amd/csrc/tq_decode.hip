@@ -238,15 +238,19 @@ struct ScanArgs {
 // unreplicated random reads cost more LDS time than they save on this part.)
 constexpr int kLutBytes = 256 * 256;
 
+// Thread (slot, quarter) writes 8 replicas of the slot's key pair and 8 of its
+// value pair (two 16-byte stores each), so each pair is formed once per thread.
 template <int KB, int VB>
 __device__ void build_lut(uint32_t* lut, const float* cK, const float* cV, int tid, int nt) {
-  for (int e = tid; e < kLutBytes / 4; e += nt) {
-    const int x = e >> 6;               // slot
-    const bool val = (e >> 5) & 1;      // value half of the slot
-    const int bits = val ? VB : KB, m = (1 << bits) - 1;
-    const int f = x & ((1 << (2 * bits)) - 1);
-    const float* cb = val ? cV : cK;
-    lut[e] = pack_half2(cb[f & m], cb[f >> bits]);
+  for (int e = tid; e < 256 * 4; e += nt) {
+    const int x = e >> 2, qr = e & 3;
+    const int fk = x & ((1 << (2 * KB)) - 1), fv = x & ((1 << (2 * VB)) - 1);
+    const uint32_t pk = pack_half2(cK[fk & ((1 << KB) - 1)], cK[fk >> KB]);
+    const uint32_t pv = pack_half2(cV[fv & ((1 << VB) - 1)], cV[fv >> VB]);
+    uint4* dk = (uint4*)(lut + x * 64 + 8 * qr);
+    uint4* dv = (uint4*)(lut + x * 64 + 32 + 8 * qr);
+    dk[0] = dk[1] = uint4{pk, pk, pk, pk};
+    dv[0] = dv[1] = uint4{pv, pv, pv, pv};
   }
 }
 
@@ -978,6 +982,17 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 
   // ---- merge the wavefront partials in LDS (fixed order)
   const bool finish = a.n_split == 1;
+  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, p)
+  // takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded now (a
+  // wavefront reads whole rows) so that the loads are in flight while the
+  // wavefront waits for the others and during the merge.
+  constexpr int FSEGS = NT / 64, RW = kD / FSEGS;
+  const int fp = tid & 63, fs = tid >> 6;
+  float2 pv[RW];
+  if (finish) {
+#pragma unroll
+    for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
+  }
   __syncthreads();   // every wavefront is done with the lookup tables
   float* mrg = R;    // [wave][MC columns][kMergeStride]: 128 coordinates, m, l
   if (c < NC) {
@@ -991,17 +1006,6 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       dst[kD] = st.m_off;
       dst[kD + 1] = l;
     }
-  }
-  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, p)
-  // takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded now
-  // (a wavefront reads whole rows) so that the loads are in flight during the
-  // merge.
-  constexpr int FSEGS = NT / 64, RW = kD / FSEGS;
-  const int fp = tid & 63, fs = tid >> 6;
-  float2 pv[RW];
-  if (finish) {
-#pragma unroll
-    for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
   }
   __syncthreads();
   // weights of the wavefront partials: lane (h, w) of the first NC * 16 threads
