@@ -920,12 +920,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
         if (vpg && (tn & ((1 << a.vpm.lg) - 1)) == 0) ev = page_entry(rtv, a.vpm, tn);                      \
         load_step<false>(NEXT, s, lo, rk, rv);                                                                     \
       }                                                                                                     \
-      uint32_t begun = 0u;                                                                                  \
-      if (lane == 0)                                                                                        \
-        begun = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);      \
+      /* count this step (an atomic add whose result is not waited for), then */                           \
+      /* read the workgroup's count after the step */                                                        \
+      if (lane == 0) __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); \
       scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);\
-      begun = __builtin_amdgcn_readfirstlane(begun);   /* by the whole workgroup */                          \
-      const uint32_t even = mine * (uint32_t)NW;        /* if every wavefront kept pace */                   \
+      const uint32_t begun = __builtin_amdgcn_readfirstlane(*(volatile uint32_t*)steps_done);                \
+      const uint32_t even = (mine + 1) * (uint32_t)NW;  /* if every wavefront kept pace */                   \
       if (begun > even + NW) __builtin_amdgcn_s_setprio(3);                                                 \
       else if (begun + NW < even) __builtin_amdgcn_s_setprio(0);                                            \
       else __builtin_amdgcn_s_setprio(1);                                                                   \
