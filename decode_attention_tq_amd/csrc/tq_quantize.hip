@@ -680,11 +680,12 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
 //
 // One token per (row, head) (T = 1) without QJL: latency, not throughput,
 // decides here, so the rotation runs as float32 FMAs with the rows of Pi read
-// straight from memory (no LDS staging of Pi, no operand split), 8 vectors per
-// 256-thread workgroup. Same steps as the tiled kernels: power-of-two scale,
-// norm, y = Pi x, threshold search, packing (a value block keeps the bits of
-// its other tokens).
-constexpr int kAppendVecs = 8;
+// straight from memory (no LDS staging of Pi, no operand split), kAppendVecs
+// vectors per 256-thread workgroup (few, so that a layer's tokens spread over
+// many compute units and each thread's dot products stay short). Same steps as
+// the tiled kernels: power-of-two scale, norm, y = Pi x, threshold search,
+// packing (a value block keeps the bits of its other tokens).
+constexpr int kAppendVecs = 1;
 
 template <int BITS, int ROLE, int XF32>
 __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
@@ -712,7 +713,8 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
   if constexpr (ROLE == TQ_VALUES) {
     const int v = tid >> 5, cg = tid & 31;
     const int64_t gv = v0 + v;
-    const int64_t row = gv < nvec ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset & ~(int64_t)7) : -1;
+    const int64_t row = (v < kAppendVecs && gv < nvec) ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset & ~(int64_t)7)
+                                                       : -1;
     if (row >= 0) {
       vdst = a.codes + row * (VBW / 8) + cg * BITS;
 #pragma unroll
@@ -722,9 +724,10 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
 
   {
     // thread (v, c4): coordinates 4c4 .. 4c4+3 of vector v
-    const int v = tid >> 5, c4 = tid & 31;
+    const int v = min(tid >> 5, kAppendVecs - 1), c4 = tid & 31;
     const int64_t gv = v0 + v;
-    const bool ok = gv < nvec;
+    const bool act = (tid >> 5) < kAppendVecs;   // (threads past the vectors only join the shuffles)
+    const bool ok = act && gv < nvec;
     const int64_t b = gv / a.H_kv, h = gv % a.H_kv;
     float x[4] = {0.f, 0.f, 0.f, 0.f};
     if (ok) {
@@ -751,8 +754,8 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
 #pragma unroll
     for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m);
     const float ns = sqrtf(ss);   // |x| * 2^sexp
-    *(float4*)&xs[v][4 * c4] = make_float4(x[0], x[1], x[2], x[3]);
-    if (c4 == 0) {
+    if (act) *(float4*)&xs[v][4 * c4] = make_float4(x[0], x[1], x[2], x[3]);
+    if (act && c4 == 0) {
       fzs[v] = ns > 0.f ? sqrt_d / ns : 0.f;
       const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset) : -1;
       if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
