@@ -4,7 +4,7 @@
 
 One step is one pass of the whole hot path for one new token per batch row:
 quantize the new token's key and value vectors of every (row, KV head) into the
-packed caches (tq_quantize_kv, append at t = T-1), then decode attention of all
+packed caches (tq_append_kv: keys and values in one launch, at t = T-1), then decode attention of all
 query heads over the T-token packed caches (tq_decode_attention). Inputs are
 resident in HBM before timing starts. Prints one JSON line on stdout.
 
@@ -208,8 +208,7 @@ def main():
     ws = tq.Workspace(tq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, T, 0, w.k_qjl), dev)
 
     def step(i):
-        tq.quantize_kv(new_k, kc, t_offset=T - 1)
-        tq.quantize_kv(new_v, vc, t_offset=T - 1)
+        tq.append_kv(new_k, new_v, kc, vc, T - 1)
         tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
 
     for i in range(args.warmup):
@@ -222,8 +221,7 @@ def main():
     for i in range(args.steps):
         a, b, c = evs[i]
         a.record()
-        tq.quantize_kv(new_k, kc, t_offset=T - 1)
-        tq.quantize_kv(new_v, vc, t_offset=T - 1)
+        tq.append_kv(new_k, new_v, kc, vc, T - 1)
         b.record()
         tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
         c.record()
@@ -272,8 +270,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(50):
-            tq.quantize_kv(new_k, pk, t_offset=T - 1)
-            tq.quantize_kv(new_v, pv, t_offset=T - 1)
+            tq.append_kv(new_k, new_v, pk, pv, T - 1)
             tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
         e1.record()
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

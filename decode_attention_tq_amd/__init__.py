@@ -45,7 +45,8 @@ KEYS, VALUES = 0, 1
 D = 128
 VALUE_BLOCK = 8
 
-EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize",
+EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
+           "tq_dequantize",
            "tq_decode_attention", "tq_prefill_attention", "tq_decode_splits", "tq_decode_workspace_bytes",
            "tq_prefill_workspace_bytes", "tq_status_string",
            "tq_last_hip_error")
@@ -73,6 +74,8 @@ def _bind(lib):
     lib.tq_make_codebook_sphere.argtypes = [_I32, _I32, _P, _P]
     lib.tq_make_rotation.argtypes = [_U64, _I32, _I32, _P]
     lib.tq_quantize_kv.argtypes = [_P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache), _I64, _P]
+    lib.tq_append_kv.argtypes = [_P, _P, _I32, _I64, _I64, _I64, _I64, _I64, _I64, ctypes.POINTER(TQCache),
+                                 ctypes.POINTER(TQCache), _I64, _P]
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P,
                                         _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
@@ -88,7 +91,8 @@ def _bind(lib):
     lib.tq_status_string.restype = ctypes.c_char_p
     lib.tq_last_hip_error.argtypes = []
     lib.tq_last_hip_error.restype = ctypes.c_char_p
-    for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_dequantize", "tq_decode_attention",
+    for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
+                 "tq_dequantize", "tq_decode_attention",
                  "tq_prefill_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -261,6 +265,25 @@ def quantize_kv(x, cache: Cache, t_offset: int = 0):
     s = cache.struct()
     _check(_lib.tq_quantize_kv(x.data_ptr(), _dtype_code(x), B, T, H, x.stride(0), x.stride(1), x.stride(2),
                                ctypes.byref(s), t_offset, _stream_handle(x.device)), "tq_quantize_kv")
+
+
+def append_kv(k, v, kcache: Cache, vcache: Cache, t_offset: int):
+    """The key and value of one new token per (row, head): k, v [B, H_kv, 128]
+    (or [B, 1, H_kv, 128]), float32 or bfloat16, last dim contiguous, into token
+    t_offset of kcache and vcache in one call (tq_append_kv)."""
+    if k.dim() == 4:
+        k = k[:, 0]
+    if v.dim() == 4:
+        v = v[:, 0]
+    if k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[-1] != D or k.stride(-1) != 1 or v.stride(-1) != 1:
+        raise ValueError("k and v must be [B, H_kv, 128] with a contiguous last dimension")
+    if k.dtype != v.dtype:
+        raise ValueError("k and v must have the same dtype")
+    B, H, _ = k.shape
+    sk, sv = kcache.struct(), vcache.struct()
+    _check(_lib.tq_append_kv(k.data_ptr(), v.data_ptr(), _dtype_code(k), B, H, k.stride(0), k.stride(1), v.stride(0),
+                             v.stride(1), ctypes.byref(sk), ctypes.byref(sv), t_offset, _stream_handle(k.device)),
+           "tq_append_kv")
 
 
 def dequantize(cache: Cache, t0: int = 0, t1: int | None = None, out=None):

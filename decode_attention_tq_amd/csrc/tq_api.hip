@@ -172,6 +172,28 @@ extern "C" int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t
                                        (hipStream_t)hip_stream));
 }
 
+extern "C" int tq_append_kv(const void* k, const void* v, int32_t x_dtype, int64_t B, int64_t H_kv,
+                            int64_t k_stride_b, int64_t k_stride_h, int64_t v_stride_b, int64_t v_stride_h,
+                            const tq_cache* kc, const tq_cache* vc, int64_t t_offset, void* hip_stream) {
+  int st = check_cache(kc);
+  if (st != TQ_OK) return st;
+  st = check_cache(vc);
+  if (st != TQ_OK) return st;
+  if (kc->role != TQ_KEYS || vc->role != TQ_VALUES) return TQ_ERR_INVALID_ARGUMENT;
+  if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
+  if (B != kc->B || B != vc->B || H_kv != kc->H_kv || H_kv != vc->H_kv) return TQ_ERR_INVALID_ARGUMENT;
+  if (t_offset < 0 || t_offset >= kc->T_cap || t_offset >= vc->T_cap) return TQ_ERR_INVALID_ARGUMENT;
+  if (k == nullptr || v == nullptr || k_stride_b < 0 || k_stride_h < 0 || v_stride_b < 0 || v_stride_h < 0)
+    return TQ_ERR_INVALID_ARGUMENT;
+  const int64_t vec_align = 16 / (x_dtype == TQ_F32 ? 4 : 2);   // every row starts on a 16-byte boundary
+  if (!aligned16(k) || !aligned16(v) || k_stride_b % vec_align || k_stride_h % vec_align ||
+      v_stride_b % vec_align || v_stride_h % vec_align)
+    return TQ_ERR_ALIGNMENT;
+  clear_pending_error();
+  return device_status(launch_append_kv(k, v, x_dtype, B, H_kv, k_stride_b, k_stride_h, v_stride_b, v_stride_h,
+                                        kc, vc, t_offset, (hipStream_t)hip_stream));
+}
+
 extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void* hip_stream) {
   int st = check_cache(src);
   if (st != TQ_OK) return st;

@@ -687,8 +687,9 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
 // packing (a value block keeps the bits of its other tokens).
 constexpr int kAppendVecs = 1;
 
+// The append of workgroup blk (vectors blk * kAppendVecs ...) of one cache.
 template <int BITS, int ROLE, int XF32>
-__global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
+__device__ void append_vectors(const QuantArgs& a, int64_t blk) {
   constexpr int KW = 4 * BITS;          // words per key token
   constexpr int VBW = 32 * BITS;        // words per value block
   __shared__ __align__(16) float xs[kAppendVecs][kD];
@@ -697,7 +698,7 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
   const Thresholds<BITS> th = load_thresholds<BITS>(a);
   const int tid = threadIdx.x;
   const int64_t nvec = a.B * a.H_kv;
-  const int64_t v0 = (int64_t)blockIdx.x * kAppendVecs;
+  const int64_t v0 = blk * kAppendVecs;
   const float sqrt_d = sqrtf((float)kD);
 
   // this thread's half row of Pi: row i, columns 64s .. 64s+63
@@ -825,6 +826,19 @@ __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
       for (int k = 0; k < BITS; ++k) vdst[k] = (old_words[k] & ~clr[k]) | w[k];
     }
   }
+}
+
+template <int BITS, int ROLE, int XF32>
+__global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
+  append_vectors<BITS, ROLE, XF32>(a, blockIdx.x);
+}
+
+// Keys and values of the same new token in one launch: the first nk
+// workgroups append to the key cache, the rest to the value cache.
+template <int KB, int VB, int XF32>
+__global__ __launch_bounds__(256) void append_pair_kernel(QuantArgs ka, QuantArgs va, int64_t nk) {
+  if ((int64_t)blockIdx.x < nk) append_vectors<KB, TQ_KEYS, XF32>(ka, blockIdx.x);
+  else append_vectors<VB, TQ_VALUES, XF32>(va, (int64_t)blockIdx.x - nk);
 }
 
 // ------------------------------------------------------------- dequantize --
@@ -1026,9 +1040,10 @@ hipError_t dispatch_append(int role, int xf32, const QuantArgs& qa, hipStream_t 
 
 }  // namespace
 
-hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
-                           int64_t sb, int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
-                           hipStream_t stream) {
+namespace {
+
+QuantArgs quant_args(const void* x, int64_t B, int64_t T, int64_t H_kv, int64_t sb, int64_t st, int64_t sh,
+                     const tq_cache* dst, int64_t t_offset) {
   QuantArgs qa;
   qa.x = x;
   qa.sb = sb;
@@ -1056,6 +1071,35 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
   for (int i = L - 1; i < 16; ++i) qa.thr[i] = INFINITY;
   qa.thr_sym = qa.thr[L / 2 - 1] == 0.0f;
   for (int k = 0; k < L / 2 - 1; ++k) qa.thr_sym &= qa.thr[L - 2 - k] == -qa.thr[k];
+  return qa;
+}
+
+template <int KB, int VB>
+hipError_t launch_append_pair(int xf32, const QuantArgs& ka, const QuantArgs& va, hipStream_t stream) {
+  const int64_t nk = (ka.B * ka.H_kv + kAppendVecs - 1) / kAppendVecs;
+  const int64_t nv = (va.B * va.H_kv + kAppendVecs - 1) / kAppendVecs;
+  if (xf32)
+    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 1>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk);
+  else
+    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 0>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk);
+  return hipGetLastError();
+}
+
+template <int KB>
+hipError_t dispatch_pair(int vbits, int xf32, const QuantArgs& ka, const QuantArgs& va, hipStream_t s) {
+  switch (vbits) {
+    case 2: return launch_append_pair<KB, 2>(xf32, ka, va, s);
+    case 3: return launch_append_pair<KB, 3>(xf32, ka, va, s);
+    default: return launch_append_pair<KB, 4>(xf32, ka, va, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
+                           int64_t sb, int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
+                           hipStream_t stream) {
+  const QuantArgs qa = quant_args(x, B, T, H_kv, sb, st, sh, dst, t_offset);
   const int xf32 = x_dtype == TQ_F32;
   const int qjl = dst->role == TQ_KEYS && dst->qjl;
   if (T == 1 && !qjl) {
@@ -1069,6 +1113,25 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
     case 2: return dispatch_role<2>(dst->role, qjl, xf32, qa, stream);
     case 3: return dispatch_role<3>(dst->role, qjl, xf32, qa, stream);
     default: return dispatch_role<4>(dst->role, qjl, xf32, qa, stream);
+  }
+}
+
+hipError_t launch_append_kv(const void* k, const void* v, int x_dtype, int64_t B, int64_t H_kv, int64_t k_sb,
+                            int64_t k_sh, int64_t v_sb, int64_t v_sh, const tq_cache* kc, const tq_cache* vc,
+                            int64_t t_offset, hipStream_t stream) {
+  if (kc->qjl) {
+    // keys with a QJL sketch take the tiled kernel: two launches
+    const hipError_t e = launch_quantize(k, x_dtype, B, 1, H_kv, k_sb, 0, k_sh, kc, t_offset, stream);
+    if (e != hipSuccess) return e;
+    return launch_quantize(v, x_dtype, B, 1, H_kv, v_sb, 0, v_sh, vc, t_offset, stream);
+  }
+  const QuantArgs ka = quant_args(k, B, 1, H_kv, k_sb, 0, k_sh, kc, t_offset);
+  const QuantArgs va = quant_args(v, B, 1, H_kv, v_sb, 0, v_sh, vc, t_offset);
+  const int xf32 = x_dtype == TQ_F32;
+  switch (kc->bits) {
+    case 2: return dispatch_pair<2>(vc->bits, xf32, ka, va, stream);
+    case 3: return dispatch_pair<3>(vc->bits, xf32, ka, va, stream);
+    default: return dispatch_pair<4>(vc->bits, xf32, ka, va, stream);
   }
 }
 

@@ -181,6 +181,21 @@ int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t T, int64_t
                    const tq_cache* dst, int64_t t_offset, void* hip_stream);
 
 /*
+ * The key and the value of one new token per (row, head), into token position
+ * t_offset of kc and vc: the same result, byte for byte, as tq_quantize_kv of
+ * k into kc and of v into vc with T = 1 (step 1 of the method, and step 2 for
+ * QJL keys), in one launch when the keys carry no QJL sketch (two otherwise).
+ * k, v: device, element (b, h, j) at k[b*k_stride_b + h*k_stride_h + j] (and
+ *   the same for v), dtype TQ_F32 or TQ_BF16, 16-byte aligned rows.
+ * Requires kc->role == TQ_KEYS, vc->role == TQ_VALUES, B == kc->B == vc->B,
+ * H_kv == kc->H_kv == vc->H_kv, 0 <= t_offset < min(kc->T_cap, vc->T_cap).
+ * The caller owns all buffers; errors are returned before anything is launched.
+ */
+int tq_append_kv(const void* k, const void* v, int32_t x_dtype, int64_t B, int64_t H_kv,
+                 int64_t k_stride_b, int64_t k_stride_h, int64_t v_stride_b, int64_t v_stride_h,
+                 const tq_cache* kc, const tq_cache* vc, int64_t t_offset, void* hip_stream);
+
+/*
  * Reconstruct tokens t0 .. t1-1 of every (row, head):
  *   x_hat = n * Pi^T (c[code]/sqrt(d) [+ gamma*sqrt(pi/2)/d * S^T sigma]),
  * sigma_i = 2*bit_i - 1 (QJL keys). out: device float32 [B][H_kv][t1-t0][d].

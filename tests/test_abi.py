@@ -171,6 +171,29 @@ def test_quantize_validation_paths():
     assert _quant(s) == tq.ERR_INVALID_ARGUMENT
 
 
+def _append(kc, vc, k=FAKE, v=FAKE, dtype=tq.BF16, B=2, H=2, strides=(2 * 128, 128, 2 * 128, 128), t_offset=5):
+    return tq.lib().tq_append_kv(k, v, dtype, B, H, *strides, ctypes.byref(kc), ctypes.byref(vc), t_offset, None)
+
+
+def test_append_validation_paths():
+    K, V = _cache(), _cache(role=tq.VALUES)
+    assert _append(V, V) == tq.ERR_INVALID_ARGUMENT                        # roles
+    assert _append(K, K) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, _cache(role=tq.VALUES, B=3)) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, B=3) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, H=1) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, t_offset=64) == tq.ERR_INVALID_ARGUMENT           # past T_cap
+    assert _append(K, _cache(role=tq.VALUES, T_cap=8), t_offset=8) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, t_offset=-1) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, k=None) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, v=None) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, V, v=FAKE + 2) == tq.ERR_ALIGNMENT
+    assert _append(K, V, strides=(2 * 128, 100, 2 * 128, 128)) == tq.ERR_ALIGNMENT
+    assert _append(K, V, dtype=9) == tq.ERR_INVALID_ARGUMENT
+    assert _append(_cache(bits=5), V) == tq.ERR_UNSUPPORTED
+    assert _append(K, _cache(role=tq.VALUES, codes=None)) == tq.ERR_INVALID_ARGUMENT
+
+
 def test_prefill_validation_paths():
     K, V = _cache(), _cache(role=tq.VALUES)
     lib = tq.lib()

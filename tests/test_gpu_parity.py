@@ -264,6 +264,35 @@ def test_single_token_appends_match_oracle(tq, name):
     _check_against_oracle(tq, w, model, "v", vc, w.T)
 
 
+@pytest.mark.parametrize("name", ["stress70b_B2", "qwen_k4v2", "qjl_k2v3", "tiny"])
+def test_append_kv_equals_two_quantize_calls(tq, name):
+    """tq_append_kv (key and value of one token in one call) writes the same bytes
+    as two single-token tq_quantize_kv calls, at every offset of a few value
+    blocks (QJL keys take the two-launch path inside the call)."""
+    w = CASES[name].scaled(T=21)
+    T_cap = tcap(w.T)
+    log(f"append_kv {name}: B={w.B} H_kv={w.H_kv} K{w.k_bits}{'+qjl' if w.k_qjl else ''}/V{w.v_bits} {w.dtype}")
+    xk, xv = device_inputs(w, "k"), device_inputs(w, "v")
+    kc, vc = _lib_caches(tq, w, T_cap)
+    kr, vr = _lib_caches(tq, w, T_cap)
+    for cache in (kc, vc, kr, vr):
+        for name_ in ("codes", "norms", "signs", "gamma"):
+            arr = getattr(cache, name_)
+            if arr is not None:
+                arr.zero_()
+    for t in range(w.T):
+        tq.append_kv(xk[:, t], xv[:, t], kc, vc, t)
+        tq.quantize_kv(xk[:, t:t + 1], kr, t_offset=t)
+        tq.quantize_kv(xv[:, t:t + 1], vr, t_offset=t)
+    torch.cuda.synchronize()
+    for got, want in ((kc, kr), (vc, vr)):
+        for name_ in ("codes", "norms", "signs", "gamma"):
+            g, r = getattr(got, name_), getattr(want, name_)
+            if g is not None:
+                assert torch.equal(g.view(torch.int32) if g.dtype == torch.float32 else g,
+                                   r.view(torch.int32) if r.dtype == torch.float32 else r), name_
+
+
 def test_value_block_partial_write_keeps_neighbours(tq):
     """A partial value block keeps the bits of tokens outside the written range."""
     w = CASES["stress70b_B2"].scaled(T=64)
