@@ -364,7 +364,9 @@ __device__ inline uint32_t page_entry(__amdgpu_buffer_rsrc_t rt, const PageMap& 
 // (blocks are multiples of 32 tokens, steps start at multiples of 32).
 __device__ inline uint32_t step_row(const PageMap& m, int kv, int H_kv, uint32_t e, int t) {
   if (m.table == nullptr) return (uint32_t)t;
-  const uint32_t p = min(__builtin_amdgcn_readfirstlane(e), (uint32_t)(m.nblk - 1));
+  // (unsigned compare written out: a mixed-type min() resolves to the double overload)
+  const uint32_t p0 = (uint32_t)__builtin_amdgcn_readfirstlane((int)e), plast = (uint32_t)(m.nblk - 1);
+  const uint32_t p = p0 < plast ? p0 : plast;
   return ((p * (uint32_t)H_kv + (uint32_t)kv) << m.lg) + ((uint32_t)t & ((1u << m.lg) - 1u));
 }
 
