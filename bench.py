@@ -2,13 +2,14 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress70b]
 
-One step is one pass of the whole hot path for one new token per batch row:
-quantize the new token's key and value vectors of every (row, KV head) into the
-packed caches (tq_append_kv: keys and values in one launch, at t = T-1), then decode attention of all
-query heads over the T-token packed caches (tq_decode_attention). Inputs are
-resident in HBM before timing starts. Prints one JSON line on stdout.
+One step is one pass of the whole hot path for one new token per batch row, in
+one call (tq_decode_attention_append): quantize the new token's key and value
+vectors of every (row, KV head) into the packed caches at t = T-1 (one launch),
+then decode attention of all query heads over the T-token packed caches (a
+second launch). Inputs are resident in HBM before timing starts. Prints one
+JSON line on stdout.
 
-Extra fields: `roofline` (decode launch group vs the HBM peak), `cpu_baseline`
+Extra fields: `roofline` (the decode launch vs the HBM peak), `cpu_baseline`
 (the CPU oracle on a bounded sample of the same step, scaled to tokens/s),
 `quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view).
 """
@@ -72,6 +73,16 @@ def decode_bytes(w, T):
     wv = d * w.v_bits // 8 + 4
     qb = 2 if w.dtype == "bf16" else 4
     return w.B * w.H_kv * T * (wk + wv) + w.B * w.H_q * d * (qb + 4) + 2 * d * d * 4
+
+
+def append_bytes(w):
+    """Algorithmic bytes of appending one token per (row, KV head): the new key and
+    value in, the key record and norm out, the value block record read and written
+    back (its other tokens' bits kept), the value norm out."""
+    d = w.d
+    xb = 2 if w.dtype == "bf16" else 4
+    vblock = 8 * d * w.v_bits // 8
+    return w.B * w.H_kv * (2 * d * xb + d * w.k_bits // 8 + 4 + 2 * vblock + 4)
 
 
 def quantize_bytes(w, ntok, which):
@@ -207,9 +218,10 @@ def main():
     out = torch.empty((w.B, w.H_q, w.d), dtype=torch.float32, device=dev)
     ws = tq.Workspace(tq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, T, 0, w.k_qjl), dev)
 
+    # one step = one call: the new key and value of every (row, KV head) go to
+    # token T - 1 (one launch), then decode attention over T tokens
     def step(i):
-        tq.append_kv(new_k, new_v, kc, vc, T - 1)
-        tq.decode_attention(kc, vc, qs[i % len(qs)], T=T, out=out, workspace=ws)
+        tq.decode_attention_append(kc, vc, new_k, new_v, qs[i % len(qs)], T=T, out=out, workspace=ws)
 
     for i in range(args.warmup):
         step(i)
@@ -221,8 +233,9 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    # the same steps again with events around each launch, for the split between
-    # append and decode and the decode launch's duration (the roofline)
+    # the same steps again as their two launches with events around each, for
+    # the split between append and decode and the decode launch's duration (the
+    # roofline)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
             torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     for i in range(args.steps):
@@ -275,8 +288,7 @@ def main():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(50):
-            tq.append_kv(new_k, new_v, pk, pv, T - 1)
-            tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
+            tq.decode_attention_append(pk, pv, new_k, new_v, qs[i % len(qs)], T=T, out=pout, workspace=ws)
         e1.record()
         e2, e3 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e2.record()
@@ -378,13 +390,14 @@ def main():
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
                      "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)},0>"
-                                + (" (the whole tq_decode_attention call: one launch)" if n_split == 1
+                                + (" (the whole tq_decode_attention launch)" if n_split == 1
                                    else f" + combine_kernel ({n_split} context chunks)")),
                      "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
         "decode": {"us": dec_ms * 1e3, "us_median": dec_med * 1e3, "us_p10": dec_p10 * 1e3,
                    "us_p90": dec_p90 * 1e3, "us_back_to_back": dec_only_us,
                    "kv_tokens_per_s": w.B * T / (dec_ms * 1e-3),
-                   "tokens_per_s": w.B / (dec_ms * 1e-3), "append_us": app_ms * 1e3},
+                   "tokens_per_s": w.B / (dec_ms * 1e-3), "append_us": app_ms * 1e3,
+                   "append_bytes": append_bytes(w)},
         "quantize_prefill": {"ms": pre, "vectors": ntok, "GB_s": qbytes / (pre * 1e-3) / 1e9,
                              "hbm_frac": qbytes / (pre * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "rotation_TFLOP_s": qflops / (pre * 1e-3) / 1e12,

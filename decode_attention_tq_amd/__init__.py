@@ -47,7 +47,7 @@ VALUE_BLOCK = 8
 
 EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
            "tq_dequantize",
-           "tq_decode_attention", "tq_prefill_attention", "tq_decode_splits", "tq_decode_workspace_bytes",
+           "tq_decode_attention", "tq_decode_attention_append", "tq_prefill_attention", "tq_decode_splits", "tq_decode_workspace_bytes",
            "tq_prefill_workspace_bytes", "tq_status_string",
            "tq_last_hip_error")
 
@@ -79,6 +79,9 @@ def _bind(lib):
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P,
                                         _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
+    lib.tq_decode_attention_append.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _P, _I32, _I64,
+                                               _I64, _I64, _I64, _P, _I32, _I64, _P, _I64, _F, _I32, _P, _P,
+                                               ctypes.c_size_t, _P]
     lib.tq_prefill_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _I64,
                                          _P, _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
     lib.tq_prefill_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I64, _I32, _I32]
@@ -92,7 +95,7 @@ def _bind(lib):
     lib.tq_last_hip_error.argtypes = []
     lib.tq_last_hip_error.restype = ctypes.c_char_p
     for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
-                 "tq_dequantize", "tq_decode_attention",
+                 "tq_dequantize", "tq_decode_attention", "tq_decode_attention_append",
                  "tq_prefill_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -330,6 +333,42 @@ def decode_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None,
     _check(_lib.tq_decode_attention(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q,
                                     cl or None, T, scale, n_split, out.data_ptr(), workspace.ptr,
                                     workspace.nbytes, _stream_handle(q.device)), "tq_decode_attention")
+    return out
+
+
+def decode_attention_append(k: Cache, v: Cache, k_new, v_new, q, ctx_lens=None, T: int | None = None,
+                            scale: float = 0.0, n_split: int = 0, out=None, workspace: Workspace | None = None):
+    """One decode step in one launch: k_new, v_new [B, H_kv, 128] (or [B, 1, H_kv, 128])
+    go to token ctx_len[b] - 1 of the caches (ctx_len = T without ctx_lens), then
+    decode attention of q [B, H_q, 128] over tokens 0 .. ctx_len[b] - 1."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    if k_new.dim() == 4:
+        k_new = k_new[:, 0]
+    if v_new.dim() == 4:
+        v_new = v_new[:, 0]
+    if (k_new.dim() != 3 or k_new.shape != v_new.shape or k_new.shape[-1] != D or k_new.stride(-1) != 1
+            or v_new.stride(-1) != 1 or k_new.dtype != v_new.dtype):
+        raise ValueError("k_new and v_new must be [B, H_kv, 128] of one dtype with a contiguous last dimension")
+    B, H_q, _ = q.shape
+    T = k.T_cap if T is None else T
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    need = decode_workspace_bytes(B, H_q, k.H_kv, T, n_split, k.qjl)
+    if workspace is None or workspace.nbytes < need:
+        workspace = Workspace(need, q.device)
+    sk, sv = k.struct(), v.struct()
+    cl = 0
+    if ctx_lens is not None:
+        if ctx_lens.dtype != torch.int32 or not ctx_lens.is_contiguous() or ctx_lens.numel() != B:
+            raise ValueError("ctx_lens must be a contiguous int32 tensor of B entries")
+        cl = ctx_lens.data_ptr()
+    _check(_lib.tq_decode_attention_append(ctypes.byref(sk), ctypes.byref(sv), k_new.data_ptr(), v_new.data_ptr(),
+                                           _dtype_code(k_new), k_new.stride(0), k_new.stride(1), v_new.stride(0),
+                                           v_new.stride(1), q.data_ptr(), _dtype_code(q), H_q, cl or None, T, scale,
+                                           n_split, out.data_ptr(), workspace.ptr, workspace.nbytes,
+                                           _stream_handle(q.device)), "tq_decode_attention_append")
     return out
 
 

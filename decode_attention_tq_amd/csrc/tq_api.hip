@@ -210,7 +210,7 @@ namespace {
 // Shared validation and launch of decode (M = 1) and chunked causal attention.
 int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype, int64_t H_q, int64_t M,
                    const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split, float* out, void* workspace,
-                   size_t workspace_bytes, void* hip_stream) {
+                   size_t workspace_bytes, void* hip_stream, const DecodeAppend* app = nullptr) {
   int st = check_cache(k);
   if (st != TQ_OK) return st;
   st = check_cache(v);
@@ -230,6 +230,26 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   if (workspace == nullptr || workspace_bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
   if (((uintptr_t)workspace & 255u) != 0) return TQ_ERR_ALIGNMENT;
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
+  if (app != nullptr) {
+    if (app->x_dtype != TQ_F32 && app->x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
+    if (app->k == nullptr || app->v == nullptr || app->k_sb < 0 || app->k_sh < 0 || app->v_sb < 0 || app->v_sh < 0)
+      return TQ_ERR_INVALID_ARGUMENT;
+    const int64_t vec_align = 16 / (app->x_dtype == TQ_F32 ? 4 : 2);
+    if (!aligned16(app->k) || !aligned16(app->v) || app->k_sb % vec_align || app->k_sh % vec_align ||
+        app->v_sb % vec_align || app->v_sh % vec_align)
+      return TQ_ERR_ALIGNMENT;
+    // keys with a QJL sketch take the tiled quantize kernel, which writes one
+    // position for all rows
+    if (k->qjl && ctx_lens != nullptr) return TQ_ERR_UNSUPPORTED;
+    clear_pending_error();
+    if (ctx_lens != nullptr || T > 0) {
+      const hipError_t e = launch_append_kv(app->k, app->v, app->x_dtype, k->B, k->H_kv, app->k_sb, app->k_sh,
+                                            app->v_sb, app->v_sh, k, v, T - 1, (hipStream_t)hip_stream, ctx_lens, T);
+      if (e != hipSuccess) return device_status(e);
+    }
+    return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
+                                       (hipStream_t)hip_stream));
+  }
   clear_pending_error();
   return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                      (hipStream_t)hip_stream));
@@ -243,6 +263,24 @@ extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const v
                                    void* hip_stream) {
   return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
                         hip_stream);
+}
+
+extern "C" int tq_decode_attention_append(const tq_cache* k, const tq_cache* v, const void* k_new, const void* v_new,
+                                          int32_t new_dtype, int64_t k_stride_b, int64_t k_stride_h,
+                                          int64_t v_stride_b, int64_t v_stride_h, const void* q, int32_t q_dtype,
+                                          int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
+                                          int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
+                                          void* hip_stream) {
+  DecodeAppend app;
+  app.k = k_new;
+  app.v = v_new;
+  app.x_dtype = new_dtype;
+  app.k_sb = k_stride_b;
+  app.k_sh = k_stride_h;
+  app.v_sb = v_stride_b;
+  app.v_sh = v_stride_h;
+  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
+                        hip_stream, &app);
 }
 
 extern "C" int tq_prefill_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,

@@ -1,6 +1,6 @@
-// Scalar-quantization helpers shared by the quantize kernels and the decode
-// kernel's fused append of a new token: the Lloyd-Max cell search over a
-// codebook's thresholds and the LSB-first packing of 32 codes.
+// Scalar-quantization helpers shared by the quantize kernels: the Lloyd-Max
+// cell search over a codebook's thresholds and the LSB-first packing of 32
+// codes.
 #pragma once
 
 #include <hip/hip_runtime.h>

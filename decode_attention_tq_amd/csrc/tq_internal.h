@@ -69,10 +69,21 @@ void thresholds_from_centroids(const float* c, int levels, float* t);
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
                            int64_t sb, int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
                            hipStream_t stream);
+// (ctx_lens != NULL: row b's token goes to clamp(ctx_lens[b], 0, T) - 1, none
+// for an empty row; no QJL keys then)
 hipError_t launch_append_kv(const void* k, const void* v, int x_dtype, int64_t B, int64_t H_kv, int64_t k_sb,
                             int64_t k_sh, int64_t v_sb, int64_t v_sh, const tq_cache* kc, const tq_cache* vc,
-                            int64_t t_offset, hipStream_t stream);
+                            int64_t t_offset, hipStream_t stream, const int32_t* ctx_lens = nullptr,
+                            int64_t T = 0);
 hipError_t launch_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, hipStream_t stream);
+// New key and value vectors of a decode step: element (b, h, j) at
+// k[b*k_sb + h*k_sh + j] (and the same for v).
+struct DecodeAppend {
+  const void* k;
+  const void* v;
+  int x_dtype;
+  int64_t k_sb, k_sh, v_sb, v_sh;
+};
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
                          hipStream_t stream);

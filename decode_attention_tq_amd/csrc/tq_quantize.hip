@@ -28,6 +28,7 @@
 
 #include <atomic>
 
+#include "tq_append.h"
 #include "tq_codec.h"
 #include "tq_device.h"
 #include "tq_internal.h"
@@ -35,48 +36,6 @@
 namespace tq {
 
 namespace {
-
-struct QuantArgs {
-  const void* x;
-  int64_t sb, st, sh;          // element strides of x
-  int64_t B, T, H_kv, T_cap;
-  int64_t t_offset, t_base;    // t_base = floor8(t_offset)
-  int64_t nslot;               // slots per head (multiple of 8)
-  int64_t n_tiles;
-  uint32_t* codes;
-  float* norms;
-  uint32_t* signs;
-  float* gamma;
-  const float* rot;
-  const float* proj;
-  float cent[16];
-  float thr[16];
-  int thr_sym;   // the thresholds mirror around 0 (middle one is 0)
-  PageMap pm;    // block table of a paged cache (pm.table == nullptr: contiguous)
-};
-
-// Token row of (row*H_kv + head, token) in a cache's arrays: contiguous, or
-// through the block table. -1 when the table maps the token's block outside
-// the arrays (such a write is skipped: the table is the caller's).
-__device__ inline int64_t tok_row(const PageMap& pm, int64_t H_kv, int64_t T_cap, int64_t bh, int64_t t) {
-  if (pm.table == nullptr) return bh * T_cap + t;
-  const uint32_t hk = (uint32_t)H_kv;
-  const uint32_t b = (uint32_t)bh / hk, h = (uint32_t)bh - b * hk;   // B, H_kv < 2^16
-  const int64_t blk = t >> pm.lg;
-  if (blk < 0 || blk >= pm.maxblk) return -1;
-  const int32_t p = pm.table[(int64_t)b * pm.maxblk + blk];
-  if (p < 0 || p >= pm.nblk) return -1;
-  return (((int64_t)p * H_kv + h) << pm.lg) + (t & ((int64_t(1) << pm.lg) - 1));
-}
-
-template <int BITS>
-__device__ inline Thresholds<BITS> load_thresholds(const QuantArgs& a) {
-  Thresholds<BITS> th;
-#pragma unroll
-  for (int i = 0; i < (1 << BITS) - 1; ++i) th.t[i] = a.thr[i];
-  th.sym = a.thr_sym != 0;
-  return th;
-}
 
 // (row * H_kv + head, token) of slot s0 + v, for a wave-uniform first slot s0
 // of a wavefront's tile and a small lane offset v: the 64-bit division runs
@@ -687,158 +646,50 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
 // packing (a value block keeps the bits of its other tokens).
 constexpr int kAppendVecs = 1;
 
-// The append of workgroup blk (vectors blk * kAppendVecs ...) of one cache.
+// The append of workgroup blk (vector blk = row * H_kv + head) of one cache,
+// at token t (t < 0: nothing).
 template <int BITS, int ROLE, int XF32>
-__device__ void append_vectors(const QuantArgs& a, int64_t blk) {
-  constexpr int KW = 4 * BITS;          // words per key token
-  constexpr int VBW = 32 * BITS;        // words per value block
-  __shared__ __align__(16) float xs[kAppendVecs][kD];
-  __shared__ __align__(16) unsigned char cb[kAppendVecs][kD];
-  __shared__ float fzs[kAppendVecs];
-  const Thresholds<BITS> th = load_thresholds<BITS>(a);
-  const int tid = threadIdx.x;
-  const int64_t nvec = a.B * a.H_kv;
-  const int64_t v0 = blk * kAppendVecs;
-  const float sqrt_d = sqrtf((float)kD);
-
-  // this thread's half row of Pi: row i, columns 64s .. 64s+63
-  const int i = tid >> 1, s = tid & 1;
-  float4 pr[16];
-#pragma unroll
-  for (int k = 0; k < 16; ++k) pr[k] = ((const float4*)(a.rot + i * kD + 64 * s))[k];
-  // values: thread (v, cg) rewrites BITS words of its block record (coordinates
-  // 4cg .. 4cg+3 of the block's 8 tokens); the old words are read now, in
-  // flight during the rotation
-  uint32_t old_words[ROLE == TQ_VALUES ? BITS : 1];
-  uint32_t* vdst = nullptr;
-  if constexpr (ROLE == TQ_VALUES) {
-    const int v = tid >> 5, cg = tid & 31;
-    const int64_t gv = v0 + v;
-    const int64_t row = (v < kAppendVecs && gv < nvec) ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset & ~(int64_t)7)
-                                                       : -1;
-    if (row >= 0) {
-      vdst = a.codes + row * (VBW / 8) + cg * BITS;
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) old_words[k] = vdst[k];
-    }
-  }
-
-  {
-    // thread (v, c4): coordinates 4c4 .. 4c4+3 of vector v
-    const int v = min(tid >> 5, kAppendVecs - 1), c4 = tid & 31;
-    const int64_t gv = v0 + v;
-    const bool act = (tid >> 5) < kAppendVecs;   // (threads past the vectors only join the shuffles)
-    const bool ok = act && gv < nvec;
-    const int64_t b = gv / a.H_kv, h = gv % a.H_kv;
-    float x[4] = {0.f, 0.f, 0.f, 0.f};
-    if (ok) {
-      const int64_t off = b * a.sb + h * a.sh + 4 * c4;
-      if constexpr (XF32) {
-        const float4 f = *(const float4*)((const float*)a.x + off);
-        x[0] = f.x; x[1] = f.y; x[2] = f.z; x[3] = f.w;
-      } else {
-        const uint2 u = *(const uint2*)((const uint16_t*)a.x + off);
-        x[0] = __uint_as_float(u.x << 16); x[1] = __uint_as_float(u.x & 0xFFFF0000u);
-        x[2] = __uint_as_float(u.y << 16); x[3] = __uint_as_float(u.y & 0xFFFF0000u);
-      }
-    }
-    float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) mx = fmaxf(mx, __shfl_xor(mx, m));
-    const int sexp = (mx > 0.f) ? 14 - __builtin_amdgcn_frexp_expf(mx) : 0;
-    float ss = 0.f;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      x[u] = ldexpf(x[u], sexp);
-      ss = fmaf(x[u], x[u], ss);
-    }
-#pragma unroll
-    for (int m = 1; m < 32; m <<= 1) ss += __shfl_xor(ss, m);
-    const float ns = sqrtf(ss);   // |x| * 2^sexp
-    if (act) *(float4*)&xs[v][4 * c4] = make_float4(x[0], x[1], x[2], x[3]);
-    if (act && c4 == 0) {
-      fzs[v] = ns > 0.f ? sqrt_d / ns : 0.f;
-      const int64_t row = ok ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset) : -1;
-      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
-    }
-  }
+__device__ void append_vectors(const QuantArgs& a, int64_t blk, int64_t t) {
+  if (t < 0) return;   // (workgroup-uniform)
+  static_assert(kAppendVecs == 1, "one vector per workgroup");
+  __shared__ __align__(16) float xs[kD];
+  __shared__ __align__(16) unsigned char cb[kD];
+  __shared__ float fz[2];
+  const int lt = threadIdx.x;
+  AppendOne<BITS, ROLE> ap;
+  PiHalfRow pr;
+  float x[4];
+  load_pi_half_row(a.rot, lt, pr);
+  ap.load_old(a, blk, t, lt);
+  AppendOne<BITS, ROLE>::load_x(a, blk, lt, XF32 != 0, x);
+  ap.begin(a, blk, t, lt, x, xs, fz);
   __syncthreads();
-
-  // y_i = sum_j Pi[i][j] x_j for the 8 vectors; the two halves of a row sit in
-  // adjacent lanes
-#pragma unroll
-  for (int v = 0; v < kAppendVecs; ++v) {
-    const float4* xv = (const float4*)&xs[v][64 * s];
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float4 q = xv[k];
-      acc = fmaf(pr[k].w, q.w, fmaf(pr[k].z, q.z, fmaf(pr[k].y, q.y, fmaf(pr[k].x, q.x, acc))));
-    }
-    acc += __shfl_xor(acc, 1);
-    if (s == (v & 1)) cb[v][i] = (unsigned char)encode<BITS>(acc * fzs[v], th);
-  }
+  ap.rotate(a, lt, pr, xs, fz, cb);
   __syncthreads();
-
-  if constexpr (ROLE == TQ_KEYS) {
-    if (tid < 4 * kAppendVecs) {
-      const int v = tid >> 2, grp = tid & 3;
-      const int64_t gv = v0 + v;
-      const int64_t row = gv < nvec ? tok_row(a.pm, a.H_kv, a.T_cap, gv, a.t_offset) : -1;
-      if (row >= 0) {
-        uint32_t q[8];
-#pragma unroll
-        for (int k = 0; k < 8; ++k) q[k] = *(const uint32_t*)&cb[v][32 * grp + 4 * k];
-        uint32_t w[BITS];
-        pack32<BITS>(q, w);
-        uint32_t* dst = a.codes + row * KW + grp * BITS;
-#pragma unroll
-        for (int k = 0; k < BITS; ++k) dst[k] = w[k];
-      }
-    }
-  } else {
-    // thread (v, cg): the BITS words of the block record that hold coordinates
-    // 4cg .. 4cg+3 of all 8 tokens; only the new token's bits change
-    const int v = tid >> 5, cg = tid & 31;
-    if (vdst != nullptr) {
-      const int ti = (int)(a.t_offset & 7);
-      uint32_t w[BITS], clr[BITS];
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) {
-        w[k] = 0u;
-        clr[k] = 0u;
-      }
-      const uint32_t q4 = *(const uint32_t*)&cb[v][4 * cg];
-      constexpr uint32_t fm = (1u << BITS) - 1u;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const uint32_t code = (q4 >> (8 * jj)) & 0xFFu;
-        const int pos = BITS * (8 * jj + ti);
-        const int wi = pos >> 5, off = pos & 31;
-        w[wi] |= code << off;
-        clr[wi] |= fm << off;
-        if (off + BITS > 32) {
-          w[wi + 1] |= code >> (32 - off);
-          clr[wi + 1] |= fm >> (32 - off);
-        }
-      }
-#pragma unroll
-      for (int k = 0; k < BITS; ++k) vdst[k] = (old_words[k] & ~clr[k]) | w[k];
-    }
-  }
+  ap.finish(a, blk, t, lt, fz, cb);
 }
 
 template <int BITS, int ROLE, int XF32>
 __global__ __launch_bounds__(256) void append_kernel(QuantArgs a) {
-  append_vectors<BITS, ROLE, XF32>(a, blockIdx.x);
+  append_vectors<BITS, ROLE, XF32>(a, blockIdx.x, a.t_offset);
 }
 
 // Keys and values of the same new token in one launch: the first nk
-// workgroups append to the key cache, the rest to the value cache.
+// workgroups append to the key cache, the rest to the value cache. With
+// context lengths, row b's token goes to clamp(ctx_lens[b], 0, T) - 1 (none
+// for an empty row), else to t_offset.
 template <int KB, int VB, int XF32>
-__global__ __launch_bounds__(256) void append_pair_kernel(QuantArgs ka, QuantArgs va, int64_t nk) {
-  if ((int64_t)blockIdx.x < nk) append_vectors<KB, TQ_KEYS, XF32>(ka, blockIdx.x);
-  else append_vectors<VB, TQ_VALUES, XF32>(va, (int64_t)blockIdx.x - nk);
+__global__ __launch_bounds__(256) void append_pair_kernel(QuantArgs ka, QuantArgs va, int64_t nk,
+                                                          const int32_t* ctx_lens, int64_t T) {
+  const bool key = (int64_t)blockIdx.x < nk;
+  const int64_t blk = key ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - nk;
+  int64_t t = ka.t_offset;
+  if (ctx_lens != nullptr) {
+    const int64_t c = ctx_lens[blk / ka.H_kv];
+    t = (c < 0 ? 0 : (c > T ? T : c)) - 1;
+  }
+  if (key) append_vectors<KB, TQ_KEYS, XF32>(ka, blk, t);
+  else append_vectors<VB, TQ_VALUES, XF32>(va, blk, t);
 }
 
 // ------------------------------------------------------------- dequantize --
@@ -1040,10 +891,8 @@ hipError_t dispatch_append(int role, int xf32, const QuantArgs& qa, hipStream_t 
 
 }  // namespace
 
-namespace {
-
-QuantArgs quant_args(const void* x, int64_t B, int64_t T, int64_t H_kv, int64_t sb, int64_t st, int64_t sh,
-                     const tq_cache* dst, int64_t t_offset) {
+QuantArgs make_quant_args(const void* x, int64_t B, int64_t T, int64_t H_kv, int64_t sb, int64_t st, int64_t sh,
+                          const tq_cache* dst, int64_t t_offset) {
   QuantArgs qa;
   qa.x = x;
   qa.sb = sb;
@@ -1074,23 +923,29 @@ QuantArgs quant_args(const void* x, int64_t B, int64_t T, int64_t H_kv, int64_t 
   return qa;
 }
 
+namespace {
+
 template <int KB, int VB>
-hipError_t launch_append_pair(int xf32, const QuantArgs& ka, const QuantArgs& va, hipStream_t stream) {
+hipError_t launch_append_pair(int xf32, const QuantArgs& ka, const QuantArgs& va, const int32_t* ctx_lens,
+                              int64_t T, hipStream_t stream) {
   const int64_t nk = (ka.B * ka.H_kv + kAppendVecs - 1) / kAppendVecs;
   const int64_t nv = (va.B * va.H_kv + kAppendVecs - 1) / kAppendVecs;
   if (xf32)
-    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 1>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk);
+    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 1>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk,
+                       ctx_lens, T);
   else
-    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 0>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk);
+    hipLaunchKernelGGL((append_pair_kernel<KB, VB, 0>), dim3((unsigned)(nk + nv)), dim3(256), 0, stream, ka, va, nk,
+                       ctx_lens, T);
   return hipGetLastError();
 }
 
 template <int KB>
-hipError_t dispatch_pair(int vbits, int xf32, const QuantArgs& ka, const QuantArgs& va, hipStream_t s) {
+hipError_t dispatch_pair(int vbits, int xf32, const QuantArgs& ka, const QuantArgs& va, const int32_t* ctx_lens,
+                         int64_t T, hipStream_t s) {
   switch (vbits) {
-    case 2: return launch_append_pair<KB, 2>(xf32, ka, va, s);
-    case 3: return launch_append_pair<KB, 3>(xf32, ka, va, s);
-    default: return launch_append_pair<KB, 4>(xf32, ka, va, s);
+    case 2: return launch_append_pair<KB, 2>(xf32, ka, va, ctx_lens, T, s);
+    case 3: return launch_append_pair<KB, 3>(xf32, ka, va, ctx_lens, T, s);
+    default: return launch_append_pair<KB, 4>(xf32, ka, va, ctx_lens, T, s);
   }
 }
 
@@ -1099,7 +954,7 @@ hipError_t dispatch_pair(int vbits, int xf32, const QuantArgs& ka, const QuantAr
 hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv,
                            int64_t sb, int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
                            hipStream_t stream) {
-  const QuantArgs qa = quant_args(x, B, T, H_kv, sb, st, sh, dst, t_offset);
+  const QuantArgs qa = make_quant_args(x, B, T, H_kv, sb, st, sh, dst, t_offset);
   const int xf32 = x_dtype == TQ_F32;
   const int qjl = dst->role == TQ_KEYS && dst->qjl;
   if (T == 1 && !qjl) {
@@ -1118,20 +973,21 @@ hipError_t launch_quantize(const void* x, int x_dtype, int64_t B, int64_t T, int
 
 hipError_t launch_append_kv(const void* k, const void* v, int x_dtype, int64_t B, int64_t H_kv, int64_t k_sb,
                             int64_t k_sh, int64_t v_sb, int64_t v_sh, const tq_cache* kc, const tq_cache* vc,
-                            int64_t t_offset, hipStream_t stream) {
+                            int64_t t_offset, hipStream_t stream, const int32_t* ctx_lens, int64_t T) {
   if (kc->qjl) {
+    // (the caller passes no context lengths with QJL keys)
     // keys with a QJL sketch take the tiled kernel: two launches
     const hipError_t e = launch_quantize(k, x_dtype, B, 1, H_kv, k_sb, 0, k_sh, kc, t_offset, stream);
     if (e != hipSuccess) return e;
     return launch_quantize(v, x_dtype, B, 1, H_kv, v_sb, 0, v_sh, vc, t_offset, stream);
   }
-  const QuantArgs ka = quant_args(k, B, 1, H_kv, k_sb, 0, k_sh, kc, t_offset);
-  const QuantArgs va = quant_args(v, B, 1, H_kv, v_sb, 0, v_sh, vc, t_offset);
+  const QuantArgs ka = make_quant_args(k, B, 1, H_kv, k_sb, 0, k_sh, kc, t_offset);
+  const QuantArgs va = make_quant_args(v, B, 1, H_kv, v_sb, 0, v_sh, vc, t_offset);
   const int xf32 = x_dtype == TQ_F32;
   switch (kc->bits) {
-    case 2: return dispatch_pair<2>(vc->bits, xf32, ka, va, stream);
-    case 3: return dispatch_pair<3>(vc->bits, xf32, ka, va, stream);
-    default: return dispatch_pair<4>(vc->bits, xf32, ka, va, stream);
+    case 2: return dispatch_pair<2>(vc->bits, xf32, ka, va, ctx_lens, T, stream);
+    case 3: return dispatch_pair<3>(vc->bits, xf32, ka, va, ctx_lens, T, stream);
+    default: return dispatch_pair<4>(vc->bits, xf32, ka, va, ctx_lens, T, stream);
   }
 }
 

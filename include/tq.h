@@ -229,6 +229,29 @@ int tq_decode_attention(const tq_cache* k, const tq_cache* v,
                         float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
 
 /*
+ * One decode step in one call: for every row b with context length
+ * ctx_b = clamp(ctx_lens[b], 0, T) (or T) >= 1, the new key and value of each
+ * KV head are written to token ctx_b - 1 of k and v (the same bytes as
+ * tq_quantize_kv / tq_append_kv at that position, one launch for keys and
+ * values), then out is tq_decode_attention over tokens 0 .. ctx_b - 1, which
+ * include the new one (a second launch, ordered after the first on the
+ * stream). Rows with ctx_b = 0 get no write and a zero output.
+ *   k_new, v_new: device, element (b, h, j) at k_new[b*k_stride_b + h*k_stride_h + j]
+ *                 (and the same for v_new), dtype new_dtype (TQ_F32 or TQ_BF16),
+ *                 16-byte aligned rows
+ * Other arguments and requirements as tq_decode_attention. Keys with a QJL
+ * sketch are appended by the tiled quantize kernel, which needs ctx_lens ==
+ * NULL (TQ_ERR_UNSUPPORTED otherwise). The caller owns all buffers; argument
+ * errors return before any launch.
+ */
+int tq_decode_attention_append(const tq_cache* k, const tq_cache* v, const void* k_new, const void* v_new,
+                               int32_t new_dtype, int64_t k_stride_b, int64_t k_stride_h,
+                               int64_t v_stride_b, int64_t v_stride_h, const void* q, int32_t q_dtype,
+                               int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
+                               int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
+                               void* hip_stream);
+
+/*
  * Chunked prefill / multi-query attention over the packed caches: M new
  * tokens per row, whose keys and values are already in the caches (appended
  * with tq_quantize_kv), attend causally to the row's context. Token i of row b

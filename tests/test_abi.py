@@ -194,6 +194,30 @@ def test_append_validation_paths():
     assert _append(K, _cache(role=tq.VALUES, codes=None)) == tq.ERR_INVALID_ARGUMENT
 
 
+def _fused(K, V, kn=FAKE, vn=FAKE, ndt=tq.BF16, strides=(2 * 128, 128, 2 * 128, 128), q=FAKE, H_q=4, ctx=None,
+           T=64, ws=FAKE, wsb=1 << 20):
+    return tq.lib().tq_decode_attention_append(ctypes.byref(K), ctypes.byref(V), kn, vn, ndt, *strides, q, tq.BF16,
+                                               H_q, ctx, T, 0.0, 0, FAKE, ws, wsb, None)
+
+
+def test_decode_append_validation_paths():
+    K, V = _cache(), _cache(role=tq.VALUES)
+    assert _fused(V, K) == tq.ERR_INVALID_ARGUMENT                       # roles
+    assert _fused(K, V, kn=None) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, vn=None) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, ndt=9) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, kn=FAKE + 2) == tq.ERR_ALIGNMENT
+    assert _fused(K, V, strides=(2 * 128, 100, 2 * 128, 128)) == tq.ERR_ALIGNMENT
+    assert _fused(K, V, strides=(-1, 128, 2 * 128, 128)) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, T=65) == tq.ERR_INVALID_ARGUMENT                 # past T_cap
+    assert _fused(K, V, q=None) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, H_q=3) == tq.ERR_INVALID_ARGUMENT
+    assert _fused(K, V, wsb=0) == tq.ERR_WORKSPACE_TOO_SMALL
+    # QJL keys with ragged contexts: the separate append launch needs one position
+    KQ = _cache(qjl=1)
+    assert _fused(KQ, V, ctx=FAKE) == tq.ERR_UNSUPPORTED
+
+
 def test_prefill_validation_paths():
     K, V = _cache(), _cache(role=tq.VALUES)
     lib = tq.lib()
