@@ -93,6 +93,15 @@ def quantize_bytes(w, ntok, which):
     return w.B * w.H_kv * ntok * (d * inb + d * bits // 8 + 4 + extra)
 
 
+def copy_cache(tq, c):
+    """A second contiguous cache holding the same packed layer."""
+    d = tq.Cache(c.role, c.bits, c.B, c.H_kv, c.T_cap, device=c.device, qjl=bool(c.qjl))
+    for x, y in ((d.codes, c.codes), (d.norms, c.norms), (d.signs, c.signs), (d.gamma, c.gamma)):
+        if x is not None:
+            x.copy_(y)
+    return d
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU oracle, as it stands, on (row, KV head) slices of the same step:
     unpack the slice's packed key and value caches, quantize one new token of
@@ -319,22 +328,27 @@ def main():
         fq = tq_synth.torch_queries(fw, dev)
         fws = tq.Workspace(tq.decode_workspace_bytes(fw.B, fw.H_q, fw.H_kv, fw.T, 0, fw.k_qjl), dev)
         fo = torch.empty((fw.B, fw.H_q, fw.d), dtype=torch.float32, device=dev)
-        for _ in range(5):
-            tq.decode_attention(fk, fv, fq, T=fw.T, out=fo, workspace=fws)
+        fb = decode_bytes(fw, fw.T)
+        # copies of the layer, so that one sweep over them (>= 1 GiB) cannot be
+        # served from the 256 MB last-level cache: calls cycle through them
+        n_layers = max(1, min(64, -(-(1 << 30) // fb)))
+        layers = [(fk, fv)] + [(copy_cache(tq, fk), copy_cache(tq, fv)) for _ in range(n_layers - 1)]
+        for i in range(5):
+            tq.decode_attention(*layers[i % n_layers], fq, T=fw.T, out=fo, workspace=fws)
+        n_calls = max(50, 2 * n_layers)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
-        for _ in range(50):
-            tq.decode_attention(fk, fv, fq, T=fw.T, out=fo, workspace=fws)
+        for i in range(n_calls):
+            tq.decode_attention(*layers[i % n_layers], fq, T=fw.T, out=fo, workspace=fws)
         e1.record()
         torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) / 50 * 1e3
-        fb = decode_bytes(fw, fw.T)
+        us = e0.elapsed_time(e1) / n_calls * 1e3
         formats[name] = {"B": fw.B, "H_q": fw.H_q, "H_kv": fw.H_kv, "T": fw.T, "k_bits": fw.k_bits,
                          "v_bits": fw.v_bits, "k_qjl": fw.k_qjl,
-                         "n_split": tq.decode_splits(fw.B, fw.H_kv, fw.T), "decode_us": us,
+                         "n_split": tq.decode_splits(fw.B, fw.H_kv, fw.T), "layers_cycled": n_layers, "decode_us": us,
                          "bytes": fb, "GB_s": fb / (us * 1e-6) / 1e9, "frac": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] {name}: decode {us:.1f} us, {fb / (us * 1e-6) / 1e9:.0f} GB/s")
-        del fk, fv, fws
+        del fk, fv, fws, layers
         torch.cuda.empty_cache()
 
     # chunked causal (prefill) attention of the M newest tokens of every row over
