@@ -16,36 +16,38 @@ struct Thresholds {
   bool sym;   // t[L-2-k] == -t[k] and the middle one is 0
 };
 
-// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i.
-// For a codebook that mirrors around 0 (the canonical one), the search runs on
-// |z| over the positive half and a negative z takes the mirrored cell
-// (2^bits - 1 - cell of |z|); an exact tie with a threshold may then land in
-// the neighbouring cell, which is the decision boundary itself. Otherwise a
-// branch-free binary search over all thresholds.
+// Symmetric codebook: the search on |z| over the positive half.
 template <int BITS>
-__device__ inline int encode(float z, const Thresholds<BITS>& th) {
+__device__ inline int encode_sym(float z, const Thresholds<BITS>& th) {
   constexpr int half = 1 << (BITS - 1);
-  const float* t = th.t;
-  if (th.sym) {
-    const float* p = t + half;   // positive thresholds
-    const float x = fabsf(z);
-    int n;
-    if constexpr (BITS == 2) {
-      n = x >= p[0];
-    } else if constexpr (BITS == 3) {
-      const bool b1 = x >= p[1];
-      const bool b0 = x >= (b1 ? p[2] : p[0]);
-      n = (b1 << 1) | b0;
-    } else {
-      const bool b2 = x >= p[3];
-      const bool b1 = x >= (b2 ? p[5] : p[1]);
-      const float tc = b2 ? (b1 ? p[6] : p[4]) : (b1 ? p[2] : p[0]);
-      const bool b0 = x >= tc;
-      n = (b2 << 2) | (b1 << 1) | b0;
-    }
-    return (half + n) ^ (z < 0.f ? 2 * half - 1 : 0);
+  const float* p = th.t + half;   // positive thresholds
+  const float x = fabsf(z);
+  int n;
+  if constexpr (BITS == 1) {
+    n = 0;
+  } else if constexpr (BITS == 2) {
+    n = x >= p[0];
+  } else if constexpr (BITS == 3) {
+    const bool b1 = x >= p[1];
+    const bool b0 = x >= (b1 ? p[2] : p[0]);
+    n = (b1 << 1) | b0;
+  } else {
+    const bool b2 = x >= p[3];
+    const bool b1 = x >= (b2 ? p[5] : p[1]);
+    const float tc = b2 ? (b1 ? p[6] : p[4]) : (b1 ? p[2] : p[0]);
+    const bool b0 = x >= tc;
+    n = (b2 << 2) | (b1 << 1) | b0;
   }
-  if constexpr (BITS == 2) {
+  return (half + n) ^ (z < 0.f ? 2 * half - 1 : 0);
+}
+
+// Any ascending thresholds: branch-free binary search.
+template <int BITS>
+__device__ inline int encode_any(float z, const Thresholds<BITS>& th) {
+  const float* t = th.t;
+  if constexpr (BITS == 1) {
+    return z >= t[0];
+  } else if constexpr (BITS == 2) {
     const bool b1 = z >= t[1];
     const bool b0 = z >= (b1 ? t[2] : t[0]);
     return (b1 << 1) | b0;
@@ -65,6 +67,20 @@ __device__ inline int encode(float z, const Thresholds<BITS>& th) {
     const bool b0 = z >= t0;
     return (b3 << 3) | (b2 << 2) | (b1 << 1) | b0;
   }
+}
+
+// Lloyd-Max cell index: number of thresholds t_i (ascending) with z >= t_i.
+// For a codebook that mirrors around 0 (the canonical one), the search runs on
+// |z| over the positive half and a negative z takes the mirrored cell
+// (2^bits - 1 - cell of |z|); an exact tie with a threshold may then land in
+// the neighbouring cell, which is the decision boundary itself. Otherwise a
+// branch-free binary search over all thresholds. SYM = 1 or 0 fixes the case
+// at compile time (the caller tested th.sym once for many codes); -1 tests it.
+template <int BITS, int SYM = -1>
+__device__ inline int encode(float z, const Thresholds<BITS>& th) {
+  if constexpr (SYM == 1) return encode_sym<BITS>(z, th);
+  else if constexpr (SYM == 0) return encode_any<BITS>(z, th);
+  else return th.sym ? encode_sym<BITS>(z, th) : encode_any<BITS>(z, th);
 }
 
 // Pack 32 codes (bytes of q[0..7], LSB first) into BITS words, stream position BITS*k.

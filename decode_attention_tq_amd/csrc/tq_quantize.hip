@@ -402,6 +402,10 @@ __global__ __launch_bounds__(64 * quant_waves<QJL>()) void quantize_kernel(Quant
 //   B[k][j]  = Pi[j][k], lane j + 32*(k/8);
 //   D[i][j]  lane j + 32*((i/4)%2), element (i%4) + 4*(i/8).
 constexpr int kQ32Waves = 16;
+template <int V>
+struct IntTag {
+  static constexpr int value = V;
+};
 constexpr int kQ32OpHalves = 8 * 4 * 64 * 8;   // one float16 pass of Pi in operand order
 // Row stride (bytes) of a wavefront's code buffer [32 vectors][128 codes]: the
 // 32 lanes that write one 4-code piece of 32 different rows hit distinct banks.
@@ -535,28 +539,37 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
     // as the A operand and x as B, lane (vi, kh) receives coordinates
     // 32jb + 8q + 4kh + r (element 4q + r) of its own vector vi, so four
     // adjacent codes leave as one 32-bit LDS write.
+    // (the codebook's symmetry is tested once per tile, so the 64 code
+    // searches of a lane are straight-line code)
+    auto rotate_encode = [&](auto sym) {
+      constexpr int SYM = decltype(sym)::value;
 #pragma unroll 1
-    for (int jb = 0; jb < 4; ++jb) {
-      floatx16 acc;
+      for (int jb = 0; jb < 4; ++jb) {
+        floatx16 acc;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) acc[e] = 0.f;
+        for (int e = 0; e < 16; ++e) acc[e] = 0.f;
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        const int o = ((ks * 4 + jb) * 64 + lane) << 3;
-        const half8 bh8 = *(const half8*)(piop + o);
-        const half8 bl8 = *(const half8*)(piop + kQ32OpHalves + o);
-        acc = mfma32(bh8, xa[ks], acc);
-        acc = mfma32(bl8, xa[ks], acc);
-        if constexpr (XF32) acc = mfma32(bh8, xl[ks], acc);
+        for (int ks = 0; ks < 8; ++ks) {
+          const int o = ((ks * 4 + jb) * 64 + lane) << 3;
+          const half8 bh8 = *(const half8*)(piop + o);
+          const half8 bl8 = *(const half8*)(piop + kQ32OpHalves + o);
+          acc = mfma32(bh8, xa[ks], acc);
+          acc = mfma32(bl8, xa[ks], acc);
+          if constexpr (XF32) acc = mfma32(bh8, xl[ks], acc);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t word = 0u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) word |= (uint32_t)encode<BITS, SYM>(acc[4 * q + r] * fz, th) << (8 * r);
+          *(uint32_t*)(cbuf + vi * kQ32Row + 32 * jb + 8 * q + 4 * kh) = word;
+        }
       }
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        uint32_t word = 0u;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) word |= (uint32_t)encode<BITS>(acc[4 * q + r] * fz, th) << (8 * r);
-        *(uint32_t*)(cbuf + vi * kQ32Row + 32 * jb + 8 * q + 4 * kh) = word;
-      }
-    }
+    };
+    if (th.sym)
+      rotate_encode(IntTag<1>{});
+    else
+      rotate_encode(IntTag<0>{});
 
     // ---- norm
     if (cur.valid && kh == 0) {
