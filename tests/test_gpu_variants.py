@@ -9,7 +9,8 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import TOL_ATTN, OracleModel, code_mismatch, device_inputs, device_queries, log, rel_l2, unpack_head
+from tqhelp import (TOL_ATTN, OracleModel, code_mismatch, device_inputs, device_queries, log, rel_l2,
+                    shifted_codebook, unpack_head)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -25,7 +26,8 @@ def tq():
     return lib
 
 
-@pytest.mark.parametrize("codebook,rotation", [("sphere", "haar"), ("gaussian", "hadamard"), ("sphere", "hadamard")])
+@pytest.mark.parametrize("codebook,rotation",
+                         [("sphere", "haar"), ("gaussian", "hadamard"), ("sphere", "hadamard"), ("shifted", "haar")])
 @pytest.mark.parametrize("name", ["stress70b_B2", "qwen_k4v2", "qjl_k2v3"])
 def test_variant_matches_oracle(tq, name, codebook, rotation):
     w = {"stress70b_B2": W["stress70b"].scaled(B=2, T=2048),
@@ -34,7 +36,7 @@ def test_variant_matches_oracle(tq, name, codebook, rotation):
     log(f"variant {name}: {codebook} codebook, {rotation} rotation")
     model = OracleModel(w, codebook=codebook, rotation=rotation)
     rot = tq.make_rotation(tq_synth.ROT_SEED, tq.HADAMARD if rotation == "hadamard" else tq.HAAR)
-    mk = tq.make_codebook_sphere if codebook == "sphere" else tq.make_codebook
+    mk = {"sphere": tq.make_codebook_sphere, "gaussian": tq.make_codebook, "shifted": shifted_codebook}[codebook]
     T_cap = (w.T + 7) // 8 * 8
     kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, rot=rot, qjl=bool(w.k_qjl), centroids=mk(w.k_bits)[0])
     vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, rot=rot, centroids=mk(w.v_bits)[0])
@@ -78,3 +80,23 @@ def test_variant_matches_oracle(tq, name, codebook, rotation):
     worst = max(rel_l2(out[b, h], ref_e2e[b, h]) for b in range(w.B) for h in range(w.H_q))
     log(f"  decode rel L2 over the output: kernel parity {kern:.2e}, end to end {e2e:.2e} (worst head {worst:.2e})")
     assert kern <= TOL_ATTN and e2e <= TOL_ATTN
+
+
+def test_shifted_codebook_bulk_kernel(tq):
+    """A codebook that does not mirror around 0 through the bulk (32-vector tile)
+    quantize kernel: 524,288 slots per cache, so every compute unit gets tiles.
+    Codes of sampled heads match the oracle outside the decision-boundary band,
+    norms to 1e-6."""
+    w = W["stress70b"].scaled(B=32, T=2048)
+    log("shifted codebook, bulk quantize: B=32 T=2048 H_kv=8, K3/V3")
+    model = OracleModel(w, codebook="shifted")
+    for which, bits, role in (("k", w.k_bits, tq.KEYS), ("v", w.v_bits, tq.VALUES)):
+        c = tq.Cache(role, bits, w.B, w.H_kv, w.T, centroids=shifted_codebook(bits)[0])
+        tq.quantize_kv(device_inputs(w, which), c)
+        codes, norms = c.codes.cpu().numpy(), c.norms.cpu().numpy()
+        thr = model.tK if which == "k" else model.tV
+        for (b, h), ref in model.heads(which, bs=[0, 13, 31], hs=[0, 7]).items():
+            _, mo, _ = code_mismatch(which, codes[b, h], ref, bits, thr, w.T)
+            assert mo == 0, (which, b, h)
+            want = ref["norm"].astype(np.float64)
+            assert np.all(np.abs(norms[b, h, : w.T] - want) <= 1e-6 * np.maximum(want, 1e-30)), (which, b, h)

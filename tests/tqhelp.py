@@ -33,6 +33,17 @@ def rel_l2(a, b) -> float:
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
 
 
+def shifted_codebook(bits: int):
+    """A codebook that does not mirror around 0: the canonical levels moved up by
+    3/16 and rounded to float16 (still ascending and float16-exact), with the
+    exact midpoints as thresholds. It takes the kernels' general code search."""
+    c, _ = ocb.canonical(bits)
+    c = np.asarray(c, dtype=np.float64) + 0.1875
+    c = c.astype(np.float16).astype(np.float64)
+    assert np.all(np.diff(c) > 0)
+    return c, (c[:-1] + c[1:]) / 2
+
+
 class OracleModel:
     """Oracle rotation, projection and codebooks of a workload."""
 
@@ -40,7 +51,12 @@ class OracleModel:
         self.w = w
         self.Pi = (orot.hadamard_rotation if rotation == "hadamard" else orot.haar_rotation)(tq_synth.ROT_SEED, D)
         self.S = orot.qjl_projection(tq_synth.QJL_SEED, D) if w.k_qjl else None
-        make = (lambda bits: ocb.canonical_sphere(bits, D)) if codebook == "sphere" else ocb.canonical
+        if codebook == "sphere":
+            make = lambda bits: ocb.canonical_sphere(bits, D)
+        elif codebook == "shifted":
+            make = shifted_codebook
+        else:
+            make = ocb.canonical
         self.cK, self.tK = make(w.k_bits)
         self.cV, self.tV = make(w.v_bits)
 
