@@ -9,6 +9,10 @@ be bitwise equal. Context lengths put the new token at the first token of a
 wavefront's share, in a masked tail step, at a chunk boundary and in a row of
 its own; rows with no context get no write and zeros. Keys with a QJL sketch
 take the tiled quantize kernel; G = 16 and float32 inputs are covered too.
+Every case also runs on paged caches (32-token blocks mapped through a seeded
+permutation), where the outputs must again be bitwise equal: context splits,
+a G = 4 ragged tail, K4/V2, QJL keys appended through the block table by the
+tiled kernel, and float32 inputs with G = 16.
 """
 import pytest
 
@@ -71,12 +75,11 @@ CASES = {
 }
 
 
-@pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("paged", [False, True])
+@pytest.mark.parametrize("name,paged", [(n, p) for p in (False, True) for n in CASES])
 def test_one_call_step_equals_two_calls(tq, name, paged):
     w, T_cap, ctx, n_split = CASES[name]
-    if paged and name not in ("stress70b_full", "stress70b_ragged"):
-        pytest.skip("paged variant on the full and ragged 70B-like cases only")
+    if paged:
+        T_cap = (T_cap + 31) // 32 * 32   # whole 32-token blocks
     log(f"one-call append + decode {name}{' paged' if paged else ''}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} "
         f"K{w.k_bits}/V{w.v_bits} ctx {ctx or [w.T] * w.B} n_split={n_split}")
     xk, xv = device_inputs(w, "k"), device_inputs(w, "v")

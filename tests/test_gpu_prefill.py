@@ -12,7 +12,7 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import TOL_ATTN, TOL_RECUT, OracleModel, device_inputs, log, rel_l2, unpack_head
+from tqhelp import TOL_ATTN, TOL_RECUT, OracleModel, assert_heads, device_inputs, log, rel_l2, unpack_head
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -91,7 +91,9 @@ def test_prefill_matches_oracle(tq, name):
             ref_kern[b, :, hs] = oa.attend_chunk_causal(qs, gk, gv, model.Pi, model.Pi, model.cK, model.cV, 128, sc,
                                                         ctx[b], S=model.S)
     kern, e2e = rel_l2(got, ref_kern), rel_l2(got, ref_e2e)
-    log(f"  rel L2 over the output: kernel parity {kern:.2e}, end to end {e2e:.2e}")
+    worst = assert_heads(got, ref_kern, TOL_ATTN, f"prefill {name}, kernel parity per (row, token, head)")
+    log(f"  rel L2 over the output: kernel parity {kern:.2e} (worst (row, token, head) {worst:.2e}), "
+        f"end to end {e2e:.2e}")
     assert kern <= TOL_ATTN and e2e <= TOL_ATTN
     for b in range(w.B):
         for i in range(M):

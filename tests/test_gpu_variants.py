@@ -9,8 +9,8 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import (TOL_ATTN, OracleModel, code_mismatch, device_inputs, device_queries, log, rel_l2,
-                    shifted_codebook, unpack_head)
+from tqhelp import (TOL_ATTN, OracleModel, assert_heads, band_report, code_mismatch, device_inputs, device_queries,
+                    head_errors, log, rel_l2, shifted_codebook, unpack_head)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -77,8 +77,14 @@ def test_variant_matches_oracle(tq, name, codebook, rotation):
             ref_e2e[b, kv * w.G:(kv + 1) * w.G] = model.decode(got["k"][0], got["v"][0], qn, b, kv)
             ref_kern[b, kv * w.G:(kv + 1) * w.G] = model.decode(got["k"][1], got["v"][1], qn, b, kv)
     kern, e2e = rel_l2(out, ref_kern), rel_l2(out, ref_e2e)
-    worst = max(rel_l2(out[b, h], ref_e2e[b, h]) for b in range(w.B) for h in range(w.H_q))
-    log(f"  decode rel L2 over the output: kernel parity {kern:.2e}, end to end {e2e:.2e} (worst head {worst:.2e})")
+    worst_k = assert_heads(out, ref_kern, TOL_ATTN, f"variant {name} {codebook}/{rotation}, kernel parity per (row, head)")
+    e = head_errors(out, ref_e2e)
+    b, h = np.unravel_index(int(np.nanargmax(e)), e.shape)
+    kv = h // w.G
+    log(f"  decode rel L2 over the output: kernel parity {kern:.2e} (worst head {worst_k:.2e}), end to end {e2e:.2e} "
+        f"(worst head {e[b, h]:.2e} at row {b}, head {h}: {band_report(w, model, got['k'][0], got['k'][1], b, kv, 'k')}; "
+        f"{band_report(w, model, got['v'][0], got['v'][1], b, kv, 'v')}; on the GPU's codes "
+        f"{head_errors(out[b, h], ref_kern[b, h]):.2e})")
     assert kern <= TOL_ATTN and e2e <= TOL_ATTN
 
 

@@ -271,6 +271,48 @@ def test_threshold_rule_ties_and_zero():
     assert np.all(q["codes"] == 4) and np.all(q["norm"] == 0)
 
 
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_boundary_distance_geometry(bits):
+    """The decision-boundary distance that decides which code mismatches the
+    parity tests exempt (coordinates within 1e-6, unit domain, of a threshold).
+    Fixed by geometry, not by the function's own formula: a coordinate placed
+    exactly on threshold t_i / sqrt(d) is at distance 0; one moved by +-5e-7 is
+    at 5e-7 (inside the band) on either side; one moved by +-2e-6 is outside;
+    the midpoint of two adjacent thresholds is half their gap from both; far
+    below the lowest or above the highest threshold the distance is to that
+    outermost threshold. A missing sqrt(d), an absolute value on the wrong
+    side or a distance to the wrong threshold fails one of these."""
+    band = 1e-6
+    _, t = codebook.canonical(bits)
+    s = math.sqrt(D)
+    for i, ti in enumerate(t):
+        tu = ti / s
+        for delta, want, inside in ((0.0, 0.0, True), (5e-7, 5e-7, True), (-5e-7, 5e-7, True),
+                                    (2e-6, 2e-6, False), (-2e-6, 2e-6, False)):
+            u = np.zeros((1, D))
+            u[0, 7] = tu + delta
+            got = quantize.boundary_distance(u, t, D)[0, 7]
+            assert abs(got - want) < 1e-12, (bits, i, delta, got)
+            assert (got < band) == inside, (bits, i, delta)
+        if i + 1 < len(t):
+            mid = (t[i] + t[i + 1]) / (2 * s)
+            gap = (t[i + 1] - t[i]) / (2 * s)
+            got = quantize.boundary_distance(np.full((1, 3), mid), t, D)
+            assert np.allclose(got, gap, rtol=0, atol=1e-15)
+            assert gap > 10 * band
+    # outside the outermost thresholds: distance to that threshold
+    lo, hi = t[0] / s, t[-1] / s
+    got = quantize.boundary_distance(np.array([[lo - 0.25, hi + 0.5]]), t, D)[0]
+    assert np.allclose(got, [0.25, 0.5], rtol=0, atol=1e-12)
+    # a coordinate inside the band of threshold i is coded either side of it by
+    # an arbitrarily small perturbation; one outside every band is not
+    u = np.array([[t[0] / s - 4e-7, t[0] / s + 4e-7, t[0] / s + 3e-6]])
+    d = quantize.boundary_distance(u, t, D)[0]
+    codes = quantize.codes_from_unit(u, t, D)[0]
+    assert d[0] < band and d[1] < band and d[2] > band
+    assert codes[0] == 0 and codes[1] == 1 and codes[2] == 1
+
+
 @pytest.mark.parametrize("bits,cos_lo,cos_hi,mse_rel", [
     (2, 0.9395, 0.9420, 0.03), (3, 0.9822, 0.9840, 0.03), (4, 0.9948, 0.9960, 0.04)])
 def test_cosine_on_random_unit_vectors(bits, cos_lo, cos_hi, mse_rel):

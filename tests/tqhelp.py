@@ -152,3 +152,66 @@ def device_queries(w: tq_synth.Workload, device="cuda"):
     q = torch.from_numpy(tq_synth.queries_full(w))
     q = q.to(torch.bfloat16) if w.dtype == "bf16" else q
     return q.to(device).contiguous()
+
+
+def gpu_heads(cache, w: tq_synth.Workload, which: str, T: int) -> dict:
+    """The GPU cache's own codes, norms (and QJL sign bits and gamma) per
+    (row, KV head), in the oracle's per-head form, so that the oracle can decode
+    exactly the bytes the kernels read (kernel parity)."""
+    bits = w.k_bits if which == "k" else w.v_bits
+    codes = cache.codes.cpu().numpy()
+    norms = cache.norms.cpu().numpy()
+    qjl = which == "k" and w.k_qjl
+    if qjl:
+        signs = cache.signs.cpu().numpy().view(np.uint32)
+        gamma = cache.gamma.cpu().numpy()
+    out = {}
+    for b in range(w.B):
+        for h in range(w.H_kv):
+            d = {"codes": unpack_head(which, codes[b, h], bits, T), "norm": norms[b, h, :T].astype(np.float64)}
+            if qjl:
+                d["signs"] = oq.unpack_signs(signs[b, h, :T], D)
+                d["gamma"] = gamma[b, h, :T].astype(np.float64)
+            out[(b, h)] = d
+    return out
+
+
+def head_errors(out, ref) -> np.ndarray:
+    """Relative L2 error of every output vector (last axis), NaN where the
+    reference vector is zero (an empty context)."""
+    a = np.asarray(out, dtype=np.float64)
+    b = np.asarray(ref, dtype=np.float64)
+    num = np.linalg.norm(a - b, axis=-1)
+    den = np.linalg.norm(b, axis=-1)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.where(den > 0, num / den, np.nan)
+
+
+def assert_heads(out, ref, tol: float, what: str) -> float:
+    """Every output vector (per row, head; per row, token, head for chunked
+    attention) within `tol` relative L2 of the reference; where the reference is
+    zero the output must be zero too. Returns the worst error."""
+    e = head_errors(out, ref)
+    zero = np.isnan(e)
+    assert np.all(np.asarray(out)[zero] == 0), f"{what}: nonzero output where the reference is zero"
+    worst = float(np.nanmax(e)) if np.any(~zero) else 0.0
+    idx = np.unravel_index(int(np.nanargmax(np.where(zero, -1.0, e))), e.shape) if np.any(~zero) else None
+    assert worst <= tol, f"{what}: worst vector {idx} rel L2 {worst:.3e} > {tol:g}"
+    return worst
+
+
+def band_report(w: tq_synth.Workload, model: "OracleModel", oracle_heads: dict, gpu: dict, b: int, kv: int,
+                which: str) -> str:
+    """Why one (row, KV head) differs end to end: how many of its codes lie in the
+    1e-6 decision-boundary band, how many codes differ from the oracle's, and for
+    QJL keys how many tokens carry sign bits that differ."""
+    thr = model.tK if which == "k" else model.tV
+    ref = oracle_heads[(b, kv)]
+    T = ref["codes"].shape[0]
+    band = oq.boundary_distance(ref["u"][:T], thr, D) < BOUNDARY
+    diff = gpu[(b, kv)]["codes"] != ref["codes"][:T]
+    msg = f"{which}: {int(band.sum())} band codes, {int(diff.sum())} codes differ"
+    if which == "k" and w.k_qjl:
+        flipped = np.any(gpu[(b, kv)]["signs"] != ref["signs"][:T], axis=1)
+        msg += f", {int(flipped.sum())} tokens with differing sign bits"
+    return msg
