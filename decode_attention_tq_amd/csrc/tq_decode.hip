@@ -56,9 +56,11 @@
 // Online softmax (log2 domain; the query operand carries log2(e) * scale / sqrt(d)):
 // the reference maximum m only moves when a score exceeds it by more than
 // kSlack, so the rescale of the accumulators is rare; weights are
-// 2^(s - m - kShift) * |v| with kShift = kSlack + log2(sqrt(d)), which keeps
-// every weight operand at or below |v| / sqrt(d) (float16 range for |v| < 7e5)
-// and leaves one 1/sqrt(d) for the combine.
+// 2^(s - m - kShift - ev) * |v| with kShift = kSlack + log2(sqrt(d)) and 2^ev
+// a per-wavefront power of two at or above the value norms of its first step,
+// which keeps every weight operand at or below (|v| / 2^ev) / sqrt(d) (float16
+// range while |v| < 7e5 * 2^ev, and no float16 underflow of the leading
+// weights however small the norms) and leaves one 1/sqrt(d) for the combine.
 #include <math.h>
 
 #include "tq_device.h"
@@ -76,6 +78,9 @@ constexpr float kShift = kSlack + 3.5f;   // + log2(sqrt(128))
 constexpr int kLutRep = 32;              // LUT replicas (power of two)
 constexpr int kStreamAux = 2;            // cache policy of the streamed cache reads: non-temporal
 constexpr int kLutShift = 5;             // log2(kLutRep)
+// Bound of the value-norm exponent (keeps the fp32 softmax denominator of a
+// wavefront far from overflow: at most 2^(60 + 2 - kShift) per token).
+constexpr int kNormExpClamp = 60;
 
 __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
@@ -452,6 +457,7 @@ struct QOps {
 template <int WIDE>
 struct SoftState {
   float m_ref, m_off, l;
+  float ev;   // wave-uniform: log2 of the power of two that scales the value norms
   floatx4 acc0[8];
 };
 
@@ -539,7 +545,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
       st.m_ref = m_new;
-      st.m_off = m_new + kShift;
+      st.m_off = m_new + kShift + st.ev;
     }
     float w[4];
 #pragma unroll
@@ -608,7 +614,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
       st.m_ref = m_new;
-      st.m_off = m_new + kShift;
+      st.m_off = m_new + kShift + st.ev;
     }
     uint32_t pw[4];
 #pragma unroll
@@ -892,6 +898,25 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   st.m_ref = -INFINITY;
   st.m_off = -INFINITY;
   st.l = 0.f;
+  {
+    // Value-norm scale: the weights 2^(s - m_off) * |v| are float16 operands,
+    // so the wavefront divides them (and its denominator, which keeps the
+    // ratio) by 2^ev, ev = the exponent of the largest value norm among the
+    // tokens of its first loaded step. The weights of those tokens then sit
+    // near the top of the float16 range whatever the norms' overall scale
+    // (tiny value norms would otherwise fall into float16 subnormals); ev
+    // enters through m_off, which the merges already carry per wavefront.
+    float vm = fabsf(buf[0].nm.vn);
+    vm = fmaxf(vm, dpp_xor1(vm));
+    vm = fmaxf(vm, dpp_xor2(vm));
+    vm = fmaxf(vm, dpp_ror4(vm));
+    vm = fmaxf(vm, dpp_ror8(vm));
+    vm = fmaxf(vm, shfl_xor_f(vm, 16));
+    vm = fmaxf(vm, shfl_xor_f(vm, 32));
+    int e = (vm > 0.f && vm < INFINITY) ? __builtin_amdgcn_frexp_expf(vm) : 0;
+    e = e < -kNormExpClamp ? -kNormExpClamp : (e > kNormExpClamp ? kNormExpClamp : e);
+    st.ev = (float)__builtin_amdgcn_readfirstlane(e);
+  }
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 

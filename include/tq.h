@@ -196,17 +196,34 @@ int tq_append_kv(const void* k, const void* v, int32_t x_dtype, int64_t B, int64
                  const tq_cache* kc, const tq_cache* vc, int64_t t_offset, void* hip_stream);
 
 /*
- * Reconstruct tokens t0 .. t1-1 of every (row, head):
+ * Reconstruct tokens t0 .. t1-1 of every (row, head): the inverse of the two
+ * steps of the method (ai-accelerate.xyz TurboQuant article, section
+ * "TurboQuantの仕組み": step 1 keeps, per rotated coordinate, the Lloyd-Max
+ * level of its cell, so undoing it maps the codes back to levels and applies
+ * the transpose of the orthogonal rotation; step 2's sign bits add the QJL
+ * estimate of the residual):
  *   x_hat = n * Pi^T (c[code]/sqrt(d) [+ gamma*sqrt(pi/2)/d * S^T sigma]),
- * sigma_i = 2*bit_i - 1 (QJL keys). out: device float32 [B][H_kv][t1-t0][d].
- * Requires 0 <= t0 <= t1 <= src->T_cap.
+ * sigma_i = 2*bit_i - 1 (QJL keys).
+ *   src: a cache filled by tq_quantize_kv / tq_append_kv (read only)
+ *   out: device float32 [B][H_kv][t1-t0][d], 16-byte aligned, owned by the caller
+ * Requires 0 <= t0 <= t1 <= src->T_cap (t0 == t1 is a no-op); paged caches
+ * read through their block table (entries of the range must be valid).
+ * Errors: TQ_ERR_INVALID_ARGUMENT / _UNSUPPORTED / _ALIGNMENT before any
+ * launch, TQ_ERR_DEVICE when the launch fails.
  */
 int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void* hip_stream);
 
 /*
  * Decode attention of one query per head over the packed caches:
  *   out[b][h] = sum_{t < ctx_len[b]} softmax_t(scale * q[b][h] . k_hat[b][h/G][t]) v_hat[b][h/G][t]
- * computed in the rotated domain (q' = Pi_K q once; scores from key codebook
+ * with k_hat, v_hat the reconstructions of tq_dequantize. Attention reads the
+ * compressed cache itself (ai-accelerate.xyz TurboQuant article, section
+ * "TurboQuantの仕組み": the rotation of step 1 is orthogonal, so a query dotted
+ * with a rotated-back key equals the rotated query dotted with the stored
+ * levels, and a sum of rotated-back values is one rotation of the sum; step 2's
+ * sign bits give the unbiased QJL correction of each score; the thefrontairview
+ * piece ties the claimed speedup to attention over the compressed keys).
+ * It is computed in the rotated domain (q' = Pi_K q once; scores from key codebook
  * levels times key norms, plus the QJL term for QJL keys; values summed in the
  * rotated domain; out = Pi_V^T o'). G = H_q / H_kv query heads share KV head
  * h / G. Work is split over the context (n_split chunks per (row, KV head),
@@ -220,8 +237,16 @@ int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void*
  *   out:      device float32 [B][H_q][d]
  *   workspace: device, at least tq_decode_workspace_bytes(...) bytes, 256-byte aligned
  * Requires k->role == TQ_KEYS, v->role == TQ_VALUES, equal B and H_kv,
- * H_q % H_kv == 0 and G <= 16. Value norms must stay below 7e5 (float16
- * range of the weighted value operand).
+ * H_q % H_kv == 0 and G <= 16. Value norms may have any overall scale: the
+ * float16 weights of the value sum are scaled per wavefront by a power of two
+ * taken from the largest value norm of its first 32 tokens, so within one
+ * (row, KV head) the largest value norm must stay below 7e5 times the
+ * smallest nonzero one (below 7e5 outright when 32 zero value vectors open a
+ * wavefront's share of the context).
+ * Errors: TQ_ERR_INVALID_ARGUMENT / _UNSUPPORTED / _ALIGNMENT /
+ * _WORKSPACE_TOO_SMALL before any launch, TQ_ERR_DEVICE when a launch fails.
+ * The caller owns every buffer; the workspace holds the context-chunk partials
+ * and may be reused by the next call once this one has run on the stream.
  */
 int tq_decode_attention(const tq_cache* k, const tq_cache* v,
                         const void* q, int32_t q_dtype, int64_t H_q,

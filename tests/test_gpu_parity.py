@@ -7,8 +7,8 @@ import numpy as np
 import pytest
 
 import tq_synth
-from tqhelp import (BOUNDARY, TOL_ATTN, TOL_RECUT, U_F16, OracleModel, code_mismatch, device_inputs, device_queries, log,
-                    rel_l2, upload_oracle_cache)
+from tqhelp import (BOUNDARY, TOL_ATTN, TOL_RECUT, U_F16, OracleModel, assert_heads, band_report, code_mismatch,
+                    device_inputs, device_queries, gpu_heads, head_errors, log, rel_l2, upload_oracle_cache)
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -101,7 +101,7 @@ def test_decode_on_oracle_cache_matches_oracle(tq, name):
         for kv in range(w.H_kv):
             ref[b, kv * w.G:(kv + 1) * w.G] = model.decode(kh, vh, qn, b, kv)
     err = rel_l2(out, ref)
-    worst = max(rel_l2(out[b, h], ref[b, h]) for b in range(w.B) for h in range(w.H_q))
+    worst = assert_heads(out, ref, TOL_ATTN, f"decode {name} per (row, head)")
     log(f"  rel L2 {err:.3e} (worst head {worst:.3e})")
     assert err <= TOL_ATTN
 
@@ -119,13 +119,23 @@ def test_end_to_end_matches_oracle(tq, name):
     tq.quantize_kv(device_inputs(w, "v"), vc)
     out = tq.decode_attention(kc, vc, device_queries(w), T=w.T).cpu().numpy()
     kh, vh = model.heads("k"), model.heads("v")
+    gk, gv = gpu_heads(kc, w, "k", w.T), gpu_heads(vc, w, "v", w.T)
     qn = tq_synth.queries_full(w)
     ref = np.zeros_like(out, dtype=np.float64)
+    kern = np.zeros_like(out, dtype=np.float64)
     for b in range(w.B):
         for kv in range(w.H_kv):
             ref[b, kv * w.G:(kv + 1) * w.G] = model.decode(kh, vh, qn, b, kv)
+            kern[b, kv * w.G:(kv + 1) * w.G] = model.decode(gk, gv, qn, b, kv)
     err = rel_l2(out, ref)
-    log(f"  rel L2 {err:.3e}")
+    # kernel parity per (row, head): the oracle decoding the GPU's own codes
+    worst_k = assert_heads(out, kern, TOL_ATTN, f"end-to-end {name}, kernel parity per (row, head)")
+    e = head_errors(out, ref)
+    b, h = np.unravel_index(int(np.nanargmax(e)), e.shape)
+    kv = h // w.G
+    log(f"  rel L2 {err:.3e}; worst head end to end {e[b, h]:.3e} at (row {b}, head {h}): "
+        f"{band_report(w, model, kh, gk, b, kv, 'k')}; {band_report(w, model, vh, gv, b, kv, 'v')}; "
+        f"on the GPU's codes that head is at {head_errors(out[b, h], kern[b, h]):.3e} (worst {worst_k:.3e})")
     assert err <= TOL_ATTN
 
 
@@ -196,6 +206,7 @@ def test_ragged_context_lengths(tq):
             assert np.all(out[b] == 0)
         else:
             assert rel_l2(out[b], ref) <= TOL_ATTN, b
+            assert_heads(out[b], ref, TOL_ATTN, f"ragged row {b} per head")
 
 
 def _check_against_oracle(tq, w, model, which, cache, T):
@@ -372,3 +383,38 @@ def test_extreme_magnitudes(tq, scale):
                     assert mo == 0, (mode, which, b, h)
                     nr = norms[b, h, :w.T].astype(np.float64)
                     assert np.all(np.abs(nr - ref["norm"]) <= 1e-6 * ref["norm"]), (mode, which, b, h)
+
+
+@pytest.mark.parametrize("name", ["stress70b_B2", "qjl_k2v3", "tiny"])
+def test_value_norm_scale(tq, name):
+    """Value norms of any overall scale: the output is linear in the value norms,
+    and the kernel scales its float16 weights by a power of two taken from the
+    norms themselves, so scaling every value norm by 2^k scales the output by
+    2^k (up to the re-rounding of the weights: the exponent offset enters the
+    float32 softmax argument, so single float16 roundings may flip) even where
+    unscaled weights would fall into float16 subnormals or to zero (2^-40) or
+    overflow (2^+24); also a scale that is not a power of two; all against the
+    oracle per (row, head)."""
+    w = CASES[name].scaled(T=min(CASES[name].T, 1024))
+    T_cap = tcap(w.T)
+    log(f"value-norm scale {name}")
+    model = OracleModel(w)
+    kh, vh = model.heads("k"), model.heads("v")
+    kc = upload_oracle_cache(tq, model, "k", kh, T_cap)
+    vc = upload_oracle_cache(tq, model, "v", vh, T_cap)
+    q = device_queries(w)
+    base = tq.decode_attention(kc, vc, q, T=w.T)
+    qn = tq_synth.queries_full(w)
+    ref = np.zeros(tuple(base.shape), dtype=np.float64)
+    for b in range(w.B):
+        for kv in range(w.H_kv):
+            ref[b, kv * w.G:(kv + 1) * w.G] = model.decode(kh, vh, qn, b, kv)
+    norms0 = vc.norms.clone()
+    for s in (2.0 ** -40, 2.0 ** -20, 2.0 ** 24, 3.7e-9):
+        vc.norms.copy_(norms0 * s)
+        o = tq.decode_attention(kc, vc, q, T=w.T).cpu().numpy() / s
+        err = rel_l2(o, base.cpu().numpy())
+        log(f"  value norms x{s:.3g}: rel L2 {err:.2e} against the unscaled output")
+        assert err <= TOL_RECUT, s
+        assert_heads(o, ref, TOL_ATTN, f"value norms x{s:g}, per (row, head)")
+    vc.norms.copy_(norms0)
