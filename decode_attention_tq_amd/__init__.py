@@ -47,7 +47,8 @@ VALUE_BLOCK = 8
 
 EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
            "tq_dequantize",
-           "tq_decode_attention", "tq_decode_attention_append", "tq_prefill_attention", "tq_decode_splits", "tq_decode_workspace_bytes",
+           "tq_decode_attention", "tq_decode_attention_noalloc", "tq_decode_attention_append", "tq_prefill_attention",
+           "tq_decode_splits", "tq_decode_workspace_bytes",
            "tq_prefill_workspace_bytes", "tq_status_string",
            "tq_last_hip_error")
 
@@ -79,6 +80,8 @@ def _bind(lib):
     lib.tq_dequantize.argtypes = [ctypes.POINTER(TQCache), _I64, _I64, _P, _P]
     lib.tq_decode_attention.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64, _P,
                                         _I64, _F, _I32, _P, _P, ctypes.c_size_t, _P]
+    lib.tq_decode_attention_noalloc.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _I32, _I64,
+                                                _P, _I64, _F, _I32, _P, _P]
     lib.tq_decode_attention_append.argtypes = [ctypes.POINTER(TQCache), ctypes.POINTER(TQCache), _P, _P, _I32, _I64,
                                                _I64, _I64, _I64, _P, _I32, _I64, _P, _I64, _F, _I32, _P, _P,
                                                ctypes.c_size_t, _P]
@@ -95,7 +98,7 @@ def _bind(lib):
     lib.tq_last_hip_error.argtypes = []
     lib.tq_last_hip_error.restype = ctypes.c_char_p
     for name in ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
-                 "tq_dequantize", "tq_decode_attention", "tq_decode_attention_append",
+                 "tq_dequantize", "tq_decode_attention", "tq_decode_attention_noalloc", "tq_decode_attention_append",
                  "tq_prefill_attention"):
         getattr(lib, name).restype = ctypes.c_int
     return lib
@@ -333,6 +336,33 @@ def decode_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None,
     _check(_lib.tq_decode_attention(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q,
                                     cl or None, T, scale, n_split, out.data_ptr(), workspace.ptr,
                                     workspace.nbytes, _stream_handle(q.device)), "tq_decode_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
+
+
+def decode_attention_noalloc(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None, scale: float = 0.0,
+                             n_split: int = 0, out=None):
+    """decode_attention without a workspace: the chunk partials live in the
+    library's static per-GPU scratch (tq_decode_attention_noalloc). Pass `out`
+    to allocate nothing at all; calls that overlap on one GPU race."""
+    torch = _torch()
+    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    B, H_q, _ = q.shape
+    T = k.T_cap if T is None else T
+    if out is None:
+        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+    sk, sv = k.struct(), v.struct()
+    cl = 0
+    if ctx_lens is not None:
+        if ctx_lens.dtype != torch.int32 or not ctx_lens.is_contiguous() or ctx_lens.numel() != B:
+            raise ValueError("ctx_lens must be a contiguous int32 tensor of B entries")
+        cl = ctx_lens.data_ptr()
+    _check(_lib.tq_decode_attention_noalloc(ctypes.byref(sk), ctypes.byref(sv), q.data_ptr(), _dtype_code(q), H_q,
+                                            cl or None, T, scale, n_split, out.data_ptr(), _stream_handle(q.device)),
+           "tq_decode_attention_noalloc")
     return out
 
 

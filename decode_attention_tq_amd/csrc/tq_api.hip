@@ -2,6 +2,8 @@
 // HIP call), workspace planning and kernel dispatch.
 #include <math.h>
 
+#include <mutex>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -207,10 +209,54 @@ extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float*
 
 namespace {
 
+// Library-owned scratch of tq_decode_attention_noalloc: the context-chunk
+// partials of one call. Each GPU the library runs on holds its own copy until
+// the process ends; calls on one GPU share it (overlapping calls race).
+static __device__ __align__(256) unsigned char scratch[TQ_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on each device (the host-side name is only a
+// stand-in for the symbol), looked up once per device with that device
+// current.
+constexpr int kMaxDevices = 64;
+void* g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Address of the current device's scratch; nullptr with *err set on failure.
+void* scratch_address(hipError_t* err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *err = e;
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *err = hipErrorInvalidDevice;
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || ptr == nullptr) {
+      *err = e != hipSuccess ? e : hipErrorInvalidSymbol;
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
+// Where the chunk partials go: the caller's workspace, or the library's scratch.
+struct WorkspaceArg {
+  void* ptr;
+  size_t bytes;
+  bool scratch;
+};
+
 // Shared validation and launch of decode (M = 1) and chunked causal attention.
 int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype, int64_t H_q, int64_t M,
-                   const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split, float* out, void* workspace,
-                   size_t workspace_bytes, void* hip_stream, const DecodeAppend* app = nullptr) {
+                   const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split, float* out, WorkspaceArg wsa,
+                   void* hip_stream, const DecodeAppend* app = nullptr) {
   int st = check_cache(k);
   if (st != TQ_OK) return st;
   st = check_cache(v);
@@ -227,8 +273,12 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
   DecodePlan p;
   if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) return TQ_ERR_UNSUPPORTED;
-  if (workspace == nullptr || workspace_bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
-  if (((uintptr_t)workspace & 255u) != 0) return TQ_ERR_ALIGNMENT;
+  if (wsa.scratch) {
+    if (p.bytes > (size_t)TQ_NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE_TOO_SMALL;
+  } else {
+    if (wsa.ptr == nullptr || wsa.bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
+    if (((uintptr_t)wsa.ptr & 255u) != 0) return TQ_ERR_ALIGNMENT;
+  }
   if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
   if (app != nullptr) {
     if (app->x_dtype != TQ_F32 && app->x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
@@ -241,7 +291,16 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
     // keys with a QJL sketch take the tiled quantize kernel, which writes one
     // position for all rows
     if (k->qjl && ctx_lens != nullptr) return TQ_ERR_UNSUPPORTED;
-    clear_pending_error();
+  }
+  // every argument is valid from here on
+  clear_pending_error();
+  void* workspace = wsa.ptr;
+  if (wsa.scratch) {
+    hipError_t e = hipSuccess;
+    workspace = scratch_address(&e);
+    if (workspace == nullptr) return device_status(e);
+  }
+  if (app != nullptr) {
     if (ctx_lens != nullptr || T > 0) {
       const hipError_t e = launch_append_kv(app->k, app->v, app->x_dtype, k->B, k->H_kv, app->k_sb, app->k_sh,
                                             app->v_sb, app->v_sh, k, v, T - 1, (hipStream_t)hip_stream, ctx_lens, T);
@@ -250,7 +309,6 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
     return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                        (hipStream_t)hip_stream));
   }
-  clear_pending_error();
   return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                      (hipStream_t)hip_stream));
 }
@@ -261,7 +319,14 @@ extern "C" int tq_decode_attention(const tq_cache* k, const tq_cache* v, const v
                                    int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
                                    int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
                                    void* hip_stream) {
-  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
+  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out,
+                        WorkspaceArg{workspace, workspace_bytes, false}, hip_stream);
+}
+
+extern "C" int tq_decode_attention_noalloc(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
+                                           int64_t H_q, const int32_t* ctx_lens, int64_t T, float scale,
+                                           int32_t n_split, float* out, void* hip_stream) {
+  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, WorkspaceArg{nullptr, 0, true},
                         hip_stream);
 }
 
@@ -279,14 +344,14 @@ extern "C" int tq_decode_attention_append(const tq_cache* k, const tq_cache* v, 
   app.k_sh = k_stride_h;
   app.v_sb = v_stride_b;
   app.v_sh = v_stride_h;
-  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
-                        hip_stream, &app);
+  return attention_call(k, v, q, q_dtype, H_q, 1, ctx_lens, T, scale, n_split, out,
+                        WorkspaceArg{workspace, workspace_bytes, false}, hip_stream, &app);
 }
 
 extern "C" int tq_prefill_attention(const tq_cache* k, const tq_cache* v, const void* q, int32_t q_dtype,
                                     int64_t H_q, int64_t M, const int32_t* ctx_lens, int64_t T, float scale,
                                     int32_t n_split, float* out, void* workspace, size_t workspace_bytes,
                                     void* hip_stream) {
-  return attention_call(k, v, q, q_dtype, H_q, M, ctx_lens, T, scale, n_split, out, workspace, workspace_bytes,
-                        hip_stream);
+  return attention_call(k, v, q, q_dtype, H_q, M, ctx_lens, T, scale, n_split, out,
+                        WorkspaceArg{workspace, workspace_bytes, false}, hip_stream);
 }

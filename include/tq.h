@@ -25,7 +25,8 @@
  *     cleared before the launch and not reported), a fault inside a kernel
  *     surfaces at the caller's next synchronisation;
  *   - the caller owns every buffer; the library never allocates or frees device
- *     memory;
+ *     memory (its one static device array, the scratch of
+ *     tq_decode_attention_noalloc, is part of its loaded code object);
  *   - head dimension d = 128 only (other values return TQ_ERR_UNSUPPORTED).
  *
  * Packed formats (one cache per tensor and layer; keys and values set their bit
@@ -252,6 +253,28 @@ int tq_decode_attention(const tq_cache* k, const tq_cache* v,
                         const void* q, int32_t q_dtype, int64_t H_q,
                         const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
                         float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
+
+/*
+ * tq_decode_attention without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation. Same arguments (minus workspace and
+ * workspace_bytes), requirements, errors and results, bit for bit, as
+ * tq_decode_attention. The context-chunk partials go to a library-owned
+ * static device array of TQ_NOALLOC_SCRATCH_BYTES bytes: each GPU the library
+ * runs on holds its own copy until the process ends, looked up on the first
+ * call on that device. Calls whose partials would exceed it return
+ * TQ_ERR_WORKSPACE_TOO_SMALL before any HIP call (tq_decode_workspace_bytes
+ * gives the size a call needs; a single-chunk plan needs none). The call makes
+ * no allocation of any kind. Every call on one GPU shares the array: calls that
+ * overlap on one GPU (different streams or threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe. Nothing in the
+ * array needs clearing between calls (a call writes every partial it reads).
+ */
+#define TQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int tq_decode_attention_noalloc(const tq_cache* k, const tq_cache* v,
+                                const void* q, int32_t q_dtype, int64_t H_q,
+                                const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
+                                float* out, void* hip_stream);
 
 /*
  * One decode step in one call: for every row b with context length

@@ -285,3 +285,32 @@ def test_dequantize_validation_paths():
     assert lib.tq_dequantize(ctypes.byref(K), 0, 8, None, None) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_dequantize(ctypes.byref(K), 0, 8, FAKE + 8, None) == tq.ERR_ALIGNMENT
     assert lib.tq_dequantize(ctypes.byref(K), 3, 3, FAKE, None) == tq.OK
+
+
+def _decode_noalloc(k, v, q=FAKE, H_q=8, T=64, scale=0.0, n_split=0, out=FAKE, dtype=tq.BF16):
+    return tq.lib().tq_decode_attention_noalloc(ctypes.byref(k), ctypes.byref(v), q, dtype, H_q, None, T, scale,
+                                                n_split, out, None)
+
+
+def test_decode_noalloc_validation_paths():
+    """The allocation-free decode reports every argument error of
+    tq_decode_attention before any HIP call, and a call whose chunk partials
+    would not fit the library's static scratch as a workspace error."""
+    K, V = _cache(), _cache(role=tq.VALUES)
+    assert _decode_noalloc(V, V) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, _cache(role=tq.VALUES, B=3)) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, H_q=7) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, H_q=34) == tq.ERR_UNSUPPORTED
+    assert _decode_noalloc(K, V, T=65) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, q=None) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, out=FAKE + 4) == tq.ERR_ALIGNMENT
+    assert _decode_noalloc(K, V, scale=float("nan")) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, n_split=-1) == tq.ERR_INVALID_ARGUMENT
+    assert _decode_noalloc(K, V, dtype=5) == tq.ERR_INVALID_ARGUMENT
+    # 8 rows x 128 query heads x 64 chunks of partials (130 floats each) is
+    # about 34 MB, beyond the 16 MiB scratch
+    big_k = _cache(B=8, H=8, T_cap=32768)
+    big_v = _cache(role=tq.VALUES, B=8, H=8, T_cap=32768)
+    need = tq.decode_workspace_bytes(8, 128, 8, 32768, 64, 0)
+    assert need > tq.NOALLOC_SCRATCH_BYTES
+    assert _decode_noalloc(big_k, big_v, H_q=128, T=32768, n_split=64) == tq.ERR_WORKSPACE_TOO_SMALL
