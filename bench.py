@@ -9,9 +9,13 @@ then decode attention of all query heads over the T-token packed caches (a
 second launch). Inputs are resident in HBM before timing starts. Prints one
 JSON line on stdout.
 
-Extra fields: `roofline` (the decode launch vs the HBM peak), `cpu_baseline`
-(the CPU oracle on a bounded sample of the same step, scaled to tokens/s),
-`quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view).
+Extra fields: `roofline` (the decode launch vs the HBM peak and vs the
+streaming-read reference measured in the same run), `cpu_baseline` (the CPU
+oracle on a bounded sample of the same step, scaled to tokens/s),
+`quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view),
+`stream` (the plain streaming-read kernel), `quality` (code mismatch rate and
+decode error of sampled slices against the oracle, cosine per bit width,
+asymmetric K/V formats and QJL keys against exact attention).
 """
 from __future__ import annotations
 
@@ -102,11 +106,18 @@ def copy_cache(tq, c):
     return d
 
 
-def cpu_baseline(w, budget_s=12.0):
+def cpu_baseline(w, budget_s=12.0, gpu_slices=()):
     """The CPU oracle, as it stands, on (row, KV head) slices of the same step:
     unpack the slice's packed key and value caches, quantize one new token of
     each, decode the G query heads over T tokens. Scaled to decode tokens/s of
-    the whole batch."""
+    the whole batch.
+
+    The same leg also checks the GPU against the oracle on `gpu_slices`
+    (sampled (row, KV head) slices of the benchmarked step, with the exact
+    input bytes the GPU quantized, its packed codes, norms and decode output):
+    code mismatches inside and outside the 1e-6 decision-boundary band, norm
+    error, and the decode relative L2 against the oracle on the GPU's own codes
+    (kernel parity) and on the oracle's codes (end to end)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -119,6 +130,50 @@ def cpu_baseline(w, budget_s=12.0):
     Pi = orot.haar_rotation(tq_synth.ROT_SEED, w.d)
     cK, tK = ocb.canonical(w.k_bits)
     cV, tV = ocb.canonical(w.v_bits)
+    scale = 1.0 / math.sqrt(w.d)
+
+    parity = None
+    if gpu_slices:
+        tot = outside = n = 0
+        band = 0
+        norm_err = 0.0
+        kern, e2e = [], []
+        for sl in gpu_slices:
+            T = sl["xk"].shape[0]
+            kq = oq.quantize_head(sl["xk"], Pi, cK, tK)
+            vq = oq.quantize_head(sl["xv"], Pi, cV, tV)
+            got = {}
+            for which, ref, bits, thr in (("k", kq, w.k_bits, tK), ("v", vq, w.v_bits, tV)):
+                words = sl[which + "_words"]
+                if which == "k":
+                    codes = oq.unpack_keys(words.reshape(-1, w.d * bits // 32), bits, w.d)[:T]
+                else:
+                    codes = oq.unpack_values(words.reshape(-1, 8 * w.d * bits // 32), bits, w.d)[:T]
+                bad = codes != ref["codes"]
+                ex = oq.boundary_distance(ref["u"], thr, w.d) < 1e-6
+                tot += int(bad.sum())
+                outside += int((bad & ~ex).sum())
+                band += int(ex.sum())
+                n += bad.size
+                nr = sl[which + "_norms"].astype(np.float64)
+                want = ref["norm"].astype(np.float64)
+                norm_err = max(norm_err, float(np.max(np.abs(nr - want) / np.maximum(want, 1e-30))))
+                got[which] = {"codes": codes, "norm": nr}
+            q = sl["q"].astype(np.float64)
+            ok = oa.attend_rotated(q, got["k"], got["v"], Pi, Pi, cK, cV, w.d, scale)
+            oe = oa.attend_rotated(q, kq, vq, Pi, Pi, cK, cV, w.d, scale)
+            o = sl["out"].astype(np.float64)
+            kern.append(float(np.max(np.linalg.norm(o - ok, axis=1) / np.linalg.norm(ok, axis=1))))
+            e2e.append(float(np.max(np.linalg.norm(o - oe, axis=1) / np.linalg.norm(oe, axis=1))))
+        parity = {"slices": [[sl["b"], sl["h"]] for sl in gpu_slices], "coordinates": n,
+                  "code_mismatches": tot, "code_mismatch_rate": tot / n,
+                  "mismatches_outside_band": outside, "coordinates_in_band": band,
+                  "band": "abs(u_j - t_i/sqrt(d)) < 1e-6 (unit domain, oracle fp64)",
+                  "norm_max_rel_err": norm_err,
+                  "decode_rel_l2_kernel_parity_worst_head": max(kern),
+                  "decode_rel_l2_end_to_end_worst_head": max(e2e),
+                  "tolerance": 2e-3}
+
     step_times = []
     slices = 0
     t_setup = time.perf_counter()
@@ -138,7 +193,7 @@ def cpu_baseline(w, budget_s=12.0):
         k = {"codes": oq.unpack_keys(kwords, w.k_bits, w.d), "norm": kq["norm"]}
         v = {"codes": oq.unpack_values(vwords, w.v_bits, w.d), "norm": vq["norm"]}
         k["codes"][-1], v["codes"][-1] = new[0]["codes"][0], new[1]["codes"][0]
-        oa.attend_rotated(q, k, v, Pi, Pi, cK, cV, w.d, 1.0 / math.sqrt(w.d))
+        oa.attend_rotated(q, k, v, Pi, Pi, cK, cV, w.d, scale)
         step_times.append(time.perf_counter() - t0)
         slices += 1
         if sum(step_times) >= budget_s or time.perf_counter() - t_setup > 3 * budget_s:
@@ -156,7 +211,149 @@ def cpu_baseline(w, budget_s=12.0):
                    f"{w.G} query heads; {per_slice * 1e3:.1f} ms per slice, scaled by {w.B * w.H_kv} slices "
                    f"to the batch of {w.B} rows"),
         "host_cpus": len(os.sched_getaffinity(0)),
-    }
+    }, parity
+
+
+def stream_reference(tq, torch, dev, nbytes=2 << 30, reps=10):
+    """The library's plain streaming-read kernel over a 2 GiB buffer (beyond the
+    256 MB last-level cache): the read rate a pure stream reaches on this part,
+    best of a few workgroup counts."""
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (nbytes // 4,), dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+    best = None
+    per_wg = {}
+    for mult in (4, 8, 16):
+        wgs = mult * cus
+        sink = tq.stream_read(buf, wgs)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            tq.stream_read(buf, wgs, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        gbs = nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+        per_wg[str(wgs)] = gbs
+        if best is None or gbs > best[0]:
+            best = (gbs, wgs)
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB_s": best[0], "frac_of_peak": best[0] / HBM_PEAK_GBS, "bytes": nbytes, "workgroups": best[1],
+            "GB_s_by_workgroups": per_wg, "kernel": "stream_read_kernel (tq_stream_read)"}
+
+
+def cosine_report(tq, torch, dev):
+    """Mean cosine between N(0,1) vectors (bfloat16, 8 x 4096 per bit width) and
+    their reconstruction by the GPU's quantize + dequantize, for 2, 3, 4 bits,
+    next to the pages' value-cache figures."""
+    out = {}
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(777)
+    x = torch.randn((1, 4096, 8, 128), generator=gen, device=dev).to(torch.bfloat16)
+    xf = x.float()[0].transpose(0, 1)   # [H, T, d]
+    for bits in (2, 3, 4):
+        c = tq.Cache(tq.VALUES, bits, 1, 8, 4096, device=dev)
+        tq.quantize_kv(x, c)
+        xh = tq.dequantize(c, 0, 4096)[0]
+        cos = torch.nn.functional.cosine_similarity(xh.double(), xf.double(), dim=-1)
+        out[str(bits)] = {"mean": float(cos.mean()), "min": float(cos.min())}
+    out["pages"] = {"2": 0.94, "4": 0.997,
+                    "source": "ai-accelerate.xyz TurboQuant article, caveats on what TurboQuant means for "
+                              "local LLM users (2-bit and 4-bit value cosine; hardware and data not stated)"}
+    out["closed_form_sqrt_1_minus_mse"] = {"2": 0.9394, "3": 0.9826, "4": 0.9952}
+    return out
+
+
+def exact_attention(torch, k, v, q, G, scale):
+    """Unquantized attention in float32 on the GPU (the quality reference):
+    k, v [B, T, H_kv, d] (any float dtype), q [B, H_q, d] -> [B, H_q, d]."""
+    B, T, H, d = k.shape
+    out = torch.empty((B, H * G, d), dtype=torch.float32, device=q.device)
+    for b in range(B):
+        for h in range(H):
+            # (plain 2-D float32 products on contiguous operands only)
+            kf = k[b, :, h].float().contiguous()
+            vf = v[b, :, h].float().contiguous()
+            qT = q[b, h * G:(h + 1) * G].float().t().contiguous()      # [d, G]
+            s = (kf @ qT) * scale                                      # [T, G]
+            p = torch.softmax(s, dim=0).t().contiguous()               # [G, T]
+            out[b, h * G:(h + 1) * G] = p @ vf
+    return out
+
+
+def _rel(torch, a, b):
+    return float(torch.linalg.vector_norm((a - b).double()) / torch.linalg.vector_norm(b.double()))
+
+
+def qwen_quality(tq, torch, dev, fw, xk, xv, q, kc, vc2):
+    """Asymmetric formats on the Qwen-like workload: K4/V2 (the workload's) and
+    K4/V4 decode against exact unquantized attention."""
+    scale = 1.0 / math.sqrt(fw.d)
+    ref = exact_attention(torch, xk, xv, q, fw.G, scale)
+    vc4 = tq.Cache(tq.VALUES, 4, fw.B, fw.H_kv, kc.T_cap, device=dev)
+    tq.quantize_kv(xv, vc4)
+    o2 = tq.decode_attention(kc, vc2, q, T=fw.T)
+    o4 = tq.decode_attention(kc, vc4, q, T=fw.T)
+    cos = lambda a: float(torch.nn.functional.cosine_similarity(a.double(), ref.double(), dim=-1).mean())
+    res = {"K4/V2": {"rel_l2_vs_exact": _rel(torch, o2, ref), "mean_cosine_vs_exact": cos(o2)},
+           "K4/V4": {"rel_l2_vs_exact": _rel(torch, o4, ref), "mean_cosine_vs_exact": cos(o4)},
+           "reference": "float32 softmax attention over the unquantized bf16 keys and values"}
+    del vc4
+    return res
+
+
+def qjl_quality(tq, torch, dev, fw, xk, xv, q, kc_qjl, vc):
+    """QJL keys (2-bit Lloyd-Max + 1-bit sign sketch) against MSE-only 3-bit keys
+    on the QJL workload: raw-score estimator statistics (regression slope through
+    0, mean error, error standard deviation) from the GPU's dequantized keys,
+    post-softmax total-variation distance, and the decode output against exact
+    attention."""
+    scale = 1.0 / math.sqrt(fw.d)
+    kc3 = tq.Cache(tq.KEYS, 3, fw.B, fw.H_kv, kc_qjl.T_cap, device=dev)
+    tq.quantize_kv(xk, kc3)
+    ref = exact_attention(torch, xk, xv, q, fw.G, scale)
+    res = {}
+    for name, kc in (("K2+QJL", kc_qjl), ("K3 MSE-only", kc3)):
+        kh = tq.dequantize(kc, 0, fw.T)   # [B, H_kv, T, d]
+        sxy = sxx = serr = serr2 = 0.0
+        tv = []
+        cnt = 0
+        for b in range(fw.B):
+            for h in range(fw.H_kv):
+                qT = q[b, h * fw.G:(h + 1) * fw.G].float().t().contiguous()   # [d, G]
+                ex = (xk[b, :, h].float().contiguous() @ qT).t().contiguous()   # [G, T]
+                est = (kh[b, h].contiguous() @ qT).t().contiguous()
+                err = (est - ex).double()
+                exd = ex.double()
+                sxy += float((est.double() * exd).sum())
+                sxx += float((exd * exd).sum())
+                serr += float(err.sum())
+                serr2 += float((err * err).sum())
+                cnt += err.numel()
+                pe = torch.softmax(est * scale, dim=-1).double()
+                px = torch.softmax(ex * scale, dim=-1).double()
+                tv.append(0.5 * (pe - px).abs().sum(dim=-1))
+        mean_err = serr / cnt
+        o = tq.decode_attention(kc, vc, q, T=fw.T)
+        res[name] = {"score_slope": sxy / sxx, "score_mean_err": mean_err,
+                     "score_err_std": math.sqrt(max(serr2 / cnt - mean_err ** 2, 0.0)),
+                     "post_softmax_tv_mean": float(torch.cat(tv).mean()),
+                     "decode_rel_l2_vs_exact": _rel(torch, o, ref)}
+        del kh
+    res["pages"] = ("ai-accelerate.xyz TurboQuant article, reports of implementers: the QJL estimate is unbiased "
+                    "but its variance, amplified by the softmax, made MSE-only keys better after softmax")
+    del kc3
+    torch.cuda.empty_cache()
+    return res
+
+
+def guarded(what, fn, *a):
+    """Run a report-only section; an error there is recorded, not fatal to the
+    benchmark line."""
+    try:
+        return fn(*a)
+    except Exception as e:   # noqa: BLE001 (report sections only)
+        log(f"[bench] {what} failed: {type(e).__name__}: {e}")
+        return {"error": f"{type(e).__name__}: {e}"}
 
 
 def main():
@@ -174,6 +371,11 @@ def main():
                     help="chunk sizes M of chunked causal attention timed on the same caches ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=256,
                     help="also time decode on paged caches with this many tokens per block (0: skip)")
+    ap.add_argument("--no-quality", action="store_true",
+                    help="skip the quality reports (cosine per bit width, asymmetric formats, QJL statistics)")
+    ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read reference")
+    ap.add_argument("--parity-slices", type=int, default=8,
+                    help="(row, KV head) slices of the benchmarked step checked against the oracle")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -219,6 +421,13 @@ def main():
     issued = 2 * 2 * w.d * w.d * ntok + (3 * 2 * w.d * w.d * w.B * w.H_kv * T if w.k_qjl else 0)
     new_k = xk[:, T - 1:T].contiguous()
     new_v = xv[:, T - 1:T].contiguous()
+    # the exact input bytes of sampled (row, KV head) slices, for the oracle check
+    import numpy as np
+    rng = np.random.default_rng(2024)
+    pairs = [(int(b), int(h)) for b in range(w.B) for h in range(w.H_kv)]
+    sel = sorted(pairs[i] for i in rng.choice(len(pairs), size=min(args.parity_slices, len(pairs)), replace=False))
+    gpu_slices = [{"b": b, "h": h, "xk": xk[b, :, h].float().cpu().numpy(), "xv": xv[b, :, h].float().cpu().numpy()}
+                  for b, h in sel] if not args.no_cpu_baseline else []
     del xk, xv
     torch.cuda.empty_cache()
 
@@ -272,6 +481,24 @@ def main():
     dbytes = decode_bytes(w, T)
     n_split = tq.decode_splits(w.B, w.H_kv, T)
     achieved = dbytes / (dec_ms * 1e-3) / 1e9
+    # the GPU's packed codes, norms and decode output of the sampled slices
+    tq.decode_attention(kc, vc, qs[0], T=T, out=out, workspace=ws)
+    torch.cuda.synchronize()
+    q0 = qs[0].float().cpu().numpy()
+    for sl in gpu_slices:
+        b, h = sl["b"], sl["h"]
+        sl["k_words"] = kc.codes[b, h].cpu().numpy().view(np.uint32)
+        sl["v_words"] = vc.codes[b, h].cpu().numpy().view(np.uint32)
+        sl["k_norms"] = kc.norms[b, h, :T].cpu().numpy()
+        sl["v_norms"] = vc.norms[b, h, :T].cpu().numpy()
+        sl["q"] = q0[b, h * w.G:(h + 1) * w.G]
+        sl["out"] = out[b, h * w.G:(h + 1) * w.G].cpu().numpy()
+    stream = None
+    if not args.no_stream:
+        stream = guarded("stream reference", stream_reference, tq, torch, dev)
+        stream = stream if "GB_s" in stream else None
+        if stream:
+            log(f"[bench] streaming-read reference: {stream['GB_s']:.0f} GB/s = {stream['frac_of_peak']:.1%} of peak")
     log(f"[bench] step {ms_step * 1e3:.1f} us (append {app_ms * 1e3:.1f} us, decode {dec_ms * 1e3:.1f} us); "
         f"decode {achieved:.0f} GB/s = {achieved / HBM_PEAK_GBS:.1%} of peak")
 
@@ -318,14 +545,26 @@ def main():
     # decode of the other workloads (other bit widths, QJL keys, G = 4 and 7,
     # context splits), each on its own caches, back to back
     formats = {}
+    quality = {}
+    if not args.no_quality:
+        quality["cosine_per_bits"] = guarded("cosine report", cosine_report, tq, torch, dev)
     for name in [n for n in args.formats.split(",") if n]:
         fw = tq_synth.WORKLOADS[name]
         fcap = (fw.T + 7) // 8 * 8
         fk = tq.Cache(tq.KEYS, fw.k_bits, fw.B, fw.H_kv, fcap, device=dev, qjl=bool(fw.k_qjl))
         fv = tq.Cache(tq.VALUES, fw.v_bits, fw.B, fw.H_kv, fcap, device=dev)
-        tq.quantize_kv(tq_synth.torch_kv(fw, "k", dev), fk)
-        tq.quantize_kv(tq_synth.torch_kv(fw, "v", dev), fv)
+        fxk, fxv = tq_synth.torch_kv(fw, "k", dev), tq_synth.torch_kv(fw, "v", dev)
+        tq.quantize_kv(fxk, fk)
+        tq.quantize_kv(fxv, fv)
         fq = tq_synth.torch_queries(fw, dev)
+        if not args.no_quality and name == "qwen":
+            quality["qwen_asymmetric"] = guarded("qwen quality", qwen_quality, tq, torch, dev, fw, fxk, fxv, fq, fk, fv)
+            log(f"[bench] qwen quality: {quality['qwen_asymmetric']}")
+        if not args.no_quality and name == "qjl":
+            quality["qjl_vs_mse_keys"] = guarded("qjl quality", qjl_quality, tq, torch, dev, fw, fxk, fxv, fq, fk, fv)
+            log(f"[bench] qjl quality: {quality['qjl_vs_mse_keys']}")
+        del fxk, fxv
+        torch.cuda.empty_cache()
         fws = tq.Workspace(tq.decode_workspace_bytes(fw.B, fw.H_q, fw.H_kv, fw.T, 0, fw.k_qjl), dev)
         fo = torch.empty((fw.B, fw.H_q, fw.d), dtype=torch.float32, device=dev)
         fb = decode_bytes(fw, fw.T)
@@ -403,6 +642,8 @@ def main():
                    "n_split": n_split},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),
+                     "stream_GB_s": stream["GB_s"] if stream else None,
+                     "frac_of_stream": achieved / stream["GB_s"] if stream else None,
                      "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)},0>"
                                 + (" (the whole tq_decode_attention launch)" if n_split == 1
                                    else f" + combine_kernel ({n_split} context chunks)")),
@@ -424,9 +665,20 @@ def main():
         res["formats"] = formats
     if prefill:
         res["prefill_attention"] = prefill
+    if stream is not None:
+        res["stream"] = stream
     if not args.no_cpu_baseline:
-        log("[bench] timing the CPU oracle on a bounded sample")
-        res["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
+        log("[bench] timing the CPU oracle on a bounded sample; oracle check of the sampled slices")
+        try:
+            res["cpu_baseline"], parity = cpu_baseline(w, args.cpu_budget, gpu_slices)
+        except Exception as e:   # noqa: BLE001
+            log(f"[bench] oracle check of the slices failed ({type(e).__name__}: {e}); timing only")
+            res["cpu_baseline"], parity = cpu_baseline(w, args.cpu_budget, ())
+        if parity is not None:
+            quality["parity_vs_oracle"] = parity
+            log(f"[bench] parity: {parity}")
+    if quality:
+        res["quality"] = quality
     print(json.dumps(res), flush=True)
 
 

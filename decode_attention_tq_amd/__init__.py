@@ -49,7 +49,7 @@ EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "t
            "tq_dequantize",
            "tq_decode_attention", "tq_decode_attention_noalloc", "tq_decode_attention_append", "tq_prefill_attention",
            "tq_decode_splits", "tq_decode_workspace_bytes",
-           "tq_prefill_workspace_bytes", "tq_status_string",
+           "tq_prefill_workspace_bytes", "tq_stream_read", "tq_status_string",
            "tq_last_hip_error")
 
 
@@ -93,6 +93,8 @@ def _bind(lib):
     lib.tq_decode_splits.restype = _I32
     lib.tq_decode_workspace_bytes.argtypes = [_I64, _I64, _I64, _I64, _I32, _I32]
     lib.tq_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.tq_stream_read.argtypes = [_P, ctypes.c_size_t, _P, _I32, _P]
+    lib.tq_stream_read.restype = ctypes.c_int
     lib.tq_status_string.argtypes = [ctypes.c_int]
     lib.tq_status_string.restype = ctypes.c_char_p
     lib.tq_last_hip_error.argtypes = []
@@ -301,6 +303,22 @@ def dequantize(cache: Cache, t0: int = 0, t1: int | None = None, out=None):
     _check(_lib.tq_dequantize(ctypes.byref(s), t0, t1, out.data_ptr(), _stream_handle(cache.device)),
            "tq_dequantize")
     return out
+
+
+def stream_read(buf, workgroups: int = 0, sink=None):
+    """Read the device tensor `buf` once with the library's plain streaming-read
+    kernel (a measurement reference, not part of the method); returns the sink
+    tensor of one XOR-folded word per workgroup (0 workgroups: 8 per compute unit)."""
+    torch = _torch()
+    if not buf.is_contiguous():
+        raise ValueError("buf must be contiguous")
+    if workgroups <= 0:
+        workgroups = 8 * torch.cuda.get_device_properties(buf.device).multi_processor_count
+    if sink is None or sink.numel() < workgroups:
+        sink = torch.empty(workgroups, dtype=torch.int32, device=buf.device)
+    _check(_lib.tq_stream_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(), workgroups,
+                               _stream_handle(buf.device)), "tq_stream_read")
+    return sink
 
 
 class Workspace:

@@ -23,7 +23,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_quantize.hip", "tq_host.cpp"]
+SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_quantize.hip", "tq_stream.hip", "tq_host.cpp"]
 ARCH = "gfx950"
 
 

@@ -155,6 +155,17 @@ extern "C" size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv
   return p.bytes;
 }
 
+extern "C" int tq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                              void* hip_stream) {
+  if (src == nullptr || sink == nullptr || bytes == 0 || workgroups <= 0 || workgroups > 65535)
+    return TQ_ERR_INVALID_ARGUMENT;
+  if (!aligned16(src) || bytes % 16 != 0 || ((uintptr_t)sink & 3u) != 0) return TQ_ERR_ALIGNMENT;
+  // each workgroup's slice is addressed with 32-bit offsets
+  if ((bytes + (size_t)workgroups - 1) / (size_t)workgroups >= ((size_t)1 << 31)) return TQ_ERR_UNSUPPORTED;
+  clear_pending_error();
+  return device_status(launch_stream_read(src, bytes, sink, workgroups, (hipStream_t)hip_stream));
+}
+
 extern "C" int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t T, int64_t H_kv,
                               int64_t stride_b, int64_t stride_t, int64_t stride_h,
                               const tq_cache* dst, int64_t t_offset, void* hip_stream) {

@@ -84,6 +84,10 @@ struct DecodeAppend {
   int x_dtype;
   int64_t k_sb, k_sh, v_sb, v_sh;
 };
+// Streaming-read reference (measurement helper): reads bytes of src once,
+// one XOR-folded word per workgroup into sink.
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                              hipStream_t stream);
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
                          hipStream_t stream);

@@ -335,6 +335,19 @@ int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split);
 size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
                                  int32_t n_split, int32_t k_qjl);
 
+/*
+ * Measurement helper, not a step of the method: reads `bytes` bytes of the
+ * device buffer src once with a plain streaming kernel (16-byte loads, each of
+ * `workgroups` 256-thread workgroups reading one contiguous slice, the
+ * non-temporal cache policy of the decode's streams) and writes one XOR-folded
+ * word per workgroup to sink (device uint32 [workgroups]), so that no read is
+ * dead. Its rate is the pure read stream the decode's packed-cache rate is
+ * compared with. src 16-byte aligned, bytes a nonzero multiple of 16,
+ * workgroups in 1..65535 with slices below 2 GiB. Errors before any launch;
+ * TQ_ERR_DEVICE when the launch fails.
+ */
+int tq_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups, void* hip_stream);
+
 /* Static text for a status code. */
 const char* tq_status_string(int status);
 

@@ -314,3 +314,13 @@ def test_decode_noalloc_validation_paths():
     need = tq.decode_workspace_bytes(8, 128, 8, 32768, 64, 0)
     assert need > tq.NOALLOC_SCRATCH_BYTES
     assert _decode_noalloc(big_k, big_v, H_q=128, T=32768, n_split=64) == tq.ERR_WORKSPACE_TOO_SMALL
+
+
+def test_stream_read_validation_paths():
+    lib = tq.lib()
+    assert lib.tq_stream_read(None, 1 << 20, FAKE, 8, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_stream_read(FAKE, 0, FAKE, 8, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_stream_read(FAKE, 1 << 20, FAKE, 0, None) == tq.ERR_INVALID_ARGUMENT
+    assert lib.tq_stream_read(FAKE + 8, 1 << 20, FAKE, 8, None) == tq.ERR_ALIGNMENT
+    assert lib.tq_stream_read(FAKE, (1 << 20) + 4, FAKE, 8, None) == tq.ERR_ALIGNMENT
+    assert lib.tq_stream_read(FAKE, 1 << 32, FAKE, 1, None) == tq.ERR_UNSUPPORTED
