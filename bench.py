@@ -367,7 +367,7 @@ def main():
     ap.add_argument("--prefill-iters", type=int, default=3)
     ap.add_argument("--formats", default="llama8b,qwen,qjl",
                     help="other workloads whose decode is also timed (their own bit widths); '' to skip")
-    ap.add_argument("--prefill-m", default="2,16",
+    ap.add_argument("--prefill-m", default="2,16,128",
                     help="chunk sizes M of chunked causal attention timed on the same caches ('' to skip)")
     ap.add_argument("--paged-block", type=int, default=256,
                     help="also time decode on paged caches with this many tokens per block (0: skip)")
@@ -607,13 +607,32 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / 20 * 1e3
-        Mt = M if M * w.G <= 8 else min(M, 16 // w.G)
-        tiles = -(-M // Mt)
-        pb = tiles * (decode_bytes(w, T) - w.B * w.H_q * w.d * 6) + w.B * M * w.H_q * w.d * 6
-        prefill[str(M)] = {"us": us, "query_tokens_per_s": w.B * M / (us * 1e-6), "tiles_per_row": tiles,
-                           "bytes": pb, "GB_s": pb / (us * 1e-6) / 1e9, "frac": pb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        # cache reads per call: the dense kernel reads each chunk once per group
+        # of up to 128 (token, head) columns; the tiled kernel once per tile of
+        # up to 8 (16) columns
+        nc = M * w.G
+        dense = not w.k_qjl and M > 1 and nc > 16
+        if dense:
+            waves = -(-nc // 32)
+            nwave = 4 if waves >= 4 else (2 if waves >= 2 else 1)
+            reads = -(-nc // (32 * nwave))
+            # issued fp16 MFMA work: QK (hi and lo parts) and PV over every
+            # (padded) column and cache token
+            flops = w.B * w.H_kv * reads * nwave * 32 * T * 2 * w.d * 3
+        else:
+            Mt = M if M * w.G <= 8 else min(M, 16 // w.G)
+            reads = -(-M // Mt)
+            flops = None
+        pb = reads * (decode_bytes(w, T) - w.B * w.H_q * w.d * 6) + w.B * M * w.H_q * w.d * 6
+        prefill[str(M)] = {"us": us, "query_tokens_per_s": w.B * M / (us * 1e-6),
+                           "kernel": "prefill_dense_kernel" if dense else "decode_scan_kernel (column tiles)",
+                           "cache_reads": reads, "bytes": pb, "GB_s": pb / (us * 1e-6) / 1e9,
+                           "frac": pb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+        if flops is not None:
+            prefill[str(M)]["mfma_issued_TFLOP_s"] = flops / (us * 1e-6) / 1e12
+            prefill[str(M)]["mfma_frac"] = flops / (us * 1e-6) / 1e12 / F16_MFMA_PEAK_TFLOPS
         log(f"[bench] prefill attention M={M}: {us:.1f} us, {w.B * M / (us * 1e-6):.0f} query tokens/s, "
-            f"{pb / (us * 1e-6) / 1e9:.0f} GB/s")
+            f"{pb / (us * 1e-6) / 1e9:.0f} GB/s ({prefill[str(M)]['kernel']}, {reads} cache reads)")
         del pws, po, pq
 
     # calibration copy of known size for the rocprofv3 byte counters (256 MiB read + write)

@@ -23,7 +23,10 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_quantize.hip", "tq_stream.hip", "tq_host.cpp"]
+SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_prefill.hip", "tq_quantize.hip", "tq_stream.hip", "tq_host.cpp"]
+# MFMA accumulators in ordinary VGPRs (no accumulation-register copies around
+# the softmax rescale); a source listed here with False keeps the default
+VGPR_FORM = {}
 ARCH = "gfx950"
 
 
@@ -34,14 +37,12 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libtq.so)")
 
 
-def _flags():
+def _flags(src: str = ""):
     return [
         f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
         # packed fp32 instructions stay off: ordinary float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        # MFMA accumulators in ordinary VGPRs (no accumulation-register copies
-        # around the softmax rescale)
-        "-mllvm", "-amdgpu-mfma-vgpr-form",
+        *(["-mllvm", "-amdgpu-mfma-vgpr-form"] if VGPR_FORM.get(src, True) else []),
         "-Wno-unused-command-line-argument",
         f"-I{INCLUDE}", f"-I{CSRC}",
     ]
@@ -49,9 +50,9 @@ def _flags():
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc(), *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc(), *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
     if src.endswith(".cpp"):
-        cmd = [hipcc(), "-x", "hip", *_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [hipcc(), "-x", "hip", *_flags(src), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

@@ -117,6 +117,47 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   return true;
 }
 
+bool plan_prefill_dense(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t M, int32_t n_split, DensePlan* p) {
+  if (B <= 0 || H_q <= 0 || H_kv <= 0 || T < 0 || n_split < 0 || M <= 1) return false;
+  if (H_q % H_kv != 0) return false;
+  const int64_t G = H_q / H_kv;
+  if (G > 16 || M * G > (int64_t)1 << 30) return false;
+  p->B = B;
+  p->H_q = H_q;
+  p->H_kv = H_kv;
+  p->T = T;
+  p->M = M;
+  p->G = (int32_t)G;
+  p->NC = (int32_t)(M * G);
+  const int64_t waves = (p->NC + kDenseWaveCols - 1) / kDenseWaveCols;
+  p->nwave = waves >= 4 ? 4 : (waves >= 2 ? 2 : 1);
+  p->ncg = (int32_t)((p->NC + kDenseWaveCols * p->nwave - 1) / (kDenseWaveCols * p->nwave));
+  if (B * p->ncg > 65535 || B * M > 65535) return false;   // grid z of the scan, grid y of the combine
+  const int64_t Tp = T > 0 ? T : 1;
+  int64_t target;
+  if (n_split > 0) {
+    target = n_split;
+  } else {
+    // about two wavefronts per SIMD of a 256-CU part; chunks of at least 512 tokens
+    const int64_t units = B * H_kv * p->ncg * p->nwave;
+    target = (8 * kDecodeTargetWGs + units - 1) / units;
+    const int64_t cap = (Tp + 511) / 512;
+    if (target > cap) target = cap;
+    if (target < 1) target = 1;
+  }
+  int64_t chunk = (Tp + target - 1) / target;
+  chunk = (chunk + kStep - 1) / kStep * kStep;
+  p->chunk = (int32_t)chunk;
+  p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
+  size_t off = 0;
+  p->off_ml = off;
+  off = align256(off + (size_t)(B * M * H_q) * p->n_split * 2 * sizeof(float));
+  p->off_acc = off;
+  off = align256(off + (size_t)(B * M * H_q) * p->n_split * kD * sizeof(float));
+  p->bytes = off;
+  return true;
+}
+
 }  // namespace tq
 
 using namespace tq;
@@ -143,6 +184,10 @@ extern "C" int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t 
 
 extern "C" size_t tq_prefill_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t M, int64_t T,
                                              int32_t n_split, int32_t k_qjl) {
+  if (H_kv > 0 && H_q % H_kv == 0 && use_dense_prefill(M, H_q / H_kv, k_qjl)) {
+    DensePlan dp;
+    return plan_prefill_dense(B, H_q, H_kv, T, M, n_split, &dp) ? dp.bytes : 0;
+  }
   DecodePlan p;
   if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p, M)) return 0;
   return p.bytes;
@@ -282,8 +327,15 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   if (M > 65535) return TQ_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
+  const bool dense = app == nullptr && use_dense_prefill(M, H_q / k->H_kv, k->qjl);
   DecodePlan p;
-  if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) return TQ_ERR_UNSUPPORTED;
+  DensePlan dp;
+  if (dense) {
+    if (!plan_prefill_dense(k->B, H_q, k->H_kv, T, M, n_split, &dp)) return TQ_ERR_UNSUPPORTED;
+    p.bytes = dp.bytes;
+  } else if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) {
+    return TQ_ERR_UNSUPPORTED;
+  }
   if (wsa.scratch) {
     if (p.bytes > (size_t)TQ_NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE_TOO_SMALL;
   } else {
@@ -320,6 +372,9 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
     return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                        (hipStream_t)hip_stream));
   }
+  if (dense)
+    return device_status(launch_prefill_dense(dp, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
+                                              (hipStream_t)hip_stream));
   return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
                                      (hipStream_t)hip_stream));
 }

@@ -1074,8 +1074,14 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   if (err != hipSuccess || p.n_split == 1) return err;
 
   // the combine sees B * M query rows of H_q heads
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)p.H_kv, (unsigned)(p.B * p.M), kD / 32), dim3(256), 0, stream, ml, acc,
-                     v->rot, out, (int)p.H_q, p.G, p.n_split, inv_sqrt_d);
+  return launch_combine(ml, acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, stream);
+}
+
+hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
+                          int64_t H_kv, int64_t H_q, int G, int n_split, hipStream_t stream) {
+  const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)H_kv, (unsigned)rows, kD / 32), dim3(256), 0, stream, ml, acc,
+                     rotV, out, (int)H_q, G, n_split, inv_sqrt_d);
   return hipGetLastError();
 }
 

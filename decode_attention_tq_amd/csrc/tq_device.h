@@ -108,6 +108,13 @@ template <int N>
 __device__ inline float bcast_row_c(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, false));
 }
+// The same broadcast as a plain DPP move (no old value to preserve: every lane
+// reads a valid lane), for a value that several instructions use.
+template <int N>
+__device__ inline float bcast_row_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x150 + N, 0xF, 0xF, true));
+}
+
 // Same with n known only after loop unrolling (the switch folds away).
 __device__ inline float bcast_row(float x, int n) {
   switch (n) {

@@ -36,6 +36,24 @@ struct DecodePlan {
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
                  DecodePlan* p, int64_t M = 1);
 
+// Dense chunked-prefill planning: every wavefront takes kDenseWaveCols
+// (token, head) columns of one KV head, a workgroup 1, 2 or 4 wavefronts
+// (nwave) that scan the same context chunk; ncg column groups per (row, KV
+// head); n_split context chunks, merged (and rotated back) by the decode's
+// combine kernel.
+constexpr int kDenseWaveCols = 32;
+struct DensePlan {
+  int64_t B, H_q, H_kv, T, M;
+  int32_t G, NC, nwave, ncg, n_split, chunk;
+  size_t off_ml, off_acc, bytes;   // chunk partials [B*M*H_q][n_split][2], [..][d]
+};
+
+// The dense kernel takes chunked attention without QJL keys once the columns
+// (M tokens x G heads) exceed one 16-column tile of the decode kernel.
+inline bool use_dense_prefill(int64_t M, int64_t G, int32_t qjl) { return qjl == 0 && M > 1 && M * G > 16; }
+
+bool plan_prefill_dense(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t M, int32_t n_split, DensePlan* p);
+
 // Block table of a cache in the paged layout; table == nullptr for the
 // contiguous layout. Token t of (row b, head h) is token row
 // (table[b][t >> lg] * H_kv + h) * 2^lg + t % 2^lg of the arrays.
@@ -88,6 +106,12 @@ struct DecodeAppend {
 // one XOR-folded word per workgroup into sink.
 hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
                               hipStream_t stream);
+hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_cache* v, const void* q, int q_dtype,
+                                const int32_t* ctx_lens, float scale, float* out, void* ws, hipStream_t stream);
+// Fixed-order merge of context-chunk partials ([rows*H_q][n_split][2] and
+// [rows*H_q][n_split][d]) and the inverse rotation, into out [rows][H_q][d].
+hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
+                          int64_t H_kv, int64_t H_q, int G, int n_split, hipStream_t stream);
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
                          hipStream_t stream);

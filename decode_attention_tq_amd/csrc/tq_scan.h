@@ -41,6 +41,12 @@ __device__ inline float bf16_bits_to_f32(uint16_t h) { return __uint_as_float((u
 // unreplicated random reads cost more LDS time than they save on this part.)
 constexpr int kLutBytes = 256 * 256;
 
+// A compile-time flag passed to generic lambdas.
+template <int V>
+struct IntConst {
+  static constexpr int value = V;
+};
+
 // Thread (slot, quarter) writes 8 replicas of the slot's key pair and 8 of its
 // value pair (two 16-byte stores each), so each pair is formed once per thread.
 template <int KB, int VB>

@@ -25,7 +25,12 @@ CASES = {
     "llama8b_M2": (W["llama8b"].scaled(T=1500), 2),               # G = 4: 8 columns, 16-wave tile
     "qwen_M5": (W["qwen"].scaled(B=2, T=1200), 5),                # G = 7, K4/V2
     "qjl_M9": (W["qjl"].scaled(B=2, T=1024), 9),                  # QJL keys
-    "tiny_M3": (W["tiny"], 3),                                    # fp32, G = 16
+    "tiny_M3": (W["tiny"], 3),                                    # fp32, G = 16 (dense: 48 columns)
+    # the dense kernel (32 (token, head) columns per wavefront, one cache read per chunk)
+    "stress70b_M16": (W["stress70b"].scaled(B=2, T=2048), 16),    # 128 columns: one 4-wavefront group
+    "llama8b_M16": (W["llama8b"].scaled(B=2, T=1500), 16),        # G = 4: 64 columns, ragged T
+    "stress70b_M100": (W["stress70b"].scaled(B=1, T=1200), 100),  # 800 columns: 7 groups, last one partial
+    "qwen_M9_k4v2": (W["qwen"].scaled(B=2, T=1000), 9),           # G = 7, K4/V2, large key norms
 }
 
 
@@ -103,6 +108,31 @@ def test_prefill_matches_oracle(tq, name):
         # the last token of the chunk is a decode over the whole context
         d = tq.decode_attention(kc, vc, q[:, -1].contiguous(), ctx_lens=cl, T=w.T)
         assert rel_l2(out[:, -1].cpu().numpy(), d.cpu().numpy()) <= TOL_RECUT
+
+
+@pytest.mark.parametrize("name", ["stress70b_M16", "llama8b_M16"])
+def test_prefill_dense_paged_equals_contiguous(tq, name):
+    """The dense kernel on paged caches (32-token blocks through a seeded
+    permutation) gives the contiguous result bit for bit."""
+    w, M = CASES[name]
+    T_cap = (w.T + 31) // 32 * 32
+    bt, maxblk = 32, T_cap // 32
+    perm = torch.randperm(w.B * maxblk, generator=torch.Generator().manual_seed(8), dtype=torch.int64)
+    table = perm.to(torch.int32).reshape(w.B, maxblk).cuda()
+    log(f"dense prefill paged {name}: M={M}")
+    out = []
+    for paged in (False, True):
+        kw = dict(block_table=table, block_tokens=bt, n_blocks=w.B * maxblk) if paged else {}
+        kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, **kw)
+        vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, **kw)
+        tq.quantize_kv(device_inputs(w, "k"), kc)
+        tq.quantize_kv(device_inputs(w, "v"), vc)
+        q, _ = _queries(w, M)
+        cl = torch.tensor([w.T] + [max(w.T - 333 * b, M // 2) for b in range(1, w.B)], dtype=torch.int32,
+                          device="cuda")
+        out.append(tq.prefill_attention(kc, vc, q, ctx_lens=cl, T=w.T))
+    torch.cuda.synchronize()
+    assert torch.equal(out[0], out[1])
 
 
 def test_prefill_single_token_is_decode(tq):
