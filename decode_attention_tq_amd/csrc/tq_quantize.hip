@@ -648,6 +648,437 @@ __global__ __launch_bounds__(64 * kQ32Waves) void quantize32_kernel(QuantArgs a)
   }
 }
 
+// ---------------------------------- quantize, bfloat16 input, 32-vector tiles --
+//
+// bfloat16 input needs no conversion on v_mfma_f32_32x32x16_bf16: the raw
+// 16-byte loads of x are the MFMA operands as they stand. Pi is split once per
+// workgroup into three bfloat16 parts (hi + mid + lo hold 24 significant bits,
+// float32's precision), so y = Pi x takes three MFMAs per 16 coordinates, each
+// product exact, accumulated in float32. The norm comes from v_dot2_f32_bf16 on
+// the same words; a vector whose squared norm leaves [2^-100, 2^100] is first
+// rescaled by a power of two (exact), so neither the norm nor y under- or
+// overflows.
+//
+// Codes leave as bits, not bytes: each comparison of the cell search yields a
+// lane mask, and v_addc_co_u32 (w + w + carry) shifts one such bit per lane into
+// a word. A lane pushes its codes in descending stream position, so the last
+// bit pushed lands at bit 0 and the words come out in the packed layout. The
+// MFMA operand roles are chosen so that what a lane holds is contiguous there:
+//  - keys: A = Pi, B = x. The rows of Pi are staged in the order that gives
+//    lane (vector v, half h) coordinate 64h + 16jb + e in element e of block
+//    jb: 2*BITS consecutive words of token v's row per lane.
+//  - values: A = x, B = Pi^T. Lane (column j, half h) receives coordinate
+//    32jb + j of the vectors of slots 16h + e (the rows of x are loaded in that
+//    order): for each of its two 8-token blocks, the 8*BITS bits of one
+//    coordinate. The four lanes of a quad (coordinates 4cg .. 4cg+3) merge
+//    their pieces into the block's BITS words of that coordinate group.
+// Keys compare y with thresholds scaled per vector (t_i |x| / sqrt(d)); values,
+// whose lanes hold 16 vectors each, compare z = y sqrt(d) / |x|.
+constexpr int kQbWaves = 16;
+constexpr int kQbPart = 8 * 4 * 64;   // 16-byte pieces of one bfloat16 part of Pi
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+__device__ inline floatx16 mfma32bf(u32x4 a, u32x4 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+// Row of Pi that operand row i (0..31) of output block jb holds.
+template <int ROLE>
+__device__ inline int qb_pi_row(int jb, int i) {
+  if constexpr (ROLE == TQ_KEYS) return 64 * ((i >> 2) & 1) + 16 * jb + (i & 3) + 4 * (i >> 3);
+  else return 32 * jb + i;
+}
+
+// Slot (within the wavefront's 32) whose vector lane row i of the x operand
+// holds: keys take slot i; values the order that gives output lane half h the
+// slots 16h .. 16h+15 in element order.
+template <int ROLE>
+__device__ inline int qb_slot(int i) {
+  if constexpr (ROLE == TQ_KEYS) return i;
+  else return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3);
+}
+
+__device__ inline uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// op[part][ks][jb][lane] (16 bytes) = part of Pi[qb_pi_row(jb, lane % 32)][16ks + 8(lane / 32) + e].
+template <int ROLE>
+__device__ void stage_matrix_bf16(const float* M, u32x4* op) {
+  constexpr int NT = 64 * kQbWaves;
+  constexpr int PER = kQbPart / NT;
+  float4 v[PER][2];
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const int piece = threadIdx.x + k * NT;
+    const int ln = piece & 63, jb = (piece >> 6) & 3, ks = piece >> 8;
+    const float4* src = (const float4*)(M + qb_pi_row<ROLE>(jb, ln & 31) * kD + 16 * ks + 8 * (ln >> 5));
+    v[k][0] = src[0];
+    v[k][1] = src[1];
+  }
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    const float x[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w, v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+    uint32_t hw[8], mw[8], lw[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const __bf16 hi = (__bf16)x[e];
+      const float r1 = x[e] - (float)hi;
+      const __bf16 mid = (__bf16)r1;
+      const float r2 = r1 - (float)mid;
+      hw[e] = __builtin_bit_cast(uint16_t, hi);
+      mw[e] = __builtin_bit_cast(uint16_t, mid);
+      lw[e] = bf16_bits(r2);
+    }
+    const int piece = threadIdx.x + k * NT;
+    op[piece] = u32x4{hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16};
+    op[kQbPart + piece] = u32x4{mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16};
+    op[2 * kQbPart + piece] =
+        u32x4{lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16};
+  }
+}
+
+// w * 2 + (bit of this lane in m): one code bit shifted into a word.
+// The instruction is written out (the compiler folds w + w + carry into a shift
+// and a select), so the compiler's hazard tracking does not see that it is a
+// vector instruction reading and writing scalar registers. Two rules keep it
+// safe: its carry-out goes to `sink`, a scalar pair that only these pushes
+// write and that stays live across the caller's loop (a scalar instruction must
+// never write a register whose vector write of lanes 32-63 may still be in
+// flight), and two wait states follow it before any other instruction may
+// overwrite the mask it reads.
+// A mask written by a vector compare also needs two wait states before a vector
+// instruction reads it: VALU_MASK = 1 puts them in front (masks made by scalar
+// instructions need none).
+template <int VALU_MASK>
+__device__ inline uint32_t push_bit(uint32_t w, uint64_t m, uint64_t& sink) {
+  uint32_t r;
+  if constexpr (VALU_MASK)
+    asm("s_nop 1\n\tv_addc_co_u32 %0, %1, %2, %2, %3\n\ts_nop 1" : "=v"(r), "+s"(sink) : "v"(w), "s"(m));
+  else
+    asm("v_addc_co_u32 %0, %1, %2, %2, %3\n\ts_nop 1" : "=v"(r), "+s"(sink) : "v"(w), "s"(m));
+  return r;
+}
+
+__device__ inline uint64_t lanes(bool c) { return __builtin_amdgcn_ballot_w64(c); }
+
+// Lane masks of the bits of code(z) (bit k in m[k]) for ascending thresholds
+// t[0 .. 2^BITS - 2], the cells encode<BITS, SYM> gives. A mirrored codebook
+// searches |z| over the positive half and takes the mirrored cell for z < 0:
+// the top bit is [z >= 0] and the others are the magnitude's bits, inverted for
+// z < 0; every mask it returns is made by a scalar instruction. The general
+// search returns the compare masks themselves.
+template <int BITS, int SYM>
+__device__ inline void code_masks(float z, const float* t, uint64_t (&m)[BITS]) {
+  if constexpr (SYM) {
+    const float* p = t + (1 << (BITS - 1));
+    const uint64_t neg = lanes(z < 0.f);
+    const float x = fabsf(z);
+    m[BITS - 1] = ~neg;
+    if constexpr (BITS == 2) {
+      m[0] = lanes(x >= p[0]) ^ neg;
+    } else if constexpr (BITS == 3) {
+      const bool c1 = x >= p[1];
+      const bool c0 = x >= (c1 ? p[2] : p[0]);
+      m[1] = lanes(c1) ^ neg;
+      m[0] = lanes(c0) ^ neg;
+    } else {
+      const bool c2 = x >= p[3];
+      const bool c1 = x >= (c2 ? p[5] : p[1]);
+      const float lo = c2 ? p[4] : p[0], hi = c2 ? p[6] : p[2];   // (flat selects, no branches)
+      const bool c0 = x >= (c1 ? hi : lo);
+      m[2] = lanes(c2) ^ neg;
+      m[1] = lanes(c1) ^ neg;
+      m[0] = lanes(c0) ^ neg;
+    }
+  } else {
+    if constexpr (BITS == 2) {
+      const bool c1 = z >= t[1];
+      const bool c0 = z >= (c1 ? t[2] : t[0]);
+      m[1] = lanes(c1);
+      m[0] = lanes(c0);
+    } else if constexpr (BITS == 3) {
+      const bool c2 = z >= t[3];
+      const bool c1 = z >= (c2 ? t[5] : t[1]);
+      const float lo = c2 ? t[4] : t[0], hi = c2 ? t[6] : t[2];
+      const bool c0 = z >= (c1 ? hi : lo);
+      m[2] = lanes(c2);
+      m[1] = lanes(c1);
+      m[0] = lanes(c0);
+    } else {
+      const bool c3 = z >= t[7];
+      const bool c2 = z >= (c3 ? t[11] : t[3]);
+      const float a1 = c3 ? t[9] : t[1], b1 = c3 ? t[13] : t[5];
+      const bool c1 = z >= (c2 ? b1 : a1);
+      const float a0 = c3 ? t[8] : t[0], b0 = c3 ? t[10] : t[2], e0 = c3 ? t[12] : t[4], f0 = c3 ? t[14] : t[6];
+      const float g0 = c2 ? e0 : a0, h0 = c2 ? f0 : b0;
+      const bool c0 = z >= (c1 ? h0 : g0);
+      m[3] = lanes(c3);
+      m[2] = lanes(c2);
+      m[1] = lanes(c1);
+      m[0] = lanes(c0);
+    }
+  }
+}
+
+// Lanes i and i + 32 combine x (both get the result). The exchange runs
+// through ds_bpermute: v_permlane32_swap on a just-copied register gave lanes
+// 32-63 a stale copy here, with the wait states the compiler puts in front.
+__device__ inline float sum_halves(float x) { return x + shfl_xor_f(x, 32); }
+__device__ inline float max_halves(float x) { return fmaxf(x, shfl_xor_f(x, 32)); }
+
+// Sum of squares of the 64 bfloat16 coordinates of a lane, two per
+// v_dot2c_f32_bf16. (Written as an instruction: with this compiler the dot2
+// builtin on bit-cast words reads the first word of each vector only.)
+__device__ inline float sumsq_bf16(const RawX32<0>& r) {
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) asm("v_dot2c_f32_bf16 %0, %1, %1" : "+v"(ss) : "v"(r.v[k][w]));
+  }
+  return ss;
+}
+
+// One 32-coordinate output block jb of y = Pi x (three bfloat16 parts of Pi, the
+// smallest first), the operands of step ks + 1 read from LDS while step ks runs.
+template <int ROLE>
+__device__ inline floatx16 rotate_bf16(const u32x4* piop, const RawX32<0>& x, int jb, int lane) {
+  floatx16 acc = {};
+  u32x4 cur[3], nxt[3];
+  auto read = [&](int ks, u32x4(&o)[3]) {
+    const int i = (ks * 4 + jb) * 64 + lane;
+    o[0] = piop[2 * kQbPart + i];
+    o[1] = piop[kQbPart + i];
+    o[2] = piop[i];
+  };
+  read(0, cur);
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) {
+    if (ks < 7) read(ks + 1, nxt);
+#pragma unroll
+    for (int part = 0; part < 3; ++part) {
+      if constexpr (ROLE == TQ_KEYS) acc = mfma32bf(cur[part], x.v[ks], acc);
+      else acc = mfma32bf(x.v[ks], cur[part], acc);
+    }
+    if (ks < 7) {
+#pragma unroll
+      for (int part = 0; part < 3; ++part) cur[part] = nxt[part];
+    }
+  }
+  return acc;
+}
+
+template <int BITS, int ROLE>
+__global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs a) {
+  constexpr int TILE = 32 * kQbWaves;
+  constexpr int NT = (1 << BITS) - 1;
+  extern __shared__ __align__(16) unsigned char smem[];
+  u32x4* piop = (u32x4*)smem;                                 // [3][ks][jb][lane]
+  float* fzs = (float*)(smem + 3 * kQbPart * sizeof(u32x4));   // [wave][32]: sqrt(d) / |x| by slot
+
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int i32 = lane & 31, kh = lane >> 5;
+  const int slot = qb_slot<ROLE>(i32);
+  RawX32<0> cur;
+  if (blockIdx.x < a.n_tiles) load_raw32<0>(cur, a, blockIdx.x, wave, slot, kh);
+  stage_matrix_bf16<ROLE>(a.rot, piop);
+  __syncthreads();
+
+  const Thresholds<BITS> th = load_thresholds<BITS>(a);
+  const float sqrt_d = sqrtf((float)kD);
+  const int64_t heads = a.B * a.H_kv;
+  uint64_t sink = 0;   // carry-outs of the bit pushes (never read)
+
+  for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
+    RawX32<0> nxt;
+    if (tile + gridDim.x < a.n_tiles) load_raw32<0>(nxt, a, tile + gridDim.x, wave, slot, kh);
+    const int64_t s0 = tile * TILE + wave * 32;
+
+    // ---- norm (and a power-of-two rescale of vectors far from 1)
+    float ss = sum_halves(sumsq_bf16(cur));
+    int sexp = 0;
+    const bool rescale = cur.valid && !(ss >= 0x1p-100f && ss <= 0x1p100f);
+    if (lanes(rescale) != 0) {
+      // (rare: one word at a time, so this path adds no register pressure)
+      uint32_t mb = 0u;   // largest magnitude, as bfloat16 bits (ordered like the values)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const uint32_t m = cur.v[k][w] & 0x7FFF7FFFu;
+          mb = max(mb, max(m & 0xFFFFu, m >> 16));
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+      const float mx = max_halves(__uint_as_float(mb << 16));
+      sexp = (rescale && mx > 0.f) ? -__builtin_amdgcn_frexp_expf(mx) : 0;   // largest entry in [1/2, 1)
+      if (sexp != 0) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+#pragma unroll
+          for (int w = 0; w < 4; ++w) {
+            const float lo = ldexpf(__uint_as_float(cur.v[k][w] << 16), sexp);
+            const float hi = ldexpf(__uint_as_float(cur.v[k][w] & 0xFFFF0000u), sexp);
+            cur.v[k][w] = bf16_bits(lo) | bf16_bits(hi) << 16;
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      ss = sum_halves(sumsq_bf16(cur));
+    }
+    // |x| * 2^sexp, and sqrt(d) / that (single instructions, within 2 ulp: the
+    // code decisions are tested outside a 1e-6 band around each threshold)
+    const float ns = __builtin_amdgcn_sqrtf(ss);
+    const float fz = ns > 0.f ? sqrt_d * __builtin_amdgcn_rcpf(ns) : 0.f;
+    if (cur.valid && kh == 0) {
+      int64_t bh, t;
+      slot_pos(a, s0, slot, bh, t);
+      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
+    }
+
+    if constexpr (ROLE == TQ_KEYS) {
+      // Mirrored codebook: y against thresholds in units of y (the positive
+      // half only, few registers). A zero vector (y = 0) belongs in the cell of
+      // z = 0, #{t_i <= 0}: the floor on the scale keeps each threshold's sign
+      // (nonzero norms are at least 2^-50 here, far above it). Any other
+      // codebook: z = y sqrt(d) / |x| against the thresholds themselves.
+      float ts[NT];
+      const float sc = fmaxf(ns * (1.f / sqrt_d), 0x1p-100f);
+#pragma unroll
+      for (int i = 0; i < NT; ++i) ts[i] = th.t[i] * sc;
+      int64_t row = -1;
+      if (cur.valid) {
+        int64_t bh, t;
+        slot_pos(a, s0, slot, bh, t);
+        row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+      }
+      auto run = [&](auto sym) {
+        constexpr int SYM = decltype(sym)::value;
+        // two output blocks (32 coordinates, BITS words) per pass
+#pragma unroll 1
+        for (int p = 0; p < 2; ++p) {
+          uint32_t w[BITS];
+#pragma unroll
+          for (int k = 0; k < BITS; ++k) w[k] = 0u;
+#pragma unroll
+          for (int jj = 1; jj >= 0; --jj) {
+            const int jb = 2 * p + jj;
+            const floatx16 acc = rotate_bf16<ROLE>(piop, cur, jb, lane);
+#pragma unroll
+            for (int e = 15; e >= 0; --e) {
+              uint64_t m[BITS];
+              if constexpr (SYM) code_masks<BITS, 1>(acc[e], ts, m);
+              else code_masks<BITS, 0>(acc[e] * fz, th.t, m);
+#pragma unroll
+              for (int k = BITS - 1; k >= 0; --k) {
+                const int pos = BITS * (16 * jj + e) + k;
+                w[pos >> 5] = push_bit<!SYM>(w[pos >> 5], m[k], sink);
+              }
+              if (e % 2 == 0) __builtin_amdgcn_sched_barrier(0);   // two codes' masks in flight at most
+            }
+          }
+          if (row >= 0) {
+            uint32_t* dst = a.codes + row * (4 * BITS) + 2 * BITS * kh + BITS * p;
+#pragma unroll
+            for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+          }
+        }
+      };
+      if (th.sym)
+        run(IntTag<1>{});
+      else
+        run(IntTag<0>{});
+    } else {
+      if (kh == 0) fzs[wave * 32 + slot] = fz;
+      wave_sync();
+      // the lane's two 8-token blocks 2kh + bi: first row, and the bits of the
+      // block's words that belong to tokens outside [t_offset, t_offset + T)
+      const int qm = lane & 3;                       // word of the coordinate group this lane forms
+      const int qa = (4 * qm) / BITS;                // first quad lane whose piece it needs
+      const uint32_t sa = 32 * qm - 8 * BITS * qa;   // that piece's shift
+      const uint32_t sb = 8 * BITS - sa;             // and the next one's
+      int64_t brow[2];
+      uint32_t keep[2];
+#pragma unroll
+      for (int bi = 0; bi < 2; ++bi) {
+        int64_t bh, tb;
+        slot_pos(a, s0, 8 * (2 * kh + bi), bh, tb);
+        int lo = 8, hi = 0;   // valid tokens [lo, hi) of the block
+        if (bh < heads) {
+          const int64_t l = a.t_offset - tb, h = a.t_offset + a.T - tb;
+          lo = (int)(l < 0 ? 0 : (l > 8 ? 8 : l));
+          hi = (int)(h < 0 ? 0 : (h > 8 ? 8 : h));
+        }
+        brow[bi] = lo < hi ? tok_row(a.pm, a.H_kv, a.T_cap, bh, tb) : -1;
+        // per piece: bits of tokens below lo or from hi on
+        const uint64_t piece_keep =
+            ((1ull << (BITS * lo)) - 1ull) | (((1ull << (8 * BITS)) - 1ull) & ~((1ull << (BITS * (lo < hi ? hi : lo))) - 1ull));
+        keep[bi] = BITS == 4 ? (uint32_t)piece_keep
+                             : (uint32_t)(piece_keep >> sa) | (uint32_t)(piece_keep << sb);
+      }
+      auto run = [&](auto sym) {
+        constexpr int SYM = decltype(sym)::value;
+#pragma unroll 1
+        for (int jb = 0; jb < 4; ++jb) {
+          const floatx16 acc = rotate_bf16<ROLE>(piop, cur, jb, lane);
+          const float4* fz4 = (const float4*)(fzs + wave * 32 + 16 * kh);
+          float fz[16];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const float4 f = fz4[q];
+            fz[4 * q] = f.x;
+            fz[4 * q + 1] = f.y;
+            fz[4 * q + 2] = f.z;
+            fz[4 * q + 3] = f.w;
+          }
+          uint32_t piece[2];
+#pragma unroll
+          for (int bi = 0; bi < 2; ++bi) {
+            uint32_t c = 0u;
+#pragma unroll
+            for (int ti = 7; ti >= 0; --ti) {
+              uint64_t m[BITS];
+              code_masks<BITS, SYM>(acc[8 * bi + ti] * fz[8 * bi + ti], th.t, m);
+#pragma unroll
+              for (int k = BITS - 1; k >= 0; --k) c = push_bit<!SYM>(c, m[k], sink);
+              // (two codes' lane masks in flight at most: they live in scalar registers)
+              if (ti % 2 == 0) __builtin_amdgcn_sched_barrier(0);
+            }
+            piece[bi] = c;
+          }
+          // quad merge: word qm of coordinate group 8jb + j/4 = bits [32qm, 32qm + 32) of the
+          // concatenated pieces of coordinates 4cg .. 4cg+3 (8*BITS bits each)
+          constexpr int PA = BITS == 2 ? 0x08 : 0xE4;   // quad lane of the first piece
+          constexpr int PB = BITS == 2 ? 0x0D : 0xF9;   // and of the second
+#pragma unroll
+          for (int bi = 0; bi < 2; ++bi) {
+            uint32_t word;
+            if constexpr (BITS == 4) {
+              word = piece[bi];
+            } else {
+              const uint32_t pa = BITS == 3 ? piece[bi] : (uint32_t)__builtin_amdgcn_mov_dpp((int)piece[bi], PA, 0xF, 0xF, false);
+              const uint32_t pb = (uint32_t)__builtin_amdgcn_mov_dpp((int)piece[bi], PB, 0xF, 0xF, false);
+              word = (pa >> sa) | (pb << sb);
+            }
+            if (qm < BITS && brow[bi] >= 0) {
+              uint32_t* dst = a.codes + brow[bi] * (4 * BITS) + (8 * jb + (i32 >> 2)) * BITS + qm;
+              *dst = keep[bi] == 0u ? word : ((*dst & keep[bi]) | (word & ~keep[bi]));
+            }
+          }
+        }
+      };
+      if (th.sym)
+        run(IntTag<1>{});
+      else
+        run(IntTag<0>{});
+    }
+    wave_sync();   // the scale buffer is rewritten by the next tile
+    cur = nxt;
+  }
+  asm volatile("" ::"s"(sink));   // the carry-out pair stays reserved to the end
+}
+
 // ------------------------------------------------- single-token append --
 //
 // One token per (row, head) (T = 1) without QJL: latency, not throughput,
@@ -851,9 +1282,25 @@ hipError_t launch_q32(const QuantArgs& qa, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int BITS, int ROLE>
+hipError_t launch_qbf(const QuantArgs& qa, hipStream_t stream) {
+  static_assert(kQbWaves == kQ32Waves, "the tile loader assumes 32 * kQ32Waves slots per tile");
+  constexpr size_t smem = 3 * kQbPart * sizeof(u32x4) + kQbWaves * 32 * sizeof(float);
+  auto kern = quantize_bf16_kernel<BITS, ROLE>;
+  static const hipError_t attr =
+      hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+  if (attr != hipSuccess) return attr;
+  int64_t grid = compute_units();   // one workgroup (16 wavefronts, ~98 KB of LDS) per compute unit
+  if (grid > qa.n_tiles) grid = qa.n_tiles;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(64 * kQbWaves), smem, stream, qa);
+  return hipGetLastError();
+}
+
 // Bulk work (at least one 512-slot tile per compute unit) takes the 32-vector
-// tiles; short appends take the 16-vector tiles, which spread the same slots
-// over 4x more workgroups and finish sooner.
+// tiles (bfloat16 input on bfloat16 MFMAs, float32 input split into float16
+// hi + lo); short appends take the 16-vector tiles, which spread the same
+// slots over 4x more workgroups and finish sooner.
 template <int BITS, int ROLE, int QJL>
 hipError_t dispatch_x(int xf32, QuantArgs qa, hipStream_t s) {
   if constexpr (!QJL) {
@@ -861,7 +1308,7 @@ hipError_t dispatch_x(int xf32, QuantArgs qa, hipStream_t s) {
     const int64_t tiles32 = (slots + 32 * kQ32Waves - 1) / (32 * kQ32Waves);
     if (tiles32 >= compute_units()) {
       qa.n_tiles = tiles32;
-      return xf32 ? launch_q32<BITS, ROLE, 1>(qa, s) : launch_q32<BITS, ROLE, 0>(qa, s);
+      return xf32 ? launch_q32<BITS, ROLE, 1>(qa, s) : launch_qbf<BITS, ROLE>(qa, s);
     }
   }
   const int64_t tile16 = 16 * quant_waves<QJL>();
