@@ -701,7 +701,12 @@ __device__ inline int qb_slot(int i) {
 
 __device__ inline uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
 
-// op[part][ks][jb][lane] (16 bytes) = part of Pi[qb_pi_row(jb, lane % 32)][16ks + 8(lane / 32) + e].
+// op[jb][ks][part][lane] (16 bytes) = part (0 hi, 1 mid, 2 lo) of
+// Pi[qb_pi_row(jb, lane % 32)][16ks + 8(lane / 32) + e]: the 24 pieces of one
+// output block lie within 24 KB, so one address register and the instruction's
+// immediate offset reach every read of two blocks.
+__device__ inline int qb_piece(int jb, int ks, int part) { return ((jb * 8 + ks) * 3 + part) * 64; }
+
 template <int ROLE>
 __device__ void stage_matrix_bf16(const float* M, u32x4* op) {
   constexpr int NT = 64 * kQbWaves;
@@ -710,7 +715,7 @@ __device__ void stage_matrix_bf16(const float* M, u32x4* op) {
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const int piece = threadIdx.x + k * NT;
-    const int ln = piece & 63, jb = (piece >> 6) & 3, ks = piece >> 8;
+    const int ln = piece & 63, ks = (piece >> 6) & 7, jb = piece >> 9;
     const float4* src = (const float4*)(M + qb_pi_row<ROLE>(jb, ln & 31) * kD + 16 * ks + 8 * (ln >> 5));
     v[k][0] = src[0];
     v[k][1] = src[1];
@@ -730,10 +735,10 @@ __device__ void stage_matrix_bf16(const float* M, u32x4* op) {
       lw[e] = bf16_bits(r2);
     }
     const int piece = threadIdx.x + k * NT;
-    op[piece] = u32x4{hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16};
-    op[kQbPart + piece] = u32x4{mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16};
-    op[2 * kQbPart + piece] =
-        u32x4{lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16};
+    const int ln = piece & 63, ks = (piece >> 6) & 7, jb = piece >> 9;
+    op[qb_piece(jb, ks, 0) + ln] = u32x4{hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16};
+    op[qb_piece(jb, ks, 1) + ln] = u32x4{mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16};
+    op[qb_piece(jb, ks, 2) + ln] = u32x4{lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16};
   }
 }
 
@@ -845,11 +850,11 @@ template <int ROLE>
 __device__ inline floatx16 rotate_bf16(const u32x4* piop, const RawX32<0>& x, int jb, int lane) {
   floatx16 acc = {};
   u32x4 cur[3], nxt[3];
+  const u32x4* blk = piop + qb_piece(jb, 0, 0) + lane;
   auto read = [&](int ks, u32x4(&o)[3]) {
-    const int i = (ks * 4 + jb) * 64 + lane;
-    o[0] = piop[2 * kQbPart + i];
-    o[1] = piop[kQbPart + i];
-    o[2] = piop[i];
+    o[0] = blk[qb_piece(0, ks, 2)];
+    o[1] = blk[qb_piece(0, ks, 1)];
+    o[2] = blk[qb_piece(0, ks, 0)];
   };
   read(0, cur);
 #pragma unroll
@@ -868,31 +873,95 @@ __device__ inline floatx16 rotate_bf16(const u32x4* piop, const RawX32<0>& x, in
   return acc;
 }
 
+// Where a wavefront's tile lies: its first slot is slot r0 of (row * H_kv +
+// head) bh0. The walk advances by the grid stride with scalar adds, so no tile
+// pays a 64-bit division (B and H_kv are below 2^16, so bh fits 32 bits).
+struct SlotWalk {
+  uint32_t bh0, r0;   // first slot of the current tile
+  uint32_t dq, dr;    // the grid stride, in (heads, slots)
+  __device__ void init(const QuantArgs& a, int64_t s0, int64_t stride) {
+    bh0 = (uint32_t)(s0 / a.nslot);
+    r0 = (uint32_t)(s0 - (int64_t)bh0 * a.nslot);
+    dq = (uint32_t)(stride / a.nslot);
+    dr = (uint32_t)(stride - (int64_t)dq * a.nslot);
+  }
+  __device__ void advance(const QuantArgs& a) {
+    const uint32_t ns = (uint32_t)a.nslot;
+    r0 += dr;
+    bh0 += dq;
+    if (r0 >= ns) {
+      r0 -= ns;
+      ++bh0;
+    }
+  }
+  // (head, slot within the head) of slot v (< 32) of the tile; the slot's token
+  // is t_base + r
+  __device__ void at(const QuantArgs& a, uint32_t v, uint32_t& bh, uint32_t& r) const {
+    const uint32_t ns = (uint32_t)a.nslot;
+    const uint32_t rr = r0 + v;
+    const uint32_t q = ns >= 32u ? (rr >= ns ? 1u : 0u) : rr / ns;
+    bh = bh0 + q;
+    r = rr - q * ns;
+  }
+};
+
+// Whether slot (bh, r) holds an input vector.
+__device__ inline bool slot_valid(const QuantArgs& a, uint32_t bh, uint32_t r) {
+  const int64_t t = a.t_base + r;
+  return (int64_t)bh < a.B * a.H_kv && t >= a.t_offset && t < a.t_offset + a.T;
+}
+
+// The lane's 64 coordinates 16ks + 8kh + e of the vector in slot (bh, sr).
+__device__ inline void load_bf16(RawX32<0>& r, const QuantArgs& a, uint32_t bh, uint32_t sr, int kh) {
+  const bool valid = slot_valid(a, bh, sr);
+  r.valid = valid;
+  if (valid) {
+    const uint32_t hk = (uint32_t)a.H_kv;
+    const uint32_t b = bh / hk, h = bh - b * hk;
+    const int64_t off = (int64_t)b * a.sb + (a.t_base + sr - a.t_offset) * a.st + (int64_t)h * a.sh + 8 * kh;
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) r.v[ks] = *(const u32x4*)((const uint16_t*)a.x + off + 16 * ks);
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) r.v[ks] = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
 template <int BITS, int ROLE>
 __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs a) {
   constexpr int TILE = 32 * kQbWaves;
   constexpr int NT = (1 << BITS) - 1;
   extern __shared__ __align__(16) unsigned char smem[];
-  u32x4* piop = (u32x4*)smem;                                 // [3][ks][jb][lane]
+  u32x4* piop = (u32x4*)smem;                                 // [jb][ks][part][lane]
   float* fzs = (float*)(smem + 3 * kQbPart * sizeof(u32x4));   // [wave][32]: sqrt(d) / |x| by slot
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i32 = lane & 31, kh = lane >> 5;
   const int slot = qb_slot<ROLE>(i32);
+  SlotWalk walk;
+  uint32_t bh = 0, sr = 0;   // the lane's vector: row * H_kv + head, slot within the head
   RawX32<0> cur;
-  if (blockIdx.x < a.n_tiles) load_raw32<0>(cur, a, blockIdx.x, wave, slot, kh);
+  if (blockIdx.x < a.n_tiles) {
+    walk.init(a, (int64_t)blockIdx.x * TILE + wave * 32, (int64_t)gridDim.x * TILE);
+    walk.at(a, slot, bh, sr);
+    load_bf16(cur, a, bh, sr, kh);
+  }
   stage_matrix_bf16<ROLE>(a.rot, piop);
   __syncthreads();
 
   const Thresholds<BITS> th = load_thresholds<BITS>(a);
   const float sqrt_d = sqrtf((float)kD);
-  const int64_t heads = a.B * a.H_kv;
   uint64_t sink = 0;   // carry-outs of the bit pushes (never read)
 
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     RawX32<0> nxt;
-    if (tile + gridDim.x < a.n_tiles) load_raw32<0>(nxt, a, tile + gridDim.x, wave, slot, kh);
-    const int64_t s0 = tile * TILE + wave * 32;
+    SlotWalk wnext = walk;
+    uint32_t bh_n = 0, sr_n = 0;
+    if (tile + gridDim.x < a.n_tiles) {
+      wnext.advance(a);
+      wnext.at(a, slot, bh_n, sr_n);
+      load_bf16(nxt, a, bh_n, sr_n, kh);
+    }
 
     // ---- norm (and a power-of-two rescale of vectors far from 1)
     float ss = sum_halves(sumsq_bf16(cur));
@@ -930,12 +999,8 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
     // code decisions are tested outside a 1e-6 band around each threshold)
     const float ns = __builtin_amdgcn_sqrtf(ss);
     const float fz = ns > 0.f ? sqrt_d * __builtin_amdgcn_rcpf(ns) : 0.f;
-    if (cur.valid && kh == 0) {
-      int64_t bh, t;
-      slot_pos(a, s0, slot, bh, t);
-      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
-      if (row >= 0) a.norms[row] = ldexpf(ns, -sexp);
-    }
+    const int64_t row = cur.valid ? tok_row(a.pm, a.H_kv, a.T_cap, bh, a.t_base + sr) : -1;
+    if (row >= 0 && kh == 0) a.norms[row] = ldexpf(ns, -sexp);
 
     if constexpr (ROLE == TQ_KEYS) {
       // Mirrored codebook: y against thresholds in units of y (the positive
@@ -947,12 +1012,6 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
       const float sc = fmaxf(ns * (1.f / sqrt_d), 0x1p-100f);
 #pragma unroll
       for (int i = 0; i < NT; ++i) ts[i] = th.t[i] * sc;
-      int64_t row = -1;
-      if (cur.valid) {
-        int64_t bh, t;
-        slot_pos(a, s0, slot, bh, t);
-        row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
-      }
       auto run = [&](auto sym) {
         constexpr int SYM = decltype(sym)::value;
         // two output blocks (32 coordinates, BITS words) per pass
@@ -1002,15 +1061,16 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
       uint32_t keep[2];
 #pragma unroll
       for (int bi = 0; bi < 2; ++bi) {
-        int64_t bh, tb;
-        slot_pos(a, s0, 8 * (2 * kh + bi), bh, tb);
+        uint32_t bhb, srb;
+        walk.at(a, 8 * (2 * kh + bi), bhb, srb);
+        const int64_t tb = a.t_base + srb;
         int lo = 8, hi = 0;   // valid tokens [lo, hi) of the block
-        if (bh < heads) {
+        if ((int64_t)bhb < a.B * a.H_kv) {
           const int64_t l = a.t_offset - tb, h = a.t_offset + a.T - tb;
           lo = (int)(l < 0 ? 0 : (l > 8 ? 8 : l));
           hi = (int)(h < 0 ? 0 : (h > 8 ? 8 : h));
         }
-        brow[bi] = lo < hi ? tok_row(a.pm, a.H_kv, a.T_cap, bh, tb) : -1;
+        brow[bi] = lo < hi ? tok_row(a.pm, a.H_kv, a.T_cap, bhb, tb) : -1;
         // per piece: bits of tokens below lo or from hi on
         const uint64_t piece_keep =
             ((1ull << (BITS * lo)) - 1ull) | (((1ull << (8 * BITS)) - 1ull) & ~((1ull << (BITS * (lo < hi ? hi : lo))) - 1ull));
@@ -1022,24 +1082,18 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
 #pragma unroll 1
         for (int jb = 0; jb < 4; ++jb) {
           const floatx16 acc = rotate_bf16<ROLE>(piop, cur, jb, lane);
-          const float4* fz4 = (const float4*)(fzs + wave * 32 + 16 * kh);
-          float fz[16];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const float4 f = fz4[q];
-            fz[4 * q] = f.x;
-            fz[4 * q + 1] = f.y;
-            fz[4 * q + 2] = f.z;
-            fz[4 * q + 3] = f.w;
-          }
           uint32_t piece[2];
 #pragma unroll
           for (int bi = 0; bi < 2; ++bi) {
+            // sqrt(d) / |x| of the block's 8 vectors (an LDS broadcast, read per block)
+            const float4* fz4 = (const float4*)(fzs + wave * 32 + 16 * kh + 8 * bi);
+            const float4 f0 = fz4[0], f1 = fz4[1];
+            const float fz[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
             uint32_t c = 0u;
 #pragma unroll
             for (int ti = 7; ti >= 0; --ti) {
               uint64_t m[BITS];
-              code_masks<BITS, SYM>(acc[8 * bi + ti] * fz[8 * bi + ti], th.t, m);
+              code_masks<BITS, SYM>(acc[8 * bi + ti] * fz[ti], th.t, m);
 #pragma unroll
               for (int k = BITS - 1; k >= 0; --k) c = push_bit<!SYM>(c, m[k], sink);
               // (two codes' lane masks in flight at most: they live in scalar registers)
@@ -1075,6 +1129,9 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
     }
     wave_sync();   // the scale buffer is rewritten by the next tile
     cur = nxt;
+    walk = wnext;
+    bh = bh_n;
+    sr = sr_n;
   }
   asm volatile("" ::"s"(sink));   // the carry-out pair stays reserved to the end
 }
