@@ -707,8 +707,13 @@ __device__ inline uint32_t bf16_bits(float x) { return __builtin_bit_cast(uint16
 // immediate offset reach every read of two blocks.
 __device__ inline int qb_piece(int jb, int ks, int part) { return ((jb * 8 + ks) * 3 + part) * 64; }
 
+// A rotation whose entries all have one magnitude c (a randomized Hadamard
+// matrix H diag(s) / sqrt(d)) is c times a sign matrix S, and S x is exact in a
+// single bfloat16 MFMA pass: only part 0, holding the signs (+-1), is staged,
+// and the caller scales y = c (S x). Otherwise the three parts of Pi. Returns
+// c for a sign matrix, 0 otherwise (the same in every thread).
 template <int ROLE>
-__device__ void stage_matrix_bf16(const float* M, u32x4* op) {
+__device__ float stage_matrix_bf16(const float* M, u32x4* op) {
   constexpr int NT = 64 * kQbWaves;
   constexpr int PER = kQbPart / NT;
   float4 v[PER][2];
@@ -720,9 +725,27 @@ __device__ void stage_matrix_bf16(const float* M, u32x4* op) {
     v[k][0] = src[0];
     v[k][1] = src[1];
   }
+  const float c = fabsf(M[0]);
+  bool one_magnitude = c > 0.f;
+#pragma unroll
+  for (int k = 0; k < PER; ++k) {
+    one_magnitude &= fabsf(v[k][0].x) == c && fabsf(v[k][0].y) == c && fabsf(v[k][0].z) == c &&
+                     fabsf(v[k][0].w) == c && fabsf(v[k][1].x) == c && fabsf(v[k][1].y) == c &&
+                     fabsf(v[k][1].z) == c && fabsf(v[k][1].w) == c;
+  }
+  const bool sign_matrix = __syncthreads_and(one_magnitude) != 0;
 #pragma unroll
   for (int k = 0; k < PER; ++k) {
     const float x[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w, v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+    const int piece = threadIdx.x + k * NT;
+    const int ln = piece & 63, ks = (piece >> 6) & 7, jb = piece >> 9;
+    if (sign_matrix) {
+      uint32_t sw[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sw[e] = x[e] < 0.f ? 0xBF80u : 0x3F80u;   // bfloat16 -1, +1
+      op[qb_piece(jb, ks, 0) + ln] = u32x4{sw[0] | sw[1] << 16, sw[2] | sw[3] << 16, sw[4] | sw[5] << 16, sw[6] | sw[7] << 16};
+      continue;
+    }
     uint32_t hw[8], mw[8], lw[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -734,12 +757,11 @@ __device__ void stage_matrix_bf16(const float* M, u32x4* op) {
       mw[e] = __builtin_bit_cast(uint16_t, mid);
       lw[e] = bf16_bits(r2);
     }
-    const int piece = threadIdx.x + k * NT;
-    const int ln = piece & 63, ks = (piece >> 6) & 7, jb = piece >> 9;
     op[qb_piece(jb, ks, 0) + ln] = u32x4{hw[0] | hw[1] << 16, hw[2] | hw[3] << 16, hw[4] | hw[5] << 16, hw[6] | hw[7] << 16};
     op[qb_piece(jb, ks, 1) + ln] = u32x4{mw[0] | mw[1] << 16, mw[2] | mw[3] << 16, mw[4] | mw[5] << 16, mw[6] | mw[7] << 16};
     op[qb_piece(jb, ks, 2) + ln] = u32x4{lw[0] | lw[1] << 16, lw[2] | lw[3] << 16, lw[4] | lw[5] << 16, lw[6] | lw[7] << 16};
   }
+  return sign_matrix ? c : 0.f;
 }
 
 // w * 2 + (bit of this lane in m): one code bit shifted into a word.
@@ -844,30 +866,30 @@ __device__ inline float sumsq_bf16(const RawX32<0>& r) {
   return ss;
 }
 
-// One 32-coordinate output block jb of y = Pi x (three bfloat16 parts of Pi, the
-// smallest first), the operands of step ks + 1 read from LDS while step ks runs.
-template <int ROLE>
+// One 32-coordinate output block jb of y = Pi x from NPART bfloat16 parts of Pi
+// (3: the smallest first; 1: the signs of a one-magnitude matrix), the
+// operands of step ks + 1 read from LDS while step ks runs.
+template <int ROLE, int NPART>
 __device__ inline floatx16 rotate_bf16(const u32x4* piop, const RawX32<0>& x, int jb, int lane) {
   floatx16 acc = {};
-  u32x4 cur[3], nxt[3];
   const u32x4* blk = piop + qb_piece(jb, 0, 0) + lane;
-  auto read = [&](int ks, u32x4(&o)[3]) {
-    o[0] = blk[qb_piece(0, ks, 2)];
-    o[1] = blk[qb_piece(0, ks, 1)];
-    o[2] = blk[qb_piece(0, ks, 0)];
+  u32x4 cur[NPART], nxt[NPART];
+  auto read = [&](int ks, u32x4(&o)[NPART]) {
+#pragma unroll
+    for (int q = 0; q < NPART; ++q) o[q] = blk[qb_piece(0, ks, NPART - 1 - q)];
   };
   read(0, cur);
 #pragma unroll
   for (int ks = 0; ks < 8; ++ks) {
     if (ks < 7) read(ks + 1, nxt);
 #pragma unroll
-    for (int part = 0; part < 3; ++part) {
-      if constexpr (ROLE == TQ_KEYS) acc = mfma32bf(cur[part], x.v[ks], acc);
-      else acc = mfma32bf(x.v[ks], cur[part], acc);
+    for (int q = 0; q < NPART; ++q) {
+      if constexpr (ROLE == TQ_KEYS) acc = mfma32bf(cur[q], x.v[ks], acc);
+      else acc = mfma32bf(x.v[ks], cur[q], acc);
     }
     if (ks < 7) {
 #pragma unroll
-      for (int part = 0; part < 3; ++part) cur[part] = nxt[part];
+      for (int q = 0; q < NPART; ++q) cur[q] = nxt[q];
     }
   }
   return acc;
@@ -938,6 +960,19 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i32 = lane & 31, kh = lane >> 5;
   const int slot = qb_slot<ROLE>(i32);
+  const float csign = stage_matrix_bf16<ROLE>(a.rot, piop);
+  __syncthreads();
+
+  const Thresholds<BITS> th = load_thresholds<BITS>(a);
+  const float sqrt_d = sqrtf((float)kD);
+
+  // NPART = 3: the MFMAs give y itself; NPART = 1 (a one-magnitude rotation):
+  // they give S x, and y = csign * (S x)
+  auto tiles = [&](auto npart) __attribute__((always_inline)) {
+  constexpr int NPART = decltype(npart)::value;
+  const float yd = (NPART == 1 ? csign : 1.f) * sqrt_d;   // z = (MFMA output) * yd / |x|
+  const float inv_yd = 1.f / yd;
+  uint64_t sink = 0;   // carry-outs of the bit pushes (never read)
   SlotWalk walk;
   uint32_t bh = 0, sr = 0;   // the lane's vector: row * H_kv + head, slot within the head
   RawX32<0> cur;
@@ -946,12 +981,6 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
     walk.at(a, slot, bh, sr);
     load_bf16(cur, a, bh, sr, kh);
   }
-  stage_matrix_bf16<ROLE>(a.rot, piop);
-  __syncthreads();
-
-  const Thresholds<BITS> th = load_thresholds<BITS>(a);
-  const float sqrt_d = sqrtf((float)kD);
-  uint64_t sink = 0;   // carry-outs of the bit pushes (never read)
 
   for (int64_t tile = blockIdx.x; tile < a.n_tiles; tile += gridDim.x) {
     RawX32<0> nxt;
@@ -998,7 +1027,7 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
     // |x| * 2^sexp, and sqrt(d) / that (single instructions, within 2 ulp: the
     // code decisions are tested outside a 1e-6 band around each threshold)
     const float ns = __builtin_amdgcn_sqrtf(ss);
-    const float fz = ns > 0.f ? sqrt_d * __builtin_amdgcn_rcpf(ns) : 0.f;
+    const float fz = ns > 0.f ? yd * __builtin_amdgcn_rcpf(ns) : 0.f;
     const int64_t row = cur.valid ? tok_row(a.pm, a.H_kv, a.T_cap, bh, a.t_base + sr) : -1;
     if (row >= 0 && kh == 0) a.norms[row] = ldexpf(ns, -sexp);
 
@@ -1009,7 +1038,7 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
       // (nonzero norms are at least 2^-50 here, far above it). Any other
       // codebook: z = y sqrt(d) / |x| against the thresholds themselves.
       float ts[NT];
-      const float sc = fmaxf(ns * (1.f / sqrt_d), 0x1p-100f);
+      const float sc = fmaxf(ns * inv_yd, 0x1p-100f);
 #pragma unroll
       for (int i = 0; i < NT; ++i) ts[i] = th.t[i] * sc;
       auto run = [&](auto sym) {
@@ -1023,7 +1052,7 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
 #pragma unroll
           for (int jj = 1; jj >= 0; --jj) {
             const int jb = 2 * p + jj;
-            const floatx16 acc = rotate_bf16<ROLE>(piop, cur, jb, lane);
+            const floatx16 acc = rotate_bf16<ROLE, NPART>(piop, cur, jb, lane);
 #pragma unroll
             for (int e = 15; e >= 0; --e) {
               uint64_t m[BITS];
@@ -1081,7 +1110,7 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
         constexpr int SYM = decltype(sym)::value;
 #pragma unroll 1
         for (int jb = 0; jb < 4; ++jb) {
-          const floatx16 acc = rotate_bf16<ROLE>(piop, cur, jb, lane);
+          const floatx16 acc = rotate_bf16<ROLE, NPART>(piop, cur, jb, lane);
           uint32_t piece[2];
 #pragma unroll
           for (int bi = 0; bi < 2; ++bi) {
@@ -1134,6 +1163,11 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
     sr = sr_n;
   }
   asm volatile("" ::"s"(sink));   // the carry-out pair stays reserved to the end
+  };
+  if (csign > 0.f)
+    tiles(IntTag<1>{});
+  else
+    tiles(IntTag<3>{});
 }
 
 // ------------------------------------------------- single-token append --
