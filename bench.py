@@ -12,7 +12,8 @@ JSON line on stdout.
 Extra fields: `roofline` (the decode launch vs the HBM peak and vs the
 streaming-read reference measured in the same run), `cpu_baseline` (the CPU
 oracle on a bounded sample of the same step, scaled to tokens/s),
-`quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view),
+`quantize_prefill` (bulk quantization of the whole context, HBM and MFMA view;
+`quantize_prefill_hadamard` the same with a randomized Hadamard rotation),
 `stream` (the plain streaming-read kernel), `quality` (code mismatch rate and
 decode error of sampled slices against the oracle, cosine per bit width,
 asymmetric K/V formats and QJL keys against exact attention).
@@ -36,8 +37,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # (calibrated against a copy of known size), valid for the kernel sources whose
 # hash it records
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_scan_stress70b_hbm_traffic.md")
-KERNEL_SOURCES = ["decode_attention_tq_amd/csrc/tq_decode.hip", "decode_attention_tq_amd/csrc/tq_device.h",
-                  "decode_attention_tq_amd/csrc/tq_internal.h"]
+KERNEL_SOURCES = ["decode_attention_tq_amd/csrc/tq_decode.hip", "decode_attention_tq_amd/csrc/tq_scan.h",
+                  "decode_attention_tq_amd/csrc/tq_device.h", "decode_attention_tq_amd/csrc/tq_internal.h"]
 
 
 def log(*a):
@@ -374,6 +375,8 @@ def main():
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the quality reports (cosine per bit width, asymmetric formats, QJL statistics)")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read reference")
+    ap.add_argument("--no-hadamard-prefill", action="store_true",
+                    help="skip the prefill timing with a randomized Hadamard rotation")
     ap.add_argument("--parity-slices", type=int, default=8,
                     help="(row, KV head) slices of the benchmarked step checked against the oracle")
     args = ap.parse_args()
@@ -415,10 +418,38 @@ def main():
     pre = sum(pre_ms) / len(pre_ms)
     ntok = w.B * w.H_kv * T * 2
     qbytes = quantize_bytes(w, T, "k") + quantize_bytes(w, T, "v")
-    # algorithmic rotation flops (y = Pi x per vector, plus S r per QJL key); the MFMA
-    # issues 2 fp16 passes per product (hi and lo halves of Pi), 3 for QJL's S r
+    # algorithmic rotation flops (y = Pi x per vector, plus S r per QJL key) and the
+    # MFMA work the kernels issue for them (passes per product): bfloat16 input in
+    # bulk takes three bfloat16 parts of Pi (one for a one-magnitude rotation);
+    # QJL keys and float32 input take float16 hi/lo operands (2 passes; 3 for x in
+    # float32 or for S r)
     qflops = 2 * w.d * w.d * ntok + (2 * w.d * w.d * w.B * w.H_kv * T if w.k_qjl else 0)
-    issued = 2 * 2 * w.d * w.d * ntok + (3 * 2 * w.d * w.d * w.B * w.H_kv * T if w.k_qjl else 0)
+
+    def issued_flops(passes_bf16):
+        per = 2 * w.d * w.d * w.B * w.H_kv * T
+        k = (2 + 3) if w.k_qjl else (passes_bf16 if w.dtype == "bf16" else 3)
+        v = passes_bf16 if w.dtype == "bf16" else 3
+        return per * (k + v)
+
+    issued = issued_flops(3)
+    # the same prefill with a randomized Hadamard rotation (one magnitude: one pass)
+    pre_h = None
+    if not w.k_qjl and not args.no_hadamard_prefill:
+        rot_h = tq.make_rotation(tq_synth.ROT_SEED, tq.HADAMARD)
+        kch = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, rot=rot_h)
+        vch = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev, rot=rot_h)
+        hm = []
+        for it in range(args.prefill_iters + 1):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            tq.quantize_kv(xk, kch)
+            tq.quantize_kv(xv, vch)
+            e1.record()
+            torch.cuda.synchronize()
+            if it > 0:
+                hm.append(e0.elapsed_time(e1))
+        pre_h = sum(hm) / len(hm)
+        del kch, vch
     new_k = xk[:, T - 1:T].contiguous()
     new_v = xv[:, T - 1:T].contiguous()
     # the exact input bytes of sampled (row, KV head) slices, for the oracle check
@@ -676,8 +707,15 @@ def main():
                              "hbm_frac": qbytes / (pre * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "rotation_TFLOP_s": qflops / (pre * 1e-3) / 1e12,
                              "mfma_issued_TFLOP_s": issued / (pre * 1e-3) / 1e12,
-                             "mfma_frac": issued / (pre * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS},
+                             "mfma_frac": issued / (pre * 1e-3) / 1e12 / F16_MFMA_PEAK_TFLOPS,
+                             "rotation": "haar (dense)"},
     }
+    if pre_h is not None:
+        res["quantize_prefill_hadamard"] = {
+            "ms": pre_h, "vectors": ntok, "GB_s": qbytes / (pre_h * 1e-3) / 1e9,
+            "hbm_frac": qbytes / (pre_h * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "mfma_issued_TFLOP_s": issued_flops(1) / (pre_h * 1e-3) / 1e12,
+            "rotation": "randomized Hadamard (one bfloat16 MFMA pass on its sign matrix)"}
     if paged is not None:
         res["paged"] = paged
     if formats:

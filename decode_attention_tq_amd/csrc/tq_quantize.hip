@@ -956,6 +956,7 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
   extern __shared__ __align__(16) unsigned char smem[];
   u32x4* piop = (u32x4*)smem;                                 // [jb][ks][part][lane]
   float* fzs = (float*)(smem + 3 * kQbPart * sizeof(u32x4));   // [wave][32]: sqrt(d) / |x| by slot
+  // (keys: then [wave][BITS][64] words of the first pass)
 
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int i32 = lane & 31, kh = lane >> 5;
@@ -1043,7 +1044,11 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
       for (int i = 0; i < NT; ++i) ts[i] = th.t[i] * sc;
       auto run = [&](auto sym) {
         constexpr int SYM = decltype(sym)::value;
-        // two output blocks (32 coordinates, BITS words) per pass
+        // two output blocks (32 coordinates, BITS words) per pass; the lane's
+        // 2 BITS words (its half of the token's row) leave in one store, so the
+        // row's cache lines are written whole
+        // pass 0's words wait in LDS ([BITS][64] per wavefront)
+        uint32_t* w0 = (uint32_t*)(fzs + kQbWaves * 32) + wave * (64 * BITS) + lane;
 #pragma unroll 1
         for (int p = 0; p < 2; ++p) {
           uint32_t w[BITS];
@@ -1066,10 +1071,15 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
               if (e % 2 == 0) __builtin_amdgcn_sched_barrier(0);   // two codes' masks in flight at most
             }
           }
-          if (row >= 0) {
-            uint32_t* dst = a.codes + row * (4 * BITS) + 2 * BITS * kh + BITS * p;
+          if (p == 0) {
 #pragma unroll
-            for (int k = 0; k < BITS; ++k) dst[k] = w[k];
+            for (int k = 0; k < BITS; ++k) w0[64 * k] = w[k];
+          } else if (row >= 0) {
+            uint32_t* dst = a.codes + row * (4 * BITS) + 2 * BITS * kh;
+#pragma unroll
+            for (int k = 0; k < BITS; ++k) dst[k] = w0[64 * k];
+#pragma unroll
+            for (int k = 0; k < BITS; ++k) dst[BITS + k] = w[k];
           }
         }
       };
@@ -1376,7 +1386,8 @@ hipError_t launch_q32(const QuantArgs& qa, hipStream_t stream) {
 template <int BITS, int ROLE>
 hipError_t launch_qbf(const QuantArgs& qa, hipStream_t stream) {
   static_assert(kQbWaves == kQ32Waves, "the tile loader assumes 32 * kQ32Waves slots per tile");
-  constexpr size_t smem = 3 * kQbPart * sizeof(u32x4) + kQbWaves * 32 * sizeof(float);
+  constexpr size_t smem = 3 * kQbPart * sizeof(u32x4) + kQbWaves * 32 * sizeof(float) +
+                          (ROLE == TQ_KEYS ? kQbWaves * 64 * BITS * sizeof(uint32_t) : 0);
   auto kern = quantize_bf16_kernel<BITS, ROLE>;
   static const hipError_t attr =
       hipFuncSetAttribute((const void*)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
