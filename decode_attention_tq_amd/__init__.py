@@ -5,10 +5,13 @@ in the library's HIP kernels. PyTorch provides device memory and the stream.
 The names follow the C ABI in include/tq.h:
 
     make_codebook(bits)                        -> (centroids, thresholds)   host
-    make_rotation(seed, kind=HAAR)             -> float32 [128, 128]        host
-    quantize_kv(x, cache, t_offset=0)          x: [B, T, H_kv, 128] on the GPU
-    dequantize(cache, t0, t1)                  -> float32 [B, H_kv, t1-t0, 128]
-    decode_attention(k, v, q, ...)             -> float32 [B, H_q, 128]
+    make_rotation(seed, kind=HAAR, d=128)      -> float32 [d, d]            host
+    quantize_kv(x, cache, t_offset=0)          x: [B, T, H_kv, d] on the GPU
+    dequantize(cache, t0, t1)                  -> float32 [B, H_kv, t1-t0, d]
+    decode_attention(k, v, q, ...)             -> float32 [B, H_q, d]
+
+d (the head dimension) is 128, 64 or 256; QJL keys and prefill_attention take
+d = 128 only.
     decode_workspace_bytes(...), decode_splits(...), status_string(code)
 
 Cache bundles the device buffers of one packed cache (keys or values) with its
@@ -43,6 +46,7 @@ F32, BF16 = 0, 1
 HAAR, GAUSSIAN, HADAMARD = 0, 1, 2
 KEYS, VALUES = 0, 1
 D = 128
+HEAD_DIMS = (64, 128, 256)
 VALUE_BLOCK = 8
 
 EXPORTS = ("tq_make_codebook", "tq_make_codebook_sphere", "tq_make_rotation", "tq_quantize_kv", "tq_append_kv",
@@ -208,10 +212,13 @@ class Cache:
 
     def __init__(self, role: int, bits: int, B: int, H_kv: int, T_cap: int, device="cuda",
                  rot=None, proj=None, qjl: bool = False, centroids=None, rot_seed: int = 42,
-                 qjl_seed: int = 4242, block_table=None, block_tokens: int = 0, n_blocks: int = 0):
+                 qjl_seed: int = 4242, block_table=None, block_tokens: int = 0, n_blocks: int = 0,
+                 d: int = D):
         torch = _torch()
+        if d not in HEAD_DIMS:
+            raise ValueError(f"head dimension d must be one of {HEAD_DIMS}")
         self.role, self.bits, self.qjl = role, bits, int(bool(qjl))
-        self.B, self.H_kv, self.T_cap, self.d = B, H_kv, T_cap, D
+        self.B, self.H_kv, self.T_cap, self.d = B, H_kv, T_cap, d
         self.device = torch.device(device)
         self.block_table = block_table
         self.block_tokens, self.n_blocks = int(block_tokens), int(n_blocks)
@@ -221,22 +228,22 @@ class Cache:
             lead, per = (n_blocks, H_kv), block_tokens
         else:
             lead, per = (B, H_kv), T_cap
-        W = D * bits // 32
+        W = d * bits // 32
         self.codes = torch.zeros((*lead, per * W), dtype=torch.int32, device=self.device)
         self.norms = torch.zeros((*lead, per), dtype=torch.float32, device=self.device)
         if rot is None:
-            rot = make_rotation(rot_seed, HAAR)
+            rot = make_rotation(rot_seed, HAAR, d)
         self.rot = torch.as_tensor(np.asarray(rot, dtype=np.float32)).to(self.device).contiguous()
         if self.qjl:
             if proj is None:
-                proj = make_rotation(qjl_seed, GAUSSIAN)
+                proj = make_rotation(qjl_seed, GAUSSIAN, d)
             self.proj = torch.as_tensor(np.asarray(proj, dtype=np.float32)).to(self.device).contiguous()
-            self.signs = torch.zeros((*lead, per, D // 32), dtype=torch.int32, device=self.device)
+            self.signs = torch.zeros((*lead, per, d // 32), dtype=torch.int32, device=self.device)
             self.gamma = torch.zeros((*lead, per), dtype=torch.float32, device=self.device)
         else:
             self.proj = self.signs = self.gamma = None
         if centroids is None:
-            centroids, _ = make_codebook(bits)
+            centroids, _ = make_codebook(bits, d)
         self.centroids = np.asarray(centroids, dtype=np.float32)
 
     def struct(self) -> TQCache:
@@ -265,10 +272,10 @@ class Cache:
 
 
 def quantize_kv(x, cache: Cache, t_offset: int = 0):
-    """Quantize x [B, T, H_kv, 128] (float32 or bfloat16, last dim contiguous, on the
+    """Quantize x [B, T, H_kv, d] (float32 or bfloat16, last dim contiguous, on the
     cache's device) into tokens t_offset .. t_offset+T-1 of `cache`."""
-    if x.dim() != 4 or x.shape[-1] != D or x.stride(-1) != 1:
-        raise ValueError("x must be [B, T, H_kv, 128] with a contiguous last dimension")
+    if x.dim() != 4 or x.shape[-1] != cache.d or x.stride(-1) != 1:
+        raise ValueError(f"x must be [B, T, H_kv, {cache.d}] with a contiguous last dimension")
     B, T, H, _ = x.shape
     s = cache.struct()
     _check(_lib.tq_quantize_kv(x.data_ptr(), _dtype_code(x), B, T, H, x.stride(0), x.stride(1), x.stride(2),
@@ -276,15 +283,16 @@ def quantize_kv(x, cache: Cache, t_offset: int = 0):
 
 
 def append_kv(k, v, kcache: Cache, vcache: Cache, t_offset: int):
-    """The key and value of one new token per (row, head): k, v [B, H_kv, 128]
-    (or [B, 1, H_kv, 128]), float32 or bfloat16, last dim contiguous, into token
+    """The key and value of one new token per (row, head): k, v [B, H_kv, d]
+    (or [B, 1, H_kv, d]), float32 or bfloat16, last dim contiguous, into token
     t_offset of kcache and vcache in one call (tq_append_kv)."""
     if k.dim() == 4:
         k = k[:, 0]
     if v.dim() == 4:
         v = v[:, 0]
-    if k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[-1] != D or k.stride(-1) != 1 or v.stride(-1) != 1:
-        raise ValueError("k and v must be [B, H_kv, 128] with a contiguous last dimension")
+    if (k.dim() != 3 or v.dim() != 3 or k.shape != v.shape or k.shape[-1] != kcache.d or k.stride(-1) != 1
+            or v.stride(-1) != 1):
+        raise ValueError(f"k and v must be [B, H_kv, {kcache.d}] with a contiguous last dimension")
     if k.dtype != v.dtype:
         raise ValueError("k and v must have the same dtype")
     B, H, _ = k.shape
@@ -298,7 +306,7 @@ def dequantize(cache: Cache, t0: int = 0, t1: int | None = None, out=None):
     torch = _torch()
     t1 = cache.T_cap if t1 is None else t1
     if out is None:
-        out = torch.empty((cache.B, cache.H_kv, t1 - t0, D), dtype=torch.float32, device=cache.device)
+        out = torch.empty((cache.B, cache.H_kv, t1 - t0, cache.d), dtype=torch.float32, device=cache.device)
     s = cache.struct()
     _check(_lib.tq_dequantize(ctypes.byref(s), t0, t1, out.data_ptr(), _stream_handle(cache.device)),
            "tq_dequantize")
@@ -334,14 +342,14 @@ class Workspace:
 
 def decode_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None, scale: float = 0.0,
                      n_split: int = 0, out=None, workspace: Workspace | None = None):
-    """Decode attention of q [B, H_q, 128] over the packed caches -> float32 [B, H_q, 128]."""
+    """Decode attention of q [B, H_q, d] over the packed caches -> float32 [B, H_q, d]."""
     torch = _torch()
-    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    if q.dim() != 3 or q.shape[-1] != k.d or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, H_q, {k.d}] tensor")
     B, H_q, _ = q.shape
     T = k.T_cap if T is None else T
     if out is None:
-        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H_q, k.d), dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(B, H_q, k.H_kv, T, n_split, k.qjl)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)
@@ -366,12 +374,12 @@ def decode_attention_noalloc(k: Cache, v: Cache, q, ctx_lens=None, T: int | None
     library's static per-GPU scratch (tq_decode_attention_noalloc). Pass `out`
     to allocate nothing at all; calls that overlap on one GPU race."""
     torch = _torch()
-    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    if q.dim() != 3 or q.shape[-1] != k.d or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, H_q, {k.d}] tensor")
     B, H_q, _ = q.shape
     T = k.T_cap if T is None else T
     if out is None:
-        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H_q, k.d), dtype=torch.float32, device=q.device)
     sk, sv = k.struct(), v.struct()
     cl = 0
     if ctx_lens is not None:
@@ -386,23 +394,23 @@ def decode_attention_noalloc(k: Cache, v: Cache, q, ctx_lens=None, T: int | None
 
 def decode_attention_append(k: Cache, v: Cache, k_new, v_new, q, ctx_lens=None, T: int | None = None,
                             scale: float = 0.0, n_split: int = 0, out=None, workspace: Workspace | None = None):
-    """One decode step in one launch: k_new, v_new [B, H_kv, 128] (or [B, 1, H_kv, 128])
+    """One decode step in one launch: k_new, v_new [B, H_kv, d] (or [B, 1, H_kv, d])
     go to token ctx_len[b] - 1 of the caches (ctx_len = T without ctx_lens), then
-    decode attention of q [B, H_q, 128] over tokens 0 .. ctx_len[b] - 1."""
+    decode attention of q [B, H_q, d] over tokens 0 .. ctx_len[b] - 1."""
     torch = _torch()
-    if q.dim() != 3 or q.shape[-1] != D or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, H_q, 128] tensor")
+    if q.dim() != 3 or q.shape[-1] != k.d or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, H_q, {k.d}] tensor")
     if k_new.dim() == 4:
         k_new = k_new[:, 0]
     if v_new.dim() == 4:
         v_new = v_new[:, 0]
-    if (k_new.dim() != 3 or k_new.shape != v_new.shape or k_new.shape[-1] != D or k_new.stride(-1) != 1
+    if (k_new.dim() != 3 or k_new.shape != v_new.shape or k_new.shape[-1] != k.d or k_new.stride(-1) != 1
             or v_new.stride(-1) != 1 or k_new.dtype != v_new.dtype):
-        raise ValueError("k_new and v_new must be [B, H_kv, 128] of one dtype with a contiguous last dimension")
+        raise ValueError(f"k_new and v_new must be [B, H_kv, {k.d}] of one dtype with a contiguous last dimension")
     B, H_q, _ = q.shape
     T = k.T_cap if T is None else T
     if out is None:
-        out = torch.empty((B, H_q, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, H_q, k.d), dtype=torch.float32, device=q.device)
     need = decode_workspace_bytes(B, H_q, k.H_kv, T, n_split, k.qjl)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)
@@ -425,7 +433,7 @@ def prefill_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None
     """Chunked causal attention of the M newest tokens of each row, q [B, M, H_q, 128]
     (their keys and values already in the caches), over the packed caches ->
     float32 [B, M, H_q, 128]; token i of row b attends to cache tokens
-    0 .. ctx_len[b] - M + i."""
+    0 .. ctx_len[b] - M + i. (d = 128 only.)"""
     torch = _torch()
     if q.dim() != 4 or q.shape[-1] != D or not q.is_contiguous():
         raise ValueError("q must be a contiguous [B, M, H_q, 128] tensor")

@@ -23,7 +23,8 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJDIR = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 
-SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_prefill.hip", "tq_quantize.hip", "tq_stream.hip", "tq_host.cpp"]
+SOURCES = ["tq_api.hip", "tq_decode.hip", "tq_generic.hip", "tq_prefill.hip", "tq_quantize.hip", "tq_stream.hip",
+           "tq_host.cpp"]
 # MFMA accumulators in ordinary VGPRs (no accumulation-register copies around
 # the softmax rescale); a source listed here with False keeps the default
 VGPR_FORM = {}

@@ -21,7 +21,9 @@ int check_cache(const tq_cache* c) {
   if (c->bits < 2 || c->bits > 4) return TQ_ERR_UNSUPPORTED;
   if (c->qjl != 0 && c->qjl != 1) return TQ_ERR_INVALID_ARGUMENT;
   if (c->qjl && c->role != TQ_KEYS) return TQ_ERR_UNSUPPORTED;
-  if (c->d != kD) return TQ_ERR_UNSUPPORTED;
+  // head dimension 128 (the tuned kernels) or 64 / 256 (the generic ones, no QJL)
+  if (c->d != 64 && c->d != kD && c->d != 256) return TQ_ERR_UNSUPPORTED;
+  if (c->d != kD && c->qjl) return TQ_ERR_UNSUPPORTED;
   if (c->B <= 0 || c->H_kv <= 0 || c->T_cap <= 0) return TQ_ERR_INVALID_ARGUMENT;
   if (c->B > 65535 || c->H_kv > 65535) return TQ_ERR_UNSUPPORTED;
   if (c->role == TQ_VALUES && c->T_cap % kValueBlock != 0) return TQ_ERR_INVALID_ARGUMENT;
@@ -33,10 +35,10 @@ int check_cache(const tq_cache* c) {
     if (c->T_cap % bt != 0 || c->n_blocks <= 0) return TQ_ERR_INVALID_ARGUMENT;
     if (((uintptr_t)c->block_table & 3) != 0) return TQ_ERR_ALIGNMENT;
     if (c->n_blocks > ((int64_t)1 << 31) / (c->H_kv * bt)) return TQ_ERR_UNSUPPORTED;
-    if (cache_rows(c) * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+    if (cache_rows(c) * (int64_t)c->d * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
   } else {
     // per-head byte ranges are addressed with 32-bit offsets
-    if (c->T_cap * (int64_t)kD * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
+    if (c->T_cap * (int64_t)c->d * c->bits / 8 >= (int64_t)1 << 31) return TQ_ERR_UNSUPPORTED;
   }
   if (c->codes == nullptr || c->norms == nullptr || c->rot == nullptr) return TQ_ERR_INVALID_ARGUMENT;
   if (c->qjl && (c->qjl_signs == nullptr || c->qjl_gamma == nullptr || c->qjl_proj == nullptr))
@@ -226,6 +228,9 @@ extern "C" int tq_quantize_kv(const void* x, int32_t x_dtype, int64_t B, int64_t
   if (!aligned16(x) || stride_b % vec_align || stride_t % vec_align || stride_h % vec_align)
     return TQ_ERR_ALIGNMENT;
   clear_pending_error();
+  if (dst->d != kD)
+    return device_status(launch_quantize_generic(x, x_dtype, B, T, H_kv, stride_b, stride_t, stride_h, dst,
+                                                 t_offset, nullptr, 0, (hipStream_t)hip_stream));
   return device_status(launch_quantize(x, x_dtype, B, T, H_kv, stride_b, stride_t, stride_h, dst, t_offset,
                                        (hipStream_t)hip_stream));
 }
@@ -238,6 +243,7 @@ extern "C" int tq_append_kv(const void* k, const void* v, int32_t x_dtype, int64
   st = check_cache(vc);
   if (st != TQ_OK) return st;
   if (kc->role != TQ_KEYS || vc->role != TQ_VALUES) return TQ_ERR_INVALID_ARGUMENT;
+  if (kc->d != vc->d) return TQ_ERR_INVALID_ARGUMENT;
   if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
   if (B != kc->B || B != vc->B || H_kv != kc->H_kv || H_kv != vc->H_kv) return TQ_ERR_INVALID_ARGUMENT;
   if (t_offset < 0 || t_offset >= kc->T_cap || t_offset >= vc->T_cap) return TQ_ERR_INVALID_ARGUMENT;
@@ -248,6 +254,13 @@ extern "C" int tq_append_kv(const void* k, const void* v, int32_t x_dtype, int64
       v_stride_b % vec_align || v_stride_h % vec_align)
     return TQ_ERR_ALIGNMENT;
   clear_pending_error();
+  if (kc->d != kD) {
+    const hipError_t e = launch_quantize_generic(k, x_dtype, B, 1, H_kv, k_stride_b, 0, k_stride_h, kc, t_offset,
+                                                 nullptr, 0, (hipStream_t)hip_stream);
+    if (e != hipSuccess) return device_status(e);
+    return device_status(launch_quantize_generic(v, x_dtype, B, 1, H_kv, v_stride_b, 0, v_stride_h, vc, t_offset,
+                                                 nullptr, 0, (hipStream_t)hip_stream));
+  }
   return device_status(launch_append_kv(k, v, x_dtype, B, H_kv, k_stride_b, k_stride_h, v_stride_b, v_stride_h,
                                         kc, vc, t_offset, (hipStream_t)hip_stream));
 }
@@ -260,6 +273,7 @@ extern "C" int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float*
   if (out == nullptr) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(out)) return TQ_ERR_ALIGNMENT;
   clear_pending_error();
+  if (src->d != kD) return device_status(launch_dequantize_generic(src, t0, t1, out, (hipStream_t)hip_stream));
   return device_status(launch_dequantize(src, t0, t1, out, (hipStream_t)hip_stream));
 }
 
@@ -327,10 +341,17 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   if (M > 65535) return TQ_ERR_UNSUPPORTED;
   if (!isfinite(scale)) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
-  const bool dense = app == nullptr && use_dense_prefill(M, H_q / k->H_kv, k->qjl);
+  if (k->d != v->d) return TQ_ERR_INVALID_ARGUMENT;
+  // head dimensions 64 / 256: one generic decode launch per call, no workspace;
+  // the chunked prefill exists for d = 128 only
+  const bool generic = k->d != kD;
+  if (generic && M != 1) return TQ_ERR_UNSUPPORTED;
+  const bool dense = !generic && app == nullptr && use_dense_prefill(M, H_q / k->H_kv, k->qjl);
   DecodePlan p;
   DensePlan dp;
-  if (dense) {
+  if (generic) {
+    p.bytes = 0;
+  } else if (dense) {
     if (!plan_prefill_dense(k->B, H_q, k->H_kv, T, M, n_split, &dp)) return TQ_ERR_UNSUPPORTED;
     p.bytes = dp.bytes;
   } else if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) {
@@ -338,11 +359,11 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   }
   if (wsa.scratch) {
     if (p.bytes > (size_t)TQ_NOALLOC_SCRATCH_BYTES) return TQ_ERR_WORKSPACE_TOO_SMALL;
-  } else {
+  } else if (!generic) {
     if (wsa.ptr == nullptr || wsa.bytes < p.bytes) return TQ_ERR_WORKSPACE_TOO_SMALL;
     if (((uintptr_t)wsa.ptr & 255u) != 0) return TQ_ERR_ALIGNMENT;
   }
-  if (scale <= 0.f) scale = 1.0f / sqrtf((float)kD);
+  if (scale <= 0.f) scale = 1.0f / sqrtf((float)k->d);
   if (app != nullptr) {
     if (app->x_dtype != TQ_F32 && app->x_dtype != TQ_BF16) return TQ_ERR_INVALID_ARGUMENT;
     if (app->k == nullptr || app->v == nullptr || app->k_sb < 0 || app->k_sh < 0 || app->v_sb < 0 || app->v_sh < 0)
@@ -357,6 +378,20 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   }
   // every argument is valid from here on
   clear_pending_error();
+  if (generic) {
+    if (app != nullptr && (ctx_lens != nullptr || T > 0)) {
+      // the new token of each row: at ctx_lens[b] - 1, or at T - 1 for every row
+      const int64_t tk = ctx_lens != nullptr ? 0 : T - 1;
+      hipError_t e = launch_quantize_generic(app->k, app->x_dtype, k->B, 1, k->H_kv, app->k_sb, 0, app->k_sh, k, tk,
+                                             ctx_lens, T, (hipStream_t)hip_stream);
+      if (e != hipSuccess) return device_status(e);
+      e = launch_quantize_generic(app->v, app->x_dtype, k->B, 1, k->H_kv, app->v_sb, 0, app->v_sh, v, tk, ctx_lens, T,
+                                  (hipStream_t)hip_stream);
+      if (e != hipSuccess) return device_status(e);
+    }
+    return device_status(
+        launch_decode_generic(k, v, q, q_dtype, H_q, ctx_lens, T, scale, out, (hipStream_t)hip_stream));
+  }
   void* workspace = wsa.ptr;
   if (wsa.scratch) {
     hipError_t e = hipSuccess;

@@ -235,7 +235,7 @@ void thresholds_from_centroids(const float* c, int levels, float* t) {
 
 extern "C" int tq_make_codebook(int32_t bits, int32_t d, float* centroids, float* thresholds) {
   if (centroids == nullptr || bits < 1 || bits > 4 || d <= 0) return TQ_ERR_INVALID_ARGUMENT;
-  if (d != tq::kD) return TQ_ERR_UNSUPPORTED;
+  if (d != 64 && d != tq::kD && d != 256) return TQ_ERR_UNSUPPORTED;
   const int L = 1 << bits;
   double c[16];
   lloyd_max(L, c);
@@ -267,7 +267,7 @@ extern "C" int tq_make_codebook_sphere(int32_t bits, int32_t d, float* centroids
 extern "C" int tq_make_rotation(uint64_t seed, int32_t d, int32_t kind, float* out) {
   if (out == nullptr || d <= 0 || (kind != TQ_MAT_HAAR && kind != TQ_MAT_GAUSSIAN && kind != TQ_MAT_HADAMARD))
     return TQ_ERR_INVALID_ARGUMENT;
-  if (d != tq::kD) return TQ_ERR_UNSUPPORTED;
+  if (d != 64 && d != tq::kD && d != 256) return TQ_ERR_UNSUPPORTED;
   if (kind == TQ_MAT_HADAMARD) {
     // H D / sqrt(d): H[i][j] = (-1)^popcount(i & j), s_j from the top bit of output j+1
     SplitMix64 sm{seed};

@@ -94,6 +94,15 @@ hipError_t launch_append_kv(const void* k, const void* v, int x_dtype, int64_t B
                             int64_t t_offset, hipStream_t stream, const int32_t* ctx_lens = nullptr,
                             int64_t T = 0);
 hipError_t launch_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, hipStream_t stream);
+// Head dimensions 64 and 256 (tq_generic.hip). Quantize: ctx_lens == nullptr
+// writes tokens [t_offset, t_offset + T); otherwise row b's single token x[b][0]
+// goes to clamp(ctx_lens[b], 0, T_all) - 1 (none when that is -1).
+hipError_t launch_quantize_generic(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv, int64_t sb,
+                                   int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
+                                   const int32_t* ctx_lens, int64_t T_all, hipStream_t stream);
+hipError_t launch_dequantize_generic(const tq_cache* src, int64_t t0, int64_t t1, float* out, hipStream_t stream);
+hipError_t launch_decode_generic(const tq_cache* k, const tq_cache* v, const void* q, int q_dtype, int64_t H_q,
+                                 const int32_t* ctx_lens, int64_t T, float scale, float* out, hipStream_t stream);
 // New key and value vectors of a decode step: element (b, h, j) at
 // k[b*k_sb + h*k_sh + j] (and the same for v).
 struct DecodeAppend {

@@ -27,7 +27,13 @@
  *   - the caller owns every buffer; the library never allocates or frees device
  *     memory (its one static device array, the scratch of
  *     tq_decode_attention_noalloc, is part of its loaded code object);
- *   - head dimension d = 128 only (other values return TQ_ERR_UNSUPPORTED).
+ *   - head dimension d = 128, 64 or 256 (other values return
+ *     TQ_ERR_UNSUPPORTED). d = 128 runs the tuned kernels (MFMA rotations,
+ *     context split over workgroups). d = 64 and 256 run generic kernels of the
+ *     same method and the same packed formats: float32 rotations, one
+ *     workgroup per 8-token block (quantize, dequantize) and one per
+ *     (row, KV head) over the whole context (decode; n_split and the workspace
+ *     are not used). QJL keys and tq_prefill_attention take d = 128 only.
  *
  * Packed formats (one cache per tensor and layer; keys and values set their bit
  * width separately):
@@ -57,7 +63,7 @@ extern "C" {
 /* status codes */
 #define TQ_OK 0
 #define TQ_ERR_INVALID_ARGUMENT 1   /* null pointer, bad size, inconsistent shapes */
-#define TQ_ERR_UNSUPPORTED 2        /* valid but not implemented (d != 128, G > 16, ...) */
+#define TQ_ERR_UNSUPPORTED 2        /* valid but not implemented (d not 64/128/256, G > 16, ...) */
 #define TQ_ERR_ALIGNMENT 3          /* a device pointer breaks its alignment rule */
 #define TQ_ERR_WORKSPACE_TOO_SMALL 4
 #define TQ_ERR_DEVICE 5             /* a HIP call or kernel launch failed */
@@ -108,7 +114,7 @@ typedef struct tq_cache {
   int32_t role;        /* TQ_KEYS or TQ_VALUES */
   int32_t bits;        /* 2, 3 or 4 bits per coordinate (the Lloyd-Max part) */
   int32_t qjl;         /* 1: keys carry the QJL sign sketch; 0 otherwise */
-  int32_t d;           /* head dimension, 128 */
+  int32_t d;           /* head dimension: 128, 64 or 256 (QJL keys: 128) */
   int64_t B;           /* batch rows */
   int64_t H_kv;        /* KV heads */
   int64_t T_cap;       /* token capacity per (row, head); multiple of 8 for values */
@@ -133,7 +139,8 @@ typedef struct tq_cache {
  * symmetrised and rounded to float16 (nearest even). thresholds[i] is the exact
  * midpoint of centroids[i] and centroids[i+1]; the middle one is +0.0.
  * centroids: host, 2^bits floats; thresholds: host, 2^bits - 1 floats (may be NULL).
- * bits in 1..4; d must be 128. Host only: no HIP call.
+ * The codebook is in standard units, so it is the same for every d.
+ * bits in 1..4; d is 64, 128 or 256. Host only: no HIP call.
  */
 int tq_make_codebook(int32_t bits, int32_t d, float* centroids, float* thresholds);
 
@@ -149,7 +156,7 @@ int tq_make_codebook(int32_t bits, int32_t d, float* centroids, float* threshold
  * Cell probabilities use the regularized incomplete beta function. At d = 128
  * the 3-bit MSE is 0.033966 against 0.034548 for the Gaussian codebook on
  * Gaussian data. bits in 1..4; d in 3..65536 (host computation; the kernels
- * use d = 128). Host only: no HIP call.
+ * take d = 64, 128, 256). Host only: no HIP call.
  */
 int tq_make_codebook_sphere(int32_t bits, int32_t d, float* centroids, float* thresholds);
 
@@ -164,7 +171,8 @@ int tq_make_codebook_sphere(int32_t bits, int32_t d, float* centroids, float* th
  * (H[i][j] = (-1)^popcount(i & j)) and s_j = -1 when the top bit of stream
  * output j+1 is set, else +1 (a randomized Hadamard rotation, a cheaper
  * orthogonal alternative for step 1; stored dense like the others).
- * Computed in double precision, rounded to float32. Host only: no HIP call.
+ * Computed in double precision, rounded to float32. d is 64, 128 or 256.
+ * Host only: no HIP call.
  */
 int tq_make_rotation(uint64_t seed, int32_t d, int32_t kind, float* out);
 
@@ -237,8 +245,10 @@ int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void*
  *   scale:    score scale; <= 0 selects 1/sqrt(d)
  *   out:      device float32 [B][H_q][d]
  *   workspace: device, at least tq_decode_workspace_bytes(...) bytes, 256-byte aligned
- * Requires k->role == TQ_KEYS, v->role == TQ_VALUES, equal B and H_kv,
- * H_q % H_kv == 0 and G <= 16. Value norms may have any overall scale: the
+ * Requires k->role == TQ_KEYS, v->role == TQ_VALUES, equal B, H_kv and d,
+ * H_q % H_kv == 0 and G <= 16. At d = 64 and 256 the decode is one launch of
+ * float32 arithmetic throughout (n_split, workspace and workspace_bytes are
+ * ignored; the workspace may be NULL). At d = 128, value norms may have any overall scale: the
  * float16 weights of the value sum are scaled per wavefront by a power of two
  * taken from the largest value norm of its first 32 tokens, so within one
  * (row, KV head) the largest value norm must stay below 7e5 times the
@@ -317,7 +327,8 @@ int tq_decode_attention_append(const tq_cache* k, const tq_cache* v, const void*
  *   out:      device float32 [B][M][H_q][d]
  *   workspace: device, at least tq_prefill_workspace_bytes(...) bytes, 256-byte aligned
  * Other arguments and requirements as tq_decode_attention; M in 1..65535 and
- * B * ceil(M / tile) <= 65535.
+ * B * ceil(M / tile) <= 65535. At d = 64 and 256 only M = 1 (the decode) is
+ * taken; M > 1 returns TQ_ERR_UNSUPPORTED.
  */
 int tq_prefill_attention(const tq_cache* k, const tq_cache* v,
                          const void* q, int32_t q_dtype, int64_t H_q, int64_t M,

@@ -78,18 +78,24 @@ def test_codebook_rejects_bad_arguments():
     assert lib.tq_make_codebook(0, 128, c.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_make_codebook(5, 128, c.ctypes.data, None) == tq.ERR_INVALID_ARGUMENT
     assert lib.tq_make_codebook(3, 128, None, None) == tq.ERR_INVALID_ARGUMENT
-    assert lib.tq_make_codebook(3, 64, c.ctypes.data, None) == tq.ERR_UNSUPPORTED
+    assert lib.tq_make_codebook(3, 96, c.ctypes.data, None) == tq.ERR_UNSUPPORTED
+    # the Gaussian codebook (standard units) is the same at every head dimension
+    for d in (64, 256):
+        c64, t64 = tq.make_codebook(3, d)
+        c128, t128 = tq.make_codebook(3)
+        assert np.array_equal(c64, c128) and np.array_equal(t64, t128)
 
 
+@pytest.mark.parametrize("d", [64, 128, 256])
 @pytest.mark.parametrize("seed", [42, 7, 2**63 + 5])
-def test_rotation_matches_oracle(seed):
-    P = tq.make_rotation(seed, tq.HAAR).astype(np.float64)
-    assert np.abs(P - orot.haar_rotation(seed, 128)).max() <= 1e-6
-    assert np.abs(P.T @ P - np.eye(128)).max() <= 1e-5
-    S = tq.make_rotation(seed, tq.GAUSSIAN).astype(np.float64)
-    assert np.abs(S - orot.qjl_projection(seed, 128)).max() <= 1e-6
-    H = tq.make_rotation(seed, tq.HADAMARD).astype(np.float64)
-    assert np.array_equal(H, orot.hadamard_rotation(seed, 128))
+def test_rotation_matches_oracle(seed, d):
+    P = tq.make_rotation(seed, tq.HAAR, d).astype(np.float64)
+    assert np.abs(P - orot.haar_rotation(seed, d)).max() <= 1e-6
+    assert np.abs(P.T @ P - np.eye(d)).max() <= 1e-5
+    S = tq.make_rotation(seed, tq.GAUSSIAN, d).astype(np.float64)
+    assert np.abs(S - orot.qjl_projection(seed, d)).max() <= 1e-6
+    H = tq.make_rotation(seed, tq.HADAMARD, d).astype(np.float64)
+    assert np.array_equal(H, orot.hadamard_rotation(seed, d))
 
 
 def test_rotation_rejects_bad_arguments():
@@ -124,9 +130,9 @@ def test_decode_planning():
 FAKE = 1 << 20   # 16-byte aligned, never touched
 
 
-def _cache(role=tq.KEYS, bits=3, qjl=0, B=2, H=2, T_cap=64, **kw):
+def _cache(role=tq.KEYS, bits=3, qjl=0, B=2, H=2, T_cap=64, d=128, **kw):
     s = tq.TQCache()
-    s.role, s.bits, s.qjl, s.d = role, bits, qjl, 128
+    s.role, s.bits, s.qjl, s.d = role, bits, qjl, d
     s.B, s.H_kv, s.T_cap = B, H, T_cap
     s.codes = s.norms = s.rot = FAKE
     if qjl:
@@ -146,7 +152,12 @@ def _quant(s, x=FAKE, dtype=tq.BF16, B=2, T=4, H=2, strides=(4 * 2 * 128, 2 * 12
 def test_quantize_validation_paths():
     assert _quant(_cache(bits=5)) == tq.ERR_UNSUPPORTED
     assert _quant(_cache(bits=1)) == tq.ERR_UNSUPPORTED
-    assert _quant(_cache(d=64)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(d=96)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(d=512)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(d=64, qjl=1)) == tq.ERR_UNSUPPORTED        # QJL keys: d = 128 only
+    assert _quant(_cache(d=256, qjl=1)) == tq.ERR_UNSUPPORTED
+    assert _quant(_cache(d=64), T=0) == tq.OK                      # d = 64 and 256 are taken
+    assert _quant(_cache(d=256, role=tq.VALUES), T=0) == tq.OK
     assert _quant(_cache(role=7)) == tq.ERR_INVALID_ARGUMENT
     assert _quant(_cache(role=tq.VALUES, qjl=1)) == tq.ERR_UNSUPPORTED
     assert _quant(_cache(role=tq.VALUES, T_cap=60)) == tq.ERR_INVALID_ARGUMENT
@@ -192,6 +203,7 @@ def test_append_validation_paths():
     assert _append(K, V, dtype=9) == tq.ERR_INVALID_ARGUMENT
     assert _append(_cache(bits=5), V) == tq.ERR_UNSUPPORTED
     assert _append(K, _cache(role=tq.VALUES, codes=None)) == tq.ERR_INVALID_ARGUMENT
+    assert _append(K, _cache(role=tq.VALUES, d=64)) == tq.ERR_INVALID_ARGUMENT   # one head dimension
 
 
 def _fused(K, V, kn=FAKE, vn=FAKE, ndt=tq.BF16, strides=(2 * 128, 128, 2 * 128, 128), q=FAKE, H_q=4, ctx=None,
@@ -229,6 +241,10 @@ def test_prefill_validation_paths():
     assert call(M=70000) == tq.ERR_UNSUPPORTED
     assert call(ws_bytes=16) == tq.ERR_WORKSPACE_TOO_SMALL
     assert call(H_q=7) == tq.ERR_INVALID_ARGUMENT                 # H_q % H_kv
+    # the chunked prefill exists for d = 128 only
+    K64, V64 = _cache(d=64), _cache(role=tq.VALUES, d=64)
+    assert lib.tq_prefill_attention(ctypes.byref(K64), ctypes.byref(V64), FAKE, tq.BF16, 8, 4, None, 64, 0.0, 0,
+                                    FAKE, FAKE, 1 << 30, None) == tq.ERR_UNSUPPORTED
     # workspace grows with M (chunk partials per query token and head)
     one = tq.prefill_workspace_bytes(2, 8, 2, 1, 4096, 4, 0)
     assert one == tq.decode_workspace_bytes(2, 8, 2, 4096, 4, 0)
@@ -275,6 +291,8 @@ def test_decode_validation_paths():
     assert _decode(K, V, scale=float("nan")) == tq.ERR_INVALID_ARGUMENT
     assert _decode(K, V, n_split=-1) == tq.ERR_INVALID_ARGUMENT
     assert _decode(K, V, dtype=5) == tq.ERR_INVALID_ARGUMENT
+    assert _decode(K, _cache(role=tq.VALUES, d=256)) == tq.ERR_INVALID_ARGUMENT   # K and V head dims differ
+    assert _decode(_cache(d=64), _cache(role=tq.VALUES, d=64), H_q=34) == tq.ERR_UNSUPPORTED
 
 
 def test_dequantize_validation_paths():

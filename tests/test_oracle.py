@@ -557,6 +557,111 @@ def test_split_merge_equals_one_pass(bounds):
     assert np.abs(o_rot - one).max() <= 1e-12 * np.abs(one).max()
 
 
+# ------------------------------------------------- head dimensions 64, 256 --
+# The method is stated for any d; these pins hold the oracle at the two other
+# head dimensions the library takes.
+
+HEAD_DIMS = (64, 256)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_rotations_other_head_dims(d):
+    P = rotation.haar_rotation_f64(42, d)
+    assert np.abs(P.T @ P - np.eye(d)).max() <= 1e-12
+    R = P.T @ rotation.gaussian_matrix(42, d)
+    assert np.abs(np.tril(R, -1)).max() < 1e-10 and np.all(np.diag(R) > 0)
+    H = rotation.hadamard_rotation(42, d)
+    assert np.abs(H.T @ H - np.eye(d)).max() <= 1e-6
+    assert np.all(np.abs(np.abs(H) - np.float32(1 / math.sqrt(d))) == 0)
+    z = rng.splitmix64(42, d)
+    assert np.array_equal(np.sign(H[0]), np.where(z >= np.uint64(1 << 63), -1.0, 1.0))
+
+
+def _sphere_law_sq_error(c, t, d):
+    """E[(sqrt(d) u - c[cell(u)])^2] for u one coordinate of a uniform unit vector
+    in d dimensions, density proportional to (1 - u^2)^((d-3)/2) on [-1, 1]:
+    E[d u^2] = 1, so the error is 1 - 2 sum c_i m_i + sum c_i^2 P_i with P_i the
+    cell's probability and m_i = sqrt(d) E[u; cell i] (the incomplete beta law
+    and the first moment in closed form)."""
+    a = (d - 1) / 2.0
+    k = (d - 3) / 2.0
+    sd = math.sqrt(d)
+    edges = np.concatenate([[-1.0], np.asarray(t) / sd, [1.0]])
+    P = np.diff(special.betainc(a, a, (1.0 + edges) / 2.0))
+    g = np.exp((k + 1.0) * np.log(np.maximum(1.0 - edges ** 2, 1e-300)) - special.betaln(0.5, k + 1.0))
+    m = sd * (g[:-1] - g[1:]) / (2.0 * (k + 1.0))
+    return 1.0 - 2.0 * float(np.sum(c * m)) + float(np.sum(c ** 2 * P))
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_quantize_error_matches_sphere_law(d, bits):
+    """Haar-rotated unit vectors in d dimensions: the mean squared error of the
+    scaled coordinates against their centroids equals the closed form under the
+    exact law of one sphere coordinate (within 4 standard errors of the sample),
+    which tells d = 64 from the Gaussian limit and from d = 128."""
+    c16, t = codebook.canonical(bits)
+    P = rotation.haar_rotation(42, d)
+    X = random_unit_vectors(4000, d, 11 + bits)
+    q = quantize.quantize_head(X, P, c16, t)
+    err = (q["u"] * math.sqrt(d) - c16[q["codes"]]) ** 2
+    per_vec = err.mean(axis=1)
+    want = _sphere_law_sq_error(c16, t, d)
+    assert abs(per_vec.mean() - want) <= 4 * per_vec.std() / math.sqrt(len(per_vec))
+    if d == 64:
+        other = _sphere_law_sq_error(c16, t, 4096)   # close to the Gaussian limit
+        assert abs(other - want) > 6 * per_vec.std() / math.sqrt(len(per_vec))
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+@pytest.mark.parametrize("bits", [2, 3, 4])
+def test_pack_roundtrip_other_head_dims(d, bits):
+    g = np.random.default_rng(bits + d)
+    codes = g.integers(0, 1 << bits, size=(24, d))
+    assert np.array_equal(quantize.unpack_keys(quantize.pack_keys(codes, bits), bits, d), codes)
+    assert np.array_equal(quantize.unpack_values(quantize.pack_values(codes, bits), bits, d), codes)
+    assert quantize.pack_keys(codes, bits).nbytes == quantize.pack_values(codes, bits).nbytes == 24 * d * bits // 8
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_value_layout_single_bit_other_head_dims(d):
+    bits = 3
+    j = d - 3
+    codes = np.zeros((16, d), dtype=np.int64)
+    codes[8 + 5, j] = 1
+    w = quantize.pack_values(codes, bits)
+    pos = bits * (8 * j + 5)
+    expect = np.zeros_like(w)
+    expect[1, pos // 32] = 1 << (pos % 32)
+    assert np.array_equal(w, expect)
+    kc = np.zeros((1, d), dtype=np.int64)
+    kc[0, j] = 5   # key layout: code j at bits [3j, 3j + 3)
+    kw = quantize.pack_keys(kc, bits)[0]
+    got = sum(int(x) << (32 * i) for i, x in enumerate(kw))
+    assert got == 5 << (bits * j)
+
+
+@pytest.mark.parametrize("d", HEAD_DIMS)
+def test_rotated_domain_equals_textbook_other_head_dims(d):
+    g = np.random.default_rng(d)
+    P = rotation.haar_rotation(42, d)
+    ck, tk = codebook.canonical(4)
+    cv, tv = codebook.canonical(2)
+    k = quantize.quantize_head(g.standard_normal((200, d)) * 3, P, ck, tk)
+    v = quantize.quantize_head(g.standard_normal((200, d)), P, cv, tv)
+    q = g.standard_normal((5, d))
+    Kh = attention.dequantize_head(k["codes"], k["norm"], P, ck, d)
+    Vh = attention.dequantize_head(v["codes"], v["norm"], P, cv, d)
+    scale = 1 / math.sqrt(d)
+    a = attention.attend_textbook(q, Kh, Vh, scale)
+    b = attention.attend_rotated(q, k, v, P, P, ck, cv, d, scale)
+    assert np.abs(a - b).max() <= 1e-12 * np.abs(a).max()
+    # one token: its value; identical keys: the mean value
+    one = attention.attend_rotated(q, {"codes": k["codes"][:1], "norm": k["norm"][:1]},
+                                   {"codes": v["codes"][:1], "norm": v["norm"][:1]}, P, P, ck, cv, d, scale)
+    assert np.allclose(one, np.repeat(Vh[:1], 5, axis=0), rtol=1e-12, atol=1e-14)
+
+
 def test_package_imports_only_numpy_scipy():
     import sys
     assert "decode_attention_tq_amd" not in oracle.__dict__

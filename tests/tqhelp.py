@@ -49,10 +49,11 @@ class OracleModel:
 
     def __init__(self, w: tq_synth.Workload, codebook: str = "gaussian", rotation: str = "haar"):
         self.w = w
-        self.Pi = (orot.hadamard_rotation if rotation == "hadamard" else orot.haar_rotation)(tq_synth.ROT_SEED, D)
-        self.S = orot.qjl_projection(tq_synth.QJL_SEED, D) if w.k_qjl else None
+        d = w.d
+        self.Pi = (orot.hadamard_rotation if rotation == "hadamard" else orot.haar_rotation)(tq_synth.ROT_SEED, d)
+        self.S = orot.qjl_projection(tq_synth.QJL_SEED, d) if w.k_qjl else None
         if codebook == "sphere":
-            make = lambda bits: ocb.canonical_sphere(bits, D)
+            make = lambda bits: ocb.canonical_sphere(bits, d)
         elif codebook == "shifted":
             make = shifted_codebook
         else:
@@ -77,33 +78,34 @@ class OracleModel:
         w = self.w
         G = w.G
         qs = np.asarray(q[b, kv * G:(kv + 1) * G], dtype=np.float64)
-        return oa.attend_rotated(qs, kh[(b, kv)], vh[(b, kv)], self.Pi, self.Pi, self.cK, self.cV, D,
-                                 1.0 / math.sqrt(D), ctx_len=ctx, S=self.S)
+        return oa.attend_rotated(qs, kh[(b, kv)], vh[(b, kv)], self.Pi, self.Pi, self.cK, self.cV, w.d,
+                                 1.0 / math.sqrt(w.d), ctx_len=ctx, S=self.S)
 
 
 def pack_head(role: str, codes: np.ndarray, bits: int, T_cap: int) -> np.ndarray:
     """Oracle-packed words of one head padded to T_cap tokens (uint32)."""
-    full = np.zeros((T_cap, D), dtype=np.int64)
+    full = np.zeros((T_cap, codes.shape[1]), dtype=np.int64)
     full[:codes.shape[0]] = codes
     if role == "k":
         return oq.pack_keys(full, bits).reshape(-1)
     return oq.pack_values(full, bits).reshape(-1)
 
 
-def unpack_head(role: str, words: np.ndarray, bits: int, T: int) -> np.ndarray:
+def unpack_head(role: str, words: np.ndarray, bits: int, T: int, d: int = D) -> np.ndarray:
     words = np.asarray(words).view(np.uint32)
-    W = D * bits // 32
+    W = d * bits // 32
     if role == "k":
-        return oq.unpack_keys(words.reshape(-1, W), bits, D)[:T]
-    return oq.unpack_values(words.reshape(-1, 8 * W), bits, D)[:T]
+        return oq.unpack_keys(words.reshape(-1, W), bits, d)[:T]
+    return oq.unpack_values(words.reshape(-1, 8 * W), bits, d)[:T]
 
 
 def code_mismatch(role, gpu_words, ref: dict, bits: int, thresholds, T: int):
     """(mismatches, mismatches outside the boundary band, coordinates compared)."""
-    got = unpack_head(role, gpu_words, bits, T)
+    d = ref["codes"].shape[1]
+    got = unpack_head(role, gpu_words, bits, T, d)
     want = ref["codes"][:T]
     bad = got != want
-    exempt = oq.boundary_distance(ref["u"][:T], thresholds, D) < BOUNDARY
+    exempt = oq.boundary_distance(ref["u"][:T], thresholds, d) < BOUNDARY
     return int(bad.sum()), int((bad & ~exempt).sum()), bad.size
 
 
@@ -117,8 +119,8 @@ def upload_oracle_cache(tq, model: OracleModel, which: str, heads: dict, T_cap: 
     qjl = which == "k" and w.k_qjl
     cache = tq.Cache(role, bits, w.B, w.H_kv, T_cap, device=device, rot=model.Pi.astype(np.float32),
                      proj=model.S.astype(np.float32) if qjl else None, qjl=qjl,
-                     centroids=(model.cK if which == "k" else model.cV).astype(np.float32))
-    codes = np.zeros((w.B, w.H_kv, T_cap * D * bits // 32), dtype=np.uint32)
+                     centroids=(model.cK if which == "k" else model.cV).astype(np.float32), d=w.d)
+    codes = np.zeros((w.B, w.H_kv, T_cap * w.d * bits // 32), dtype=np.uint32)
     norms = np.zeros((w.B, w.H_kv, T_cap), dtype=np.float32)
     signs = np.zeros((w.B, w.H_kv, T_cap, 4), dtype=np.uint32) if qjl else None
     gamma = np.zeros((w.B, w.H_kv, T_cap), dtype=np.float32) if qjl else None
@@ -168,9 +170,9 @@ def gpu_heads(cache, w: tq_synth.Workload, which: str, T: int) -> dict:
     out = {}
     for b in range(w.B):
         for h in range(w.H_kv):
-            d = {"codes": unpack_head(which, codes[b, h], bits, T), "norm": norms[b, h, :T].astype(np.float64)}
+            d = {"codes": unpack_head(which, codes[b, h], bits, T, w.d), "norm": norms[b, h, :T].astype(np.float64)}
             if qjl:
-                d["signs"] = oq.unpack_signs(signs[b, h, :T], D)
+                d["signs"] = oq.unpack_signs(signs[b, h, :T], w.d)
                 d["gamma"] = gamma[b, h, :T].astype(np.float64)
             out[(b, h)] = d
     return out
@@ -208,7 +210,7 @@ def band_report(w: tq_synth.Workload, model: "OracleModel", oracle_heads: dict, 
     thr = model.tK if which == "k" else model.tV
     ref = oracle_heads[(b, kv)]
     T = ref["codes"].shape[0]
-    band = oq.boundary_distance(ref["u"][:T], thr, D) < BOUNDARY
+    band = oq.boundary_distance(ref["u"][:T], thr, w.d) < BOUNDARY
     diff = gpu[(b, kv)]["codes"] != ref["codes"][:T]
     msg = f"{which}: {int(band.sum())} band codes, {int(diff.sum())} codes differ"
     if which == "k" and w.k_qjl:
