@@ -246,7 +246,23 @@ class Cache:
             centroids, _ = make_codebook(bits, d)
         self.centroids = np.asarray(centroids, dtype=np.float32)
 
+    def __setattr__(self, name, value):
+        # any change of an attribute drops the cached C struct
+        object.__setattr__(self, name, value)
+        if name != "_struct":
+            object.__setattr__(self, "_struct", None)
+
     def struct(self) -> TQCache:
+        """The tq_cache struct of this cache (built once, rebuilt after an
+        attribute is reassigned; in-place edits of the centroids array need a
+        reassignment to be seen)."""
+        s = self.__dict__.get("_struct")
+        if s is None:
+            s = self._make_struct()
+            object.__setattr__(self, "_struct", s)
+        return s
+
+    def _make_struct(self) -> TQCache:
         s = TQCache()
         s.role, s.bits, s.qjl, s.d = self.role, self.bits, self.qjl, self.d
         s.B, s.H_kv, s.T_cap = self.B, self.H_kv, self.T_cap

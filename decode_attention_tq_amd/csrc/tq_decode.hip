@@ -888,96 +888,98 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 // Workgroup (kv, b, chunk): merge the context-chunk partials of the G query
 // heads of KV head kv (every workgroup of the KV head merges all 128
 // coordinates), then output coordinates 32*chunk .. 32*chunk+31 of
-// o = Pi_V^T o', with those 32 columns of Pi_V staged in LDS. The merge first
-// takes each head's largest chunk maximum M, then sums the chunks in chunk
-// order with weights 2^(m - M) kept in LDS (blocks of kCombineBlock chunks),
-// so the loads of a thread's chunk partials are independent of each other.
-constexpr int kCombineBlock = 256;
+// o = Pi_V^T o', with those 32 columns of Pi_V staged in LDS. Entry e =
+// (group gr, pair pr) of the S groups of the G*128 (head, coordinate) pairs
+// takes chunks gr, gr + S, ... in order, kCombineBatch at a time with all
+// their loads in flight together, under a running maximum; the groups are
+// then merged in group order. The order of every step is fixed by the plan.
+constexpr int kCombineThreads = 512;
+constexpr int kCombineBatch = 16;
 
-__global__ __launch_bounds__(256) void combine_kernel(const float* ml, const float* acc, const float* rotV,
-                                                       float* out, int H_q, int G, int n_split, float inv_sqrt_d) {
+__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* ml, const float* acc,
+                                                                  const float* rotV, float* out, int H_q, int G,
+                                                                  int n_split, float inv_sqrt_d) {
+  constexpr int NT = kCombineThreads;
   __shared__ __align__(16) float colv[kD * 32];
   __shared__ __align__(16) float ov[16 * kD];
-  __shared__ float wsp[16 * kCombineBlock];
-  __shared__ float Mh[16], dh[16];
+  __shared__ float gsh[3][NT];
   const int kv = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z, tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
   const int64_t bh0 = (int64_t)b * H_q + (int64_t)kv * G;
   {
-    // Pi_V[j][32*chunk + 0..31] for all j: 1024 16-byte pieces, 4 per thread
-    float4 v[4];
+    // Pi_V[j][32*chunk + 0..31] for all j: 1024 16-byte pieces, 2 per thread
+    float4 v[2];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int f = tid + 256 * k, j = f >> 3, c4 = f & 7;
+    for (int k = 0; k < 2; ++k) {
+      const int f = tid + NT * k, j = f >> 3, c4 = f & 7;
       v[k] = *(const float4*)(rotV + j * kD + 32 * chunk + 4 * c4);
     }
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int f = tid + 256 * k;
-      *(float4*)(colv + 4 * f) = v[k];
-    }
+    for (int k = 0; k < 2; ++k) *(float4*)(colv + 4 * (tid + NT * k)) = v[k];
   }
-  // per-head maximum of the chunk maxima: wavefront w takes heads w, w + 4, ...
-  for (int h = wave; h < G; h += 4) {
+  const int NP = G * kD;
+  const int S = NT / NP > 0 ? NT / NP : 1;
+  for (int e = tid; e < S * NP; e += NT) {
+    const int gr = e / NP, pr = e % NP, h = pr / kD, j = pr % kD;
     const float* mlb = ml + (bh0 + h) * n_split * 2;
-    float M = -INFINITY;
-    for (int sp = lane; sp < n_split; sp += 64) M = fmaxf(M, mlb[2 * sp]);
+    const float* ab = acc + (bh0 + h) * n_split * kD + j;
+    float M = -INFINITY, num = 0.f, den = 0.f;
+    for (int sp0 = gr; sp0 < n_split; sp0 += kCombineBatch * S) {
+      float mv[kCombineBatch], lv[kCombineBatch], xv[kCombineBatch];
 #pragma unroll
-    for (int m = 1; m < 64; m <<= 1) M = fmaxf(M, __shfl_xor(M, m));
-    if (lane == 0) Mh[h] = M;
+      for (int u = 0; u < kCombineBatch; ++u) {
+        // (chunks past n_split read chunk gr again and are dropped below)
+        const int sp = sp0 + u * S < n_split ? sp0 + u * S : gr;
+        mv[u] = mlb[2 * sp];
+        lv[u] = mlb[2 * sp + 1];
+        xv[u] = ab[(int64_t)sp * kD];
+      }
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u)
+        if (sp0 + u * S >= n_split) mv[u] = -INFINITY;   // (empty chunks carry -inf as well)
+      float bm = M;
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) bm = fmaxf(bm, mv[u]);
+      if (bm == -INFINITY) continue;
+      const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
+      num *= f;
+      den *= f;
+#pragma unroll
+      for (int u = 0; u < kCombineBatch; ++u) {
+        const float w = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - bm);
+        num = fmaf(w, xv[u], num);
+        den = fmaf(w, lv[u], den);
+      }
+      M = bm;
+    }
+    if (S == 1) {
+      ov[pr] = den > 0.f ? num / den * inv_sqrt_d : 0.f;
+    } else {
+      gsh[0][e] = M;
+      gsh[1][e] = num;
+      gsh[2][e] = den;
+    }
+  }
+  if (S > 1) {
+    __syncthreads();
+    for (int pr = tid; pr < NP; pr += NT) {
+      float M = -INFINITY, num = 0.f, den = 0.f;
+      for (int gr = 0; gr < S; ++gr) {
+        const float m = gsh[0][gr * NP + pr];
+        if (m == -INFINITY) continue;
+        const float Mn = fmaxf(M, m);
+        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+        const float fn = __builtin_amdgcn_exp2f(m - Mn);
+        num = num * fo + gsh[1][gr * NP + pr] * fn;
+        den = den * fo + gsh[2][gr * NP + pr] * fn;
+        M = Mn;
+      }
+      ov[pr] = den > 0.f ? num / den * inv_sqrt_d : 0.f;
+    }
   }
   __syncthreads();
-
-  constexpr int PER = 16 * kD / 256;   // (head, coordinate) pairs per thread, for G <= 16
-  float num[PER];
-#pragma unroll
-  for (int k = 0; k < PER; ++k) num[k] = 0.f;
-  float den = 0.f;   // thread h < G: denominator of head h
-  for (int base = 0; base < n_split; base += kCombineBlock) {
-    const int nb = min(kCombineBlock, n_split - base);
-    for (int e = tid; e < G * kCombineBlock; e += 256) {
-      const int h = e / kCombineBlock, sp = e % kCombineBlock;
-      float w = 0.f;
-      if (sp < nb) {
-        const float m = ml[((bh0 + h) * n_split + base + sp) * 2];
-        w = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(m - Mh[h]);
-      }
-      wsp[e] = w;
-    }
-    __syncthreads();
-    if (tid < G) {
-      const float* mlb = ml + ((bh0 + tid) * n_split + base) * 2;
-#pragma unroll 8
-      for (int sp = 0; sp < nb; ++sp) den = fmaf(wsp[tid * kCombineBlock + sp], mlb[2 * sp + 1], den);
-      dh[tid] = den;
-    }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int idx = tid + 256 * k;
-      if (idx < G * kD) {
-        const int h = idx / kD, j = idx % kD;
-        const float* ab = acc + ((bh0 + h) * n_split + base) * kD + j;
-        const float* wh = wsp + h * kCombineBlock;
-        float x = num[k];
-#pragma unroll 8
-        for (int sp = 0; sp < nb; ++sp) x = fmaf(wh[sp], ab[(int64_t)sp * kD], x);
-        num[k] = x;
-      }
-    }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int k = 0; k < PER; ++k) {
-    const int idx = tid + 256 * k;
-    if (idx < G * kD) {
-      const float d = dh[idx / kD];
-      ov[idx] = d > 0.f ? num[k] / d * inv_sqrt_d : 0.f;
-    }
-  }
-  __syncthreads();
-  // thread (i, hq): out[h][32*chunk + i] for heads hq, hq + 8
+  // thread (i, hq): out[h][32*chunk + i] for heads hq, hq + NT/32, ...
   const int i = tid & 31, hq = tid >> 5;
-  for (int h = hq; h < G; h += 8) {
+  for (int h = hq; h < G; h += NT / 32) {
     float r = 0.f;
 #pragma unroll 8
     for (int j = 0; j < kD; ++j) r = fmaf(colv[j * 32 + i], ov[h * kD + j], r);
@@ -1080,7 +1082,7 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
 hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
                           int64_t H_kv, int64_t H_q, int G, int n_split, hipStream_t stream) {
   const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)H_kv, (unsigned)rows, kD / 32), dim3(256), 0, stream, ml, acc,
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)H_kv, (unsigned)rows, kD / 32), dim3(kCombineThreads), 0, stream, ml, acc,
                      rotV, out, (int)H_q, G, n_split, inv_sqrt_d);
   return hipGetLastError();
 }
