@@ -10,8 +10,7 @@ The names follow the C ABI in include/tq.h:
     dequantize(cache, t0, t1)                  -> float32 [B, H_kv, t1-t0, d]
     decode_attention(k, v, q, ...)             -> float32 [B, H_q, d]
 
-d (the head dimension) is 128, 64 or 256; QJL keys and prefill_attention take
-d = 128 only.
+d (the head dimension) is 128, 64 or 256; QJL keys take d = 128 only.
     decode_workspace_bytes(...), decode_splits(...), status_string(code)
 
 Cache bundles the device buffers of one packed cache (keys or values) with its
@@ -446,17 +445,17 @@ def decode_attention_append(k: Cache, v: Cache, k_new, v_new, q, ctx_lens=None, 
 
 def prefill_attention(k: Cache, v: Cache, q, ctx_lens=None, T: int | None = None, scale: float = 0.0,
                       n_split: int = 0, out=None, workspace: Workspace | None = None):
-    """Chunked causal attention of the M newest tokens of each row, q [B, M, H_q, 128]
+    """Chunked causal attention of the M newest tokens of each row, q [B, M, H_q, d]
     (their keys and values already in the caches), over the packed caches ->
-    float32 [B, M, H_q, 128]; token i of row b attends to cache tokens
-    0 .. ctx_len[b] - M + i. (d = 128 only.)"""
+    float32 [B, M, H_q, d]; token i of row b attends to cache tokens
+    0 .. ctx_len[b] - M + i. (d = 256: at most 8 (token, head) columns per KV head.)"""
     torch = _torch()
-    if q.dim() != 4 or q.shape[-1] != D or not q.is_contiguous():
-        raise ValueError("q must be a contiguous [B, M, H_q, 128] tensor")
+    if q.dim() != 4 or q.shape[-1] != k.d or not q.is_contiguous():
+        raise ValueError(f"q must be a contiguous [B, M, H_q, {k.d}] tensor")
     B, M, H_q, _ = q.shape
     T = k.T_cap if T is None else T
     if out is None:
-        out = torch.empty((B, M, H_q, D), dtype=torch.float32, device=q.device)
+        out = torch.empty((B, M, H_q, k.d), dtype=torch.float32, device=q.device)
     need = prefill_workspace_bytes(B, H_q, k.H_kv, M, T, n_split, k.qjl)
     if workspace is None or workspace.nbytes < need:
         workspace = Workspace(need, q.device)

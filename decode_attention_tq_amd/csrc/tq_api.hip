@@ -76,7 +76,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 }  // namespace
 
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
-                 DecodePlan* p, int64_t M) {
+                 DecodePlan* p, int64_t M, int32_t d) {
   if (B <= 0 || H_q <= 0 || H_kv <= 0 || T < 0 || n_split < 0 || M <= 0) return false;
   if (H_q % H_kv != 0) return false;
   const int64_t G = H_q / H_kv;
@@ -114,7 +114,7 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   p->off_ml = off;
   off = align256(off + (size_t)(B * M * H_q) * p->n_split * 2 * sizeof(float));
   p->off_acc = off;
-  off = align256(off + (size_t)(B * M * H_q) * p->n_split * kD * sizeof(float));
+  off = align256(off + (size_t)(B * M * H_q) * p->n_split * d * sizeof(float));
   p->bytes = off;
   return true;
 }
@@ -186,19 +186,26 @@ extern "C" int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t 
 
 extern "C" size_t tq_prefill_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t M, int64_t T,
                                              int32_t n_split, int32_t k_qjl) {
-  if (H_kv > 0 && H_q % H_kv == 0 && use_dense_prefill(M, H_q / H_kv, k_qjl)) {
+  // enough for every head dimension: the dense plan (d = 128) where it
+  // applies, and the scan tiles' plan at the largest d that takes them (256
+  // up to 8 (token, head) columns per KV head, else 128; d = 64 needs less)
+  if (H_kv <= 0 || H_q % H_kv != 0 || M <= 0) return 0;
+  size_t bytes = 0;
+  if (use_dense_prefill(M, H_q / H_kv, k_qjl)) {
     DensePlan dp;
-    return plan_prefill_dense(B, H_q, H_kv, T, M, n_split, &dp) ? dp.bytes : 0;
+    if (!plan_prefill_dense(B, H_q, H_kv, T, M, n_split, &dp)) return 0;
+    bytes = dp.bytes;
   }
   DecodePlan p;
-  if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p, M)) return 0;
-  return p.bytes;
+  const int32_t dmax = M * (H_q / H_kv) <= 8 ? 256 : kD;
+  if (plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p, M, dmax)) bytes = bytes > p.bytes ? bytes : p.bytes;
+  return bytes;
 }
 
 extern "C" size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
                                             int32_t n_split, int32_t k_qjl) {
-  DecodePlan p;
-  if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p)) return 0;
+  DecodePlan p;   // (sized for the largest head dimension, 256)
+  if (!plan_decode(B, H_q, H_kv, T, n_split, k_qjl, &p, 1, 256)) return 0;
   return p.bytes;
 }
 
@@ -342,11 +349,13 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   if (!isfinite(scale)) return TQ_ERR_INVALID_ARGUMENT;
   if (!aligned16(q) || !aligned16(out)) return TQ_ERR_ALIGNMENT;
   if (k->d != v->d) return TQ_ERR_INVALID_ARGUMENT;
-  // head dimensions 64 / 256: one generic decode launch per call, no workspace;
-  // the chunked prefill exists for d = 128 only
-  const bool generic = k->d != kD;
+  // The scan tiles take every head dimension except d = 256 with more than 8
+  // (query token, head) columns per KV head: a decode with G > 8 there runs
+  // the generic kernel (one launch, no workspace), and chunked prefill with
+  // M * G > 8 is not offered. The dense prefill kernel is d = 128 only.
+  const bool generic = k->d > kD && M * (H_q / k->H_kv) > 8;
   if (generic && M != 1) return TQ_ERR_UNSUPPORTED;
-  const bool dense = !generic && app == nullptr && use_dense_prefill(M, H_q / k->H_kv, k->qjl);
+  const bool dense = k->d == kD && app == nullptr && use_dense_prefill(M, H_q / k->H_kv, k->qjl);
   DecodePlan p;
   DensePlan dp;
   if (generic) {
@@ -354,7 +363,7 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
   } else if (dense) {
     if (!plan_prefill_dense(k->B, H_q, k->H_kv, T, M, n_split, &dp)) return TQ_ERR_UNSUPPORTED;
     p.bytes = dp.bytes;
-  } else if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M)) {
+  } else if (!plan_decode(k->B, H_q, k->H_kv, T, n_split, k->qjl, &p, M, k->d)) {
     return TQ_ERR_UNSUPPORTED;
   }
   if (wsa.scratch) {
@@ -399,9 +408,18 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
     if (workspace == nullptr) return device_status(e);
   }
   if (app != nullptr) {
-    if (ctx_lens != nullptr || T > 0) {
+    if ((ctx_lens != nullptr || T > 0) && k->d == kD) {
       const hipError_t e = launch_append_kv(app->k, app->v, app->x_dtype, k->B, k->H_kv, app->k_sb, app->k_sh,
                                             app->v_sb, app->v_sh, k, v, T - 1, (hipStream_t)hip_stream, ctx_lens, T);
+      if (e != hipSuccess) return device_status(e);
+    } else if (ctx_lens != nullptr || T > 0) {
+      // other head dimensions: the generic quantize, in its one-token mode
+      const int64_t tk = ctx_lens != nullptr ? 0 : T - 1;
+      hipError_t e = launch_quantize_generic(app->k, app->x_dtype, k->B, 1, k->H_kv, app->k_sb, 0, app->k_sh, k, tk,
+                                             ctx_lens, T, (hipStream_t)hip_stream);
+      if (e != hipSuccess) return device_status(e);
+      e = launch_quantize_generic(app->v, app->x_dtype, k->B, 1, k->H_kv, app->v_sb, 0, app->v_sh, v, tk, ctx_lens, T,
+                                  (hipStream_t)hip_stream);
       if (e != hipSuccess) return device_status(e);
     }
     return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,

@@ -76,9 +76,13 @@ namespace {
 // ------------------------------------------------------ small matrix work --
 
 constexpr int kVecWords = 16 * kD;         // [16][d] float vectors
+template <int D>
+constexpr int vec_words() { return 16 * D; }
 // Column stride (in halves) of the float16 query operand in LDS: the 16 lanes
 // that read one 16-byte piece of 16 different columns then hit distinct banks.
 constexpr int kQStride = kD + 8;
+template <int D>
+constexpr int qstride() { return D + 8; }
 // Scratch region of a decode workgroup, in 32-bit words: the lookup tables
 // (scan), then the wavefront partials (merge) and the partial sums of the final
 // rotation, followed by two [16][d] float vector sets.
@@ -86,7 +90,10 @@ constexpr int kRegionWords = 16896;
 // Row stride (in floats) of a wavefront partial in the merge area: 128
 // coordinates, m and l, padded to a 16-byte multiple.
 constexpr int kMergeStride = kD + 4;
-constexpr int kScratchWords = kRegionWords + 2 * kVecWords;
+template <int D>
+constexpr int merge_stride() { return D + 4; }
+template <int D>
+constexpr int scratch_words() { return kRegionWords + 2 * vec_words<D>(); }
 
 // q' = M q for the G query heads of a workgroup: out[h][i] = sum_j M[i][j]
 // in[h][j] (in, out: LDS [G][d]). Thread t takes rows R*(t/16) .. R*(t/16)+R-1
@@ -159,17 +166,18 @@ __device__ void rotate_rows(const RowSegment<NT>& rs, const float* in, float* ou
 // dst holds the hi halves, column half_cols + h the lo halves, ~22 bits
 // together (zero columns for absent heads). Needs NT >= 256; ends with the
 // operand written by each thread, no barrier.
-template <int NT>
+template <int NT, int D = kD>
 __device__ void emit_operand(const float* vals, float sc, int G, int half_cols, _Float16* dst, float* cs,
                              int* hexp) {
+  constexpr int QS = qstride<D>();
   const int tid = threadIdx.x;
   if (tid < 256) {
-    // thread (h, seg): largest magnitude over 8 entries, then over the 16 segments
+    // thread (h, seg): largest magnitude over D/16 entries, then over the 16 segments
     const int h = tid >> 4, seg = tid & 15;
     float mx = 0.f;
     if (h < G) {
 #pragma unroll
-      for (int k = 0; k < 8; ++k) mx = fmaxf(mx, fabsf(vals[h * kD + 8 * seg + k] * sc));
+      for (int k = 0; k < D / 16; ++k) mx = fmaxf(mx, fabsf(vals[h * D + (D / 16) * seg + k] * sc));
     }
     // maximum over the 16 lanes of the row: quads, then rotates by 4 and 8
     mx = fmaxf(mx, dpp_xor1(mx));
@@ -183,14 +191,52 @@ __device__ void emit_operand(const float* vals, float sc, int G, int half_cols, 
     }
   }
   __syncthreads();
-  for (int idx = tid; idx < 2 * half_cols * kD; idx += NT) {
-    const int col = idx / kD, i = idx % kD;
+  for (int idx = tid; idx < 2 * half_cols * D; idx += NT) {
+    const int col = idx / D, i = idx % D;
     const int h = col % half_cols;
     float v = 0.f;
-    if (h < G) v = ldexpf(vals[h * kD + i] * sc, -hexp[h]);
+    if (h < G) v = ldexpf(vals[h * D + i] * sc, -hexp[h]);
     const _Float16 hi = (_Float16)v;
-    dst[col * kQStride + i] = col >= half_cols ? (_Float16)(v - (float)hi) : hi;
+    dst[col * QS + i] = col >= half_cols ? (_Float16)(v - (float)hi) : hi;
   }
+}
+
+// out[h][i] = sum_j M[i][j] in[h][j] for the G vectors in[G][D] (LDS), D != 128
+// (128 takes rotate_rows): thread (i, part) sums the part's NT/D-th of row i
+// (float4 reads of M, every element read once per workgroup), the parts meet
+// in `part_buf` ([NT/D][16][D] floats) in a fixed order. Ends with out
+// written, after a barrier.
+template <int NT, int D, int MAXG>
+__device__ void rotate_generic(const float* M, const float* in, float* out, float* part_buf, int G) {
+  constexpr int P = NT / D, SPAN = D / P;
+  const int tid = threadIdx.x, i = tid % D, pt = tid / D;
+  float acc[MAXG];
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h) acc[h] = 0.f;
+  const float4* row = (const float4*)(M + (int64_t)i * D + pt * SPAN);
+#pragma unroll 4
+  for (int k = 0; k < SPAN / 4; ++k) {
+    const float4 m = row[k];
+#pragma unroll
+    for (int h = 0; h < MAXG; ++h) {
+      if (h < G) {
+        const float4 x = *(const float4*)(in + h * D + pt * SPAN + 4 * k);   // (same address across the row's lanes)
+        acc[h] = fmaf(m.w, x.w, fmaf(m.z, x.z, fmaf(m.y, x.y, fmaf(m.x, x.x, acc[h]))));
+      }
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < MAXG; ++h)
+    if (h < G) part_buf[(pt * 16 + h) * D + i] = acc[h];
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += NT) {
+    const int h = idx / D, ii = idx % D;
+    float r = 0.f;
+#pragma unroll
+    for (int q = 0; q < P; ++q) r += part_buf[(q * 16 + h) * D + ii];
+    out[h * D + ii] = r;
+  }
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------- scan --
@@ -207,9 +253,9 @@ struct ScanArgs {
   const float* proj;   // S (QJL keys), or null
   const float* rotV;   // Pi_V
   const int32_t* ctx_lens;
-  float* out;    // [B][H_q][128], written when n_split == 1
+  float* out;    // [B][H_q][d], written when n_split == 1
   float* ml;     // [B][H_q][n_split][2], partials when n_split > 1
-  float* acc;    // [B][H_q][n_split][128]
+  float* acc;    // [B][H_q][n_split][d]
   int64_t TcK, TcV;
   PageMap kpm, vpm;   // block tables of paged caches (table == nullptr: contiguous)
   int q_dtype, H_kv, H_q, G, T, n_split, wg_chunk, wave_chunk;
@@ -218,24 +264,39 @@ struct ScanArgs {
   float kc[16], vc[16];
 };
 
-template <int WIDE, int QJL>
+template <int WIDE, int QJL, int D = 128>
 struct QOps {
-  half8 q0[4], q1[4], r0[4], r1[4];   // column c (and c + 16), coordinates 32g + 8kk + 0..7
+  // column c (and c + 16), coordinates (D/4)g + 8kk + 0..7
+  half8 q0[Geom<D>::NKK], q1[Geom<D>::NKK], r0[Geom<D>::NKK], r1[Geom<D>::NKK];
   float cs1, cs2;
   bool hf;   // G <= 8: lane holds the lo half of its query column (column >= 8)
 };
 
-template <int WIDE>
+template <int WIDE, int D = 128>
 struct SoftState {
   float m_ref, m_off, l;
   float ev;   // wave-uniform: log2 of the power of two that scales the value norms
-  floatx4 acc0[8];
+  floatx4 acc0[Geom<D>::CV];
 };
 
-template <int KB, int VB, int QJL, int WIDE, bool MASK>
-__device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, const QOps<WIDE, QJL>& q,
-                                          SoftState<WIDE>& st, const char* lut, LutRegs& lr,
+template <int KB, int VB, int QJL, int WIDE, bool MASK, int D>
+__device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE, D>& d0, const QOps<WIDE, QJL, D>& q,
+                                          SoftState<WIDE, D>& st, const char* lut, LutRegs& lr,
                                           const uint32_t* lutS, int lane, int tg, int lim) {
+  constexpr int NKK = Geom<D>::NKK, CV = Geom<D>::CV;
+  // a key slice that starts inside a word (d = 64, 3 bits: lane groups 1 and 3
+  // at bit 16) is first aligned in registers
+  StepData<KB, VB, QJL, WIDE, D> dsh;
+  if constexpr (key_slice_shifted<KB, D>()) {
+    dsh = d0;
+    const uint32_t sh = (uint32_t)((lane >> 4) * (D / 4 * KB)) & 31u;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      dsh.kw[m][0] = __builtin_amdgcn_alignbit(dsh.kw[m][1], dsh.kw[m][0], sh);
+      dsh.kw[m][1] = dsh.kw[m][1] >> sh;
+    }
+  }
+  const StepData<KB, VB, QJL, WIDE, D>& d = key_slice_shifted<KB, D>() ? dsh : d0;
   const StepNorms<QJL>& nm = d.nm;
   // ---- scores on MFMA: coordinate block KK outer, the two row blocks inner
   // (two independent accumulation chains; one query block live at a time)
@@ -247,18 +308,15 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
     z0[m] = s0[m];
     z1[m] = s0[m];
   }
-  {
-#define TQ_QK(KK)                                                     \
-    {                                                                 \
-      _Pragma("unroll") for (int m = 0; m < 2; ++m) {                 \
-        const half8 ka = key_operand<KB, KK>(d.kw[m], lut, m ? lr.b : lr.a); \
-        s0[m] = mfma16(ka, q.q0[KK], s0[m]);                          \
-        if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);      \
-      }                                                               \
+  static_for<0, NKK>([&](auto kk) {
+    constexpr int KK = decltype(kk)::value;
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const half8 ka = key_operand<KB, KK, D>(d.kw[m], lut, m ? lr.b : lr.a);
+      s0[m] = mfma16(ka, q.q0[KK], s0[m]);
+      if constexpr (WIDE) s1[m] = mfma16(ka, q.q1[KK], s1[m]);
     }
-    TQ_QK(0) TQ_QK(1) TQ_QK(2) TQ_QK(3)
-#undef TQ_QK
-  }
+  });
   if constexpr (QJL) {
 #define TQ_QJ(KK)                                                     \
     _Pragma("unroll") for (int m = 0; m < 2; ++m) {                   \
@@ -314,7 +372,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       const float alpha = st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
+      for (int nb = 0; nb < CV; ++nb) st.acc0[nb] *= alpha;
       st.m_ref = m_new;
       st.m_off = m_new + kShift + st.ev;
     }
@@ -348,13 +406,11 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       op[2 + k] = q.hf ? h2[k] : 0u;
     }
     const half8 pb0 = words_to_half8(op[0], op[1], op[2], op[3]);
-#define TQ_PV(NB)                                                     \
-    {                                                                 \
-      const half8 va = value_operand<VB, NB>(d.vw, lut, (NB & 1) ? lr.b : lr.a); \
-      st.acc0[NB] = mfma16(va, pb0, st.acc0[NB]);                     \
-    }
-    TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
-#undef TQ_PV
+    static_for<0, CV>([&](auto nb) {
+      constexpr int NB = decltype(nb)::value;
+      const half8 va = value_operand<VB, NB, D>(d.vw, lut, (NB & 1) ? lr.b : lr.a);
+      st.acc0[NB] = mfma16(va, pb0, st.acc0[NB]);
+    });
   } else {
     // ---- 8 < G <= 16: separate hi and lo query tiles; every lane holds 8 tokens
     float y[8];
@@ -383,7 +439,7 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       const float alpha = st.m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(st.m_ref - m_new);
       st.l *= alpha;
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) st.acc0[nb] *= alpha;
+      for (int nb = 0; nb < CV; ++nb) st.acc0[nb] *= alpha;
       st.m_ref = m_new;
       st.m_off = m_new + kShift + st.ev;
     }
@@ -402,28 +458,28 @@ __device__ __forceinline__ void scan_step(const StepData<KB, VB, QJL, WIDE>& d, 
       pw[k] = __builtin_bit_cast(uint32_t, half2v{(_Float16)w2[0], (_Float16)w2[1]});
     }
     const half8 pb = words_to_half8(pw[0], pw[1], pw[2], pw[3]);
-#define TQ_PV(NB)                                                     \
-    {                                                                 \
-      const half8 va = value_operand<VB, NB>(d.vw, lut, (NB & 1) ? lr.b : lr.a); \
-      st.acc0[NB] = mfma16(va, pb, st.acc0[NB]);                      \
-    }
-    TQ_PV(0) TQ_PV(1) TQ_PV(2) TQ_PV(3) TQ_PV(4) TQ_PV(5) TQ_PV(6) TQ_PV(7)
-#undef TQ_PV
+    static_for<0, CV>([&](auto nb) {
+      constexpr int NB = decltype(nb)::value;
+      const half8 va = value_operand<VB, NB, D>(d.vw, lut, (NB & 1) ? lr.b : lr.a);
+      st.acc0[NB] = mfma16(va, pb, st.acc0[NB]);
+    });
   }
 }
 
 
 // Wavefronts per workgroup: one workgroup fills a compute unit (4 wavefronts
 // per SIMD, <= 128 VGPRs, for the common tiles; the QJL and G > 8 tiles carry
-// more operands and run 2 per SIMD).
+// more operands and run 2 per SIMD;
+// d = 256 doubles the value accumulators and the key words and takes the
+// 8-wavefront tile as well.)
 constexpr int kCommonWaves = 16;
-template <int QJL, int WIDE>
-constexpr int scan_waves() { return (QJL || WIDE) ? 8 : kCommonWaves; }
+template <int QJL, int WIDE, int D = 128>
+constexpr int scan_waves() { return (QJL || WIDE || D > 128) ? 8 : kCommonWaves; }
 // Steps whose loads are in flight while a wavefront computes one (register
 // buffers: ahead + 1).
 constexpr int kCommonAhead = 1;
-template <int QJL, int WIDE>
-constexpr int scan_ahead() { return (QJL || WIDE) ? 1 : kCommonAhead; }
+template <int QJL, int WIDE, int D = 128>
+constexpr int scan_ahead() { return (QJL || WIDE || D > 128) ? 1 : kCommonAhead; }
 
 // merge buffer: [wave][column][kMergeStride] floats, 8 columns (G <= 8) or 16
 template <int WIDE>
@@ -432,17 +488,17 @@ constexpr int merge_cols() { return WIDE ? 16 : 8; }
 // LDS of a decode workgroup, in 32-bit words: the float16 query operand
 // ([1 + QJL][operand columns][d]), 32 column scales, 16 exponents, 32 codebook
 // levels, the step counter (padded to 4 words), then the scratch region.
-template <int QJL, int WIDE>
-constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * kQStride / 2 + 84; }
+template <int QJL, int WIDE, int D = 128>
+constexpr int scan_head_words() { return (1 + QJL) * (WIDE ? 32 : 16) * qstride<D>() / 2 + 84; }
 
-template <int KB, int VB, int QJL, int WIDE>
+template <int KB, int VB, int QJL, int WIDE, int D = 128>
 constexpr size_t scan_lds_bytes() {
+  constexpr int NW = scan_waves<QJL, WIDE, D>();
   static_assert(kLutBytes / 4 + (QJL ? 4 : 0) * kLutRep <= kRegionWords, "lookup tables exceed the scratch region");
-  static_assert(scan_waves<QJL, WIDE>() * merge_cols<WIDE>() * kMergeStride <= kRegionWords,
-                "merge area exceeds the scratch region");
-  static_assert(scan_waves<QJL, WIDE>() * (WIDE ? 16 : 8) * kD <= kRegionWords,
-                "rotation partials exceed the scratch region");
-  return (size_t)(scan_head_words<QJL, WIDE>() + kScratchWords) * 4;
+  static_assert(NW * merge_cols<WIDE>() * merge_stride<D>() <= kRegionWords, "merge area exceeds the scratch region");
+  static_assert(D != kD || NW * (WIDE ? 16 : 8) * D <= kRegionWords, "rotation partials exceed the scratch region");
+  static_assert(D == kD || 64 * NW * 16 <= kRegionWords, "rotation parts exceed the scratch region");
+  return (size_t)(scan_head_words<QJL, WIDE, D>() + scratch_words<D>()) * 4;
 }
 
 // One workgroup per (context chunk, KV head, row):
@@ -453,24 +509,27 @@ constexpr size_t scan_lds_bytes() {
 //   epilogue  the wavefront partials are merged in LDS in a fixed order; with
 //             one chunk the workgroup finishes the heads (o = Pi_V^T o'),
 //             otherwise it writes the chunk partial for the combine.
-template <int KB, int VB, int QJL, int WIDE, int PAGED>
-__global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_kernel(ScanArgs a) {
-  constexpr int NW = scan_waves<QJL, WIDE>(), NT = 64 * NW;
+template <int KB, int VB, int QJL, int WIDE, int PAGED, int D>
+__global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan_kernel(ScanArgs a) {
+  constexpr int NW = scan_waves<QJL, WIDE, D>(), NT = 64 * NW;
   constexpr int NS = QJL ? 4 : 0;
-  constexpr int KW = 4 * KB;
+  constexpr int KW = key_record_words<KB, D>();   // words of a key record
+  constexpr int VWT = D * VB / 32;                // value words per token row
+  constexpr int NKK = Geom<D>::NKK, CV = Geom<D>::CV;
+  constexpr int QS = qstride<D>(), MS = merge_stride<D>();
   constexpr int MC = merge_cols<WIDE>();
   constexpr int NQ = WIDE ? 32 : 16;   // operand columns per part
   constexpr int HALF = NQ / 2;
-  __shared__ __align__(16) uint32_t smem[scan_lds_bytes<KB, VB, QJL, WIDE>() / 4];
-  _Float16* qlds = (_Float16*)smem;                              // [1 + QJL][NQ][kQStride]
-  float* qcs = (float*)(smem + (1 + QJL) * NQ * kQStride / 2);   // [2][16]
+  __shared__ __align__(16) uint32_t smem[scan_lds_bytes<KB, VB, QJL, WIDE, D>() / 4];
+  _Float16* qlds = (_Float16*)smem;                              // [1 + QJL][NQ][QS]
+  float* qcs = (float*)(smem + (1 + QJL) * NQ * QS / 2);   // [2][16]
   int* hexp = (int*)(qcs + 32);                            // [16]
   float* cents = qcs + 48;                                 // [2][16] key, value levels
   uint32_t* steps_done = (uint32_t*)(qcs + 80);            // steps begun by the workgroup
-  uint32_t* U = smem + scan_head_words<QJL, WIDE>();       // scratch, 16-byte aligned
+  uint32_t* U = smem + scan_head_words<QJL, WIDE, D>();    // scratch, 16-byte aligned
   float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
   float* vA = R + kRegionWords;
-  float* vB = vA + kVecWords;
+  float* vB = vA + vec_words<D>();
   uint32_t* lut = U;                      // keys and values
   uint32_t* lutS = U + kLutBytes / 4;     // QJL signs
 
@@ -506,7 +565,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   Streams s;
   s.rk = make_rsrc(a.kcodes + kbase * KW, (uint32_t)(krows * KW * 4));
   s.rkn = make_rsrc(a.knorms + kbase, (uint32_t)(krows * 4));
-  s.rv = make_rsrc(a.vcodes + vbase * 4 * VB, (uint32_t)(vrows * 4 * VB * 4));
+  s.rv = make_rsrc(a.vcodes + vbase * VWT, (uint32_t)(vrows * VWT * 4));
   s.rvn = make_rsrc(a.vnorms + vbase, (uint32_t)(vrows * 4));
   // QJL sketch (empty ranges when the keys carry none)
   s.rs = make_rsrc(QJL ? (const void*)(a.ksigns + kbase * 4) : (const void*)a.knorms,
@@ -525,10 +584,11 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   LaneOffsets lo;
   {
     const int tk = 8 * (c >> 2) + (c & 3);   // MFMA row c of row block 0 (block 1: tk + 4)
-    lo.k = (uint32_t)(tk * KW + g * KB) * 4u;
+    // lane group g's key slice starts at bit (D/4) * KB * g of the record
+    lo.k = (uint32_t)(tk * KW + ((D / 4) * KB * g) / 32) * 4u;
     lo.s = (uint32_t)(tk * 4 + g) * 4u;
   }
-  lo.v = (uint32_t)(g * 32 * VB + c * 2 * VB) * 4u;
+  lo.v = (uint32_t)(g * value_block_words<VB, D>() + c * value_slice_words<VB, D>()) * 4u;
   lo.n = (uint32_t)(WIDE ? 8 * g + (c & 7) : 8 * g + (hf ? 4 : 0) + (c & 3)) * 4u;
 
   // ---- prologue loads, in issue order: this thread's segment of the rows of
@@ -537,9 +597,10 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // query never waits for the code words. The first steps are read before the
   // context length is known: reads past the end of the cache return zeros
   // (buffer range check), and steps past the context are never used.
+  // (d = 128; the other head dimensions read the matrix rows in the rotation)
   RowSegment<NT> rseg;
-  load_row_segment<NT>(rseg, a.rotK);
-  constexpr int QE = 16 * kD / NT;   // query elements per thread (G <= 16)
+  if constexpr (D == kD) load_row_segment<NT>(rseg, a.rotK);
+  constexpr int QE = 16 * D / NT;   // query elements per thread (G <= 16)
   uint32_t qraw[QE];
   {
     // one 32-bit load per element for either dtype (a bfloat16 element is
@@ -547,18 +608,18 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     // column c's vector: token i0 + c / G, head kv * G + c % G of row b
     const bool qbf = a.q_dtype == TQ_BF16;
     const __amdgpu_buffer_rsrc_t rq =
-        make_rsrc((const char*)a.q + ((((int64_t)b * a.M + i0) * a.H_q + (int64_t)kv * G) * kD) * (qbf ? 2 : 4),
-                  (uint32_t)((((int64_t)mq - 1) * a.H_q + G) * kD * (qbf ? 2 : 4)));
+        make_rsrc((const char*)a.q + ((((int64_t)b * a.M + i0) * a.H_q + (int64_t)kv * G) * D) * (qbf ? 2 : 4),
+                  (uint32_t)((((int64_t)mq - 1) * a.H_q + G) * D * (qbf ? 2 : 4)));
 #pragma unroll
     for (int k = 0; k < QE; ++k) {
       const uint32_t idx = tid + k * NT;
-      const uint32_t cq = idx / kD;
-      const uint32_t el = ((cq / (uint32_t)G) * (uint32_t)a.H_q + cq % (uint32_t)G) * kD + idx % kD;
+      const uint32_t cq = idx / D;
+      const uint32_t el = ((cq / (uint32_t)G) * (uint32_t)a.H_q + cq % (uint32_t)G) * D + idx % D;
       qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (el * 2u) & ~3u : el * 4u, 0, 0);
     }
   }
-  constexpr int AH = scan_ahead<QJL, WIDE>();
-  StepData<KB, VB, QJL, WIDE> buf[AH + 1];
+  constexpr int AH = scan_ahead<QJL, WIDE, D>();
+  StepData<KB, VB, QJL, WIDE, D> buf[AH + 1];
   // the first AH steps of the share (a step past the caches is replaced by the
   // first step of the row: such a wavefront, or such a step, is never used,
   // and the scalar offset of a buffer load is not range checked, only the
@@ -598,27 +659,37 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   }
   if (tid == 0) *steps_done = 0u;
   __syncthreads();
-  build_lut<KB, VB>(lut, cents, cents + 16, tid, NT);
-  if constexpr (QJL) {
-    for (int e = tid; e < NS * kLutRep; e += NT) {
-      const int f = e >> kLutShift;
-      lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+  auto build_tables = [&]() {
+    build_lut<KB, VB>(lut, cents, cents + 16, tid, NT);
+    if constexpr (QJL) {
+      for (int e = tid; e < NS * kLutRep; e += NT) {
+        const int f = e >> kLutShift;
+        lutS[e] = pack_half2((f & 1) ? 1.f : -1.f, (f & 2) ? 1.f : -1.f);
+      }
     }
-  }
+  };
+  // (d = 128 builds the tables first; the other head dimensions use the
+  // region for the rotation's parts first)
+  if constexpr (D == kD) build_tables();
   {
     // the NC column vectors as float32 in vA ([NC][d])
 #pragma unroll
     for (int k = 0; k < QE; ++k) {
       const int idx = tid + k * NT;
-      if (idx < NC * kD)
+      if (idx < NC * D)
         vA[idx] = a.q_dtype == TQ_BF16 ? __uint_as_float(((qraw[k] >> (16 * (idx & 1))) & 0xFFFFu) << 16)
                                        : __uint_as_float(qraw[k]);
     }
     __syncthreads();
-    rotate_rows<NT, NQ / 2>(rseg, vA, vB, NC);   // q' = Pi_K q
-    __syncthreads();
-    emit_operand<NT>(vB, a.sc1, NC, HALF, qlds, qcs, hexp);
+    if constexpr (D == kD) {
+      rotate_rows<NT, NQ / 2>(rseg, vA, vB, NC);   // q' = Pi_K q
+      __syncthreads();
+    } else {
+      rotate_generic<NT, D, NQ / 2>(a.rotK, vA, vB, R, NC);   // q' = Pi_K q
+    }
+    emit_operand<NT, D>(vB, a.sc1, NC, HALF, qlds, qcs, hexp);
     if constexpr (QJL) {
+      static_assert(D == kD, "QJL keys take d = 128");
       load_row_segment<NT>(rseg, a.proj);
       rotate_rows<NT, NQ / 2>(rseg, vB, vA, NC);   // q'' = S q'
       __syncthreads();
@@ -626,16 +697,20 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     }
   }
   __syncthreads();
+  if constexpr (D != kD) {
+    build_tables();
+    __syncthreads();
+  }
 
-  // query operand (B of QK) for this lane: column c, coordinates 32g + 8kk + 0..7
-  QOps<WIDE, QJL> q;
+  // query operand (B of QK) for this lane: column c, coordinates (D/4)g + 8kk + 0..7
+  QOps<WIDE, QJL, D> q;
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) {
-    q.q0[kk] = *(const half8*)(qlds + c * kQStride + 32 * g + 8 * kk);
-    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * kQStride + 32 * g + 8 * kk);
+  for (int kk = 0; kk < NKK; ++kk) {
+    q.q0[kk] = *(const half8*)(qlds + c * QS + (D / 4) * g + 8 * kk);
+    if constexpr (WIDE) q.q1[kk] = *(const half8*)(qlds + (16 + c) * QS + (D / 4) * g + 8 * kk);
     if constexpr (QJL) {
-      q.r0[kk] = *(const half8*)(qlds + (NQ + c) * kQStride + 32 * g + 8 * kk);
-      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qlds + (NQ + 16 + c) * kQStride + 32 * g + 8 * kk);
+      q.r0[kk] = *(const half8*)(qlds + (NQ + c) * QS + (D / 4) * g + 8 * kk);
+      if constexpr (WIDE) q.r1[kk] = *(const half8*)(qlds + (NQ + 16 + c) * QS + (D / 4) * g + 8 * kk);
     }
   }
   const int hc = WIDE ? c : (c & 7);
@@ -664,7 +739,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   LutRegs lr;
 #pragma unroll
   for (int i = 0; i < 4; ++i) lr.a[i] = lr.b[i] = (uint32_t)lrep * 4u;
-  SoftState<WIDE> st;
+  SoftState<WIDE, D> st;
   st.m_ref = -INFINITY;
   st.m_off = -INFINITY;
   st.l = 0.f;
@@ -688,7 +763,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     st.ev = (float)__builtin_amdgcn_readfirstlane(e);
   }
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int nb = 0; nb < CV; ++nb) st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // ---- stream the share: full 32-token steps with two register buffers in
   // turn, then at most one masked step for a ragged end. A step first waits
@@ -722,7 +797,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
       /* have completed anyway */                                                                              \
       uint32_t prior = 0u;                                                                                  \
       if (lane == 0) prior = __hip_atomic_fetch_add(steps_done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP); \
-      scan_step<KB, VB, QJL, WIDE, false>(CUR, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);\
+      scan_step<KB, VB, QJL, WIDE, false, D>(CUR, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);\
       const uint32_t begun = __builtin_amdgcn_readfirstlane(prior) + 1u;                                    \
       const uint32_t even = (mine + 1) * (uint32_t)NW;  /* if every wavefront kept pace */                   \
       if (begun > even + NW) __builtin_amdgcn_s_setprio(3);                                                 \
@@ -755,18 +830,19 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   // steps where their causal limits differ (at most two, limits differ by < 16)
   t0 = __builtin_amdgcn_readfirstlane(t0);   // wave-uniform (scalar buffer offsets)
   while (t0 < t_end) {
-    StepData<KB, VB, QJL, WIDE> E;
+    StepData<KB, VB, QJL, WIDE, D> E;
     if (kpg) ek = page_entry(rtk, a.kpm, t0);
     if (vpg) ev = page_entry(rtv, a.vpm, t0);
     load_step<true>(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
-    scan_step<KB, VB, QJL, WIDE, true>(E, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);
+    scan_step<KB, VB, QJL, WIDE, true, D>(E, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);
     t0 += kStep;
   }
 
-  // ---- this wavefront's partial: lane (g, c) holds coordinates 32g + 8r + nb of column c
-  float o[8][4];
+  // ---- this wavefront's partial: lane (g, c) holds coordinates
+  // (D/16)(4g + r) + nb of column c
+  float o[CV][4];
 #pragma unroll
-  for (int nb = 0; nb < 8; ++nb) {
+  for (int nb = 0; nb < CV; ++nb) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       float x = st.acc0[nb][r];
@@ -781,29 +857,33 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 
   // ---- merge the wavefront partials in LDS (fixed order)
   const bool finish = a.n_split == 1;
-  // With one chunk the workgroup finishes with o = Pi_V^T o': thread (s, p)
-  // takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded now (a
-  // wavefront reads whole rows) so that the loads are in flight while the
-  // wavefront waits for the others and during the merge.
+  // With one chunk the workgroup finishes with o = Pi_V^T o' (d = 128: thread
+  // (s, p) takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded
+  // now (a wavefront reads whole rows) so that the loads are in flight while
+  // the wavefront waits for the others and during the merge).
   constexpr int FSEGS = NT / 64, RW = kD / FSEGS;
   const int fp = tid & 63, fs = tid >> 6;
   float2 pv[RW];
-  if (finish) {
+  if constexpr (D == kD) {
+    if (finish) {
 #pragma unroll
-    for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
+      for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
+    }
   }
   __syncthreads();   // every wavefront is done with the lookup tables
-  float* mrg = R;    // [wave][MC columns][kMergeStride]: 128 coordinates, m, l
+  float* mrg = R;    // [wave][MC columns][MS]: D coordinates, m, l
   if (c < NC) {
-    float* dst = mrg + (wave * MC + c) * kMergeStride;
+    float* dst = mrg + (wave * MC + c) * MS;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      *(float4*)(dst + 32 * g + 8 * r) = float4{o[0][r], o[1][r], o[2][r], o[3][r]};
-      *(float4*)(dst + 32 * g + 8 * r + 4) = float4{o[4][r], o[5][r], o[6][r], o[7][r]};
+#pragma unroll
+      for (int q4 = 0; q4 < CV / 4; ++q4)
+        *(float4*)(dst + CV * (4 * g + r) + 4 * q4) =
+            float4{o[4 * q4][r], o[4 * q4 + 1][r], o[4 * q4 + 2][r], o[4 * q4 + 3][r]};
     }
     if (g == 0) {
-      dst[kD] = st.m_off;
-      dst[kD + 1] = l;
+      dst[D] = st.m_off;
+      dst[D + 1] = l;
     }
   }
   __syncthreads();
@@ -817,8 +897,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
     const int h = tid >> 4, w = tid & 15;
     float m = -INFINITY, lw = 0.f;
     if (w < NW) {
-      m = mrg[(w * MC + h) * kMergeStride + kD];
-      lw = mrg[(w * MC + h) * kMergeStride + kD + 1];
+      m = mrg[(w * MC + h) * MS + D];
+      lw = mrg[(w * MC + h) * MS + D + 1];
     }
     float M = fmaxf(m, dpp_xor1(m));
     M = fmaxf(M, dpp_xor2(M));
@@ -841,17 +921,17 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   auto out_row = [&](int h) -> int64_t {
     return ((int64_t)b * a.M + i0 + h / G) * a.H_q + (int64_t)kv * G + h % G;
   };
-  for (int idx = tid; idx < NC * kD; idx += NT) {
-    const int h = idx / kD, j = idx % kD;
+  for (int idx = tid; idx < NC * D; idx += NT) {
+    const int h = idx / D, j = idx % D;
     float num = 0.f;
 #pragma unroll
-    for (int wv = 0; wv < NW; ++wv) num = fmaf(fw[h * 16 + wv], mrg[(wv * MC + h) * kMergeStride + j], num);
+    for (int wv = 0; wv < NW; ++wv) num = fmaf(fw[h * 16 + wv], mrg[(wv * MC + h) * MS + j], num);
     const float den = dh[h];
     if (finish) {
       vB[idx] = den > 0.f ? num / den * a.inv_sqrt_d : 0.f;
     } else {
       const int64_t pidx = out_row(h) * a.n_split + split;
-      a.acc[pidx * kD + j] = num;
+      a.acc[pidx * D + j] = num;
       if (j == 0) {
         a.ml[pidx * 2] = Mh[h];
         a.ml[pidx * 2 + 1] = den;
@@ -860,25 +940,49 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
   }
   if (finish) {
     __syncthreads();   // o' is complete in vB; the merge area takes the partial sums
-    float* P = R;      // [FSEGS][NC][d]
-    for (int h = 0; h < NC; ++h) {
-      const float4* x = (const float4*)(vB + h * kD + fs * RW);   // same address across the wavefront
-      float acc0 = 0.f, acc1 = 0.f;
+    if constexpr (D == kD) {
+      float* P = R;      // [FSEGS][NC][d]
+      for (int h = 0; h < NC; ++h) {
+        const float4* x = (const float4*)(vB + h * kD + fs * RW);   // same address across the wavefront
+        float acc0 = 0.f, acc1 = 0.f;
 #pragma unroll
-      for (int k = 0; k < RW / 4; ++k) {
-        const float4 v = x[k];
-        acc0 = fmaf(pv[4 * k + 3].x, v.w, fmaf(pv[4 * k + 2].x, v.z, fmaf(pv[4 * k + 1].x, v.y, fmaf(pv[4 * k].x, v.x, acc0))));
-        acc1 = fmaf(pv[4 * k + 3].y, v.w, fmaf(pv[4 * k + 2].y, v.z, fmaf(pv[4 * k + 1].y, v.y, fmaf(pv[4 * k].y, v.x, acc1))));
+        for (int k = 0; k < RW / 4; ++k) {
+          const float4 v = x[k];
+          acc0 = fmaf(pv[4 * k + 3].x, v.w, fmaf(pv[4 * k + 2].x, v.z, fmaf(pv[4 * k + 1].x, v.y, fmaf(pv[4 * k].x, v.x, acc0))));
+          acc1 = fmaf(pv[4 * k + 3].y, v.w, fmaf(pv[4 * k + 2].y, v.z, fmaf(pv[4 * k + 1].y, v.y, fmaf(pv[4 * k].y, v.x, acc1))));
+        }
+        *(float2*)(P + (fs * NC + h) * kD + 2 * fp) = float2{acc0, acc1};
       }
-      *(float2*)(P + (fs * NC + h) * kD + 2 * fp) = float2{acc0, acc1};
-    }
-    __syncthreads();
-    for (int idx = tid; idx < NC * kD; idx += NT) {
-      const int h = idx / kD, i = idx % kD;
-      float r = 0.f;
+      __syncthreads();
+      for (int idx = tid; idx < NC * kD; idx += NT) {
+        const int h = idx / kD, i = idx % kD;
+        float r = 0.f;
 #pragma unroll
-      for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * NC + h) * kD + i];
-      a.out[out_row(h) * kD + i] = r;
+        for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * NC + h) * kD + i];
+        a.out[out_row(h) * kD + i] = r;
+      }
+    } else {
+      // thread (i, hg): coordinate i of heads hg, hg + NT/D, ... from column i
+      // of Pi_V (a wavefront reads consecutive columns of one row per load)
+      constexpr int HG = NT / D;
+      const int i = tid % D, hg = tid / D;
+      float r[16 / HG];
+#pragma unroll
+      for (int k = 0; k < 16 / HG; ++k) r[k] = 0.f;
+#pragma unroll 8
+      for (int j = 0; j < D; ++j) {
+        const float pj = a.rotV[(int64_t)j * D + i];
+#pragma unroll
+        for (int k = 0; k < 16 / HG; ++k) {
+          const int h = hg + k * HG;
+          if (h < NC) r[k] = fmaf(pj, vB[h * D + j], r[k]);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 16 / HG; ++k) {
+        const int h = hg + k * HG;
+        if (h < NC) a.out[out_row(h) * D + i] = r[k];
+      }
     }
   }
 }
@@ -896,32 +1000,34 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE>())) void decode_scan_ke
 constexpr int kCombineThreads = 512;
 constexpr int kCombineBatch = 16;
 
+template <int D>
 __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* ml, const float* acc,
                                                                   const float* rotV, float* out, int H_q, int G,
                                                                   int n_split, float inv_sqrt_d) {
   constexpr int NT = kCombineThreads;
-  __shared__ __align__(16) float colv[kD * 32];
-  __shared__ __align__(16) float ov[16 * kD];
+  constexpr int PIECES = 8 * D / NT;   // 16-byte pieces of the staged columns per thread
+  __shared__ __align__(16) float colv[D * 32];
+  __shared__ __align__(16) float ov[16 * D];
   __shared__ float gsh[3][NT];
   const int kv = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z, tid = threadIdx.x;
   const int64_t bh0 = (int64_t)b * H_q + (int64_t)kv * G;
   {
-    // Pi_V[j][32*chunk + 0..31] for all j: 1024 16-byte pieces, 2 per thread
-    float4 v[2];
+    // Pi_V[j][32*chunk + 0..31] for all j: 8*D 16-byte pieces
+    float4 v[PIECES];
 #pragma unroll
-    for (int k = 0; k < 2; ++k) {
+    for (int k = 0; k < PIECES; ++k) {
       const int f = tid + NT * k, j = f >> 3, c4 = f & 7;
-      v[k] = *(const float4*)(rotV + j * kD + 32 * chunk + 4 * c4);
+      v[k] = *(const float4*)(rotV + j * D + 32 * chunk + 4 * c4);
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k) *(float4*)(colv + 4 * (tid + NT * k)) = v[k];
+    for (int k = 0; k < PIECES; ++k) *(float4*)(colv + 4 * (tid + NT * k)) = v[k];
   }
-  const int NP = G * kD;
+  const int NP = G * D;
   const int S = NT / NP > 0 ? NT / NP : 1;
   for (int e = tid; e < S * NP; e += NT) {
-    const int gr = e / NP, pr = e % NP, h = pr / kD, j = pr % kD;
+    const int gr = e / NP, pr = e % NP, h = pr / D, j = pr % D;
     const float* mlb = ml + (bh0 + h) * n_split * 2;
-    const float* ab = acc + (bh0 + h) * n_split * kD + j;
+    const float* ab = acc + (bh0 + h) * n_split * D + j;
     float M = -INFINITY, num = 0.f, den = 0.f;
     for (int sp0 = gr; sp0 < n_split; sp0 += kCombineBatch * S) {
       float mv[kCombineBatch], lv[kCombineBatch], xv[kCombineBatch];
@@ -931,7 +1037,7 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* m
         const int sp = sp0 + u * S < n_split ? sp0 + u * S : gr;
         mv[u] = mlb[2 * sp];
         lv[u] = mlb[2 * sp + 1];
-        xv[u] = ab[(int64_t)sp * kD];
+        xv[u] = ab[(int64_t)sp * D];
       }
 #pragma unroll
       for (int u = 0; u < kCombineBatch; ++u)
@@ -982,39 +1088,51 @@ __global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* m
   for (int h = hq; h < G; h += NT / 32) {
     float r = 0.f;
 #pragma unroll 8
-    for (int j = 0; j < kD; ++j) r = fmaf(colv[j * 32 + i], ov[h * kD + j], r);
-    out[((int64_t)b * H_q + kv * G + h) * kD + 32 * chunk + i] = r;
+    for (int j = 0; j < D; ++j) r = fmaf(colv[j * 32 + i], ov[h * D + j], r);
+    out[((int64_t)b * H_q + kv * G + h) * D + 32 * chunk + i] = r;
   }
 }
 
-template <int KB, int VB, int QJL, int WIDE>
+template <int KB, int VB, int QJL, int WIDE, int D>
 hipError_t launch_scan(const DecodePlan& p, const ScanArgs& sa, hipStream_t stream) {
   dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)(p.B * p.nqt));
+  constexpr int NT = 64 * scan_waves<QJL, WIDE, D>();
   if (sa.kpm.table != nullptr || sa.vpm.table != nullptr)
-    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 1>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0,
-                       stream, sa);
+    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 1, D>), grid, dim3(NT), 0, stream, sa);
   else
-    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 0>), grid, dim3(64 * scan_waves<QJL, WIDE>()), 0,
-                       stream, sa);
+    hipLaunchKernelGGL((decode_scan_kernel<KB, VB, QJL, WIDE, 0, D>), grid, dim3(NT), 0, stream, sa);
   return hipGetLastError();
 }
 
-template <int KB, int VB, int QJL>
+template <int KB, int VB, int QJL, int D>
 hipError_t dispatch_wide(const DecodePlan& p, const ScanArgs& sa, hipStream_t s) {
-  return p.wide ? launch_scan<KB, VB, QJL, 1>(p, sa, s) : launch_scan<KB, VB, QJL, 0>(p, sa, s);
+  // (d = 256 has no 16-column tile: the host takes such calls elsewhere)
+  if constexpr (D > kD) return launch_scan<KB, VB, QJL, 0, D>(p, sa, s);
+  else return p.wide ? launch_scan<KB, VB, QJL, 1, D>(p, sa, s) : launch_scan<KB, VB, QJL, 0, D>(p, sa, s);
 }
 
-template <int KB, int VB>
+template <int KB, int VB, int D>
 hipError_t dispatch_qjl(const DecodePlan& p, const ScanArgs& sa, hipStream_t s) {
-  return p.qjl ? dispatch_wide<KB, VB, 1>(p, sa, s) : dispatch_wide<KB, VB, 0>(p, sa, s);
+  // (QJL keys exist at d = 128 only)
+  if constexpr (D != kD) return dispatch_wide<KB, VB, 0, D>(p, sa, s);
+  else return p.qjl ? dispatch_wide<KB, VB, 1, D>(p, sa, s) : dispatch_wide<KB, VB, 0, D>(p, sa, s);
 }
 
-template <int KB>
+template <int KB, int D>
 hipError_t dispatch_vb(int vb, const DecodePlan& p, const ScanArgs& sa, hipStream_t s) {
   switch (vb) {
-    case 2: return dispatch_qjl<KB, 2>(p, sa, s);
-    case 3: return dispatch_qjl<KB, 3>(p, sa, s);
-    default: return dispatch_qjl<KB, 4>(p, sa, s);
+    case 2: return dispatch_qjl<KB, 2, D>(p, sa, s);
+    case 3: return dispatch_qjl<KB, 3, D>(p, sa, s);
+    default: return dispatch_qjl<KB, 4, D>(p, sa, s);
+  }
+}
+
+template <int D>
+hipError_t dispatch_kb(int kb, int vb, const DecodePlan& p, const ScanArgs& sa, hipStream_t s) {
+  switch (kb) {
+    case 2: return dispatch_vb<2, D>(vb, p, sa, s);
+    case 3: return dispatch_vb<3, D>(vb, p, sa, s);
+    default: return dispatch_vb<4, D>(vb, p, sa, s);
   }
 }
 
@@ -1026,7 +1144,8 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   char* base = (char*)ws;
   float* ml = (float*)(base + p.off_ml);
   float* acc = (float*)(base + p.off_acc);
-  const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
+  const int d = k->d;
+  const float inv_sqrt_d = 1.0f / sqrtf((float)d);
 
   ScanArgs sa;
   sa.kcodes = k->codes;
@@ -1057,7 +1176,7 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   sa.Mt = p.Mt;
   sa.nqt = p.nqt;
   sa.wg_chunk = p.chunk;
-  sa.wave_chunk = p.chunk / ((p.qjl || p.wide) ? 8 : kCommonWaves);
+  sa.wave_chunk = p.chunk / ((p.qjl || p.wide || d > kD) ? 8 : kCommonWaves);
   // the query operand carries log2(e) * scale / sqrt(d) (scores in the log2
   // domain); the QJL part log2(e) * scale * sqrt(pi/2) / d
   sa.sc1 = scale * kLog2e * inv_sqrt_d;
@@ -1068,22 +1187,28 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
     sa.vc[i] = i < (1 << v->bits) ? v->centroids[i] : 0.f;
   }
   hipError_t err;
-  switch (k->bits) {
-    case 2: err = dispatch_vb<2>(v->bits, p, sa, stream); break;
-    case 3: err = dispatch_vb<3>(v->bits, p, sa, stream); break;
-    default: err = dispatch_vb<4>(v->bits, p, sa, stream); break;
-  }
+  if (d == 64) err = dispatch_kb<64>(k->bits, v->bits, p, sa, stream);
+  else if (d == 256) err = dispatch_kb<256>(k->bits, v->bits, p, sa, stream);
+  else err = dispatch_kb<kD>(k->bits, v->bits, p, sa, stream);
   if (err != hipSuccess || p.n_split == 1) return err;
 
   // the combine sees B * M query rows of H_q heads
-  return launch_combine(ml, acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, stream);
+  return launch_combine(ml, acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, d, stream);
 }
 
 hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
-                          int64_t H_kv, int64_t H_q, int G, int n_split, hipStream_t stream) {
-  const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)H_kv, (unsigned)rows, kD / 32), dim3(kCombineThreads), 0, stream, ml, acc,
-                     rotV, out, (int)H_q, G, n_split, inv_sqrt_d);
+                          int64_t H_kv, int64_t H_q, int G, int n_split, int d, hipStream_t stream) {
+  const float inv_sqrt_d = 1.0f / sqrtf((float)d);
+  const dim3 grid((unsigned)H_kv, (unsigned)rows, (unsigned)(d / 32));
+  if (d == 64)
+    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
+                       n_split, inv_sqrt_d);
+  else if (d == 256)
+    hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
+                       n_split, inv_sqrt_d);
+  else
+    hipLaunchKernelGGL(combine_kernel<kD>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
+                       n_split, inv_sqrt_d);
   return hipGetLastError();
 }
 

@@ -34,7 +34,7 @@ struct DecodePlan {
 // columns take the 16-column tile (8 wavefronts) with floor(16/G) tokens per
 // tile.
 bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_split, int32_t qjl,
-                 DecodePlan* p, int64_t M = 1);
+                 DecodePlan* p, int64_t M = 1, int32_t d = kD);
 
 // Dense chunked-prefill planning: every wavefront takes kDenseWaveCols
 // (token, head) columns of one KV head, a workgroup 1, 2 or 4 wavefronts
@@ -120,7 +120,7 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
 // Fixed-order merge of context-chunk partials ([rows*H_q][n_split][2] and
 // [rows*H_q][n_split][d]) and the inverse rotation, into out [rows][H_q][d].
 hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
-                          int64_t H_kv, int64_t H_q, int G, int n_split, hipStream_t stream);
+                          int64_t H_kv, int64_t H_q, int G, int n_split, int d, hipStream_t stream);
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
                          hipStream_t stream);

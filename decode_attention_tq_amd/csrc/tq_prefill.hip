@@ -536,7 +536,7 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
     default: err = launch_dense1<4>(v->bits, p, da, stream); break;
   }
   if (err != hipSuccess) return err;
-  return launch_combine(da.ml, da.acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, stream);
+  return launch_combine(da.ml, da.acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, kD, stream);
 }
 
 }  // namespace tq

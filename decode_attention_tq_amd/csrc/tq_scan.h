@@ -47,6 +47,41 @@ struct IntConst {
   static constexpr int value = V;
 };
 
+// f(IntConst<I>()) for I = I0 .. N-1, unrolled at compile time.
+template <int I0, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(IntConst<I0>());
+    static_for<I0 + 1, N>(f);
+  }
+}
+
+// Tile geometry of head dimension D (64, 128 or 256). QK MFMA: lane group g
+// (lane / 16) holds D/4 consecutive coordinates of its token (its key slice),
+// D/32 MFMAs of 32 coordinates each per row block. PV MFMA: lane row i
+// (lane % 16) holds D/16 consecutive coordinates of the 8 tokens of block g
+// (its value slice), one MFMA per coordinate of the slice.
+template <int D>
+struct Geom {
+  static_assert(D == 64 || D == 128 || D == 256, "head dimension");
+  static constexpr int NKK = D / 32;   // QK MFMAs per row block
+  static constexpr int CV = D / 16;    // PV MFMAs (coordinates per value slice)
+};
+// Words of a key record (one token) and of a value block record (8 tokens).
+template <int KB, int D>
+constexpr int key_record_words() { return D * KB / 32; }
+template <int VB, int D>
+constexpr int value_block_words() { return D * VB / 4; }
+// Bit offset of lane group g's key slice in the record; a slice that does not
+// start on a word (d = 64, 3 bits) is read as the two words that hold it and
+// aligned in registers.
+template <int KB, int D>
+constexpr bool key_slice_shifted() { return (D / 4 * KB) % 32 != 0; }
+template <int KB, int D>
+constexpr int key_slice_words() { return (D / 4 * KB) / 32 + (key_slice_shifted<KB, D>() ? 1 : 0); }
+template <int VB, int D>
+constexpr int value_slice_words() { return D / 16 * VB / 4; }
+
 // Thread (slot, quarter) writes 8 replicas of the slot's key pair and 8 of its
 // value pair (two 16-byte stores each), so each pair is formed once per thread.
 template <int KB, int VB>
@@ -101,19 +136,19 @@ __device__ inline half8 levels8(const uint32_t* w, const char* lut, uint32_t (&r
   return words_to_half8(r0, r1, r2, r3);
 }
 
-// A operand of the QK MFMA for step KK: coordinates 32g + 8KK + 0..7 of the
-// lane's token, from the lane's KB-word slice (coordinates 32g .. 32g+31).
-template <int KB, int KK>
+// A operand of the QK MFMA for step KK: coordinates (D/4)g + 8KK + 0..7 of the
+// lane's token, from the lane's key slice (coordinates (D/4)g .. (D/4)g + D/4 - 1).
+template <int KB, int KK, int D = 128>
 __device__ inline half8 key_operand(const uint32_t* w, const char* lut, uint32_t (&r)[4]) {
-  return levels8<KB, KB, 8 * KB * KK, 0>(w, lut, r);
+  return levels8<KB, key_slice_words<KB, D>(), 8 * KB * KK, 0>(w, lut, r);
 }
 
-// A operand of the PV MFMA for coordinate block NB: value codes of the 8 tokens
-// of the lane's block at coordinate 8i + NB (i = lane % 16), from the lane's
-// 2*VB-word slice of the block record (coordinates 8i .. 8i+7).
-template <int VB, int NB>
+// A operand of the PV MFMA for coordinate NB of the value slice: value codes
+// of the 8 tokens of the lane's block at coordinate (D/16)i + NB (i = lane %
+// 16), from the lane's slice of the block record (coordinates (D/16)i ..).
+template <int VB, int NB, int D = 128>
 __device__ inline half8 value_operand(const uint32_t* w, const char* lut, uint32_t (&r)[4]) {
-  return levels8<VB, 2 * VB, 8 * VB * NB, 128>(w, lut, r);
+  return levels8<VB, value_slice_words<VB, D>(), 8 * VB * NB, 128>(w, lut, r);
 }
 
 // A operand of the QJL MFMA for step KK: +-1 for coordinates 32g + 8KK + 0..7.
@@ -150,11 +185,11 @@ struct StepNorms {
 };
 
 // Raw words of one 32-token step for one lane, with the step's norms.
-template <int KB, int VB, int QJL, int WIDE>
+template <int KB, int VB, int QJL, int WIDE, int D = 128>
 struct StepData {
-  uint32_t kw[2][KB];
+  uint32_t kw[2][key_slice_words<KB, D>()];
   uint32_t sw[2];
-  uint32_t vw[2 * VB];
+  uint32_t vw[value_slice_words<VB, D>()];
   StepNorms<QJL> nm;
 };
 
@@ -187,7 +222,9 @@ __device__ inline uint32_t step_row(const PageMap& m, int kv, int H_kv, uint32_t
 // hardware range-checks only that one).
 template <int N, bool RC = false>
 __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
-  if constexpr (N == 2) {
+  if constexpr (N == 1) {
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamAux);
+  } else if constexpr (N == 2) {
     const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamAux);
     w[0] = v.x; w[1] = v.y;
   } else if constexpr (N == 3) {
@@ -200,24 +237,24 @@ __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, ui
     bload_words_s<3>(r, voff, soff, w);
     bload_words_s<3>(r, RC ? voff + 12u : voff, RC ? soff : soff + 12u, w + 3);
   } else {
-    static_assert(N == 8, "unsupported word count");
+    static_assert(N == 8 || N == 12 || N == 16, "unsupported word count");
     bload_words_s<4>(r, voff, soff, w);
-    bload_words_s<4>(r, RC ? voff + 16u : voff, RC ? soff : soff + 16u, w + 4);
+    bload_words_s<N - 4, RC>(r, RC ? voff + 16u : voff, RC ? soff : soff + 16u, w + 4);
   }
 }
 
 // Waits until the loads of d have landed (an empty asm that reads every word:
 // the compiler places the counter wait before it).
-template <int KB, int VB, int QJL, int WIDE>
-__device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE>& d) {
+template <int KB, int VB, int QJL, int WIDE, int D>
+__device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE, D>& d) {
 #pragma unroll
   for (int m = 0; m < 2; ++m) {
 #pragma unroll
-    for (int k = 0; k < KB; ++k) asm volatile("" ::"v"(d.kw[m][k]));
+    for (int k = 0; k < key_slice_words<KB, D>(); ++k) asm volatile("" ::"v"(d.kw[m][k]));
     if constexpr (QJL) asm volatile("" ::"v"(d.sw[m]));
   }
 #pragma unroll
-  for (int k = 0; k < 2 * VB; ++k) asm volatile("" ::"v"(d.vw[k]));
+  for (int k = 0; k < value_slice_words<VB, D>(); ++k) asm volatile("" ::"v"(d.vw[k]));
   asm volatile("" ::"v"(d.nm.kn), "v"(d.nm.vn));
   if constexpr (QJL) asm volatile("" ::"v"(d.nm.kg));
 }
@@ -229,10 +266,11 @@ __device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE>& d) {
 // A step that may run past the end of a stream (the ragged end of a row whose
 // capacity is not a multiple of 32) adds it to the per-lane offsets instead,
 // so that lanes past the end read zeros.
-template <bool CHECKED, int KB, int VB, int QJL, int WIDE>
-__device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& s, const LaneOffsets& lo,
+template <bool CHECKED, int KB, int VB, int QJL, int WIDE, int D>
+__device__ inline void load_step(StepData<KB, VB, QJL, WIDE, D>& d, const Streams& s, const LaneOffsets& lo,
                                  uint32_t rk, uint32_t rv) {
-  constexpr int KW = 4 * KB, VBW = 32 * VB;
+  constexpr int KW = key_record_words<KB, D>(), VBW = value_block_words<VB, D>();
+  constexpr int KSW = key_slice_words<KB, D>(), VSW = value_slice_words<VB, D>();
   // wave-uniform; readfirstlane keeps the step offsets in scalar registers
   rk = __builtin_amdgcn_readfirstlane(rk);
   rv = __builtin_amdgcn_readfirstlane(rv);
@@ -246,14 +284,14 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE>& d, const Streams& 
   for (int m = 0; m < 2; ++m) {
     const uint32_t vk = CHECKED ? lo.k + ok + (m ? dk1 : 0u) : lo.k;
     const uint32_t sk = CHECKED ? 0u : ok + (m ? dk1 : 0u);
-    bload_words_s<KB, CHECKED>(s.rk, vk, sk, d.kw[m]);
+    bload_words_s<KSW, CHECKED>(s.rk, vk, sk, d.kw[m]);
     if constexpr (QJL) {
       const uint32_t vs = CHECKED ? lo.s + os + (m ? ds1 : 0u) : lo.s;
       const uint32_t ss = CHECKED ? 0u : os + (m ? ds1 : 0u);
       d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, vs, ss, kStreamAux);
     }
   }
-  bload_words_s<2 * VB, CHECKED>(s.rv, TQ_VOF(lo.v, ov), TQ_OFF(ov), d.vw);
+  bload_words_s<VSW, CHECKED>(s.rv, TQ_VOF(lo.v, ov), TQ_OFF(ov), d.vw);
   d.nm.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, TQ_VOF(lo.n, onk), TQ_OFF(onk), kStreamAux));
   d.nm.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, TQ_VOF(lo.n, onv), TQ_OFF(onv), kStreamAux));
   if constexpr (QJL)

@@ -241,14 +241,15 @@ def test_prefill_validation_paths():
     assert call(M=70000) == tq.ERR_UNSUPPORTED
     assert call(ws_bytes=16) == tq.ERR_WORKSPACE_TOO_SMALL
     assert call(H_q=7) == tq.ERR_INVALID_ARGUMENT                 # H_q % H_kv
-    # the chunked prefill exists for d = 128 only
-    K64, V64 = _cache(d=64), _cache(role=tq.VALUES, d=64)
-    assert lib.tq_prefill_attention(ctypes.byref(K64), ctypes.byref(V64), FAKE, tq.BF16, 8, 4, None, 64, 0.0, 0,
+    # d = 256 takes chunked prefill only up to 8 (query token, head) columns per KV head
+    K256, V256 = _cache(d=256), _cache(role=tq.VALUES, d=256)
+    assert lib.tq_prefill_attention(ctypes.byref(K256), ctypes.byref(V256), FAKE, tq.BF16, 8, 4, None, 64, 0.0, 0,
                                     FAKE, FAKE, 1 << 30, None) == tq.ERR_UNSUPPORTED
     # workspace grows with M (chunk partials per query token and head)
     one = tq.prefill_workspace_bytes(2, 8, 2, 1, 4096, 4, 0)
     assert one == tq.decode_workspace_bytes(2, 8, 2, 4096, 4, 0)
-    assert tq.prefill_workspace_bytes(2, 8, 2, 6, 4096, 4, 0) > 5 * (one - 512)
+    # M = 6 query tokens: at least 6 tokens' partials (2 + 128 floats per row, head and chunk)
+    assert tq.prefill_workspace_bytes(2, 8, 2, 6, 4096, 4, 0) >= 6 * 2 * 8 * 4 * 130 * 4
     assert tq.prefill_workspace_bytes(2, 8, 2, 0, 4096, 4, 0) == 0
 
 
