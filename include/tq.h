@@ -28,12 +28,13 @@
  *     memory (its one static device array, the scratch of
  *     tq_decode_attention_noalloc, is part of its loaded code object);
  *   - head dimension d = 128, 64 or 256 (other values return
- *     TQ_ERR_UNSUPPORTED). d = 128 runs the tuned kernels (MFMA rotations,
- *     context split over workgroups). d = 64 and 256 run generic kernels of the
- *     same method and the same packed formats: float32 rotations, one
- *     workgroup per 8-token block (quantize, dequantize) and one per
- *     (row, KV head) over the whole context (decode; n_split and the workspace
- *     are not used). QJL keys and tq_prefill_attention take d = 128 only.
+ *     TQ_ERR_UNSUPPORTED), the same packed formats at every d. Decode and
+ *     chunked prefill run the same MFMA scan tiles at every d (d = 256 up to 8
+ *     (query token, head) columns per KV head; a decode with G > 8 there runs
+ *     a generic float32 kernel, one workgroup per (row, KV head), and a
+ *     prefill with M * G > 8 returns TQ_ERR_UNSUPPORTED). Quantize, append and
+ *     dequantize at d = 64 and 256 run generic kernels (float32 rotations,
+ *     one workgroup per 8-token block). QJL keys take d = 128 only.
  *
  * Packed formats (one cache per tensor and layer; keys and values set their bit
  * width separately):
@@ -246,9 +247,9 @@ int tq_dequantize(const tq_cache* src, int64_t t0, int64_t t1, float* out, void*
  *   out:      device float32 [B][H_q][d]
  *   workspace: device, at least tq_decode_workspace_bytes(...) bytes, 256-byte aligned
  * Requires k->role == TQ_KEYS, v->role == TQ_VALUES, equal B, H_kv and d,
- * H_q % H_kv == 0 and G <= 16. At d = 64 and 256 the decode is one launch of
- * float32 arithmetic throughout (n_split, workspace and workspace_bytes are
- * ignored; the workspace may be NULL). At d = 128, value norms may have any overall scale: the
+ * H_q % H_kv == 0 and G <= 16. At d = 256 with G > 8 the decode is one launch
+ * of float32 arithmetic throughout (n_split, workspace and workspace_bytes are
+ * ignored; the workspace may be NULL). On the scan tiles, value norms may have any overall scale: the
  * float16 weights of the value sum are scaled per wavefront by a power of two
  * taken from the largest value norm of its first 32 tokens, so within one
  * (row, KV head) the largest value norm must stay below 7e5 times the
@@ -327,22 +328,23 @@ int tq_decode_attention_append(const tq_cache* k, const tq_cache* v, const void*
  *   out:      device float32 [B][M][H_q][d]
  *   workspace: device, at least tq_prefill_workspace_bytes(...) bytes, 256-byte aligned
  * Other arguments and requirements as tq_decode_attention; M in 1..65535 and
- * B * ceil(M / tile) <= 65535. At d = 64 and 256 only M = 1 (the decode) is
- * taken; M > 1 returns TQ_ERR_UNSUPPORTED.
+ * B * ceil(M / tile) <= 65535. At d = 256, M * G <= 8 (TQ_ERR_UNSUPPORTED
+ * otherwise); the dense path for many columns is d = 128 only, so d = 64
+ * takes the scan tiles for every M.
  */
 int tq_prefill_attention(const tq_cache* k, const tq_cache* v,
                          const void* q, int32_t q_dtype, int64_t H_q, int64_t M,
                          const int32_t* ctx_lens, int64_t T, float scale, int32_t n_split,
                          float* out, void* workspace, size_t workspace_bytes, void* hip_stream);
 
-/* Workspace bytes tq_prefill_attention needs; 0 for invalid sizes. */
+/* Workspace bytes tq_prefill_attention needs at any head dimension; 0 for invalid sizes. */
 size_t tq_prefill_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t M, int64_t T,
                                   int32_t n_split, int32_t k_qjl);
 
 /* Number of context chunks tq_decode_attention uses for these sizes (n_split 0 = auto). */
 int32_t tq_decode_splits(int64_t B, int64_t H_kv, int64_t T, int32_t n_split);
 
-/* Workspace bytes tq_decode_attention needs; 0 for invalid sizes. */
+/* Workspace bytes tq_decode_attention needs at any head dimension; 0 for invalid sizes. */
 size_t tq_decode_workspace_bytes(int64_t B, int64_t H_q, int64_t H_kv, int64_t T,
                                  int32_t n_split, int32_t k_qjl);
 
