@@ -100,7 +100,8 @@ def quantize_bytes(w, ntok, which):
 
 def copy_cache(tq, c):
     """A second contiguous cache holding the same packed layer."""
-    d = tq.Cache(c.role, c.bits, c.B, c.H_kv, c.T_cap, device=c.device, qjl=bool(c.qjl))
+    d = tq.Cache(c.role, c.bits, c.B, c.H_kv, c.T_cap, device=c.device, qjl=bool(c.qjl), d=c.d,
+                 rot=c.rot.cpu().numpy(), centroids=c.centroids)
     for x, y in ((d.codes, c.codes), (d.norms, c.norms), (d.signs, c.signs), (d.gamma, c.gamma)):
         if x is not None:
             x.copy_(y)
@@ -375,6 +376,8 @@ def main():
     ap.add_argument("--no-quality", action="store_true",
                     help="skip the quality reports (cosine per bit width, asymmetric formats, QJL statistics)")
     ap.add_argument("--no-stream", action="store_true", help="skip the streaming-read reference")
+    ap.add_argument("--head-dims", default="64,256",
+                    help="other head dimensions timed on the workload's shape ('' to skip)")
     ap.add_argument("--no-hadamard-prefill", action="store_true",
                     help="skip the prefill timing with a randomized Hadamard rotation")
     ap.add_argument("--parity-slices", type=int, default=8,
@@ -621,6 +624,54 @@ def main():
         del fk, fv, fws, layers
         torch.cuda.empty_cache()
 
+    # the other head dimensions: the workload's shape at d = 64 and 256 (same bit
+    # widths and G), bulk quantize of both tensors and decode back to back
+    head_dims = {}
+    for hd in [int(x) for x in args.head_dims.split(",") if x]:
+        hw = w.scaled(d=hd)
+        hcap = (hw.T + 7) // 8 * 8
+        hk = tq.Cache(tq.KEYS, hw.k_bits, hw.B, hw.H_kv, hcap, device=dev, d=hd)
+        hv = tq.Cache(tq.VALUES, hw.v_bits, hw.B, hw.H_kv, hcap, device=dev, d=hd)
+        hxk, hxv = tq_synth.torch_kv(hw, "k", dev), tq_synth.torch_kv(hw, "v", dev)
+        tq.quantize_kv(hxk, hk)
+        tq.quantize_kv(hxv, hv)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        tq.quantize_kv(hxk, hk)
+        tq.quantize_kv(hxv, hv)
+        e1.record()
+        torch.cuda.synchronize()
+        q_us = e0.elapsed_time(e1) * 1e3
+        q_bytes = 2 * hxk.numel() * hxk.element_size() + hk.nbytes + hv.nbytes
+        del hxk, hxv
+        torch.cuda.empty_cache()
+        hq = tq_synth.torch_queries(hw, dev)
+        hws = tq.Workspace(tq.decode_workspace_bytes(hw.B, hw.H_q, hw.H_kv, hw.T, 0, 0), dev)
+        ho = torch.empty((hw.B, hw.H_q, hd), dtype=torch.float32, device=dev)
+        hb = decode_bytes(hw, hw.T)
+        n_layers = max(1, min(64, -(-(1 << 30) // hb)))
+        layers = [(hk, hv)] + [(copy_cache(tq, hk), copy_cache(tq, hv)) for _ in range(n_layers - 1)]
+        for i in range(3):
+            tq.decode_attention(*layers[i % n_layers], hq, T=hw.T, out=ho, workspace=hws)
+        n_calls = max(20, 2 * n_layers)
+        e0.record()
+        for i in range(n_calls):
+            tq.decode_attention(*layers[i % n_layers], hq, T=hw.T, out=ho, workspace=hws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) / n_calls * 1e3
+        head_dims[str(hd)] = {
+            "kernel": "decode_scan_kernel" if not (hd > 128 and hw.G > 8) else "decode_generic_kernel",
+            "decode_us": us, "decode_bytes": hb, "decode_GB_s": hb / (us * 1e-6) / 1e9,
+            "decode_frac": hb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
+            "n_split": tq.decode_splits(hw.B, hw.H_kv, hw.T), "layers_cycled": n_layers,
+            "quantize_kernel": "quantize_generic_kernel", "quantize_both_us": q_us,
+            "quantize_GB_s": q_bytes / (q_us * 1e-6) / 1e9}
+        log(f"[bench] d = {hd}: decode {us:.1f} us ({hb / (us * 1e-6) / 1e9:.0f} GB/s), "
+            f"quantize K+V {q_us / 1e3:.2f} ms")
+        del hk, hv, hws, layers
+        torch.cuda.empty_cache()
+
     # chunked causal (prefill) attention of the M newest tokens of every row over
     # the same caches; the cache is read once per tile of query tokens
     prefill = {}
@@ -720,6 +771,7 @@ def main():
         res["paged"] = paged
     if formats:
         res["formats"] = formats
+        res["head_dims"] = head_dims
     if prefill:
         res["prefill_attention"] = prefill
     if stream is not None:
