@@ -665,7 +665,7 @@ def main():
             "decode_us": us, "decode_bytes": hb, "decode_GB_s": hb / (us * 1e-6) / 1e9,
             "decode_frac": hb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS,
             "n_split": tq.decode_splits(hw.B, hw.H_kv, hw.T), "layers_cycled": n_layers,
-            "quantize_kernel": "quantize_generic_kernel", "quantize_both_us": q_us,
+            "quantize_kernel": "quantize_mfma_kernel", "quantize_both_us": q_us,
             "quantize_GB_s": q_bytes / (q_us * 1e-6) / 1e9}
         log(f"[bench] d = {hd}: decode {us:.1f} us ({hb / (us * 1e-6) / 1e9:.0f} GB/s), "
             f"quantize K+V {q_us / 1e3:.2f} ms")

@@ -204,6 +204,248 @@ __global__ __launch_bounds__(D, D == 256 ? 2 : 4) void quantize_generic_kernel(Q
   }
 }
 
+// ------------------------------------ bulk quantize, bfloat16 input, on MFMA --
+//
+// y = Pi x for 32 vectors per wavefront on v_mfma_f32_32x32x16_bf16: A = the
+// raw bfloat16 input words of the vectors (lane i + 32*(k/8) holds vector i's
+// coordinates 16ks + 8(k/8) .. +7), B = 32 rows of Pi (one output block of 32
+// coordinates) split into bfloat16 hi + mid + lo (together float32's 24
+// significant bits, so every product is exact and the sum is float32
+// accurate; the hi products accumulate apart from the small parts). The rows of
+// an output block are staged in LDS in fragment order by the whole workgroup,
+// two blocks in turn, the next block's loads in flight while the current one
+// is used. Codes go to LDS as bytes and leave packed, as in the plain kernel.
+// A vector whose largest entry lies outside [2^-60, 2^60] is scaled by a power
+// of two first (exact), so that no product of a small Pi part underflows.
+
+typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
+typedef float gfloatx16 __attribute__((ext_vector_type(16)));
+
+__device__ inline gfloatx16 mfma_bf16_32(u32x4 a, u32x4 b, gfloatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, a), __builtin_bit_cast(gbf16x8, b), c,
+                                                 0, 0, 0);
+}
+
+__device__ inline uint32_t bf16_rne_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
+
+// Wavefronts per workgroup (d = 256: the staged blocks and codes of 4 fill
+// most of the LDS).
+template <int D>
+constexpr int qm_waves() { return D > 128 ? 4 : 8; }
+
+template <int D, int BITS, int ROLE>
+__global__ __launch_bounds__(64 * qm_waves<D>()) void quantize_mfma_kernel(QuantArgs a, int64_t total,
+                                                                            int64_t tile0) {
+  constexpr int NW = qm_waves<D>(), NT = 64 * NW, TV = 32 * NW;   // vectors of a workgroup tile
+  constexpr int NKS = D / 16, NJB = D / 32, W = D * BITS / 32;
+  constexpr int FR = 3 * NKS * 64;            // 16-byte fragments of one staged output block
+  constexpr int SPT = (NKS * 64 + NT - 1) / NT;   // staged (ks, lane) items per thread
+  __shared__ u32x4 pib[2][FR];
+  __shared__ unsigned char cs[TV][D];
+  __shared__ float vscale[TV], vnorm[TV];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t s0 = (tile0 + blockIdx.x) * TV;   // first (row * H_kv + head) * nslot + slot of the tile
+  const int64_t t_hi = a.t_offset + a.T;
+
+  // ---- this lane's vector (i = lane % 32 of the wavefront's 32) and its words
+  u32x4 xa[NKS];
+  int eA = 0;   // power of two applied to the A operand
+  {
+    const int v = 32 * wave + (lane & 31), kq = lane >> 5;
+    const int64_t sl = s0 + v;
+    bool wr = false;
+    int64_t off = 0;
+    if (sl < total) {
+      const int64_t bh = sl / a.nslot, t = a.t_base + sl % a.nslot;
+      wr = t >= a.t_offset && t < t_hi;
+      off = (bh / a.H_kv) * a.sb + (t - a.t_offset) * a.st + (bh % a.H_kv) * a.sh + 8 * kq;
+    }
+    const uint16_t* xp = (const uint16_t*)a.x + off;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) xa[ks] = wr ? *(const u32x4*)(xp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
+    // largest magnitude, then the squared norm of x * 2^-e (pairwise partial sums)
+    float mx = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        mx = fmaxf(mx, fabsf(__uint_as_float(xa[ks][q] << 16)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(xa[ks][q] & 0xFFFF0000u)));
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    float ps[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) ps[k] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const float lo = ldexpf(__uint_as_float(xa[ks][q] << 16), -e);
+        const float hi = ldexpf(__uint_as_float(xa[ks][q] & 0xFFFF0000u), -e);
+        ps[2 * q] = fmaf(lo, lo, ps[2 * q]);
+        ps[2 * q + 1] = fmaf(hi, hi, ps[2 * q + 1]);
+      }
+    float ss = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    ss += __shfl_xor(ss, 32);
+    if (e < -60 || e > 60) {
+      // (rare: rescale this vector's words so its largest entry lies in [1/2, 1))
+      eA = e;
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t lo = bf16_rne_bits(ldexpf(__uint_as_float(xa[ks][q] << 16), -e));
+          const uint32_t hi = bf16_rne_bits(ldexpf(__uint_as_float(xa[ks][q] & 0xFFFF0000u), -e));
+          xa[ks][q] = lo | (hi << 16);
+        }
+    }
+    if (kq == 0) {
+      const float r = sqrtf(ss);
+      vscale[v] = ss > 0.f ? ldexpf(sqrtf((float)D) / r, eA - e) : 0.f;
+      vnorm[v] = ldexpf(r, e);
+    }
+  }
+
+  // ---- staging of output block jb (rows 32jb .. 32jb+31 of Pi) in fragment order
+  float4 st[SPT][2];
+  auto stage_load = [&](int jb) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int item = tid + u * NT;
+      if (item < NKS * 64) {
+        const int ks = item >> 6, ln = item & 63;
+        const float4* src = (const float4*)(a.rot + (int64_t)(32 * jb + (ln & 31)) * D + 16 * ks + 8 * (ln >> 5));
+        st[u][0] = src[0];
+        st[u][1] = src[1];
+      }
+    }
+  };
+  auto stage_store = [&](int buf) {
+#pragma unroll
+    for (int u = 0; u < SPT; ++u) {
+      const int item = tid + u * NT;
+      if (item < NKS * 64) {
+        const float x[8] = {st[u][0].x, st[u][0].y, st[u][0].z, st[u][0].w,
+                            st[u][1].x, st[u][1].y, st[u][1].z, st[u][1].w};
+        uint32_t hw[4], mw[4], lw[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uint32_t h2[2], m2[2], l2[2];
+#pragma unroll
+          for (int k = 0; k < 2; ++k) {
+            const float p = x[2 * q + k];
+            const __bf16 hi = (__bf16)p;
+            const float r1 = p - (float)hi;
+            const __bf16 mid = (__bf16)r1;
+            h2[k] = __builtin_bit_cast(uint16_t, hi);
+            m2[k] = __builtin_bit_cast(uint16_t, mid);
+            l2[k] = bf16_rne_bits(r1 - (float)mid);
+          }
+          hw[q] = h2[0] | (h2[1] << 16);
+          mw[q] = m2[0] | (m2[1] << 16);
+          lw[q] = l2[0] | (l2[1] << 16);
+        }
+        const int ks = item >> 6, ln = item & 63;
+        pib[buf][(0 * NKS + ks) * 64 + ln] = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        pib[buf][(1 * NKS + ks) * 64 + ln] = u32x4{mw[0], mw[1], mw[2], mw[3]};
+        pib[buf][(2 * NKS + ks) * 64 + ln] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+      }
+    }
+  };
+  stage_load(0);
+  stage_store(0);
+  __syncthreads();
+
+  // scales of the 16 vectors whose outputs this lane holds: rows 8q + 4(lane/32) + r
+  float sc[16];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) sc[4 * q + r] = vscale[32 * wave + 8 * q + 4 * (lane >> 5) + r];
+
+  for (int jb = 0; jb < NJB; ++jb) {
+    if (jb + 1 < NJB) stage_load(jb + 1);
+    const u32x4* P = pib[jb & 1];
+    gfloatx16 ah = {}, al = {};
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      ah = mfma_bf16_32(xa[ks], P[(0 * NKS + ks) * 64 + lane], ah);
+      al = mfma_bf16_32(xa[ks], P[(1 * NKS + ks) * 64 + lane], al);
+      al = mfma_bf16_32(xa[ks], P[(2 * NKS + ks) * 64 + lane], al);
+    }
+    // output (vector 8q + 4(lane/32) + r, coordinate 32jb + lane % 32) in element r + 4q
+    const int j = 32 * jb + (lane & 31);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float z = (ah[4 * q + r] + al[4 * q + r]) * sc[4 * q + r];
+        cs[32 * wave + 8 * q + 4 * (lane >> 5) + r][j] = (unsigned char)cell_count<BITS>(z, a.thr);
+      }
+    if (jb + 1 < NJB) stage_store((jb + 1) & 1);
+    __syncthreads();
+  }
+
+  // ---- pack and store (codes from LDS), then the norms
+  auto written = [&](int64_t sl, int64_t* bh, int64_t* t) -> bool {
+    if (sl >= total) return false;
+    *bh = sl / a.nslot;
+    *t = a.t_base + sl % a.nslot;
+    return *t >= a.t_offset && *t < t_hi;
+  };
+  if constexpr (ROLE == TQ_KEYS) {
+    for (int e = tid; e < TV * W; e += NT) {
+      const int v = e / W, w = e % W;
+      int64_t bh, t;
+      if (!written(s0 + v, &bh, &t)) continue;
+      const int q0 = 32 * w, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
+      uint64_t acc = 0;
+      for (int c = c0; c <= c1; ++c) {
+        const int sh = BITS * c - q0;
+        const uint64_t val = cs[v][c];
+        acc |= sh >= 0 ? val << sh : val >> (-sh);
+      }
+      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+      if (row >= 0) a.codes[row * W + w] = (uint32_t)acc;
+    }
+  } else {
+    // block record of 8 tokens: group g (coordinates 4g .. 4g+3) holds the
+    // code of (coordinate 4g + jj, token i) at bits BITS * (8jj + i) of its words
+    for (int e = tid; e < (TV / 8) * 8 * W; e += NT) {
+      const int blk = e / (8 * W), j8 = e % (8 * W), g = j8 / BITS, ws = j8 % BITS;
+      const int64_t sb0 = s0 + 8 * blk;
+      if (sb0 >= total) continue;
+      const int64_t bh = sb0 / a.nslot, tb = a.t_base + sb0 % a.nslot;
+      const int q0 = 32 * ws, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
+      uint64_t acc = 0, keep = 0;
+      bool any = false;
+      for (int ci = c0; ci <= c1; ++ci) {
+        const int sh = BITS * ci - q0, ti = ci & 7, jj = ci >> 3;
+        const int64_t t = tb + ti;
+        const bool wr = t >= a.t_offset && t < t_hi;
+        any |= wr;
+        const uint64_t val = wr ? (uint64_t)cs[8 * blk + ti][4 * g + jj] : 0u;
+        const uint64_t m = wr ? 0u : (uint64_t)((1u << BITS) - 1u);
+        acc |= sh >= 0 ? val << sh : val >> (-sh);
+        keep |= sh >= 0 ? m << sh : m >> (-sh);
+      }
+      if (!any) continue;
+      const int64_t row0 = tok_row(a.pm, a.H_kv, a.T_cap, bh, tb);
+      if (row0 < 0) continue;
+      uint32_t* dst = a.codes + row0 * W + j8;
+      const uint32_t kp = (uint32_t)keep, word = (uint32_t)acc;
+      *dst = kp == 0u ? word : ((*dst & kp) | word);
+    }
+  }
+  for (int v = tid; v < TV; v += NT) {
+    int64_t bh, t;
+    if (!written(s0 + v, &bh, &t)) continue;
+    const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+    if (row >= 0) a.norms[row] = vnorm[v];
+  }
+}
+
 struct GenericDequantArgs {
   const uint32_t* codes;
   const float* norms;
@@ -508,12 +750,42 @@ hipError_t dispatch_decg(int kbits, int vbits, const GenericDecodeArgs& ga, int6
   }
 }
 
+template <int D, int BITS, int ROLE>
+hipError_t launch_qm(const QuantArgs& qa, int64_t total, hipStream_t s) {
+  constexpr int TV = 32 * qm_waves<D>();
+  const int64_t tiles = (total + TV - 1) / TV;
+  for (int64_t t0 = 0; t0 < tiles; t0 += kGenMaxGrid) {
+    const unsigned n = (unsigned)(tiles - t0 < kGenMaxGrid ? tiles - t0 : kGenMaxGrid);
+    hipLaunchKernelGGL((quantize_mfma_kernel<D, BITS, ROLE>), dim3(n), dim3(64 * qm_waves<D>()), 0, s, qa, total, t0);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t dispatch_qm(int bits, int role, const QuantArgs& qa, int64_t total, hipStream_t s) {
+  const bool keys = role == TQ_KEYS;
+  switch (bits) {
+    case 2: return keys ? launch_qm<D, 2, TQ_KEYS>(qa, total, s) : launch_qm<D, 2, TQ_VALUES>(qa, total, s);
+    case 3: return keys ? launch_qm<D, 3, TQ_KEYS>(qa, total, s) : launch_qm<D, 3, TQ_VALUES>(qa, total, s);
+    default: return keys ? launch_qm<D, 4, TQ_KEYS>(qa, total, s) : launch_qm<D, 4, TQ_VALUES>(qa, total, s);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_quantize_generic(const void* x, int x_dtype, int64_t B, int64_t T, int64_t H_kv, int64_t sb,
                                    int64_t st, int64_t sh, const tq_cache* dst, int64_t t_offset,
                                    const int32_t* ctx_lens, int64_t T_all, hipStream_t stream) {
   const QuantArgs qa = make_quant_args(x, B, ctx_lens != nullptr ? 1 : T, H_kv, sb, st, sh, dst, t_offset);
+  if (ctx_lens == nullptr && T > 1 && x_dtype == TQ_BF16) {
+    // bulk bfloat16 input: the MFMA kernel, tiles of 32 vectors per wavefront
+    const int64_t total = B * H_kv * qa.nslot;
+    if (total <= 0) return hipSuccess;
+    if (dst->d == 64) return dispatch_qm<64>(dst->bits, dst->role, qa, total, stream);
+    return dispatch_qm<256>(dst->bits, dst->role, qa, total, stream);
+  }
   const int64_t blocks = ctx_lens != nullptr ? B * H_kv : B * H_kv * (qa.nslot / kValueBlock);
   if (blocks <= 0) return hipSuccess;
   const int xf32 = x_dtype == TQ_F32;

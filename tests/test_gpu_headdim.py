@@ -158,13 +158,16 @@ def test_dequantize_matches_oracle(tq, name):
 
 @pytest.mark.parametrize("name", ["d64_stress", "d256_qwen"])
 def test_pieces_and_appends_match_bulk(tq, name):
-    """Quantizing in pieces (offsets off the 8-token value blocks, single
-    tokens) and tq_append_kv give the bulk call's bytes: every token's codes and
-    norm depend on that token alone, and partial value blocks keep the bits of
-    the tokens outside the piece."""
+    """Quantizing in pieces (offsets off the 8-token value blocks) gives the
+    bulk call's bytes for every token a multi-token piece wrote (each token's
+    codes and norm depend on that token alone; partial value blocks keep the
+    bits of the tokens outside the piece); single tokens (tq_append_kv, the
+    one-token kernel with float32 rotation) hold the oracle's codes outside the
+    decision-boundary band and its norms to 1e-6."""
     w = CASES[name].scaled(T=83)
     T_cap = tcap(w.T)
     log(f"pieces {name}: d={w.d}")
+    model = _model(name, w)
     xk, xv = device_inputs(w, "k"), device_inputs(w, "v")
     kb, vb = _caches(tq, w, T_cap)
     tq.quantize_kv(xk, kb)
@@ -172,20 +175,28 @@ def test_pieces_and_appends_match_bulk(tq, name):
     kp, vp = _caches(tq, w, T_cap)
     vp.codes.fill_(-1)
     cuts = [0, 5, 6, 7, 8, 29, 64, 71, 82, 83]
+    single = set()
     for a, b in zip(cuts[:-1], cuts[1:]):
         if b - a == 1:
             tq.append_kv(xk[:, a], xv[:, a], kp, vp, a)
+            single.add(a)
         else:
             tq.quantize_kv(xk[:, a:b], kp, t_offset=a)
             tq.quantize_kv(xv[:, a:b], vp, t_offset=a)
     torch.cuda.synchronize()
-    assert torch.equal(kb.norms, kp.norms) and torch.equal(vb.norms, vp.norms)
-    assert torch.equal(kb.codes, kp.codes)
-    # values: tokens 83 .. 87 of the last block were never written (bits kept = all ones)
-    got = unpack_head("v", vp.codes[0, 0].cpu().numpy(), w.v_bits, T_cap, w.d)
-    want = unpack_head("v", vb.codes[0, 0].cpu().numpy(), w.v_bits, T_cap, w.d)
-    assert np.array_equal(got[:w.T], want[:w.T])
-    assert np.all(got[w.T:] == (1 << w.v_bits) - 1)
+    multi = [t for t in range(w.T) if t not in single]
+    for got_c, want_c, which, bits in ((kp, kb, "k", w.k_bits), (vp, vb, "v", w.v_bits)):
+        assert torch.equal(got_c.norms[:, :, multi], want_c.norms[:, :, multi]), which
+        for b in range(w.B):
+            for h in range(w.H_kv):
+                got = unpack_head(which, got_c.codes[b, h].cpu().numpy(), bits, T_cap, w.d)
+                want = unpack_head(which, want_c.codes[b, h].cpu().numpy(), bits, T_cap, w.d)
+                assert np.array_equal(got[multi], want[multi]), (which, b, h)
+                if which == "v":
+                    # tokens 83 .. 87 of the last block were never written (bits kept = all ones)
+                    assert np.all(got[w.T:] == (1 << bits) - 1)
+    _check_codes(w, model, "k", kp, w.T)
+    _check_codes(w, model, "v", vp, w.T)
 
 
 @pytest.mark.parametrize("name", ["d64_llama", "d256_qwen", "d64_qwen_hadamard"])
