@@ -199,7 +199,7 @@ def test_pieces_and_appends_match_bulk(tq, name):
     _check_codes(w, model, "v", vp, w.T)
 
 
-@pytest.mark.parametrize("name", ["d64_llama", "d256_qwen", "d64_qwen_hadamard"])
+@pytest.mark.parametrize("name", ["d64_llama", "d256_qwen", "d64_qwen_hadamard", "d256_tiny"])
 def test_fused_append_decode_step(tq, name):
     """decode_attention_append: the new token of each row goes to
     ctx_len[b] - 1, then decode over tokens 0 .. ctx_len[b] - 1; the caches then
@@ -352,3 +352,21 @@ def test_prefill_matches_oracle(tq, name, M):
     if M == 1:
         dec = tq.decode_attention(kc, vc, q[:, 0].contiguous(), ctx_lens=cl, T=w.T).cpu().numpy()
         assert np.array_equal(dec, out[:, 0])
+
+
+@pytest.mark.parametrize("name", ["d64_stress", "d256_qwen", "d256_tiny"])
+def test_noalloc_equals_workspace_call(tq, name):
+    """tq_decode_attention_noalloc (partials in the library's static scratch)
+    gives tq_decode_attention's output bit for bit at d = 64 and 256, with
+    context splits and ragged contexts, twice in a row."""
+    w = CASES[name]
+    model = _model(name)
+    kc = upload_oracle_cache(tq, model, "k", model.heads("k"), tcap(w.T))
+    vc = upload_oracle_cache(tq, model, "v", model.heads("v"), tcap(w.T))
+    q = device_queries(w)
+    cl = torch.tensor([max(w.T - 37 * b, 1) for b in range(w.B)], dtype=torch.int32, device="cuda")
+    for ns in (0, 3):
+        want = tq.decode_attention(kc, vc, q, ctx_lens=cl, T=w.T, n_split=ns)
+        for _ in range(2):
+            got = tq.decode_attention_noalloc(kc, vc, q, ctx_lens=cl, T=w.T, n_split=ns)
+            assert torch.equal(got, want), (name, ns)
