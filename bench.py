@@ -616,9 +616,20 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) / n_calls * 1e3
+        # single-call latency: one call between two events on an idle stream
+        lat = []
+        for i in range(20):
+            torch.cuda.synchronize()
+            e0.record()
+            tq.decode_attention(*layers[i % n_layers], fq, T=fw.T, out=fo, workspace=fws)
+            e1.record()
+            torch.cuda.synchronize()
+            lat.append(e0.elapsed_time(e1) * 1e3)
+        lat.sort()
         formats[name] = {"B": fw.B, "H_q": fw.H_q, "H_kv": fw.H_kv, "T": fw.T, "k_bits": fw.k_bits,
                          "v_bits": fw.v_bits, "k_qjl": fw.k_qjl,
                          "n_split": tq.decode_splits(fw.B, fw.H_kv, fw.T), "layers_cycled": n_layers, "decode_us": us,
+                         "single_call_us_median": lat[len(lat) // 2],
                          "bytes": fb, "GB_s": fb / (us * 1e-6) / 1e9, "frac": fb / (us * 1e-6) / 1e9 / HBM_PEAK_GBS}
         log(f"[bench] {name}: decode {us:.1f} us, {fb / (us * 1e-6) / 1e9:.0f} GB/s")
         del fk, fv, fws, layers

@@ -206,30 +206,25 @@ __global__ __launch_bounds__(D, D == 256 ? 2 : 4) void quantize_generic_kernel(Q
 
 // ------------------------------------ bulk quantize, bfloat16 input, on MFMA --
 //
-// y = Pi x for 32 vectors per wavefront on v_mfma_f32_32x32x16_bf16: A = the
-// raw bfloat16 input words of the vectors (lane i + 32*(k/8) holds vector i's
-// coordinates 16ks + 8(k/8) .. +7), B = 32 rows of Pi (one output block of 32
-// coordinates) split into bfloat16 hi + mid + lo (together float32's 24
-// significant bits, so every product is exact and the sum is float32
-// accurate; the hi products accumulate apart from the small parts). The rows of
-// an output block are staged in LDS in fragment order by the whole workgroup,
-// two blocks in turn, the next block's loads in flight while the current one
-// is used. Codes go to LDS as bytes and leave packed, as in the plain kernel.
-// A vector whose largest entry lies outside [2^-60, 2^60] is scaled by a power
-// of two first (exact), so that no product of a small Pi part underflows.
+// y = Pi x for 32 vectors per wavefront on v_mfma_f32_32x32x16_f16: A = the
+// vector in float16 (the bfloat16 words scaled by a power of two that puts the
+// largest entry in [2^13, 2^14): exact, 8 significant bits in float16's 11),
+// B = a 32-row output block of Pi split into float16 hi + lo (~22 significant
+// bits; the hi and lo products accumulate apart). The workgroup stages the
+// output blocks in LDS in fragment order, two in turn (the next block's rows
+// load while the current one is used), and packs each block's 32 coordinates
+// as soon as their codes are known: a key record's words 3jb .. (bits) and a
+// value block's coordinate groups 8jb .. 8jb+7 are contiguous, so the codes
+// need 32 bytes per vector of LDS, not d.
 
-typedef __bf16 gbf16x8 __attribute__((ext_vector_type(8)));
 typedef float gfloatx16 __attribute__((ext_vector_type(16)));
 
-__device__ inline gfloatx16 mfma_bf16_32(u32x4 a, u32x4 b, gfloatx16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(gbf16x8, a), __builtin_bit_cast(gbf16x8, b), c,
-                                                 0, 0, 0);
+__device__ inline gfloatx16 mfma_f16_32(half8 a, half8 b, gfloatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
-__device__ inline uint32_t bf16_rne_bits(float x) { return __builtin_bit_cast(uint16_t, (__bf16)x); }
-
-// Wavefronts per workgroup (d = 256: the staged blocks and codes of 4 fill
-// most of the LDS).
+// Wavefronts per workgroup (d = 256: 4, so that two workgroups share a
+// compute unit's LDS).
 template <int D>
 constexpr int qm_waves() { return D > 128 ? 4 : 8; }
 
@@ -237,43 +232,48 @@ template <int D, int BITS, int ROLE>
 __global__ __launch_bounds__(64 * qm_waves<D>()) void quantize_mfma_kernel(QuantArgs a, int64_t total,
                                                                             int64_t tile0) {
   constexpr int NW = qm_waves<D>(), NT = 64 * NW, TV = 32 * NW;   // vectors of a workgroup tile
-  constexpr int NKS = D / 16, NJB = D / 32, W = D * BITS / 32;
-  constexpr int FR = 3 * NKS * 64;            // 16-byte fragments of one staged output block
+  constexpr int NKS = D / 16, NJB = D / 32;
+  constexpr int W = D * BITS / 32;            // words of a key record
+  constexpr int FR = 2 * NKS * 64;            // 16-byte fragments of one staged output block (hi, lo)
   constexpr int SPT = (NKS * 64 + NT - 1) / NT;   // staged (ks, lane) items per thread
-  __shared__ u32x4 pib[2][FR];
-  __shared__ unsigned char cs[TV][D];
+  __shared__ half8 pib[2][FR];
+  __shared__ unsigned char cs[2][TV][32];     // codes of one output block, two blocks in turn
   __shared__ float vscale[TV], vnorm[TV];
+  __shared__ int64_t vrow[TV];                // token row of each vector (-1: not written)
+  __shared__ int64_t brow[TV / 8];            // token row of each 8-token block's first token
+  __shared__ uint32_t bmask[TV / 8];          // tokens of the block that are written (bit i)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t s0 = (tile0 + blockIdx.x) * TV;   // first (row * H_kv + head) * nslot + slot of the tile
   const int64_t t_hi = a.t_offset + a.T;
+  auto written = [&](int64_t sl, int64_t* bh, int64_t* t) -> bool {
+    if (sl >= total) return false;
+    *bh = sl / a.nslot;
+    *t = a.t_base + sl % a.nslot;
+    return *t >= a.t_offset && *t < t_hi;
+  };
 
-  // ---- this lane's vector (i = lane % 32 of the wavefront's 32) and its words
-  u32x4 xa[NKS];
-  int eA = 0;   // power of two applied to the A operand
+  // ---- this lane's vector (i = lane % 32 of the wavefront's 32) as float16 A operands
+  half8 xa[NKS];
   {
     const int v = 32 * wave + (lane & 31), kq = lane >> 5;
-    const int64_t sl = s0 + v;
-    bool wr = false;
-    int64_t off = 0;
-    if (sl < total) {
-      const int64_t bh = sl / a.nslot, t = a.t_base + sl % a.nslot;
-      wr = t >= a.t_offset && t < t_hi;
-      off = (bh / a.H_kv) * a.sb + (t - a.t_offset) * a.st + (bh % a.H_kv) * a.sh + 8 * kq;
-    }
+    int64_t bh = 0, t = 0;
+    const bool wr = written(s0 + v, &bh, &t);
+    const int64_t off = wr ? (bh / a.H_kv) * a.sb + (t - a.t_offset) * a.st + (bh % a.H_kv) * a.sh + 8 * kq : 0;
     const uint16_t* xp = (const uint16_t*)a.x + off;
+    u32x4 raw[NKS];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) xa[ks] = wr ? *(const u32x4*)(xp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
-    // largest magnitude, then the squared norm of x * 2^-e (pairwise partial sums)
+    for (int ks = 0; ks < NKS; ++ks) raw[ks] = wr ? *(const u32x4*)(xp + 16 * ks) : u32x4{0u, 0u, 0u, 0u};
     float mx = 0.f;
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        mx = fmaxf(mx, fabsf(__uint_as_float(xa[ks][q] << 16)));
-        mx = fmaxf(mx, fabsf(__uint_as_float(xa[ks][q] & 0xFFFF0000u)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[ks][q] << 16)));
+        mx = fmaxf(mx, fabsf(__uint_as_float(raw[ks][q] & 0xFFFF0000u)));
       }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const int e = mx > 0.f ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    // squared norm of x * 2^-e in pairwise partial sums; the operand is x * 2^(14 - e)
     float ps[8];
 #pragma unroll
     for (int k = 0; k < 8; ++k) ps[k] = 0.f;
@@ -281,29 +281,34 @@ __global__ __launch_bounds__(64 * qm_waves<D>()) void quantize_mfma_kernel(Quant
     for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float lo = ldexpf(__uint_as_float(xa[ks][q] << 16), -e);
-        const float hi = ldexpf(__uint_as_float(xa[ks][q] & 0xFFFF0000u), -e);
+        const float lo = ldexpf(__uint_as_float(raw[ks][q] << 16), -e);
+        const float hi = ldexpf(__uint_as_float(raw[ks][q] & 0xFFFF0000u), -e);
         ps[2 * q] = fmaf(lo, lo, ps[2 * q]);
         ps[2 * q + 1] = fmaf(hi, hi, ps[2 * q + 1]);
+        xa[ks][2 * q] = (_Float16)(lo * 16384.f);
+        xa[ks][2 * q + 1] = (_Float16)(hi * 16384.f);
       }
     float ss = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
     ss += __shfl_xor(ss, 32);
-    if (e < -60 || e > 60) {
-      // (rare: rescale this vector's words so its largest entry lies in [1/2, 1))
-      eA = e;
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t lo = bf16_rne_bits(ldexpf(__uint_as_float(xa[ks][q] << 16), -e));
-          const uint32_t hi = bf16_rne_bits(ldexpf(__uint_as_float(xa[ks][q] & 0xFFFF0000u), -e));
-          xa[ks][q] = lo | (hi << 16);
-        }
-    }
     if (kq == 0) {
       const float r = sqrtf(ss);
-      vscale[v] = ss > 0.f ? ldexpf(sqrtf((float)D) / r, eA - e) : 0.f;
+      // z = y * sqrt(d) / |x|, with y and |x| both carrying 2^(14 - e) and 2^-e
+      vscale[v] = ss > 0.f ? ldexpf(sqrtf((float)D) / r, -14) : 0.f;
       vnorm[v] = ldexpf(r, e);
+      vrow[v] = wr ? tok_row(a.pm, a.H_kv, a.T_cap, bh, t) : -1;
+    } else if ((v & 7) == 0) {
+      // (lane 32 + i of a block's first vector: the block's first row and written tokens)
+      const int64_t sb0 = s0 + v;
+      uint32_t m = 0;
+      int64_t r0 = -1;
+      if (sb0 < total) {
+        const int64_t bb = sb0 / a.nslot, tb = a.t_base + sb0 % a.nslot;
+        for (int i = 0; i < 8; ++i)
+          if (tb + i >= a.t_offset && tb + i < t_hi) m |= 1u << i;
+        r0 = tok_row(a.pm, a.H_kv, a.T_cap, bb, tb);
+      }
+      bmask[v >> 3] = m;
+      brow[v >> 3] = r0;
     }
   }
 
@@ -328,28 +333,15 @@ __global__ __launch_bounds__(64 * qm_waves<D>()) void quantize_mfma_kernel(Quant
       if (item < NKS * 64) {
         const float x[8] = {st[u][0].x, st[u][0].y, st[u][0].z, st[u][0].w,
                             st[u][1].x, st[u][1].y, st[u][1].z, st[u][1].w};
-        uint32_t hw[4], mw[4], lw[4];
+        half8 hi, lo;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          uint32_t h2[2], m2[2], l2[2];
-#pragma unroll
-          for (int k = 0; k < 2; ++k) {
-            const float p = x[2 * q + k];
-            const __bf16 hi = (__bf16)p;
-            const float r1 = p - (float)hi;
-            const __bf16 mid = (__bf16)r1;
-            h2[k] = __builtin_bit_cast(uint16_t, hi);
-            m2[k] = __builtin_bit_cast(uint16_t, mid);
-            l2[k] = bf16_rne_bits(r1 - (float)mid);
-          }
-          hw[q] = h2[0] | (h2[1] << 16);
-          mw[q] = m2[0] | (m2[1] << 16);
-          lw[q] = l2[0] | (l2[1] << 16);
+        for (int k = 0; k < 8; ++k) {
+          hi[k] = (_Float16)x[k];
+          lo[k] = (_Float16)(x[k] - (float)hi[k]);
         }
         const int ks = item >> 6, ln = item & 63;
-        pib[buf][(0 * NKS + ks) * 64 + ln] = u32x4{hw[0], hw[1], hw[2], hw[3]};
-        pib[buf][(1 * NKS + ks) * 64 + ln] = u32x4{mw[0], mw[1], mw[2], mw[3]};
-        pib[buf][(2 * NKS + ks) * 64 + ln] = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        pib[buf][(0 * NKS + ks) * 64 + ln] = hi;
+        pib[buf][(1 * NKS + ks) * 64 + ln] = lo;
       }
     }
   };
@@ -366,82 +358,67 @@ __global__ __launch_bounds__(64 * qm_waves<D>()) void quantize_mfma_kernel(Quant
 
   for (int jb = 0; jb < NJB; ++jb) {
     if (jb + 1 < NJB) stage_load(jb + 1);
-    const u32x4* P = pib[jb & 1];
+    const half8* P = pib[jb & 1];
     gfloatx16 ah = {}, al = {};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      ah = mfma_bf16_32(xa[ks], P[(0 * NKS + ks) * 64 + lane], ah);
-      al = mfma_bf16_32(xa[ks], P[(1 * NKS + ks) * 64 + lane], al);
-      al = mfma_bf16_32(xa[ks], P[(2 * NKS + ks) * 64 + lane], al);
+      ah = mfma_f16_32(xa[ks], P[(0 * NKS + ks) * 64 + lane], ah);
+      al = mfma_f16_32(xa[ks], P[(1 * NKS + ks) * 64 + lane], al);
     }
     // output (vector 8q + 4(lane/32) + r, coordinate 32jb + lane % 32) in element r + 4q
-    const int j = 32 * jb + (lane & 31);
+    unsigned char (*cb)[32] = cs[jb & 1];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float z = (ah[4 * q + r] + al[4 * q + r]) * sc[4 * q + r];
-        cs[32 * wave + 8 * q + 4 * (lane >> 5) + r][j] = (unsigned char)cell_count<BITS>(z, a.thr);
+        cb[32 * wave + 8 * q + 4 * (lane >> 5) + r][lane & 31] = (unsigned char)cell_count<BITS>(z, a.thr);
       }
     if (jb + 1 < NJB) stage_store((jb + 1) & 1);
     __syncthreads();
-  }
 
-  // ---- pack and store (codes from LDS), then the norms
-  auto written = [&](int64_t sl, int64_t* bh, int64_t* t) -> bool {
-    if (sl >= total) return false;
-    *bh = sl / a.nslot;
-    *t = a.t_base + sl % a.nslot;
-    return *t >= a.t_offset && *t < t_hi;
-  };
-  if constexpr (ROLE == TQ_KEYS) {
-    for (int e = tid; e < TV * W; e += NT) {
-      const int v = e / W, w = e % W;
-      int64_t bh, t;
-      if (!written(s0 + v, &bh, &t)) continue;
-      const int q0 = 32 * w, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
-      uint64_t acc = 0;
-      for (int c = c0; c <= c1; ++c) {
-        const int sh = BITS * c - q0;
-        const uint64_t val = cs[v][c];
-        acc |= sh >= 0 ? val << sh : val >> (-sh);
+    // ---- pack the 32 coordinates of block jb for every vector of the tile
+    if constexpr (ROLE == TQ_KEYS) {
+      // words BITS*jb .. BITS*jb + BITS - 1 of each key record
+      for (int e = tid; e < TV * BITS; e += NT) {
+        const int v = e / BITS, w = e % BITS;
+        const int64_t row = vrow[v];
+        if (row < 0) continue;
+        const int q0 = 32 * w, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
+        uint64_t acc = 0;
+        for (int c = c0; c <= c1; ++c) {
+          const int sh = BITS * c - q0;
+          const uint64_t val = cb[v][c];
+          acc |= sh >= 0 ? val << sh : val >> (-sh);
+        }
+        a.codes[row * W + BITS * jb + w] = (uint32_t)acc;
       }
-      const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
-      if (row >= 0) a.codes[row * W + w] = (uint32_t)acc;
-    }
-  } else {
-    // block record of 8 tokens: group g (coordinates 4g .. 4g+3) holds the
-    // code of (coordinate 4g + jj, token i) at bits BITS * (8jj + i) of its words
-    for (int e = tid; e < (TV / 8) * 8 * W; e += NT) {
-      const int blk = e / (8 * W), j8 = e % (8 * W), g = j8 / BITS, ws = j8 % BITS;
-      const int64_t sb0 = s0 + 8 * blk;
-      if (sb0 >= total) continue;
-      const int64_t bh = sb0 / a.nslot, tb = a.t_base + sb0 % a.nslot;
-      const int q0 = 32 * ws, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
-      uint64_t acc = 0, keep = 0;
-      bool any = false;
-      for (int ci = c0; ci <= c1; ++ci) {
-        const int sh = BITS * ci - q0, ti = ci & 7, jj = ci >> 3;
-        const int64_t t = tb + ti;
-        const bool wr = t >= a.t_offset && t < t_hi;
-        any |= wr;
-        const uint64_t val = wr ? (uint64_t)cs[8 * blk + ti][4 * g + jj] : 0u;
-        const uint64_t m = wr ? 0u : (uint64_t)((1u << BITS) - 1u);
-        acc |= sh >= 0 ? val << sh : val >> (-sh);
-        keep |= sh >= 0 ? m << sh : m >> (-sh);
+    } else {
+      // coordinate groups 8jb .. 8jb+7 of each 8-token block: group g holds the
+      // code of (coordinate 4g + jj, token i) at bits BITS * (8jj + i) of its words
+      for (int e = tid; e < (TV / 8) * 8 * BITS; e += NT) {
+        const int blk = e / (8 * BITS), j8 = e % (8 * BITS), gl = j8 / BITS, ws = j8 % BITS;
+        const uint32_t wm = bmask[blk];
+        const int64_t row0 = brow[blk];
+        if (wm == 0u || row0 < 0) continue;
+        const int q0 = 32 * ws, c0 = q0 / BITS, c1 = (q0 + 31) / BITS;
+        uint64_t acc = 0, keep = 0;
+        for (int ci = c0; ci <= c1; ++ci) {
+          const int sh = BITS * ci - q0, ti = ci & 7, jj = ci >> 3;
+          const bool wr = (wm >> ti) & 1u;
+          const uint64_t val = wr ? (uint64_t)cb[8 * blk + ti][4 * gl + jj] : 0u;
+          const uint64_t m = wr ? 0u : (uint64_t)((1u << BITS) - 1u);
+          acc |= sh >= 0 ? val << sh : val >> (-sh);
+          keep |= sh >= 0 ? m << sh : m >> (-sh);
+        }
+        uint32_t* dst = a.codes + row0 * W + 8 * BITS * jb + j8;
+        const uint32_t kp = (uint32_t)keep, word = (uint32_t)acc;
+        *dst = kp == 0u ? word : ((*dst & kp) | word);
       }
-      if (!any) continue;
-      const int64_t row0 = tok_row(a.pm, a.H_kv, a.T_cap, bh, tb);
-      if (row0 < 0) continue;
-      uint32_t* dst = a.codes + row0 * W + j8;
-      const uint32_t kp = (uint32_t)keep, word = (uint32_t)acc;
-      *dst = kp == 0u ? word : ((*dst & kp) | word);
     }
   }
   for (int v = tid; v < TV; v += NT) {
-    int64_t bh, t;
-    if (!written(s0 + v, &bh, &t)) continue;
-    const int64_t row = tok_row(a.pm, a.H_kv, a.T_cap, bh, t);
+    const int64_t row = vrow[v];
     if (row >= 0) a.norms[row] = vnorm[v];
   }
 }
