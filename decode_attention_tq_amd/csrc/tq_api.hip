@@ -134,7 +134,8 @@ bool plan_prefill_dense(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t
   const int64_t waves = (p->NC + kDenseWaveCols - 1) / kDenseWaveCols;
   p->nwave = waves >= 4 ? 4 : (waves >= 2 ? 2 : 1);
   p->ncg = (int32_t)((p->NC + kDenseWaveCols * p->nwave - 1) / (kDenseWaveCols * p->nwave));
-  if (B * p->ncg > 65535 || B * M > 65535) return false;   // grid z of the scan, grid y of the combine
+  if (B * p->ncg > 65535 || B * M > 65535) return false;   // grid z of the scan; rows
+  if (B * M * H_q / 8 >= INT32_MAX) return false;             // grid of the chunk merge (kD / 4 threads a vector)
   const int64_t Tp = T > 0 ? T : 1;
   int64_t target;
   if (n_split > 0) {

@@ -21,9 +21,13 @@
 //             of 16 (hi and lo parts accumulate into one result), online
 //             softmax per column (log2 domain, lazy rescale), value codes ->
 //             operands, PV on MFMA into 128 coordinates x 32 columns;
-//   epilogue  the column partials (m, l, acc) go to the workspace; the
-//             decode's combine kernel merges the context chunks in a fixed
-//             order and applies Pi_V^T.
+//   epilogue  o = Pi_V^T acc per column on MFMA (Pi_V^T staged in LDS as
+//             float16 hi + lo, each column's sums split the same way under a
+//             power of two); with one context chunk the normalised output is
+//             written at once, else the chunk's partial (m, l, rotated sums)
+//             goes to the workspace and merge_kernel combines the chunks in
+//             a fixed order (the inverse rotation is linear, so it commutes
+//             with the merge).
 // Keys with a QJL sketch take the tiled path (tq_decode.hip).
 #include <math.h>
 
@@ -36,6 +40,10 @@ namespace {
 constexpr int kDenseCB = kDenseWaveCols / 16;  // 16-column MFMA blocks per wavefront
 constexpr int kDenseCols = kDenseWaveCols;     // columns per wavefront
 constexpr int kStageStride = kD + 4;           // floats per staged query row (bank spread)
+// halves per staged row of Pi_V^T: a 16-byte pad spreads the 16 rows that one
+// operand read touches over the banks
+constexpr int kPtStride = kD + 8;
+constexpr int kPtBytes = 2 * kD * kPtStride * 2;   // hi and lo parts
 
 struct DenseArgs {
   const uint32_t* kcodes;
@@ -44,19 +52,23 @@ struct DenseArgs {
   const float* vnorms;
   const void* q;          // [B][M][H_q][d]
   const float* rotK;      // Pi_K
+  const float* rotV;      // Pi_V
   const int32_t* ctx_lens;
+  float* out;             // [B][M][H_q][d] (written here when n_split == 1)
   float* ml;              // [B*M*H_q][n_split][2]: m (log2 domain reference), l
   float* acc;             // [B*M*H_q][n_split][d]: unnormalised rotated-domain sums
   int64_t TcK, TcV;
   PageMap kpm, vpm;
   int q_dtype, H_kv, H_q, G, T, M, n_split, chunk, ncg, NC;
-  float sc1;
+  float sc1, inv_sqrt_d;
   float kc[16], vc[16];
 };
 
+constexpr int cmax(int x, int y) { return x > y ? x : y; }
+
 template <int NWAVE>
 constexpr int dense_region_bytes() {
-  return kLutBytes > NWAVE * kDenseCols * kStageStride * 4 ? kLutBytes : NWAVE * kDenseCols * kStageStride * 4;
+  return cmax(cmax(kLutBytes, NWAVE * kDenseCols * kStageStride * 4), kPtBytes);
 }
 
 // Float16 hi and lo parts of 8 floats (an MFMA operand pair).
@@ -78,6 +90,8 @@ void prefill_dense_kernel(DenseArgs a) {
   __shared__ __align__(16) unsigned char smem[REGION + 32 * 4 + 16];
   uint32_t* lut = (uint32_t*)smem;
   float* stage_all = (float*)smem;                 // prologue: [NWAVE][64][kStageStride]
+  _Float16* pth = (_Float16*)smem;                 // epilogue: Pi_V^T hi [kD][kPtStride]
+  _Float16* ptl = pth + kD * kPtStride;            //                 lo
   float* cents = (float*)(smem + REGION);          // [32] key, value levels
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -439,31 +453,116 @@ void prefill_dense_kernel(DenseArgs a) {
     t0 += kStep;
   }
 
-  // ---- partials of the columns: lane (g, c) of block cb holds coordinates
-  // 32g + 8r + nb of column c (PV row i = coordinate 8i + nb, rows 4g + r);
-  // l summed over the column's 4 lanes
+  // ---- epilogue: Pi_V^T staged in LDS (the lookup tables are done with)
+  __syncthreads();
+  {
+    // item (i, jg): rows 8jg .. 8jg+7 of column i of Pi_V (lanes take
+    // consecutive columns: each load reads 256 contiguous bytes)
+    constexpr int ITEMS = kD * (kD / 8), PER = ITEMS / NT;
+    static_assert(ITEMS % NT == 0, "staging items");
+#pragma unroll 8
+    for (int u = 0; u < PER; ++u) {
+      const int item = tid + u * NT, i = item % kD, jg = item / kD;
+      float x[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) x[k] = a.rotV[(8 * jg + k) * kD + i];
+      half8 hi, lo;
+      split8(x, hi, lo);
+      *(half8*)(pth + i * kPtStride + 8 * jg) = hi;
+      *(half8*)(ptl + i * kPtStride + 8 * jg) = lo;
+    }
+  }
+  __syncthreads();
+
+  // ---- o = Pi_V^T acc per column (16x16x32: A = rows 16ob.. of Pi_V^T, lane
+  // (g, i): entries (16ob + i, 32g + 8kb + 0..7); B = the column sums, lane
+  // (g, c): coordinates 32g + 8kb + nb, nb = 0..7, which are acc[cb][nb][kb];
+  // D lane (g, c): output coordinates 16ob + 4g + 0..3 of column c). l is
+  // summed over the column's 4 lanes.
 #pragma unroll
   for (int cb = 0; cb < kDenseCB; ++cb) {
     float lt = l[cb];
     lt += shfl_xor_f(lt, 16);
     lt += shfl_xor_f(lt, 32);
+    float mx = 0.f;
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, fabsf(acc[cb][nb][r]));
+    mx = fmaxf(mx, shfl_xor_f(mx, 16));
+    mx = fmaxf(mx, shfl_xor_f(mx, 32));
+    const int e = (mx > 0.f && mx < INFINITY) ? __builtin_amdgcn_frexp_expf(mx) : 0;
+    half8 bh[4], bl[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      float t[8];
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) t[nb] = ldexpf(acc[cb][nb][kb], 14 - e);
+      split8(t, bh[kb], bl[kb]);
+    }
     const int col = col0 + 16 * cb + c;
+    const bool one = a.n_split == 1;
+    // one chunk: out = o / l / sqrt(d) (0 where no token is visible); else the
+    // chunk's unnormalised partial
+    const float f = one ? (lt > 0.f ? ldexpf(a.inv_sqrt_d / lt, e - 14) : 0.f) : ldexpf(1.0f, e - 14);
+    int64_t base = 0;
     if (col < a.NC) {
       const int i = col / G, h = col - (col / G) * G;
       const int64_t row = ((int64_t)b * a.M + i) * a.H_q + (int64_t)kv * G + h;
       const int64_t pidx = row * a.n_split + split;
-      float* dst = a.acc + pidx * kD;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        *(float4*)(dst + 32 * g + 8 * r) = float4{acc[cb][0][r], acc[cb][1][r], acc[cb][2][r], acc[cb][3][r]};
-        *(float4*)(dst + 32 * g + 8 * r + 4) = float4{acc[cb][4][r], acc[cb][5][r], acc[cb][6][r], acc[cb][7][r]};
-      }
-      if (g == 0) {
+      base = one ? row * kD : pidx * kD;
+      if (!one && g == 0) {
         a.ml[pidx * 2] = m_off[cb];
         a.ml[pidx * 2 + 1] = lt;
       }
     }
+    float* dst = one ? a.out : a.acc;
+#pragma unroll
+    for (int ob = 0; ob < 8; ++ob) {
+      floatx4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const int off = (16 * ob + c) * kPtStride + 32 * g + 8 * kb;
+        const half8 ah = *(const half8*)(pth + off);
+        const half8 al = *(const half8*)(ptl + off);
+        d = mfma16(ah, bh[kb], d);
+        d = mfma16(al, bh[kb], d);
+        d = mfma16(ah, bl[kb], d);
+      }
+      if (col < a.NC) *(float4*)(dst + base + 16 * ob + 4 * g) = float4{d[0] * f, d[1] * f, d[2] * f, d[3] * f};
+    }
   }
+}
+
+// Merge of the context-chunk partials of the dense kernel (already in the
+// output basis): thread (vector, 4 coordinates); chunks in order, under their
+// largest reference.
+__global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float* acc, float* out, int64_t nvec,
+                                                    int n_split, float inv_sqrt_d) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= nvec * (kD / 4)) return;
+  const int64_t v = t / (kD / 4);
+  const int q4 = (int)(t % (kD / 4));
+  const float* mlv = ml + v * n_split * 2;
+  float M = -INFINITY;
+  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlv[2 * sp]);
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  if (M != -INFINITY) {
+    for (int sp = 0; sp < n_split; ++sp) {
+      const float m = mlv[2 * sp];
+      if (m == -INFINITY) continue;   // (a chunk that saw no token)
+      const float w = __builtin_amdgcn_exp2f(m - M);
+      const float4 x = *(const float4*)(acc + (v * n_split + sp) * kD + 4 * q4);
+      num.x = fmaf(w, x.x, num.x);
+      num.y = fmaf(w, x.y, num.y);
+      num.z = fmaf(w, x.z, num.z);
+      num.w = fmaf(w, x.w, num.w);
+      den = fmaf(w, mlv[2 * sp + 1], den);
+    }
+  }
+  const float f = den > 0.f ? inv_sqrt_d / den : 0.f;
+  *(float4*)(out + v * kD + 4 * q4) = float4{num.x * f, num.y * f, num.z * f, num.w * f};
 }
 
 template <int KB, int VB, int NWAVE>
@@ -506,7 +605,9 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
   da.vnorms = v->norms;
   da.q = q;
   da.rotK = k->rot;
+  da.rotV = v->rot;
   da.ctx_lens = ctx_lens;
+  da.out = out;
   da.ml = (float*)(base + p.off_ml);
   da.acc = (float*)(base + p.off_acc);
   da.TcK = k->T_cap;
@@ -525,6 +626,7 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
   da.NC = p.NC;
   const float inv_sqrt_d = 1.0f / sqrtf((float)kD);
   da.sc1 = scale * kLog2e * inv_sqrt_d;
+  da.inv_sqrt_d = inv_sqrt_d;
   for (int i = 0; i < 16; ++i) {
     da.kc[i] = i < (1 << k->bits) ? k->centroids[i] : 0.f;
     da.vc[i] = i < (1 << v->bits) ? v->centroids[i] : 0.f;
@@ -535,8 +637,12 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
     case 3: err = launch_dense1<3>(v->bits, p, da, stream); break;
     default: err = launch_dense1<4>(v->bits, p, da, stream); break;
   }
-  if (err != hipSuccess) return err;
-  return launch_combine(da.ml, da.acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, kD, stream);
+  if (err != hipSuccess || p.n_split == 1) return err;
+  const int64_t nvec = p.B * p.M * p.H_q;
+  const int64_t blocks = (nvec * (kD / 4) + 255) / 256;
+  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, da.ml, da.acc, out, nvec,
+                     p.n_split, inv_sqrt_d);
+  return hipGetLastError();
 }
 
 }  // namespace tq
