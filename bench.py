@@ -3,11 +3,13 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload stress70b]
 
 One step is one pass of the whole hot path for one new token per batch row, in
-one call (tq_decode_attention_append): quantize the new token's key and value
-vectors of every (row, KV head) into the packed caches at t = T-1 (one launch),
-then decode attention of all query heads over the T-token packed caches (a
-second launch). Inputs are resident in HBM before timing starts. Prints one
-JSON line on stdout.
+one call and one launch (tq_decode_attention_append): the decode kernel
+quantizes the new token's key and value vectors of every (row, KV head) into
+the packed caches at t = T-1 in its prologue, then runs decode attention of all
+query heads over the T-token packed caches. Inputs are resident in HBM before
+timing starts. Before the W warmup steps, steps run untimed for --settle-ms
+(the GPU raises its clocks over tens of milliseconds of load; without this a
+short timed run measures the ramp). Prints one JSON line on stdout.
 
 Extra fields: `roofline` (the decode launch vs the HBM peak and vs the
 streaming-read reference measured in the same run), `cpu_baseline` (the CPU
@@ -38,7 +40,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 # hash it records
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_scan_stress70b_hbm_traffic.md")
 KERNEL_SOURCES = ["decode_attention_tq_amd/csrc/tq_decode.hip", "decode_attention_tq_amd/csrc/tq_scan.h",
-                  "decode_attention_tq_amd/csrc/tq_device.h", "decode_attention_tq_amd/csrc/tq_internal.h"]
+                  "decode_attention_tq_amd/csrc/tq_device.h", "decode_attention_tq_amd/csrc/tq_internal.h",
+                  "decode_attention_tq_amd/csrc/tq_rotate.h", "decode_attention_tq_amd/csrc/tq_append.h",
+                  "decode_attention_tq_amd/csrc/tq_codec.h"]
 
 
 def log(*a):
@@ -363,6 +367,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps before the warmup steps, for this long (clock ramp)")
     ap.add_argument("--workload", default="stress70b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -475,6 +481,14 @@ def main():
     def step(i):
         tq.decode_attention_append(kc, vc, new_k, new_v, qs[i % len(qs)], T=T, out=out, workspace=ws)
 
+    # untimed: steps until the clocks have settled, then the W warmup steps
+    t_settle = time.perf_counter()
+    n_settle = 0
+    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
+        for _ in range(20):
+            step(n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
     for i in range(args.warmup):
         step(i)
     # the timed steps: nothing but the steps between the two synchronizations
@@ -742,6 +756,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"ms": args.settle_ms, "steps": n_settle},
         "ms_per_step": ms_step,
         "higher_is_better": True,
         "scaling": "weak",
@@ -750,7 +765,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "H_q": w.H_q, "H_kv": w.H_kv, "d": w.d, "T": T,
                    "k_bits": w.k_bits, "v_bits": w.v_bits, "k_qjl": w.k_qjl, "input_dtype": w.dtype,
-                   "step": "quantize 1 new K,V token per (row, KV head) + decode attention over T tokens",
+                   "step": "quantize 1 new K,V token per (row, KV head) + decode attention over T tokens (one launch)",
                    "n_split": n_split},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": recorded_traffic(w.name),

@@ -409,6 +409,11 @@ int attention_call(const tq_cache* k, const tq_cache* v, const void* q, int32_t 
     if (workspace == nullptr) return device_status(e);
   }
   if (app != nullptr) {
+    // d = 128 keys without a QJL sketch: the decode kernel appends the token
+    // in its prologue (one launch); otherwise an append launch first
+    if (k->d == kD && !k->qjl)
+      return device_status(launch_decode(p, k, v, q, q_dtype, ctx_lens, scale, out, workspace,
+                                         (hipStream_t)hip_stream, app));
     if ((ctx_lens != nullptr || T > 0) && k->d == kD) {
       const hipError_t e = launch_append_kv(app->k, app->v, app->x_dtype, k->B, k->H_kv, app->k_sb, app->k_sh,
                                             app->v_sb, app->v_sh, k, v, T - 1, (hipStream_t)hip_stream, ctx_lens, T);

@@ -1,16 +1,18 @@
-// Single-token append of the append kernels: one vector per 256 threads
-// (quantize step of the ai-accelerate.xyz TurboQuant article, section
-// "TurboQuantの仕組み", step 1), in phases that the caller orders (a workgroup
-// barrier between begin and rotate and between rotate and finish):
-//   loads   each thread's half row of Pi, the vector (threads 0-31), a value
-//           block's words (threads 0-31 of the finishing wavefront), all
+// Single-token append (quantize step of the ai-accelerate.xyz TurboQuant
+// article, section "TurboQuantの仕組み", step 1), in phases that the caller
+// orders with workgroup barriers between them; used by the append kernels and
+// by the decode kernel when it takes the new token itself:
+//   loads   the row segments of Pi (tq_rotate.h), the vector (threads 0-31),
+//           a value block's words (threads 0-31 of the finishing wavefront),
 //           issued early and in flight meanwhile;
-//   begin   the power-of-two scale and norm (norm stored), the scaled vector
-//           and sqrt(d)/|x| into LDS;
-//   rotate  y = Pi x in float32 FMAs, z = y * sqrt(d)/|x|, the Lloyd-Max cell
-//           of each coordinate into LDS;
-//   finish  the codes packed and stored (a value block keeps the bits of its
-//           other tokens); keys need threads 0-3, values 0-31 of one wavefront.
+//   begin   the power-of-two scale and norm, the scaled vector and
+//           sqrt(d)/|x| into LDS;
+//   rotate  y = Pi x in float32 FMAs (rotate_rows, one vector);
+//   encode  z = y * sqrt(d)/|x| and the Lloyd-Max cell of each coordinate
+//           into LDS (threads 0-127);
+//   finish  the norm and the codes packed and stored (a value block keeps the
+//           bits of its other tokens); keys need threads 0-3, values 0-31 of
+//           the wavefront that loaded the block's words.
 #pragma once
 
 #include <math.h>
@@ -18,6 +20,7 @@
 
 #include "tq_codec.h"
 #include "tq_internal.h"
+#include "tq_rotate.h"
 
 namespace tq {
 
@@ -68,18 +71,9 @@ __device__ inline Thresholds<BITS> load_thresholds(const QuantArgs& a) {
   return th;
 }
 
-// Thread lt's half row of Pi: Pi[i][64s .. 64s+63], i = lt / 2, s = lt % 2.
-typedef float4 PiHalfRow[16];
-
-__device__ inline void load_pi_half_row(const float* rot, int lt, PiHalfRow& pr) {
-  const int i = lt >> 1, s = lt & 1;
-#pragma unroll
-  for (int k = 0; k < 16; ++k) pr[k] = ((const float4*)(rot + i * kD + 64 * s))[k];
-}
-
-// One vector gv = row*H_kv + head at token t, by the 256 threads lt = 0..255 of
-// a workgroup (LDS: xs 128 floats, fz 2 floats (sqrt(d)/|x| and |x|), cb 128
-// bytes), with the half rows of Pi loaded by load_pi_half_row.
+// One vector gv = row*H_kv + head at token t (LDS: xs and ys 128 floats each,
+// fz 2 floats (sqrt(d)/|x| and |x|), cb 128 bytes); lt numbers the threads
+// of each phase from 0.
 template <int BITS, int ROLE>
 struct AppendOne {
   static constexpr int KW = 4 * BITS;     // words per key token
@@ -141,20 +135,10 @@ struct AppendOne {
     }
   }
 
-  // y_i = sum_j Pi[i][j] x_j; the two halves of a row sit in adjacent lanes
-  __device__ void rotate(const QuantArgs& a, int lt, const PiHalfRow& pr, const float* xs, const float* fz,
-                         unsigned char* cb) {
-    const Thresholds<BITS> th = load_thresholds<BITS>(a);
-    const int i = lt >> 1, s = lt & 1;
-    const float4* xv = (const float4*)&xs[64 * s];
-    float acc = 0.f;
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const float4 q = xv[k];
-      acc = fmaf(pr[k].w, q.w, fmaf(pr[k].z, q.z, fmaf(pr[k].y, q.y, fmaf(pr[k].x, q.x, acc))));
-    }
-    acc += __shfl_xor(acc, 1);
-    if (s == 0) cb[i] = (unsigned char)encode<BITS>(acc * *fz, th);
+  // coordinate i < 128: its Lloyd-Max cell from y_i (ys = Pi x of the scaled vector)
+  __device__ static void encode_coord(const Thresholds<BITS>& th, int i, const float* ys, const float* fz,
+                                      unsigned char* cb) {
+    cb[i] = (unsigned char)encode<BITS>(ys[i] * *fz, th);
   }
 
   __device__ void finish(const QuantArgs& a, int64_t gv, int64_t t, int lt, const float* fz,

@@ -65,6 +65,8 @@
 
 #include "tq_device.h"
 #include "tq_internal.h"
+#include "tq_append.h"
+#include "tq_rotate.h"
 #include "tq_scan.h"
 
 namespace tq {
@@ -87,77 +89,27 @@ constexpr int qstride() { return D + 8; }
 // (scan), then the wavefront partials (merge) and the partial sums of the final
 // rotation, followed by two [16][d] float vector sets.
 constexpr int kRegionWords = 16896;
+// A one-token append taken by the prologue: the scaled key and value, their
+// rotations, their codes, sqrt(d)/|x| and |x| of each, the two codebooks'
+// thresholds (in LDS: a search over registers would index a stack copy).
+constexpr int kAppWords = 4 * kD + 2 * kD / 4 + 4 + 2 * 16;
 // Row stride (in floats) of a wavefront partial in the merge area: 128
 // coordinates, m and l, padded to a 16-byte multiple.
 constexpr int kMergeStride = kD + 4;
 template <int D>
 constexpr int merge_stride() { return D + 4; }
 template <int D>
-constexpr int scratch_words() { return kRegionWords + 2 * vec_words<D>(); }
+constexpr int scratch_words() { return kRegionWords + 2 * vec_words<D>() + kAppWords; }
 
-// q' = M q for the G query heads of a workgroup: out[h][i] = sum_j M[i][j]
-// in[h][j] (in, out: LDS [G][d]). Thread t takes rows R*(t/16) .. R*(t/16)+R-1
-// of M (R = 2048 / NT) over the 8 columns 8*(t%16) .. 8*(t%16)+7, loaded
-// straight from memory (16 consecutive lanes read whole rows; each element of
-// M is read once, no staging), so every query element read from LDS serves R
-// rows. The 16 segments of a row group sit in the 16 lanes of a DPP row and
-// are summed with DPP exchanges, for all heads at once.
-template <int NT>
-struct RowSegment {
-  static constexpr int R = 16 * kD / NT;   // rows per thread
-  float4 r[2 * R];                        // row k: r[2k], r[2k + 1]
-};
-
-template <int NT>
-__device__ inline void load_row_segment(RowSegment<NT>& rs, const float* M) {
+// Codes of a vector rotated by rotate_rows<NT, 1> (y in LDS), by the lanes
+// that wrote its rows: cell of y_i * sqrt(d)/|x| (the append kernels' encode).
+template <int NT, int BITS>
+__device__ inline void app_encode(const float* y, float fz, const Thresholds<BITS>& th, unsigned char* cb) {
   constexpr int R = RowSegment<NT>::R;
   const int i0 = R * (threadIdx.x / 16), sg = threadIdx.x % 16;
+  if (sg == 0) {
 #pragma unroll
-  for (int k = 0; k < R; ++k) {
-    rs.r[2 * k] = *(const float4*)(M + (i0 + k) * kD + 8 * sg);
-    rs.r[2 * k + 1] = *(const float4*)(M + (i0 + k) * kD + 8 * sg + 4);
-  }
-}
-
-template <int NT, int MAXG>
-__device__ void rotate_rows(const RowSegment<NT>& rs, const float* in, float* out, int G) {
-  constexpr int R = RowSegment<NT>::R;
-  const int i0 = R * (threadIdx.x / 16), sg = threadIdx.x % 16;
-  float acc[MAXG][R];
-#pragma unroll
-  for (int h = 0; h < MAXG; ++h) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) acc[h][k] = 0.f;
-    if (h < G) {
-      const float4 a = *(const float4*)(in + h * kD + 8 * sg);
-      const float4 b = *(const float4*)(in + h * kD + 8 * sg + 4);
-#pragma unroll
-      for (int k = 0; k < R; ++k) {
-        const float4 m0 = rs.r[2 * k], m1 = rs.r[2 * k + 1];
-        const float v = fmaf(m0.x, a.x, fmaf(m0.y, a.y, fmaf(m0.z, a.z, m0.w * a.w)));
-        acc[h][k] = fmaf(m1.x, b.x, fmaf(m1.y, b.y, fmaf(m1.z, b.z, fmaf(m1.w, b.w, v))));
-      }
-    }
-  }
-  // sums over the 16 lanes of the row: quads, then rotates by 4 and 8 (every
-  // lane ends with the full sum)
-#pragma unroll
-  for (int h = 0; h < MAXG; ++h) {
-#pragma unroll
-    for (int k = 0; k < R; ++k) {
-      float v = acc[h][k] + dpp_xor1(acc[h][k]);
-      v += dpp_xor2(v);
-      v += dpp_ror4(v);
-      v += dpp_ror8(v);
-      acc[h][k] = v;
-    }
-  }
-#pragma unroll
-  for (int h = 0; h < MAXG; ++h) {
-    if (h < G && sg == h) {
-#pragma unroll
-      for (int k = 0; k < R; ++k) out[h * kD + i0 + k] = acc[h][k];
-    }
+    for (int k = 0; k < R; ++k) cb[i0 + k] = (unsigned char)encode<BITS>(y[i0 + k] * fz, th);
   }
 }
 
@@ -262,6 +214,12 @@ struct ScanArgs {
   int M, Mt, nqt;   // query tokens per row, per workgroup tile, tiles per row
   float sc1, sc2, inv_sqrt_d;
   float kc[16], vc[16];
+  // One-token append taken by the prologue (app != 0: d = 128 keys without a
+  // QJL sketch, a decode): the new key and value of each (row, KV head), x
+  // [B][H_kv][d] in qk.x and qv.x, go to token clamp(ctx_len, 0, T) - 1 (T - 1
+  // without context lengths) before the scan reads that token.
+  int app, app_xf32;
+  QuantArgs qk, qv;
 };
 
 template <int WIDE, int QJL, int D = 128>
@@ -530,6 +488,14 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
   float* R = (float*)U;   // region: lookup tables, then merge area / rotation partials
   float* vA = R + kRegionWords;
   float* vB = vA + vec_words<D>();
+  float* axk = vB + vec_words<D>();       // appended key: scaled vector, then its rotation
+  float* ayk = axk + kD;
+  float* axv = ayk + kD;                  // appended value
+  float* ayv = axv + kD;
+  unsigned char* acb = (unsigned char*)(ayv + kD);   // [2][d] codes
+  float* afz = ayv + kD + 2 * kD / 4;     // sqrt(d)/|x|, |x| of the key, then of the value
+  Thresholds<KB>* athk = (Thresholds<KB>*)(afz + 4);
+  Thresholds<VB>* athv = (Thresholds<VB>*)(afz + 4 + 16);
   uint32_t* lut = U;                      // keys and values
   uint32_t* lutS = U + kLutBytes / 4;     // QJL signs
 
@@ -591,13 +557,20 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
   lo.v = (uint32_t)(g * value_block_words<VB, D>() + c * value_slice_words<VB, D>()) * 4u;
   lo.n = (uint32_t)(WIDE ? 8 * g + (c & 7) : 8 * g + (hf ? 4 : 0) + (c & 3)) * 4u;
 
-  // ---- prologue loads, in issue order: this thread's segment of the rows of
-  // Pi_K, its query elements, the code words of the first steps, the context
-  // length. Loads complete in issue order, so waiting for the matrix and the
-  // query never waits for the code words. The first steps are read before the
-  // context length is known: reads past the end of the cache return zeros
-  // (buffer range check), and steps past the context are never used.
+  // ---- prologue loads, in issue order: the context length, this thread's
+  // segment of the rows of Pi_K, its query elements, the appended vectors,
+  // the code words of the first steps. Loads complete in issue order, so
+  // waiting for the matrix and the query never waits for the code words. The
+  // first steps are read before the context length is used: reads past the
+  // end of the cache return zeros (buffer range check), and steps past the
+  // context are never used.
   // (d = 128; the other head dimensions read the matrix rows in the rotation)
+  // (the context length: unconditional, through an empty range when there are
+  // none, and first: a load under a branch would make its first use wait for
+  // every load issued before it)
+  uint32_t ctx_word = __builtin_amdgcn_raw_buffer_load_b32(
+      make_rsrc(a.ctx_lens ? (const void*)a.ctx_lens : (const void*)a.knorms, a.ctx_lens ? (uint32_t)((b + 1) * 4) : 0u),
+      (uint32_t)b * 4u, 0, 0);
   RowSegment<NT> rseg;
   if constexpr (D == kD) load_row_segment<NT>(rseg, a.rotK);
   constexpr int QE = 16 * D / NT;   // query elements per thread (G <= 16)
@@ -616,6 +589,25 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
       const uint32_t cq = idx / D;
       const uint32_t el = ((cq / (uint32_t)G) * (uint32_t)a.H_q + cq % (uint32_t)G) * D + idx % D;
       qraw[k] = __builtin_amdgcn_raw_buffer_load_b32(rq, qbf ? (el * 2u) & ~3u : el * 4u, 0, 0);
+    }
+  }
+  // appended key (wavefront 0) and value (wavefront 1): lanes 0-31 read 4
+  // coordinates each
+  constexpr bool APP = D == kD && !QJL;
+  float ax[4] = {0.f, 0.f, 0.f, 0.f};
+  if constexpr (APP) {
+    if (a.app && wave < 2 && lane < 32) {
+      const bool vw = wave == 1;
+      const int64_t off = (int64_t)b * (vw ? a.qv.sb : a.qk.sb) + (int64_t)kv * (vw ? a.qv.sh : a.qk.sh) + 4 * lane;
+      const void* xp = vw ? a.qv.x : a.qk.x;
+      if (a.app_xf32) {
+        const float4 f = *(const float4*)((const float*)xp + off);
+        ax[0] = f.x; ax[1] = f.y; ax[2] = f.z; ax[3] = f.w;
+      } else {
+        const uint2 u = *(const uint2*)((const uint16_t*)xp + off);
+        ax[0] = __uint_as_float(u.x << 16); ax[1] = __uint_as_float(u.x & 0xFFFF0000u);
+        ax[2] = __uint_as_float(u.y << 16); ax[3] = __uint_as_float(u.y & 0xFFFF0000u);
+      }
     }
   }
   constexpr int AH = scan_ahead<QJL, WIDE, D>();
@@ -637,14 +629,24 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
     if (kpg) ek = page_entry(rtk, a.kpm, tn);
     if (vpg) ev = page_entry(rtv, a.vpm, tn);
   }
-  // (unconditional, through an empty range when there are no context lengths,
-  // and first touched after the prologue: a load under a branch, or one moved
-  // to a scalar register at once, would make the prologue wait for every load
-  // issued before it)
-  uint32_t ctx_word = __builtin_amdgcn_raw_buffer_load_b32(
-      make_rsrc(a.ctx_lens ? (const void*)a.ctx_lens : (const void*)a.knorms, a.ctx_lens ? (uint32_t)((b + 1) * 4) : 0u),
-      (uint32_t)b * 4u, 0, 0);
   __builtin_amdgcn_sched_barrier(0);
+
+  // The appended token (if any) and whether this workgroup's chunk holds it
+  // (the token of a row goes where a separate append would put it).
+  // The wavefront whose share holds the token stores it (and alone reads it
+  // back, in its last step), so no other wavefront waits for the stores.
+  int app_t = -1, app_wave = -1;
+  bool appending = false;
+  AppendOne<VB, TQ_VALUES> apv;   // the value block's other words (wavefront app_wave)
+  if constexpr (APP) {
+    if (a.app) {
+      int cx = a.ctx_lens ? (int)ctx_word : a.T;
+      cx = cx < 0 ? 0 : (cx > a.T ? a.T : cx);
+      app_t = __builtin_amdgcn_readfirstlane(cx - 1);
+      appending = app_t >= 0 && app_t >= split * a.wg_chunk && app_t < (split + 1) * a.wg_chunk;
+      if (appending) app_wave = (app_t - split * a.wg_chunk) / a.wave_chunk;
+    }
+  }
 
   // ---- prologue: lookup tables, then the query operand of this (row, KV head)
   if (tid < 32) {
@@ -680,9 +682,36 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
         vA[idx] = a.q_dtype == TQ_BF16 ? __uint_as_float(((qraw[k] >> (16 * (idx & 1))) & 0xFFFFu) << 16)
                                        : __uint_as_float(qraw[k]);
     }
+    if constexpr (APP) {
+      // the codebooks' thresholds, the appended vectors' scale and norm
+      // (wavefronts 0 and 1), the value block's other words
+      if (appending) {
+        if (tid < 15) {
+          if (tid < (1 << KB) - 1) athk->t[tid] = a.qk.thr[tid];
+          if (tid < (1 << VB) - 1) athv->t[tid] = a.qv.thr[tid];
+        }
+        if (tid == 15) {
+          athk->sym = a.qk.thr_sym != 0;
+          athv->sym = a.qv.thr_sym != 0;
+        }
+        if (wave == 0) AppendOne<KB, TQ_KEYS>().begin(a.qk, bkv, app_t, lane, ax, axk, afz);
+        else if (wave == 1) AppendOne<VB, TQ_VALUES>().begin(a.qv, bkv, app_t, lane, ax, axv, afz + 2);
+        if (wave == app_wave) apv.load_old(a.qv, bkv, app_t, lane);
+      }
+    }
     __syncthreads();
     if constexpr (D == kD) {
       rotate_rows<NT, NQ / 2>(rseg, vA, vB, NC);   // q' = Pi_K q
+      if constexpr (APP) {
+        if (appending) {
+          // the appended key on the same row segments of Pi_K (the arithmetic
+          // of the append kernels), its codes by the lanes that hold the rows;
+          // then Pi_V's segments, in flight while the query operand is written
+          rotate_rows<NT, 1>(rseg, axk, ayk, 1);
+          app_encode<NT, KB>(ayk, afz[0], *athk, acb);
+          load_row_segment<NT>(rseg, a.rotV);
+        }
+      }
       __syncthreads();
     } else {
       rotate_generic<NT, D, NQ / 2>(a.rotK, vA, vB, R, NC);   // q' = Pi_K q
@@ -694,6 +723,21 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
       rotate_rows<NT, NQ / 2>(rseg, vB, vA, NC);   // q'' = S q'
       __syncthreads();
       emit_operand<NT>(vA, a.sc2, NC, HALF, qlds + NQ * kQStride, qcs + 16, hexp);
+    }
+    if constexpr (APP) {
+      if (appending) {
+        // the appended value on Pi_V's row segments, its codes, then the
+        // stores by the wavefront that reads the token back (after its own
+        // stores have completed)
+        rotate_rows<NT, 1>(rseg, axv, ayv, 1);
+        app_encode<NT, VB>(ayv, afz[2], *athv, acb + kD);
+        __syncthreads();
+        if (wave == app_wave) {
+          AppendOne<KB, TQ_KEYS>().finish(a.qk, bkv, app_t, lane, afz, acb);
+          apv.finish(a.qv, bkv, app_t, lane, afz + 2, acb + kD);
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        }
+      }
     }
   }
   __syncthreads();
@@ -729,8 +773,13 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
   const int lim_lo = max(lim0, 0), lim_hi = max(lim0 + mq - 1, 0);
   const int t_end = __builtin_amdgcn_readfirstlane(min(t_begin + a.wave_chunk, lim_hi));
   const int t_unm = min(t_end, lim_lo);   // below this every column sees every token
-  const int t_full =
+  int t_full =
       __builtin_amdgcn_readfirstlane(t_begin + (t_unm > t_begin ? (t_unm - t_begin) / kStep * kStep : 0));
+  // the step holding a token appended by the prologue is read after it, in the
+  // masked steps, past the vector L1 (the steps read ahead before the append
+  // may hold the old words)
+  if (appending && app_t >= t_begin && app_t < t_end)
+    t_full = __builtin_amdgcn_readfirstlane(min(t_full, t_begin + (app_t - t_begin) / kStep * kStep));
   // this lane's column limit for the masked steps (columns past NC carry a zero
   // query and keep the widest limit)
   const int lcol = WIDE ? c : (c & 7);
@@ -743,15 +792,15 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
   st.m_ref = -INFINITY;
   st.m_off = -INFINITY;
   st.l = 0.f;
-  {
-    // Value-norm scale: the weights 2^(s - m_off) * |v| are float16 operands,
-    // so the wavefront divides them (and its denominator, which keeps the
-    // ratio) by 2^ev, ev = the exponent of the largest value norm among the
-    // tokens of its first loaded step. The weights of those tokens then sit
-    // near the top of the float16 range whatever the norms' overall scale
-    // (tiny value norms would otherwise fall into float16 subnormals); ev
-    // enters through m_off, which the merges already carry per wavefront.
-    float vm = fabsf(buf[0].nm.vn);
+  // Value-norm scale: the weights 2^(s - m_off) * |v| are float16 operands,
+  // so the wavefront divides them (and its denominator, which keeps the
+  // ratio) by 2^ev, ev = the exponent of the largest value norm among the
+  // tokens of its first step. The weights of those tokens then sit near the
+  // top of the float16 range whatever the norms' overall scale (tiny value
+  // norms would otherwise fall into float16 subnormals); ev enters through
+  // m_off, which the merges already carry per wavefront.
+  auto set_ev = [&](float vn) {
+    float vm = fabsf(vn);
     vm = fmaxf(vm, dpp_xor1(vm));
     vm = fmaxf(vm, dpp_xor2(vm));
     vm = fmaxf(vm, dpp_ror4(vm));
@@ -761,7 +810,11 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
     int e = (vm > 0.f && vm < INFINITY) ? __builtin_amdgcn_frexp_expf(vm) : 0;
     e = e < -kNormExpClamp ? -kNormExpClamp : (e > kNormExpClamp ? kNormExpClamp : e);
     st.ev = (float)__builtin_amdgcn_readfirstlane(e);
-  }
+  };
+  // (from the first full step, read ahead; a share without full steps takes
+  // its first masked step below)
+  st.ev = 0.f;
+  if (t_begin < t_full) set_ev(buf[0].nm.vn);
 #pragma unroll
   for (int nb = 0; nb < CV; ++nb) st.acc0[nb] = floatx4{0.f, 0.f, 0.f, 0.f};
 
@@ -833,7 +886,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
     StepData<KB, VB, QJL, WIDE, D> E;
     if (kpg) ek = page_entry(rtk, a.kpm, t0);
     if (vpg) ev = page_entry(rtv, a.vpm, t0);
-    load_step<true>(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
+    load_step<true, kFreshAux>(E, s, lo, step_row(a.kpm, kv, a.H_kv, ek, t0), step_row(a.vpm, kv, a.H_kv, ev, t0));
+    if (t0 == t_begin) set_ev(E.nm.vn);
     scan_step<KB, VB, QJL, WIDE, true, D>(E, q, st, (const char*)lut, lr, lutS, lrep, t0 + 8 * g, lim_lane);
     t0 += kStep;
   }
@@ -1140,7 +1194,7 @@ hipError_t dispatch_kb(int kb, int vb, const DecodePlan& p, const ScanArgs& sa, 
 
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,
                          int q_dtype, const int32_t* ctx_lens, float scale, float* out, void* ws,
-                         hipStream_t stream) {
+                         hipStream_t stream, const DecodeAppend* app) {
   char* base = (char*)ws;
   float* ml = (float*)(base + p.off_ml);
   float* acc = (float*)(base + p.off_acc);
@@ -1185,6 +1239,15 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   for (int i = 0; i < 16; ++i) {
     sa.kc[i] = i < (1 << k->bits) ? k->centroids[i] : 0.f;
     sa.vc[i] = i < (1 << v->bits) ? v->centroids[i] : 0.f;
+  }
+  sa.app = app != nullptr ? 1 : 0;
+  sa.app_xf32 = app != nullptr && app->x_dtype == TQ_F32 ? 1 : 0;
+  if (app != nullptr) {
+    sa.qk = make_quant_args(app->k, p.B, 1, p.H_kv, app->k_sb, 0, app->k_sh, k, p.T - 1);
+    sa.qv = make_quant_args(app->v, p.B, 1, p.H_kv, app->v_sb, 0, app->v_sh, v, p.T - 1);
+  } else {
+    sa.qk = QuantArgs{};
+    sa.qv = QuantArgs{};
   }
   hipError_t err;
   if (d == 64) err = dispatch_kb<64>(k->bits, v->bits, p, sa, stream);

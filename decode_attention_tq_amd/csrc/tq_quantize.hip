@@ -1184,7 +1184,9 @@ __global__ __launch_bounds__(64 * kQbWaves) void quantize_bf16_kernel(QuantArgs 
 //
 // One token per (row, head) (T = 1) without QJL: latency, not throughput,
 // decides here, so the rotation runs as float32 FMAs with the rows of Pi read
-// straight from memory (no LDS staging of Pi, no operand split), kAppendVecs
+// straight from memory in segments (rotate_rows, the arithmetic the decode
+// kernel repeats when it appends the token itself; no LDS staging of Pi, no
+// operand split), kAppendVecs
 // vectors per 256-thread workgroup (few, so that a layer's tokens spread over
 // many compute units and each thread's dot products stay short). Same steps as
 // the tiled kernels: power-of-two scale, norm, y = Pi x, threshold search,
@@ -1198,18 +1200,21 @@ __device__ void append_vectors(const QuantArgs& a, int64_t blk, int64_t t) {
   if (t < 0) return;   // (workgroup-uniform)
   static_assert(kAppendVecs == 1, "one vector per workgroup");
   __shared__ __align__(16) float xs[kD];
+  __shared__ __align__(16) float ys[kD];
   __shared__ __align__(16) unsigned char cb[kD];
   __shared__ float fz[2];
   const int lt = threadIdx.x;
   AppendOne<BITS, ROLE> ap;
-  PiHalfRow pr;
+  RowSegment<256> rs;
   float x[4];
-  load_pi_half_row(a.rot, lt, pr);
+  load_row_segment<256>(rs, a.rot);
   ap.load_old(a, blk, t, lt);
   AppendOne<BITS, ROLE>::load_x(a, blk, lt, XF32 != 0, x);
   ap.begin(a, blk, t, lt, x, xs, fz);
   __syncthreads();
-  ap.rotate(a, lt, pr, xs, fz, cb);
+  rotate_rows<256, 1>(rs, xs, ys, 1);
+  __syncthreads();
+  if (lt < kD) AppendOne<BITS, ROLE>::encode_coord(load_thresholds<BITS>(a), lt, ys, fz, cb);
   __syncthreads();
   ap.finish(a, blk, t, lt, fz, cb);
 }

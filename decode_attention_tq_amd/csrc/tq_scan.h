@@ -21,6 +21,10 @@ constexpr float kSlack = 2.0f;
 constexpr float kShift = kSlack + 3.5f;   // + log2(sqrt(128))
 constexpr int kLutRep = 32;              // LUT replicas (power of two)
 constexpr int kStreamAux = 2;            // cache policy of the streamed cache reads: non-temporal
+// the last step of a decode that appended its token in the prologue: device
+// scope (sc1), so the read misses the compute unit's vector L1 and sees the
+// words just written through it
+constexpr int kFreshAux = kStreamAux | 16;
 constexpr int kLutShift = 5;             // log2(kLutRep)
 // Bound of the value-norm exponent (keeps the fp32 softmax denominator of a
 // wavefront far from overflow: at most 2^(60 + 2 - kShift) per token).
@@ -220,26 +224,26 @@ __device__ inline uint32_t step_row(const PageMap& m, int kv, int H_kv, uint32_t
 // puts the second part's distance in the scalar offset when the per-lane
 // offset needs no range check (RC false), else in the per-lane offset (the
 // hardware range-checks only that one).
-template <int N, bool RC = false>
+template <int N, bool RC = false, int AUX = kStreamAux>
 __device__ inline void bload_words_s(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
   if constexpr (N == 1) {
-    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kStreamAux);
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
   } else if constexpr (N == 2) {
-    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kStreamAux);
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX);
     w[0] = v.x; w[1] = v.y;
   } else if constexpr (N == 3) {
-    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, kStreamAux);
+    const u32x3 v = __builtin_amdgcn_raw_buffer_load_b96(r, voff, soff, AUX);
     w[0] = v.x; w[1] = v.y; w[2] = v.z;
   } else if constexpr (N == 4) {
-    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kStreamAux);
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX);
     w[0] = v.x; w[1] = v.y; w[2] = v.z; w[3] = v.w;
   } else if constexpr (N == 6) {
-    bload_words_s<3>(r, voff, soff, w);
-    bload_words_s<3>(r, RC ? voff + 12u : voff, RC ? soff : soff + 12u, w + 3);
+    bload_words_s<3, false, AUX>(r, voff, soff, w);
+    bload_words_s<3, false, AUX>(r, RC ? voff + 12u : voff, RC ? soff : soff + 12u, w + 3);
   } else {
     static_assert(N == 8 || N == 12 || N == 16, "unsupported word count");
-    bload_words_s<4>(r, voff, soff, w);
-    bload_words_s<N - 4, RC>(r, RC ? voff + 16u : voff, RC ? soff : soff + 16u, w + 4);
+    bload_words_s<4, false, AUX>(r, voff, soff, w);
+    bload_words_s<N - 4, RC, AUX>(r, RC ? voff + 16u : voff, RC ? soff : soff + 16u, w + 4);
   }
 }
 
@@ -266,7 +270,7 @@ __device__ inline void wait_step(const StepData<KB, VB, QJL, WIDE, D>& d) {
 // A step that may run past the end of a stream (the ragged end of a row whose
 // capacity is not a multiple of 32) adds it to the per-lane offsets instead,
 // so that lanes past the end read zeros.
-template <bool CHECKED, int KB, int VB, int QJL, int WIDE, int D>
+template <bool CHECKED, int AUX = kStreamAux, int KB, int VB, int QJL, int WIDE, int D>
 __device__ inline void load_step(StepData<KB, VB, QJL, WIDE, D>& d, const Streams& s, const LaneOffsets& lo,
                                  uint32_t rk, uint32_t rv) {
   constexpr int KW = key_record_words<KB, D>(), VBW = value_block_words<VB, D>();
@@ -284,18 +288,18 @@ __device__ inline void load_step(StepData<KB, VB, QJL, WIDE, D>& d, const Stream
   for (int m = 0; m < 2; ++m) {
     const uint32_t vk = CHECKED ? lo.k + ok + (m ? dk1 : 0u) : lo.k;
     const uint32_t sk = CHECKED ? 0u : ok + (m ? dk1 : 0u);
-    bload_words_s<KSW, CHECKED>(s.rk, vk, sk, d.kw[m]);
+    bload_words_s<KSW, CHECKED, AUX>(s.rk, vk, sk, d.kw[m]);
     if constexpr (QJL) {
       const uint32_t vs = CHECKED ? lo.s + os + (m ? ds1 : 0u) : lo.s;
       const uint32_t ss = CHECKED ? 0u : os + (m ? ds1 : 0u);
-      d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, vs, ss, kStreamAux);
+      d.sw[m] = __builtin_amdgcn_raw_buffer_load_b32(s.rs, vs, ss, AUX);
     }
   }
-  bload_words_s<VSW, CHECKED>(s.rv, TQ_VOF(lo.v, ov), TQ_OFF(ov), d.vw);
-  d.nm.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, TQ_VOF(lo.n, onk), TQ_OFF(onk), kStreamAux));
-  d.nm.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, TQ_VOF(lo.n, onv), TQ_OFF(onv), kStreamAux));
+  bload_words_s<VSW, CHECKED, AUX>(s.rv, TQ_VOF(lo.v, ov), TQ_OFF(ov), d.vw);
+  d.nm.kn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rkn, TQ_VOF(lo.n, onk), TQ_OFF(onk), AUX));
+  d.nm.vn = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rvn, TQ_VOF(lo.n, onv), TQ_OFF(onv), AUX));
   if constexpr (QJL)
-    d.nm.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, TQ_VOF(lo.n, onk), TQ_OFF(onk), kStreamAux));
+    d.nm.kg = as_float(__builtin_amdgcn_raw_buffer_load_b32(s.rg, TQ_VOF(lo.n, onk), TQ_OFF(onk), AUX));
 #undef TQ_OFF
 #undef TQ_VOF
 }

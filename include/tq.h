@@ -291,10 +291,13 @@ int tq_decode_attention_noalloc(const tq_cache* k, const tq_cache* v,
  * One decode step in one call: for every row b with context length
  * ctx_b = clamp(ctx_lens[b], 0, T) (or T) >= 1, the new key and value of each
  * KV head are written to token ctx_b - 1 of k and v (the same bytes as
- * tq_quantize_kv / tq_append_kv at that position, one launch for keys and
- * values), then out is tq_decode_attention over tokens 0 .. ctx_b - 1, which
- * include the new one (a second launch, ordered after the first on the
- * stream). Rows with ctx_b = 0 get no write and a zero output.
+ * tq_quantize_kv / tq_append_kv at that position), then out is
+ * tq_decode_attention over tokens 0 .. ctx_b - 1, which include the new one
+ * (the same output, bit for bit, as tq_append_kv followed by
+ * tq_decode_attention). Rows with ctx_b = 0 get no write and a zero output.
+ * d = 128 keys without a QJL sketch: one launch (the decode kernel writes the
+ * new token itself before reading it); otherwise an append launch, then the
+ * decode launch, ordered on the stream.
  *   k_new, v_new: device, element (b, h, j) at k_new[b*k_stride_b + h*k_stride_h + j]
  *                 (and the same for v_new), dtype new_dtype (TQ_F32 or TQ_BF16),
  *                 16-byte aligned rows
