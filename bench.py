@@ -49,6 +49,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def settle(torch, fn, ms):
+    """Untimed calls of fn(i) for about ms milliseconds (the clocks ramp up
+    under load after an idle spell); returns the number of calls."""
+    t = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t) * 1e3 < ms:
+        for _ in range(4):
+            fn(n)
+            n += 1
+        torch.cuda.synchronize()
+    return n
+
+
 def kernel_source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -482,13 +495,7 @@ def main():
         tq.decode_attention_append(kc, vc, new_k, new_v, qs[i % len(qs)], T=T, out=out, workspace=ws)
 
     # untimed: steps until the clocks have settled, then the W warmup steps
-    t_settle = time.perf_counter()
-    n_settle = 0
-    while (time.perf_counter() - t_settle) * 1e3 < args.settle_ms:
-        for _ in range(20):
-            step(n_settle)
-            n_settle += 1
-        torch.cuda.synchronize()
+    n_settle = settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     # the timed steps: nothing but the steps between the two synchronizations
@@ -567,8 +574,8 @@ def main():
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         pout = torch.empty_like(out)
-        for i in range(5):
-            tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws)
+        settle(torch, lambda i: tq.decode_attention(pk, pv, qs[i % len(qs)], T=T, out=pout, workspace=ws),
+               args.settle_ms / 3)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for i in range(50):
@@ -620,8 +627,8 @@ def main():
         # served from the 256 MB last-level cache: calls cycle through them
         n_layers = max(1, min(64, -(-(1 << 30) // fb)))
         layers = [(fk, fv)] + [(copy_cache(tq, fk), copy_cache(tq, fv)) for _ in range(n_layers - 1)]
-        for i in range(5):
-            tq.decode_attention(*layers[i % n_layers], fq, T=fw.T, out=fo, workspace=fws)
+        settle(torch, lambda i: tq.decode_attention(*layers[i % n_layers], fq, T=fw.T, out=fo, workspace=fws),
+               args.settle_ms / 3)
         n_calls = max(50, 2 * n_layers)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
@@ -676,8 +683,8 @@ def main():
         hb = decode_bytes(hw, hw.T)
         n_layers = max(1, min(64, -(-(1 << 30) // hb)))
         layers = [(hk, hv)] + [(copy_cache(tq, hk), copy_cache(tq, hv)) for _ in range(n_layers - 1)]
-        for i in range(3):
-            tq.decode_attention(*layers[i % n_layers], hq, T=hw.T, out=ho, workspace=hws)
+        settle(torch, lambda i: tq.decode_attention(*layers[i % n_layers], hq, T=hw.T, out=ho, workspace=hws),
+               args.settle_ms / 3)
         n_calls = max(20, 2 * n_layers)
         e0.record()
         for i in range(n_calls):
@@ -705,8 +712,7 @@ def main():
         pq = pq.to(torch.bfloat16) if w.dtype == "bf16" else pq
         pws = tq.Workspace(tq.prefill_workspace_bytes(w.B, w.H_q, w.H_kv, M, T, 0, w.k_qjl), dev)
         po = torch.empty((w.B, M, w.H_q, w.d), dtype=torch.float32, device=dev)
-        for _ in range(3):
-            tq.prefill_attention(kc, vc, pq, T=T, out=po, workspace=pws)
+        settle(torch, lambda i: tq.prefill_attention(kc, vc, pq, T=T, out=po, workspace=pws), args.settle_ms / 3)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(20):
