@@ -779,7 +779,7 @@ def main():
                      "frac_of_stream": achieved / stream["GB_s"] if stream else None,
                      "kernel": (f"decode_scan_kernel<{w.k_bits},{w.v_bits},{int(bool(w.k_qjl))},{int(w.G > 8)},0>"
                                 + (" (the whole tq_decode_attention launch)" if n_split == 1
-                                   else f" + combine_kernel ({n_split} context chunks)")),
+                                   else f" + merge_kernel ({n_split} context chunks)")),
                      "bytes_per_launch": dbytes, "launch_us": dec_ms * 1e3},
         "decode": {"us": dec_ms * 1e3, "us_median": dec_med * 1e3, "us_p10": dec_p10 * 1e3,
                    "us_p90": dec_p90 * 1e3, "us_back_to_back": dec_only_us,

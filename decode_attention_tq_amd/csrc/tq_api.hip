@@ -109,7 +109,7 @@ bool plan_decode(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int32_t n_spli
   chunk = (chunk + quantum - 1) / quantum * quantum;
   p->chunk = (int32_t)chunk;
   p->n_split = (int32_t)((Tp + chunk - 1) / chunk);
-  if (p->n_split > 1 && B * M > 65535) return false;   // grid y of the combine
+  if (p->n_split > 1 && B * M * H_q * d / 256 >= INT32_MAX) return false;   // grid of the chunk merge
   size_t off = 0;
   p->off_ml = off;
   off = align256(off + (size_t)(B * M * H_q) * p->n_split * 2 * sizeof(float));
@@ -135,7 +135,7 @@ bool plan_prefill_dense(int64_t B, int64_t H_q, int64_t H_kv, int64_t T, int64_t
   p->nwave = waves >= 4 ? 4 : (waves >= 2 ? 2 : 1);
   p->ncg = (int32_t)((p->NC + kDenseWaveCols * p->nwave - 1) / (kDenseWaveCols * p->nwave));
   if (B * p->ncg > 65535 || B * M > 65535) return false;   // grid z of the scan; rows
-  if (B * M * H_q / 8 >= INT32_MAX) return false;             // grid of the chunk merge (kD / 4 threads a vector)
+  if (B * M * H_q * kD / 256 >= INT32_MAX) return false;      // grid of the chunk merge (d threads a vector)
   const int64_t Tp = T > 0 ? T : 1;
   int64_t target;
   if (n_split > 0) {

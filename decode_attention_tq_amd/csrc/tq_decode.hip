@@ -11,14 +11,16 @@
 //   scan      each wavefront streams its share of the chunk: scores from the
 //             packed key codes on MFMA, online softmax in registers, values
 //             accumulated in the rotated domain on MFMA;
-//   epilogue  the wavefront partials are merged in LDS in a fixed order; with
-//             a single chunk (the usual case once B * H_kv fills the part) the
-//             workgroup applies o = Pi_V^T o' and writes the output itself.
+//   epilogue  the wavefront partials are merged in LDS in a fixed order and
+//             the workgroup applies Pi_V^T: with a single chunk (the usual
+//             case once B * H_kv fills the part) to o' / l, writing the output
+//             itself; otherwise to the chunk's unnormalised sums, its partial.
 // Paged caches: a step's token rows come from the block table (an entry read
 // one step ahead); a 32-token step never crosses a block. A separate
 // instantiation keeps the contiguous path free of that work.
-// combine (only when the context is split into several chunks): fixed-order
-// merge of the chunk partials of each query head, then o = Pi_V^T o'.
+// merge (only when the context is split into several chunks): fixed-order
+// merge of the chunk partials of each query head, already in the output basis
+// (the rotation is linear, so it commutes with the merge).
 // (Merging chunks inside decode_scan would need a device-scope release per
 // workgroup, which on this multi-die part writes back L2; the kernel boundary
 // provides that ordering once.)
@@ -60,7 +62,7 @@
 // a per-wavefront power of two at or above the value norms of its first step,
 // which keeps every weight operand at or below (|v| / 2^ev) / sqrt(d) (float16
 // range while |v| < 7e5 * 2^ev, and no float16 underflow of the leading
-// weights however small the norms) and leaves one 1/sqrt(d) for the combine.
+// weights however small the norms) and leaves one 1/sqrt(d) for the end.
 #include <math.h>
 
 #include "tq_device.h"
@@ -464,9 +466,9 @@ constexpr size_t scan_lds_bytes() {
 //             into the float16 operand in LDS, while the first code words are
 //             already in flight;
 //   scan      each wavefront streams its share of the chunk;
-//   epilogue  the wavefront partials are merged in LDS in a fixed order; with
-//             one chunk the workgroup finishes the heads (o = Pi_V^T o'),
-//             otherwise it writes the chunk partial for the combine.
+//   epilogue  the wavefront partials are merged in LDS in a fixed order, then
+//             Pi_V^T: with one chunk the output, otherwise the chunk partial
+//             for the merge kernel.
 template <int KB, int VB, int QJL, int WIDE, int PAGED, int D>
 __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan_kernel(ScanArgs a) {
   constexpr int NW = scan_waves<QJL, WIDE, D>(), NT = 64 * NW;
@@ -911,15 +913,17 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
 
   // ---- merge the wavefront partials in LDS (fixed order)
   const bool finish = a.n_split == 1;
-  // With one chunk the workgroup finishes with o = Pi_V^T o' (d = 128: thread
-  // (s, p) takes columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded
-  // now (a wavefront reads whole rows) so that the loads are in flight while
-  // the wavefront waits for the others and during the merge).
+  // The workgroup ends with Pi_V^T applied: to o' / l with one chunk (the
+  // output), to the chunk's unnormalised sums otherwise (the rotation is
+  // linear, so the chunk merge can follow it). d = 128: thread (s, p) takes
+  // columns 2p, 2p+1 of Pi_V over rows s*RW .. s*RW+RW-1, loaded now (a
+  // wavefront reads whole rows) so that the loads are in flight while the
+  // wavefront waits for the others and during the merge.
   constexpr int FSEGS = NT / 64, RW = kD / FSEGS;
   const int fp = tid & 63, fs = tid >> 6;
   float2 pv[RW];
   if constexpr (D == kD) {
-    if (finish) {
+    {
 #pragma unroll
       for (int k = 0; k < RW; ++k) pv[k] = *(const float2*)(a.rotV + (fs * RW + k) * kD + 2 * fp);
     }
@@ -984,16 +988,20 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
     if (finish) {
       vB[idx] = den > 0.f ? num / den * a.inv_sqrt_d : 0.f;
     } else {
-      const int64_t pidx = out_row(h) * a.n_split + split;
-      a.acc[pidx * D + j] = num;
+      vB[idx] = num;
       if (j == 0) {
+        const int64_t pidx = out_row(h) * a.n_split + split;
         a.ml[pidx * 2] = Mh[h];
         a.ml[pidx * 2 + 1] = den;
       }
     }
   }
-  if (finish) {
-    __syncthreads();   // o' is complete in vB; the merge area takes the partial sums
+  // destination of column h's rotated vector: the output, or the chunk partial
+  auto rot_dst = [&](int h) -> float* {
+    return finish ? a.out + out_row(h) * D : a.acc + (out_row(h) * a.n_split + split) * D;
+  };
+  {
+    __syncthreads();   // vB is complete; the merge area takes the partial sums
     if constexpr (D == kD) {
       float* P = R;      // [FSEGS][NC][d]
       for (int h = 0; h < NC; ++h) {
@@ -1013,7 +1021,7 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
         float r = 0.f;
 #pragma unroll
         for (int sg = 0; sg < FSEGS; ++sg) r += P[(sg * NC + h) * kD + i];
-        a.out[out_row(h) * kD + i] = r;
+        rot_dst(h)[i] = r;
       }
     } else {
       // thread (i, hg): coordinate i of heads hg, hg + NT/D, ... from column i
@@ -1035,115 +1043,94 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
 #pragma unroll
       for (int k = 0; k < 16 / HG; ++k) {
         const int h = hg + k * HG;
-        if (h < NC) a.out[out_row(h) * D + i] = r[k];
+        if (h < NC) rot_dst(h)[i] = r[k];
       }
     }
   }
 }
 
-// ---------------------------------------------------------------- combine --
+// ------------------------------------------------------------------ merge --
 
-// Workgroup (kv, b, chunk): merge the context-chunk partials of the G query
-// heads of KV head kv (every workgroup of the KV head merges all 128
-// coordinates), then output coordinates 32*chunk .. 32*chunk+31 of
-// o = Pi_V^T o', with those 32 columns of Pi_V staged in LDS. Entry e =
-// (group gr, pair pr) of the S groups of the G*128 (head, coordinate) pairs
-// takes chunks gr, gr + S, ... in order, kCombineBatch at a time with all
-// their loads in flight together, under a running maximum; the groups are
-// then merged in group order. The order of every step is fixed by the plan.
-constexpr int kCombineThreads = 512;
-constexpr int kCombineBatch = 16;
+// Fixed-order merge of the context-chunk partials of each query vector (m, l
+// and the chunk's sums already in the output basis): out = sum_c 2^(m_c - M)
+// acc_c / sum_c 2^(m_c - M) l_c / sqrt(d), M the largest m_c. Four consecutive
+// lanes take one (vector, 4 coordinates): lane p merges chunks p, p + 4, ...,
+// kMergeBatch at a time with every load in flight together, under a running
+// reference; the four parts then meet over lane exchanges (xor 1, then xor 2).
+constexpr int kMergeBatch = 8;
 
 template <int D>
-__global__ __launch_bounds__(kCombineThreads) void combine_kernel(const float* ml, const float* acc,
-                                                                  const float* rotV, float* out, int H_q, int G,
-                                                                  int n_split, float inv_sqrt_d) {
-  constexpr int NT = kCombineThreads;
-  constexpr int PIECES = 8 * D / NT;   // 16-byte pieces of the staged columns per thread
-  __shared__ __align__(16) float colv[D * 32];
-  __shared__ __align__(16) float ov[16 * D];
-  __shared__ float gsh[3][NT];
-  const int kv = blockIdx.x, b = blockIdx.y, chunk = blockIdx.z, tid = threadIdx.x;
-  const int64_t bh0 = (int64_t)b * H_q + (int64_t)kv * G;
-  {
-    // Pi_V[j][32*chunk + 0..31] for all j: 8*D 16-byte pieces
-    float4 v[PIECES];
+__global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float* acc, float* out, int64_t nvec,
+                                                    int n_split, float inv_sqrt_d) {
+  constexpr int Q = D / 4;   // coordinate quads of a vector
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int part = threadIdx.x & 3;
+  const int64_t vq = t >> 2;   // (vector, quad)
+  const bool live = vq < nvec * Q;
+  const int64_t v = live ? vq / Q : 0;
+  const int q4 = live ? (int)(vq % Q) : 0;
+  const float* mlv = ml + v * n_split * 2;
+  const float* av = acc + v * n_split * D + 4 * q4;
+  float M = -INFINITY, den = 0.f;
+  float4 num = {0.f, 0.f, 0.f, 0.f};
+  if (live) {
+    for (int c0 = part; c0 < n_split; c0 += 4 * kMergeBatch) {
+      float mv[kMergeBatch], lv[kMergeBatch];
+      float4 xv[kMergeBatch];
 #pragma unroll
-    for (int k = 0; k < PIECES; ++k) {
-      const int f = tid + NT * k, j = f >> 3, c4 = f & 7;
-      v[k] = *(const float4*)(rotV + j * D + 32 * chunk + 4 * c4);
-    }
-#pragma unroll
-    for (int k = 0; k < PIECES; ++k) *(float4*)(colv + 4 * (tid + NT * k)) = v[k];
-  }
-  const int NP = G * D;
-  const int S = NT / NP > 0 ? NT / NP : 1;
-  for (int e = tid; e < S * NP; e += NT) {
-    const int gr = e / NP, pr = e % NP, h = pr / D, j = pr % D;
-    const float* mlb = ml + (bh0 + h) * n_split * 2;
-    const float* ab = acc + (bh0 + h) * n_split * D + j;
-    float M = -INFINITY, num = 0.f, den = 0.f;
-    for (int sp0 = gr; sp0 < n_split; sp0 += kCombineBatch * S) {
-      float mv[kCombineBatch], lv[kCombineBatch], xv[kCombineBatch];
-#pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
-        // (chunks past n_split read chunk gr again and are dropped below)
-        const int sp = sp0 + u * S < n_split ? sp0 + u * S : gr;
-        mv[u] = mlb[2 * sp];
-        lv[u] = mlb[2 * sp + 1];
-        xv[u] = ab[(int64_t)sp * D];
+      for (int u = 0; u < kMergeBatch; ++u) {
+        // (chunks past n_split read chunk part again and are dropped below)
+        const int c = c0 + 4 * u < n_split ? c0 + 4 * u : part;
+        mv[u] = mlv[2 * c];
+        lv[u] = mlv[2 * c + 1];
+        xv[u] = *(const float4*)(av + (int64_t)c * D);
       }
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u)
-        if (sp0 + u * S >= n_split) mv[u] = -INFINITY;   // (empty chunks carry -inf as well)
+      for (int u = 0; u < kMergeBatch; ++u)
+        if (c0 + 4 * u >= n_split) mv[u] = -INFINITY;   // (a chunk that saw no token carries -inf too)
       float bm = M;
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) bm = fmaxf(bm, mv[u]);
+      for (int u = 0; u < kMergeBatch; ++u) bm = fmaxf(bm, mv[u]);
       if (bm == -INFINITY) continue;
       const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
-      num *= f;
+      num.x *= f; num.y *= f; num.z *= f; num.w *= f;
       den *= f;
 #pragma unroll
-      for (int u = 0; u < kCombineBatch; ++u) {
+      for (int u = 0; u < kMergeBatch; ++u) {
         const float w = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - bm);
-        num = fmaf(w, xv[u], num);
+        num.x = fmaf(w, xv[u].x, num.x);
+        num.y = fmaf(w, xv[u].y, num.y);
+        num.z = fmaf(w, xv[u].z, num.z);
+        num.w = fmaf(w, xv[u].w, num.w);
         den = fmaf(w, lv[u], den);
       }
       M = bm;
     }
-    if (S == 1) {
-      ov[pr] = den > 0.f ? num / den * inv_sqrt_d : 0.f;
-    } else {
-      gsh[0][e] = M;
-      gsh[1][e] = num;
-      gsh[2][e] = den;
-    }
   }
-  if (S > 1) {
-    __syncthreads();
-    for (int pr = tid; pr < NP; pr += NT) {
-      float M = -INFINITY, num = 0.f, den = 0.f;
-      for (int gr = 0; gr < S; ++gr) {
-        const float m = gsh[0][gr * NP + pr];
-        if (m == -INFINITY) continue;
-        const float Mn = fmaxf(M, m);
-        const float fo = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
-        const float fn = __builtin_amdgcn_exp2f(m - Mn);
-        num = num * fo + gsh[1][gr * NP + pr] * fn;
-        den = den * fo + gsh[2][gr * NP + pr] * fn;
-        M = Mn;
-      }
-      ov[pr] = den > 0.f ? num / den * inv_sqrt_d : 0.f;
-    }
+  // the four parts of a (vector, quad), in a fixed order
+#pragma unroll
+  for (int x = 1; x <= 2; x <<= 1) {
+    const float Mo = shfl_xor_f(M, x);
+    const float Mn = fmaxf(M, Mo);
+    const float fs = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - Mn);
+    const float fo = Mo == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(Mo - Mn);
+    const float4 no = {shfl_xor_f(num.x, x), shfl_xor_f(num.y, x), shfl_xor_f(num.z, x), shfl_xor_f(num.w, x)};
+    const float dno = shfl_xor_f(den, x);
+    // (the lower lane's part first, so both lanes of a pair compute the same sums)
+    const bool low = (part & x) == 0;
+    const float fa = low ? fs : fo, fb = low ? fo : fs;
+    const float4 na = low ? num : no, nb = low ? no : num;
+    const float da = low ? den : dno, db = low ? dno : den;
+    num.x = na.x * fa + nb.x * fb;
+    num.y = na.y * fa + nb.y * fb;
+    num.z = na.z * fa + nb.z * fb;
+    num.w = na.w * fa + nb.w * fb;
+    den = da * fa + db * fb;
+    M = Mn;
   }
-  __syncthreads();
-  // thread (i, hq): out[h][32*chunk + i] for heads hq, hq + NT/32, ...
-  const int i = tid & 31, hq = tid >> 5;
-  for (int h = hq; h < G; h += NT / 32) {
-    float r = 0.f;
-#pragma unroll 8
-    for (int j = 0; j < D; ++j) r = fmaf(colv[j * 32 + i], ov[h * D + j], r);
-    out[((int64_t)b * H_q + kv * G + h) * D + 32 * chunk + i] = r;
+  if (live && part == 0) {
+    const float g = den > 0.f ? inv_sqrt_d / den : 0.f;
+    *(float4*)(out + v * D + 4 * q4) = float4{num.x * g, num.y * g, num.z * g, num.w * g};
   }
 }
 
@@ -1254,24 +1241,20 @@ hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache*
   else if (d == 256) err = dispatch_kb<256>(k->bits, v->bits, p, sa, stream);
   else err = dispatch_kb<kD>(k->bits, v->bits, p, sa, stream);
   if (err != hipSuccess || p.n_split == 1) return err;
-
-  // the combine sees B * M query rows of H_q heads
-  return launch_combine(ml, acc, v->rot, out, p.B * p.M, p.H_kv, p.H_q, p.G, p.n_split, d, stream);
+  return launch_merge(ml, acc, out, p.B * p.M * p.H_q, p.n_split, d, stream);
 }
 
-hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
-                          int64_t H_kv, int64_t H_q, int G, int n_split, int d, hipStream_t stream) {
+hipError_t launch_merge(const float* ml, const float* acc, float* out, int64_t nvec, int n_split, int d,
+                        hipStream_t stream) {
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
-  const dim3 grid((unsigned)H_kv, (unsigned)rows, (unsigned)(d / 32));
+  const int64_t threads = nvec * (d / 4) * 4;
+  const dim3 grid((unsigned)((threads + 255) / 256));
   if (d == 64)
-    hipLaunchKernelGGL(combine_kernel<64>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
-                       n_split, inv_sqrt_d);
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
   else if (d == 256)
-    hipLaunchKernelGGL(combine_kernel<256>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
-                       n_split, inv_sqrt_d);
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
   else
-    hipLaunchKernelGGL(combine_kernel<kD>, grid, dim3(kCombineThreads), 0, stream, ml, acc, rotV, out, (int)H_q, G,
-                       n_split, inv_sqrt_d);
+    hipLaunchKernelGGL(merge_kernel<kD>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
   return hipGetLastError();
 }
 

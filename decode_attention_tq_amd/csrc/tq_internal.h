@@ -117,10 +117,11 @@ hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int
                               hipStream_t stream);
 hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_cache* v, const void* q, int q_dtype,
                                 const int32_t* ctx_lens, float scale, float* out, void* ws, hipStream_t stream);
-// Fixed-order merge of context-chunk partials ([rows*H_q][n_split][2] and
-// [rows*H_q][n_split][d]) and the inverse rotation, into out [rows][H_q][d].
-hipError_t launch_combine(const float* ml, const float* acc, const float* rotV, float* out, int64_t rows,
-                          int64_t H_kv, int64_t H_q, int G, int n_split, int d, hipStream_t stream);
+// Fixed-order merge of context-chunk partials of nvec query vectors
+// ([nvec][n_split][2]: m, l; [nvec][n_split][d]: sums in the output basis)
+// into out [nvec][d].
+hipError_t launch_merge(const float* ml, const float* acc, float* out, int64_t nvec, int n_split, int d,
+                        hipStream_t stream);
 // app: the new token's key and value, quantized and appended by the decode
 // kernel itself (d = 128 keys without a QJL sketch; the caller checks)
 hipError_t launch_decode(const DecodePlan& p, const tq_cache* k, const tq_cache* v, const void* q,

@@ -25,8 +25,8 @@
 //             float16 hi + lo, each column's sums split the same way under a
 //             power of two); with one context chunk the normalised output is
 //             written at once, else the chunk's partial (m, l, rotated sums)
-//             goes to the workspace and merge_kernel combines the chunks in
-//             a fixed order (the inverse rotation is linear, so it commutes
+//             goes to the workspace and the decode's merge_kernel combines
+//             the chunks in a fixed order (the inverse rotation is linear, so it commutes
 //             with the merge).
 // Keys with a QJL sketch take the tiled path (tq_decode.hip).
 #include <math.h>
@@ -534,37 +534,6 @@ void prefill_dense_kernel(DenseArgs a) {
   }
 }
 
-// Merge of the context-chunk partials of the dense kernel (already in the
-// output basis): thread (vector, 4 coordinates); chunks in order, under their
-// largest reference.
-__global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float* acc, float* out, int64_t nvec,
-                                                    int n_split, float inv_sqrt_d) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (t >= nvec * (kD / 4)) return;
-  const int64_t v = t / (kD / 4);
-  const int q4 = (int)(t % (kD / 4));
-  const float* mlv = ml + v * n_split * 2;
-  float M = -INFINITY;
-  for (int sp = 0; sp < n_split; ++sp) M = fmaxf(M, mlv[2 * sp]);
-  float4 num = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  if (M != -INFINITY) {
-    for (int sp = 0; sp < n_split; ++sp) {
-      const float m = mlv[2 * sp];
-      if (m == -INFINITY) continue;   // (a chunk that saw no token)
-      const float w = __builtin_amdgcn_exp2f(m - M);
-      const float4 x = *(const float4*)(acc + (v * n_split + sp) * kD + 4 * q4);
-      num.x = fmaf(w, x.x, num.x);
-      num.y = fmaf(w, x.y, num.y);
-      num.z = fmaf(w, x.z, num.z);
-      num.w = fmaf(w, x.w, num.w);
-      den = fmaf(w, mlv[2 * sp + 1], den);
-    }
-  }
-  const float f = den > 0.f ? inv_sqrt_d / den : 0.f;
-  *(float4*)(out + v * kD + 4 * q4) = float4{num.x * f, num.y * f, num.z * f, num.w * f};
-}
-
 template <int KB, int VB, int NWAVE>
 hipError_t launch_dense3(const DensePlan& p, const DenseArgs& da, hipStream_t stream) {
   dim3 grid((unsigned)p.n_split, (unsigned)p.H_kv, (unsigned)(p.B * p.ncg));
@@ -638,11 +607,7 @@ hipError_t launch_prefill_dense(const DensePlan& p, const tq_cache* k, const tq_
     default: err = launch_dense1<4>(v->bits, p, da, stream); break;
   }
   if (err != hipSuccess || p.n_split == 1) return err;
-  const int64_t nvec = p.B * p.M * p.H_q;
-  const int64_t blocks = (nvec * (kD / 4) + 255) / 256;
-  hipLaunchKernelGGL(merge_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, da.ml, da.acc, out, nvec,
-                     p.n_split, inv_sqrt_d);
-  return hipGetLastError();
+  return launch_merge(da.ml, da.acc, out, p.B * p.M * p.H_q, p.n_split, kD, stream);
 }
 
 }  // namespace tq
