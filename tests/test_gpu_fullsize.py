@@ -138,7 +138,7 @@ def test_fullsize_stress70b(tq):
     decoded in one launch (one context chunk per (row, KV head))."""
     _, w, kc, vc, q, out, cl, ws = _full_case(tq, "stress70b", n_sample=8)
     assert tq.decode_splits(w.B, w.H_kv, w.T) == 1
-    # the same heads through the split path: 4 context chunks and the combine
+    # the same heads through the split path: 4 context chunks and the merge
     ws4 = tq.Workspace(tq.decode_workspace_bytes(w.B, w.H_q, w.H_kv, w.T, 4, 0), torch.device("cuda"))
     out4 = tq.decode_attention(kc, vc, q, T=w.T, n_split=4, workspace=ws4)
     err = rel_l2(out4.cpu().numpy(), out.cpu().numpy())

@@ -302,7 +302,7 @@ def test_degenerate_inputs(tq, d):
 
 @pytest.mark.parametrize("name", ["d64_stress", "d256_stress_hadamard", "d64_tiny"])
 def test_split_plans_match_one_pass(tq, name):
-    """Context splits (chunk partials merged by the combine kernel) give the
+    """Context splits (chunk partials merged by the merge kernel) give the
     one-chunk result within the float16-weight recut bound, and repeat bit for
     bit; both match the oracle."""
     from tqhelp import TOL_RECUT
