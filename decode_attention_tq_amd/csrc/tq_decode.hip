@@ -1055,11 +1055,12 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
 // and the chunk's sums already in the output basis): out = sum_c 2^(m_c - M)
 // acc_c / sum_c 2^(m_c - M) l_c / sqrt(d), M the largest m_c. Four consecutive
 // lanes take one (vector, 4 coordinates): lane p merges chunks p, p + 4, ...,
-// kMergeBatch at a time with every load in flight together, under a running
+// BATCH at a time with every load in flight together, under a running
 // reference; the four parts then meet over lane exchanges (xor 1, then xor 2).
-constexpr int kMergeBatch = 8;
-
-template <int D>
+// The batch is the smallest of 1, 2, 4, 8 that covers the chunks (8 above 32
+// chunks), so few chunks are not read again in place of the empty slots; up
+// to 32 chunks every lane merges its chunks in one batch either way.
+template <int D, int BATCH>
 __global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float* acc, float* out, int64_t nvec,
                                                     int n_split, float inv_sqrt_d) {
   constexpr int Q = D / 4;   // coordinate quads of a vector
@@ -1074,11 +1075,11 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float
   float M = -INFINITY, den = 0.f;
   float4 num = {0.f, 0.f, 0.f, 0.f};
   if (live) {
-    for (int c0 = part; c0 < n_split; c0 += 4 * kMergeBatch) {
-      float mv[kMergeBatch], lv[kMergeBatch];
-      float4 xv[kMergeBatch];
+    for (int c0 = part; c0 < n_split; c0 += 4 * BATCH) {
+      float mv[BATCH], lv[BATCH];
+      float4 xv[BATCH];
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
+      for (int u = 0; u < BATCH; ++u) {
         // (chunks past n_split read chunk part again and are dropped below)
         const int c = c0 + 4 * u < n_split ? c0 + 4 * u : part;
         mv[u] = mlv[2 * c];
@@ -1086,17 +1087,17 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float
         xv[u] = *(const float4*)(av + (int64_t)c * D);
       }
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u)
+      for (int u = 0; u < BATCH; ++u)
         if (c0 + 4 * u >= n_split) mv[u] = -INFINITY;   // (a chunk that saw no token carries -inf too)
       float bm = M;
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) bm = fmaxf(bm, mv[u]);
+      for (int u = 0; u < BATCH; ++u) bm = fmaxf(bm, mv[u]);
       if (bm == -INFINITY) continue;
       const float f = M == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(M - bm);
       num.x *= f; num.y *= f; num.z *= f; num.w *= f;
       den *= f;
 #pragma unroll
-      for (int u = 0; u < kMergeBatch; ++u) {
+      for (int u = 0; u < BATCH; ++u) {
         const float w = mv[u] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mv[u] - bm);
         num.x = fmaf(w, xv[u].x, num.x);
         num.y = fmaf(w, xv[u].y, num.y);
@@ -1249,12 +1250,20 @@ hipError_t launch_merge(const float* ml, const float* acc, float* out, int64_t n
   const float inv_sqrt_d = 1.0f / sqrtf((float)d);
   const int64_t threads = nvec * (d / 4) * 4;
   const dim3 grid((unsigned)((threads + 255) / 256));
-  if (d == 64)
-    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
-  else if (d == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
-  else
-    hipLaunchKernelGGL(merge_kernel<kD>, grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
+  const int nb = n_split <= 4 ? 1 : n_split <= 8 ? 2 : n_split <= 16 ? 4 : 8;
+  auto go = [&](auto dt, auto bt) {
+    constexpr int DD = decltype(dt)::value, NB = decltype(bt)::value;
+    hipLaunchKernelGGL((merge_kernel<DD, NB>), grid, dim3(256), 0, stream, ml, acc, out, nvec, n_split, inv_sqrt_d);
+  };
+  auto by_batch = [&](auto dt) {
+    if (nb == 1) go(dt, IntConst<1>());
+    else if (nb == 2) go(dt, IntConst<2>());
+    else if (nb == 4) go(dt, IntConst<4>());
+    else go(dt, IntConst<8>());
+  };
+  if (d == 64) by_batch(IntConst<64>());
+  else if (d == 256) by_batch(IntConst<256>());
+  else by_batch(IntConst<kD>());
   return hipGetLastError();
 }
 
