@@ -1058,8 +1058,8 @@ __global__ __launch_bounds__((64 * scan_waves<QJL, WIDE, D>())) void decode_scan
 // BATCH at a time with every load in flight together, under a running
 // reference; the four parts then meet over lane exchanges (xor 1, then xor 2).
 // The batch is the smallest of 1, 2, 4, 8 that covers the chunks (8 above 32
-// chunks), so few chunks are not read again in place of the empty slots; up
-// to 32 chunks every lane merges its chunks in one batch either way.
+// chunks), so that with few chunks a lane does not re-read its own chunk to
+// fill empty slots; up to 32 chunks a lane merges all its chunks in one batch.
 template <int D, int BATCH>
 __global__ __launch_bounds__(256) void merge_kernel(const float* ml, const float* acc, float* out, int64_t nvec,
                                                     int n_split, float inv_sqrt_d) {
