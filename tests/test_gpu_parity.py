@@ -188,15 +188,17 @@ def test_split_invariance_and_determinism(tq):
         assert rel_l2(o.cpu().numpy(), base.cpu().numpy()) <= TOL_RECUT, ns
 
 
-def test_merge_batches_at_full_context(tq):
+@pytest.mark.parametrize("d", [128, 64, 256])
+def test_merge_batches_at_full_context(tq, d):
     """Context splits that reach every batch size of the chunk merge (one chunk
     per lane up to 4 chunks, 2 up to 8, 4 up to 16, 8 up to 32, and more than
-    one batch above 32) on the Llama-8B-like layer at its full 32k context:
-    each within the recut bound of one chunk, repeated bit for bit, and the
-    oracle decoding the GPU's own codes per (row, head)."""
-    w = W["llama8b"]
+    one batch above 32) on the Llama-8B-like layer at its full 32k context, at
+    each head dimension: each within the recut bound of one chunk, repeated bit
+    for bit, and the oracle decoding the GPU's own codes per (row, head)."""
+    w = W["llama8b"].scaled(d=d)
     T_cap = tcap(w.T)
-    kc, vc = _lib_caches(tq, w, T_cap)
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, d=d)
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, d=d)
     tq.quantize_kv(device_inputs(w, "k"), kc)
     tq.quantize_kv(device_inputs(w, "v"), vc)
     q = device_queries(w)
@@ -207,7 +209,7 @@ def test_merge_batches_at_full_context(tq):
     kern = np.zeros_like(one, dtype=np.float64)
     for kv in range(w.H_kv):
         kern[0, kv * w.G:(kv + 1) * w.G] = model.decode(gk, gv, qn, 0, kv)
-    assert_heads(one, kern, TOL_ATTN, "llama8b one chunk, kernel parity per (row, head)")
+    assert_heads(one, kern, TOL_ATTN, f"llama8b d={d} one chunk, kernel parity per (row, head)")
     seen = set()
     for ns in (2, 5, 11, 22, 64):
         got = tq.decode_splits(w.B, w.H_kv, w.T, ns)
@@ -216,9 +218,9 @@ def test_merge_batches_at_full_context(tq):
         again = tq.decode_attention(kc, vc, q, T=w.T, n_split=ns)
         assert torch.equal(o, again), ns
         o = o.cpu().numpy()
-        log(f"llama8b n_split={ns}: vs one chunk {rel_l2(o, one):.2e}")
+        log(f"llama8b d={d} n_split={ns}: vs one chunk {rel_l2(o, one):.2e}")
         assert rel_l2(o, one) <= TOL_RECUT, ns
-        assert_heads(o, kern, TOL_ATTN, f"llama8b n_split={ns}, kernel parity per (row, head)")
+        assert_heads(o, kern, TOL_ATTN, f"llama8b d={d} n_split={ns}, kernel parity per (row, head)")
         seen.add(1 if ns <= 4 else 2 if ns <= 8 else 4 if ns <= 16 else 8 if ns <= 32 else 0)
     assert seen == {0, 1, 2, 4, 8}
 
