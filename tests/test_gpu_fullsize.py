@@ -222,3 +222,45 @@ def test_fullsize_stress70b_prefill(tq):
                     assert e <= TOL_ATTN, (M, b, h, i, g, e)
         log(f"  prefill M={M} at full size: kernel parity worst (row, token, head) {worst:.2e} over "
             f"{len(heads)} slices x {len(toks)} tokens")
+
+
+def test_fullsize_stress70b_one_call_step(tq):
+    """The step the benchmark times, at full size: one call that appends a new
+    key and value per (row, KV head) at token T - 1 and decodes (one launch)
+    equals the separate append (tq_append_kv) followed by the decode, bit for
+    bit in the outputs and in every byte of both caches. The fresh token (not
+    the one the prefill quantized there) rewrites token T - 1's codes and moves
+    the output (not in every row: where a few outlier tokens dominate a row's
+    scores, the new token's weight is below float32's range)."""
+    w = W["stress70b"]
+    dev = torch.device("cuda")
+    T = w.T
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T, device=dev)
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T, device=dev)
+    tq.quantize_kv(tq_synth.torch_kv(w, "k", dev), kc)
+    tq.quantize_kv(tq_synth.torch_kv(w, "v", dev), vc)
+    q = tq_synth.torch_queries(w, dev)
+    before = tq.decode_attention(kc, vc, q, T=T)
+    old_last = kc.codes.view(w.B, w.H_kv, T, -1)[:, :, T - 1].clone()
+    g = torch.Generator(device=dev).manual_seed(5)
+    new_k = (4 * torch.randn((w.B, 1, w.H_kv, w.d), generator=g, device=dev)).to(torch.bfloat16)
+    new_v = (4 * torch.randn((w.B, 1, w.H_kv, w.d), generator=g, device=dev)).to(torch.bfloat16)
+    k2 = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T, device=dev)
+    v2 = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T, device=dev)
+    for dst, src in ((k2, kc), (v2, vc)):
+        dst.codes.copy_(src.codes)
+        dst.norms.copy_(src.norms)
+    one = tq.decode_attention_append(kc, vc, new_k, new_v, q, T=T)
+    tq.append_kv(new_k, new_v, k2, v2, T - 1)
+    two = tq.decode_attention(k2, v2, q, T=T)
+    torch.cuda.synchronize()
+    assert torch.equal(one, two)
+    for x, y in ((kc, k2), (vc, v2)):
+        assert torch.equal(x.codes, y.codes)
+        assert torch.equal(x.norms, y.norms)
+    moved = (one - before).abs().flatten(1).amax(dim=1)
+    log(f"  one-call step at full size: bitwise equal to append + decode; output moved by "
+        f"{moved.min().item():.3e} .. {moved.max().item():.3e} per row")
+    assert bool((moved > 0).any())
+    changed = (kc.codes.view(w.B, w.H_kv, T, -1)[:, :, T - 1] != old_last).any(dim=-1)
+    assert bool(changed.all()), "the appended key codes did not replace token T - 1's"
