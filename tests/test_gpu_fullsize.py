@@ -48,7 +48,7 @@ def _gpu_head(tq, w, which, cache, b, h, T):
     """The GPU's packed slice (b, h) as the oracle's code dictionary."""
     bits = w.k_bits if which == "k" else w.v_bits
     words = cache.codes[b, h].cpu().numpy()
-    r = {"codes": unpack_head(which, words, bits, T),
+    r = {"codes": unpack_head(which, words, bits, T, w.d),
          "norm": cache.norms[b, h, :T].cpu().numpy().astype(np.float64)}
     if which == "k" and w.k_qjl:
         from oracle import quantize as oq
@@ -62,7 +62,7 @@ def _check_codes(model, which, ref, got, w, b, h):
     bits = w.k_bits if which == "k" else w.v_bits
     thr = model.tK if which == "k" else model.tV
     bad = got["codes"] != ref["codes"]
-    exempt = oq.boundary_distance(ref["u"], thr, 128) < BOUNDARY
+    exempt = oq.boundary_distance(ref["u"], thr, w.d) < BOUNDARY
     outside = int((bad & ~exempt).sum())
     nr, want = got["norm"], ref["norm"].astype(np.float64)
     assert np.all(np.abs(nr - want) <= 1e-6 * np.maximum(want, 1e-30)), (which, b, h)
@@ -75,16 +75,16 @@ def _check_codes(model, which, ref, got, w, b, h):
     return int(bad.sum()), outside, bad.size
 
 
-def _full_case(tq, name, n_sample, ctx_lens=None, seed=7):
-    w = W[name]
+def _full_case(tq, name, n_sample, ctx_lens=None, seed=7, w=None):
+    w = W[name] if w is None else w
     dev = torch.device("cuda")
     T = w.T
     T_cap = (T + 7) // 8 * 8
-    log(f"full size {name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} T={T} K{w.k_bits}{'+qjl' if w.k_qjl else ''}"
+    log(f"full size {name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} d={w.d} T={T} K{w.k_bits}{'+qjl' if w.k_qjl else ''}"
         f"/V{w.v_bits}, {n_sample} sampled (row, KV head) slices")
     model = OracleModel(w)
-    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl))
-    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev)
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl), d=w.d)
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev, d=w.d)
     xk = tq_synth.torch_kv(w, "k", dev)
     xv = tq_synth.torch_kv(w, "v", dev)
     tq.quantize_kv(xk, kc)
@@ -154,6 +154,14 @@ def test_fullsize_stress70b_ragged(tq):
     ctx = rng.integers(0, w.T + 1, size=w.B)
     ctx[:6] = [0, 1, 7, 33, w.T - 1, w.T]
     _full_case(tq, "stress70b", n_sample=8, ctx_lens=[int(c) for c in ctx], seed=3)
+
+
+@pytest.mark.parametrize("d", [64, 256])
+def test_fullsize_stress70b_head_dims(tq, d):
+    """The benchmark's head-dimension legs: the 70B-like shape (B=32, H_q=64,
+    H_kv=8, T=32768, K3/V3) at d = 64 and 256, quantized on MFMA and decoded
+    in one launch on the scan tiles."""
+    _full_case(tq, f"stress70b_d{d}", n_sample=6, w=W["stress70b"].scaled(d=d))
 
 
 def test_fullsize_llama8b(tq):
