@@ -272,3 +272,49 @@ def test_fullsize_stress70b_one_call_step(tq):
     assert bool((moved > 0).any())
     changed = (kc.codes.view(w.B, w.H_kv, T, -1)[:, :, T - 1] != old_last).any(dim=-1)
     assert bool(changed.all()), "the appended key codes did not replace token T - 1's"
+
+
+def test_fullsize_stress70b_paged(tq):
+    """The benchmark's paged leg at full size: the 70B-like layer quantized into
+    caches of 256-token blocks mapped through a seeded permutation of the
+    physical blocks equals the contiguous caches byte for byte (read through the
+    table), and decode and the one-call step on them equal the contiguous ones
+    bit for bit."""
+    w = W["stress70b"]
+    dev = torch.device("cuda")
+    T, bt = w.T, 256
+    maxblk = T // bt
+    perm = torch.randperm(w.B * maxblk, generator=torch.Generator().manual_seed(5), dtype=torch.int64)
+    table = perm.to(torch.int32).reshape(w.B, maxblk).to(dev)
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T, device=dev)
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T, device=dev)
+    pk = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T, device=dev, block_table=table, block_tokens=bt,
+                  n_blocks=w.B * maxblk)
+    pv = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T, device=dev, block_table=table, block_tokens=bt,
+                  n_blocks=w.B * maxblk)
+    for which, c, p in (("k", kc, pk), ("v", vc, pv)):
+        x = tq_synth.torch_kv(w, which, dev)
+        tq.quantize_kv(x, c)
+        tq.quantize_kv(x, p)
+        del x
+    torch.cuda.synchronize()
+    # physical block table[b, j] holds logical block j of row b, all heads
+    tl = table.long()
+    for c, p in ((kc, pk), (vc, pv)):
+        per_tok = c.codes.shape[-1] // T
+        got = p.codes.view(w.B * maxblk, w.H_kv, bt * per_tok)[tl.flatten()]
+        got = got.view(w.B, maxblk, w.H_kv, bt * per_tok).permute(0, 2, 1, 3).reshape(c.codes.shape)
+        assert torch.equal(got, c.codes)
+        gn = p.norms.view(w.B * maxblk, w.H_kv, bt)[tl.flatten()].view(w.B, maxblk, w.H_kv, bt)
+        assert torch.equal(gn.permute(0, 2, 1, 3).reshape(c.norms.shape), c.norms)
+    q = tq_synth.torch_queries(w, dev)
+    assert torch.equal(tq.decode_attention(pk, pv, q, T=T), tq.decode_attention(kc, vc, q, T=T))
+    g = torch.Generator(device=dev).manual_seed(6)
+    new_k = torch.randn((w.B, 1, w.H_kv, w.d), generator=g, device=dev).to(torch.bfloat16)
+    new_v = torch.randn((w.B, 1, w.H_kv, w.d), generator=g, device=dev).to(torch.bfloat16)
+    one_p = tq.decode_attention_append(pk, pv, new_k, new_v, q, T=T)
+    one_c = tq.decode_attention_append(kc, vc, new_k, new_v, q, T=T)
+    torch.cuda.synchronize()
+    assert torch.equal(one_p, one_c)
+    log("  paged caches at full size (256-token blocks, seeded permutation): bytes, decode and the "
+        "one-call step equal the contiguous ones")
