@@ -75,16 +75,17 @@ def _check_codes(model, which, ref, got, w, b, h):
     return int(bad.sum()), outside, bad.size
 
 
-def _full_case(tq, name, n_sample, ctx_lens=None, seed=7, w=None):
+def _full_case(tq, name, n_sample, ctx_lens=None, seed=7, w=None, rotation="haar"):
     w = W[name] if w is None else w
     dev = torch.device("cuda")
     T = w.T
     T_cap = (T + 7) // 8 * 8
     log(f"full size {name}: B={w.B} H_q={w.H_q} H_kv={w.H_kv} d={w.d} T={T} K{w.k_bits}{'+qjl' if w.k_qjl else ''}"
         f"/V{w.v_bits}, {n_sample} sampled (row, KV head) slices")
-    model = OracleModel(w)
-    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl), d=w.d)
-    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev, d=w.d)
+    model = OracleModel(w, rotation=rotation)
+    rot = tq.make_rotation(tq_synth.ROT_SEED, tq.HADAMARD, w.d) if rotation == "hadamard" else None
+    kc = tq.Cache(tq.KEYS, w.k_bits, w.B, w.H_kv, T_cap, device=dev, qjl=bool(w.k_qjl), d=w.d, rot=rot)
+    vc = tq.Cache(tq.VALUES, w.v_bits, w.B, w.H_kv, T_cap, device=dev, d=w.d, rot=rot)
     xk = tq_synth.torch_kv(w, "k", dev)
     xv = tq_synth.torch_kv(w, "v", dev)
     tq.quantize_kv(xk, kc)
@@ -162,6 +163,13 @@ def test_fullsize_stress70b_head_dims(tq, d):
     H_kv=8, T=32768, K3/V3) at d = 64 and 256, quantized on MFMA and decoded
     in one launch on the scan tiles."""
     _full_case(tq, f"stress70b_d{d}", n_sample=6, w=W["stress70b"].scaled(d=d))
+
+
+def test_fullsize_stress70b_hadamard(tq):
+    """The benchmark's second prefill: the 70B-like layer quantized with the
+    randomized Hadamard rotation (the bulk kernel's one-pass sign-matrix path),
+    codes against the oracle built with the same rotation, then decoded."""
+    _full_case(tq, "stress70b_hadamard", n_sample=6, w=W["stress70b"], rotation="hadamard")
 
 
 def test_fullsize_llama8b(tq):
