@@ -246,6 +246,30 @@ def test_value_cosine_per_bit_width(tq, bits, cos_lo, cos_hi):
         assert abs(cos - 0.94) < 0.005
 
 
+@pytest.mark.parametrize("bits,qjl,slope,tol", [(2, True, 1.0, 0.02), (2, False, 1 - 0.1175, 0.01),
+                                                 (3, False, 1 - 0.03455, 0.006)])
+def test_key_score_slope(tq, bits, qjl, slope, tol):
+    """Inner products with the GPU's dequantized keys (65,536 random Gaussian
+    keys, float32 input, 8 random queries per KV head) regressed on the exact
+    ones: with the QJL sign sketch the slope is 1 (the estimate is unbiased);
+    MSE-only Lloyd-Max keys shrink it to 1 - MSE of the codebook (the centroid
+    condition E[c(z) z] = E[c(z)^2] = 1 - MSE)."""
+    B, H, T = 1, 8, 8192
+    g = torch.Generator(device="cuda").manual_seed(200 + bits + 10 * qjl)
+    k = torch.randn((B, T, H, 128), generator=g, device="cuda", dtype=torch.float32)
+    q = torch.randn((H, 8, 128), generator=g, device="cuda", dtype=torch.float64)
+    kc = tq.Cache(tq.KEYS, bits, B, H, T, qjl=qjl)
+    tq.quantize_kv(k, kc)
+    kh = tq.dequantize(kc, 0, T)[0].double()           # [H, T, d]
+    kt = k[0].permute(1, 0, 2).double()                 # [H, T, d]
+    s = torch.bmm(q, kt.transpose(1, 2).contiguous()).flatten()
+    sh = torch.bmm(q, kh.transpose(1, 2).contiguous()).flatten()
+    sc = s - s.mean()
+    b = ((sh - sh.mean()) * sc).sum().item() / (sc * sc).sum().item()
+    log(f"  keys {bits} bits{' + QJL' if qjl else ''}: score slope {b:.4f} (expected {slope:.4f})")
+    assert abs(b - slope) < tol
+
+
 def test_ragged_context_lengths(tq):
     w = CASES["stress70b_B2"].scaled(B=4)
     T_cap = tcap(w.T)
